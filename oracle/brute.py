@@ -1,0 +1,130 @@
+"""Pure-Python re-derivation of the shuffle for tiny inputs (test infrastructure only).
+
+Nested loops over lists, no numpy in the arithmetic, so that a slip in the
+vectorised oracle (a transposed index, a wrong scan, an unstable sort) shows
+up as a disagreement.  Same definitions and readings as ``oracle.shuffle``.
+"""
+
+from __future__ import annotations
+
+import struct
+
+
+def _part_starts(n: int, parts: int) -> list[int]:
+    # Walk the ranks, handing out one extra element while the remainder lasts.
+    starts, pos, extra = [0], 0, n - (n // parts) * parts
+    for _ in range(parts):
+        take = n // parts
+        if extra > 0:
+            take += 1
+            extra -= 1
+        pos += take
+        starts.append(pos)
+    return starts
+
+
+def plan(idx: list[list[int]], E: int, R: int, G: int) -> dict:
+    T = len(idx)
+    k = len(idx[0]) if T else 0
+    estarts = _part_starts(E, R)
+    tstarts = _part_starts(T, R)
+
+    def rank_of(e):
+        d = 0
+        while not (estarts[d] <= e < estarts[d + 1]):
+            d += 1
+        return d
+
+    def owner(t):
+        d = 0
+        while not (tstarts[d] <= t < tstarts[d + 1]):
+            d += 1
+        return d
+
+    counts = [0] * E
+    for t in range(T):
+        for j in range(k):
+            counts[idx[t][j]] += 1
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + counts[e])
+    rank_offsets = [offsets[estarts[d]] for d in range(R + 1)]
+
+    # Rows in (expert, token) order.
+    row_src, slot_of = [], [[None] * k for _ in range(T)]
+    for e in range(E):
+        for t in range(T):
+            for j in range(k):
+                if idx[t][j] == e:
+                    slot_of[t][j] = len(row_src)
+                    row_src.append(t)
+
+    send_rows = [[0] * R for _ in range(R)]
+    send_copies = [[0] * R for _ in range(R)]
+    N = R // G
+    node_copies = [[0] * N for _ in range(R)]
+    for t in range(T):
+        s = owner(t)
+        ranks = set()
+        nodes = set()
+        for j in range(k):
+            d = rank_of(idx[t][j])
+            send_rows[s][d] += 1
+            ranks.add(d)
+            nodes.add(d // G)
+        for d in ranks:
+            send_copies[s][d] += 1
+        for n in nodes:
+            node_copies[s][n] += 1
+
+    # Forwarder staging: walk forwarders in order, then tokens.
+    stage_src, stage_node, stage_offsets = [], [], [0]
+    pos = {}
+    for f in range(R):
+        n, g = f // G, f % G
+        for t in range(T):
+            if owner(t) % G != g:
+                continue
+            if any(rank_of(idx[t][j]) // G == n for j in range(k)):
+                pos[(t, n)] = len(stage_src)
+                stage_src.append(t)
+                stage_node.append(n)
+        stage_offsets.append(len(stage_src))
+    stage_of = [[pos[(t, rank_of(idx[t][j]) // G)] for j in range(k)] for t in range(T)]
+
+    return dict(counts=counts, expert_offsets=offsets, rank_offsets=rank_offsets,
+                row_src=row_src, slot_of=slot_of, send_rows=send_rows,
+                send_copies=send_copies, node_copies=node_copies,
+                stage_src=stage_src, stage_node=stage_node,
+                stage_offsets=stage_offsets, stage_of=stage_of,
+                num_staged=len(stage_src))
+
+
+def dispatch(x: list[list[int]], p: dict) -> list[list[int]]:
+    T = len(p["slot_of"])
+    k = len(p["slot_of"][0]) if T else 0
+    recv = [None] * (T * k)
+    for t in range(T):
+        for j in range(k):
+            recv[p["slot_of"][t][j]] = list(x[t])
+    return recv
+
+
+def bf16_value(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (bits & 0xFFFF) << 16))[0]
+
+
+def combine(y: list[list[int]], w: list[list[float]], p: dict) -> list[list[float]]:
+    T = len(p["slot_of"])
+    k = len(p["slot_of"][0]) if T else 0
+    H = len(y[0]) if y else 0
+    out = []
+    for t in range(T):
+        row = []
+        for h in range(H):
+            acc = 0.0
+            for j in range(k):
+                acc += float(w[t][j]) * bf16_value(y[p["slot_of"][t][j]][h])
+            row.append(acc)
+        out.append(row)
+    return out
