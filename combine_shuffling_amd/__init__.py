@@ -1,0 +1,176 @@
+"""MI355X (gfx950) MoE expert-parallel shuffle.
+
+A thin binding over the C ABI of ``libmoeshuffle.so`` (include/moe_shuffle.h):
+the same calls, with torch tensors for device memory and torch's current
+stream.  Every step of the shuffle runs in the library's HIP kernels; this
+module only checks shapes and passes pointers.
+
+    plan = route_plan(topk_idx, num_experts=E, num_ranks=R, hidden=H,
+                      ranks_per_node=G, node_dedup=False)
+    recv, staging = dispatch(plan, x)           # x: [T, H] bf16 on the GPU
+    out = combine(plan, y, topk_w)              # y: [T*k, H] bf16, receive layout
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _abi
+from ._abi import MoeError, ITEM  # noqa: F401
+
+__all__ = ["Plan", "MoeError", "expert_partition", "route_plan", "dispatch", "combine"]
+
+
+def expert_partition(num_experts: int, num_ranks: int) -> list[int]:
+    """moe_expert_partition: rank d holds experts [lo[d], lo[d+1])."""
+    lo = (ctypes.c_int32 * (num_ranks + 1))() if num_ranks > 0 else (ctypes.c_int32 * 1)()
+    _abi.check(_abi.lib().moe_expert_partition(num_experts, num_ranks, lo), "moe_expert_partition")
+    return list(lo)
+
+
+def _stream_handle(device: torch.device, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, shape, dtypes, name: str, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+class Plan:
+    """Owns one moe_plan (host) and, once routed, its device workspace tensor."""
+
+    def __init__(self, num_tokens: int, hidden: int, num_experts: int, top_k: int,
+                 num_ranks: int, ranks_per_node: int | None = None, node_dedup: bool = False):
+        G = num_ranks if ranks_per_node is None else ranks_per_node
+        self.cfg = _abi.MoeConfig(num_tokens, hidden, num_experts, top_k, num_ranks, G,
+                                  _abi.FLAG_NODE_DEDUP if node_dedup else 0)
+        self._lib = _abi.lib()
+        h = ctypes.c_void_p()
+        _abi.check(self._lib.moe_plan_create(ctypes.byref(self.cfg), ctypes.byref(h)),
+                   "moe_plan_create")
+        self._h = h
+        self.T, self.H, self.E, self.k = num_tokens, hidden, num_experts, top_k
+        self.R, self.G, self.N = num_ranks, G, num_ranks // G
+        self.node_dedup = node_dedup
+        self.workspace_bytes = int(self._lib.moe_plan_workspace_bytes(h))
+        self.recv_rows = int(self._lib.moe_plan_recv_rows(h))
+        self.staging_rows_max = int(self._lib.moe_plan_staging_rows_max(h))
+        self.workspace = None
+        self.topk_idx = None
+        self.device = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.moe_plan_destroy(h)
+            self._h = None
+
+    # -- moe_route_plan
+    def route(self, topk_idx: torch.Tensor, workspace: torch.Tensor | None = None, stream=None):
+        dev = topk_idx.device
+        _need(topk_idx, (self.T, self.k), (torch.int32,), "topk_idx", dev)
+        if workspace is None:
+            if self.workspace is None or self.workspace.device != dev:
+                self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=dev)
+            workspace = self.workspace
+        elif workspace.numel() * workspace.element_size() < self.workspace_bytes:
+            raise ValueError("workspace too small")
+        self.workspace, self.topk_idx, self.device = workspace, topk_idx, dev
+        _abi.check(self._lib.moe_route_plan(self._h, _ptr(topk_idx), _ptr(workspace),
+                                            _stream_handle(dev, stream)), "moe_route_plan")
+        return self
+
+    # -- moe_dispatch
+    def dispatch(self, x: torch.Tensor, recv: torch.Tensor | None = None,
+                 staging: torch.Tensor | None = None, stream=None):
+        dev = self.device
+        if dev is None:
+            raise MoeError(_abi.ERR_PLAN_NOT_ROUTED, "dispatch")
+        _need(x, (self.T, self.H), _BF16_LIKE, "x", dev)
+        if recv is None:
+            recv = torch.empty((self.recv_rows, self.H), dtype=x.dtype, device=dev)
+        _need(recv, (self.recv_rows, self.H), _BF16_LIKE, "recv", dev)
+        if self.node_dedup:
+            if staging is None:
+                staging = torch.empty((self.staging_rows_max, self.H), dtype=x.dtype, device=dev)
+            _need(staging, (self.staging_rows_max, self.H), _BF16_LIKE, "staging", dev)
+        _abi.check(self._lib.moe_dispatch(self._h, _ptr(x), _ptr(recv), _ptr(staging),
+                                          _stream_handle(dev, stream)), "moe_dispatch")
+        return recv, staging
+
+    # -- moe_combine
+    def combine(self, y: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor | None = None,
+                out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+        dev = self.device
+        if dev is None:
+            raise MoeError(_abi.ERR_PLAN_NOT_ROUTED, "combine")
+        _need(y, (self.recv_rows, self.H), _BF16_LIKE, "y", dev)
+        _need(topk_w, (self.T, self.k), (torch.float32,), "topk_w", dev)
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+        if out is None:
+            out = torch.empty((self.T, self.H), dtype=out_dtype, device=dev)
+        _need(out, (self.T, self.H), (out_dtype,), "out", dev)
+        code = _abi.OUT_F32 if out_dtype == torch.float32 else _abi.OUT_BF16
+        _abi.check(self._lib.moe_combine(self._h, _ptr(y), _ptr(topk_w), _ptr(out), code,
+                                         _stream_handle(dev, stream)), "moe_combine")
+        return out
+
+    # -- moe_plan_read
+    def read(self, item: str, stream=None) -> np.ndarray:
+        n = {"status": 1, "num_staged": 1, "counts": self.E, "expert_offsets": self.E + 1,
+             "rank_offsets": self.R + 1, "slot_of": self.T * self.k, "row_src": self.T * self.k,
+             "stage_offsets": self.R + 1, "stage_of": self.T * self.k,
+             "stage_src": self.staging_rows_max, "send_rows": self.R * self.R,
+             "send_copies": self.R * self.R, "node_copies": self.R * self.N}[item]
+        buf = np.zeros(max(n, 1), dtype=np.int32)
+        dev = self.device
+        if dev is None:
+            raise MoeError(_abi.ERR_PLAN_NOT_ROUTED, "read")
+        _abi.check(self._lib.moe_plan_read(self._h, _abi.ITEM[item],
+                                           buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes,
+                                           _stream_handle(dev, stream)), f"moe_plan_read({item})")
+        return buf[:n]
+
+    def status(self) -> int:
+        return int(self.read("status")[0])
+
+
+def route_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, hidden: int,
+               ranks_per_node: int | None = None, node_dedup: bool = False,
+               workspace: torch.Tensor | None = None, stream=None) -> Plan:
+    """moe_plan_create + moe_route_plan for a [T, k] int32 routing on the GPU."""
+    T, k = topk_idx.shape
+    plan = Plan(T, hidden, num_experts, k, num_ranks, ranks_per_node, node_dedup)
+    return plan.route(topk_idx, workspace, stream)
+
+
+def dispatch(plan: Plan, x: torch.Tensor, recv=None, staging=None, stream=None):
+    """moe_dispatch: returns (recv [T*k, H], staging or None)."""
+    return plan.dispatch(x, recv, staging, stream)
+
+
+def combine(plan: Plan, y: torch.Tensor, topk_w: torch.Tensor, out=None,
+            out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """moe_combine: returns out [T, H] (bf16 or float32)."""
+    return plan.combine(y, topk_w, out, out_dtype, stream)

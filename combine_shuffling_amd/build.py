@@ -1,0 +1,56 @@
+"""Build the gfx950 shuffle library in-tree: combine_shuffling_amd/libmoeshuffle.so.
+
+Run ``python -m combine_shuffling_amd.build`` (or ``__graft_entry__.build()``).
+Cross-compiles with hipcc; no GPU is needed to build.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libmoeshuffle.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+SOURCES = ("route_plan.hip", "move.hip", "moe_api.cpp")
+
+# -packed-fp32-ops: no packed fp32 instructions in device code.
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: install ROCm or put hipcc on PATH")
+    return path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into LIB_PATH (always recompiles). Returns the path."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = ("packed-fp32-ops", "is not a recognized feature for this target")
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if not any(n in ln for n in noise)]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

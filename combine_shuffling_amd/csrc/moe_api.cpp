@@ -1,0 +1,274 @@
+// Host side of the C ABI declared in include/moe_shuffle.h: argument checks,
+// workspace layout, and the launch sequence of each call.  moe_plan_create
+// makes no HIP call, so plans can be built and checked on a machine without
+// a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "moe_internal.h"
+
+struct moe_plan {
+  moe_config cfg;
+  moe::Dims d;
+  moe::Layout layout;
+  int64_t staging_rows_max;
+  // Bound by moe_route_plan.
+  const int32_t* idx;
+  void* ws;
+  moe::Work work;
+  bool routed;
+};
+
+namespace moe {
+namespace {
+
+int ceil_log2(int n) {
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+Layout make_layout(const Dims& d, int64_t staging_rows_max) {
+  Layout l{};
+  size_t at = 0;
+  auto take = [&](size_t& field, int64_t ints) {
+    field = at;
+    at = align_up(at + (size_t)std::max<int64_t>(ints, 1) * sizeof(int32_t), 256);
+  };
+  const int64_t tk = (int64_t)d.T * d.k;
+  take(l.ctrl, 64);
+  take(l.tile_flags, d.nblk);
+  take(l.tile_counts, (int64_t)d.nblk * d.E);
+  take(l.counts, d.E);
+  take(l.expert_off, d.E + 1);
+  take(l.rank_off, d.R + 1);
+  take(l.slot_of, tk);
+  take(l.row_src, tk);
+  take(l.tile_fcounts, d.dedup ? (int64_t)d.nblk * d.R : 1);
+  take(l.stage_off, d.dedup ? d.R + 1 : 1);
+  take(l.stage_of, d.dedup ? tk : 1);
+  take(l.stage_src, d.dedup ? staging_rows_max : 1);
+  take(l.send_rows, (int64_t)d.R * d.R);
+  take(l.send_copies, (int64_t)d.R * d.R);
+  take(l.node_copies, (int64_t)d.R * d.N);
+  l.total = at;
+  return l;
+}
+
+Work bind_work(const Layout& l, void* base) {
+  char* b = static_cast<char*>(base);
+  auto p = [&](size_t off) { return reinterpret_cast<int32_t*>(b + off); };
+  Work w{};
+  w.ctrl = p(l.ctrl);
+  w.tile_flags = p(l.tile_flags);
+  w.tile_counts = p(l.tile_counts);
+  w.counts = p(l.counts);
+  w.expert_off = p(l.expert_off);
+  w.rank_off = p(l.rank_off);
+  w.slot_of = p(l.slot_of);
+  w.row_src = p(l.row_src);
+  w.tile_fcounts = p(l.tile_fcounts);
+  w.stage_off = p(l.stage_off);
+  w.stage_of = p(l.stage_of);
+  w.stage_src = p(l.stage_src);
+  w.send_rows = p(l.send_rows);
+  w.send_copies = p(l.send_copies);
+  w.node_copies = p(l.node_copies);
+  return w;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_EXPERTS_LT_RANKS: return "fewer experts than ranks: the split would leave ranks without experts";
+    case MOE_ERR_BAD_ROUTING: return "routing names an expert outside [0, E) or repeats one in a row";
+    case MOE_ERR_PLAN_NOT_ROUTED: return "plan has not been routed (call moe_route_plan first)";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_UNSUPPORTED: return "sizes beyond the library's limits";
+  }
+  return "unknown status";
+}
+
+moe_status moe_expert_partition(int32_t num_experts, int32_t num_ranks, int32_t* lo_out) {
+  if (!lo_out || num_experts <= 0 || num_ranks <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (num_experts < num_ranks) return MOE_ERR_EXPERTS_LT_RANKS;
+  const int32_t base = num_experts / num_ranks, rem = num_experts % num_ranks;
+  for (int32_t d = 0; d <= num_ranks; ++d) lo_out[d] = d * base + std::min(d, rem);
+  return MOE_OK;
+}
+
+moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
+  if (!cfg || !out) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config c = *cfg;
+  if (c.num_tokens < 0 || c.hidden <= 0 || c.hidden % 8 || c.num_experts <= 0 || c.top_k <= 0 ||
+      c.num_ranks <= 0 || c.ranks_per_node <= 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c.flags & ~MOE_FLAG_NODE_DEDUP) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.num_experts > MOE_MAX_EXPERTS || c.top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (c.top_k > c.num_experts) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.num_experts < c.num_ranks) return MOE_ERR_EXPERTS_LT_RANKS;
+  if (c.num_ranks % c.ranks_per_node) return MOE_ERR_INVALID_ARGUMENT;
+  const int32_t nodes = c.num_ranks / c.ranks_per_node;
+  const bool dedup = (c.flags & MOE_FLAG_NODE_DEDUP) != 0;
+  if (dedup && nodes < 2) return MOE_ERR_INVALID_ARGUMENT;
+
+  const int64_t T = c.num_tokens, chunks = c.hidden / 8;
+  const int64_t staging_max = dedup ? T * std::min<int64_t>(c.top_k, nodes) : 0;
+  const int64_t lim = INT32_MAX;
+  if (T * c.top_k >= lim || T * chunks >= lim || staging_max * chunks >= lim)
+    return MOE_ERR_UNSUPPORTED;
+
+  moe::Dims d{};
+  d.T = (int32_t)T;
+  d.H = c.hidden;
+  d.E = c.num_experts;
+  d.k = c.top_k;
+  d.R = c.num_ranks;
+  d.G = c.ranks_per_node;
+  d.N = nodes;
+  d.ebase = d.E / d.R;
+  d.erem = d.E % d.R;
+  d.tbase = d.T / d.R;
+  d.trem = d.T % d.R;
+  const int64_t per_tile_cap = (int64_t)moe::kPlanBlock * moe::kMaxPlanTiles;
+  d.passes = (int32_t)std::max<int64_t>(1, (T + per_tile_cap - 1) / per_tile_cap);
+  const int64_t tile = (int64_t)moe::kPlanBlock * d.passes;
+  d.nblk = (int32_t)std::max<int64_t>(1, (T + tile - 1) / tile);
+  d.ebits = moe::ceil_log2(d.E);
+  d.fbits = moe::ceil_log2(d.R);
+  d.dedup = dedup ? 1 : 0;
+  d.chunks = (int32_t)chunks;
+  d.smax = (int32_t)staging_max;
+
+  moe_plan* p = new (std::nothrow) moe_plan();
+  if (!p) return MOE_ERR_UNSUPPORTED;
+  p->cfg = c;
+  p->d = d;
+  p->staging_rows_max = staging_max;
+  p->layout = moe::make_layout(d, staging_max);
+  p->idx = nullptr;
+  p->ws = nullptr;
+  p->routed = false;
+  *out = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan* plan) { delete plan; }
+
+size_t moe_plan_workspace_bytes(const moe_plan* plan) { return plan ? plan->layout.total : 0; }
+
+int64_t moe_plan_recv_rows(const moe_plan* plan) {
+  return plan ? (int64_t)plan->d.T * plan->d.k : 0;
+}
+
+int64_t moe_plan_staging_rows_max(const moe_plan* plan) {
+  return plan ? plan->staging_rows_max : 0;
+}
+
+moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspace, void* stream) {
+  if (!plan || !workspace || !moe::aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->d.T > 0 && (!topk_idx || !moe::aligned(topk_idx, 4))) return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  plan->routed = false;
+  plan->idx = topk_idx;
+  plan->ws = workspace;
+  plan->work = moe::bind_work(plan->layout, workspace);
+  moe_status st = moe::from_hip(moe::launch_route_count(plan->d, topk_idx, plan->work, s));
+  if (st == MOE_OK) st = moe::from_hip(moe::launch_route_assign(plan->d, topk_idx, plan->work, s));
+  plan->routed = st == MOE_OK;
+  return st;
+}
+
+moe_status moe_dispatch(const moe_plan* plan, const uint16_t* x, uint16_t* recv, uint16_t* staging,
+                        void* stream) {
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
+  if (plan->d.T == 0) return MOE_OK;
+  if (!x || !recv || !moe::aligned(x, 16) || !moe::aligned(recv, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!plan->d.dedup) return moe::from_hip(moe::launch_gather(plan->d, x, recv, plan->work, s));
+  if (!staging || !moe::aligned(staging, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = moe::from_hip(moe::launch_stage_a(plan->d, x, staging, plan->work, plan->staging_rows_max, s));
+  if (st != MOE_OK) return st;
+  return moe::from_hip(
+      moe::launch_stage_b(plan->d, staging, recv, plan->work, plan->staging_rows_max, s));
+}
+
+moe_status moe_combine(const moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
+                       int32_t out_dtype, void* stream) {
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->d.T == 0) return MOE_OK;
+  if (!y || !topk_w || !out || !moe::aligned(y, 16) || !moe::aligned(topk_w, 4) ||
+      !moe::aligned(out, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return moe::from_hip(moe::launch_combine(plan->d, y, topk_w, out, out_dtype == MOE_OUT_F32,
+                                           plan->work, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_plan_read(const moe_plan* plan, int32_t item, void* host_dst, size_t bytes,
+                         void* stream) {
+  if (!plan || !host_dst) return MOE_ERR_INVALID_ARGUMENT;
+  if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
+  const moe::Dims& d = plan->d;
+  const moe::Work& w = plan->work;
+  const int64_t tk = (int64_t)d.T * d.k;
+  const int32_t* src = nullptr;
+  int64_t n = 0;
+  bool traffic = false;
+  switch (item) {
+    case MOE_ITEM_STATUS: src = w.ctrl; n = 1; break;
+    case MOE_ITEM_COUNTS: src = w.counts; n = d.E; break;
+    case MOE_ITEM_EXPERT_OFFSETS: src = w.expert_off; n = d.E + 1; break;
+    case MOE_ITEM_RANK_OFFSETS: src = w.rank_off; n = d.R + 1; break;
+    case MOE_ITEM_SLOT_OF: src = w.slot_of; n = tk; break;
+    case MOE_ITEM_ROW_SRC: src = w.row_src; n = tk; break;
+    case MOE_ITEM_NUM_STAGED: src = w.ctrl + 1; n = 1; break;
+    case MOE_ITEM_STAGE_OFFSETS: src = w.stage_off; n = d.R + 1; break;
+    case MOE_ITEM_STAGE_OF: src = w.stage_of; n = tk; break;
+    case MOE_ITEM_STAGE_SRC: src = w.stage_src; n = plan->staging_rows_max; break;
+    case MOE_ITEM_SEND_ROWS: src = w.send_rows; n = (int64_t)d.R * d.R; traffic = true; break;
+    case MOE_ITEM_SEND_COPIES: src = w.send_copies; n = (int64_t)d.R * d.R; traffic = true; break;
+    case MOE_ITEM_NODE_COPIES: src = w.node_copies; n = (int64_t)d.R * d.N; traffic = true; break;
+    default: return MOE_ERR_INVALID_ARGUMENT;
+  }
+  const bool dedup_item = item == MOE_ITEM_NUM_STAGED || item == MOE_ITEM_STAGE_OFFSETS ||
+                          item == MOE_ITEM_STAGE_OF || item == MOE_ITEM_STAGE_SRC;
+  if (dedup_item && !d.dedup) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = (size_t)n * sizeof(int32_t);
+  if (bytes < need) return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (traffic) {
+    const size_t mat = (size_t)d.R * d.R * sizeof(int32_t);
+    hipError_t e = hipMemsetAsync(w.send_rows, 0, mat, s);
+    if (e == hipSuccess) e = hipMemsetAsync(w.send_copies, 0, mat, s);
+    if (e == hipSuccess) e = hipMemsetAsync(w.node_copies, 0, (size_t)d.R * d.N * sizeof(int32_t), s);
+    if (e == hipSuccess && d.T > 0) e = moe::launch_traffic(d, plan->idx, w, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (need > 0) {
+    if (hipMemcpyAsync(host_dst, src, need, hipMemcpyDeviceToHost, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  return moe::from_hip(hipStreamSynchronize(s));
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+/*
+ * moe_shuffle.h -- C ABI of the MI355X (gfx950) MoE expert-parallel shuffle.
+ *
+ * What it computes.  Under expert parallelism the experts live on different
+ * ranks, so every token must travel to the ranks that host the experts it was
+ * routed to, and the experts' outputs must travel back (FUSCO article,
+ * "pain points").  Dispatch moves tokens to the ranks hosting their selected
+ * experts; combine returns the expert outputs to each token's owner (INC-MoE
+ * abstract).  Here the R expert-parallel ranks are R virtual ranks, i.e.
+ * partitions of one GPU's HBM, and every "send" is an HBM-to-HBM row copy.
+ *
+ *   moe_route_plan   top-k routing -> per-expert histogram -> exclusive scan ->
+ *                    segment descriptors (FUSCO article, "core innovation":
+ *                    gather-send is driven by segment descriptors);
+ *   moe_dispatch     gather-send fused with scatter-recv: each source row is
+ *                    read once and written straight into its final, expert-
+ *                    contiguous receive row (same section).  With
+ *                    MOE_FLAG_NODE_DEDUP the row first goes once to a
+ *                    staging row per destination node (the node's forwarding
+ *                    GPU), then fans out inside the node (FUSCO article,
+ *                    "load balancing and cross-node deduplication");
+ *   moe_combine      out[t] = sum_j w[t,j] * y[slot_of[t,j]], fp32 accumulate
+ *                    in ascending j (INC-MoE abstract: combine back to the
+ *                    owner).
+ *
+ * Expert-to-rank partition: contiguous ceil/floor split, the first E % R
+ * ranks hold E / R + 1 experts (TensorRT-LLM PR #13888, "support non-
+ * divisible EP in MoE alltoall", performance commit message: 256 experts over
+ * 7 ranks -> base 36, remainder 4).  E < R is rejected (same PR, commit on
+ * ranks left without experts).
+ *
+ * Layouts (all row-major, all device buffers 16-byte aligned):
+ *   x        [T, H]      bf16 bit patterns (uint16), the tokens;
+ *   topk_idx [T, k]      int32 expert ids, each in [0, E), distinct in a row;
+ *   topk_w   [T, k]      float32 combine weights, applied as given;
+ *   recv     [T*k, H]    bf16: rank d's rows are [rank_off[d], rank_off[d+1]),
+ *                        expert e's rows [expert_off[e], expert_off[e+1]),
+ *                        tokens ascending inside an expert;
+ *   staging  [Dmax, H]   bf16, rows ordered by (forwarder rank, token); the
+ *                        forwarder of (token t, node n) is rank
+ *                        n*G + owner(t) % G, owner(t) being the contiguous
+ *                        ceil/floor split of the T tokens over the R ranks;
+ *   out      [T, H]      bf16 (round to nearest even) or float32.
+ *
+ * Ownership.  The caller owns every device buffer (inputs, outputs and the
+ * workspace).  The library owns only the host-side plan object; it never
+ * allocates device memory and never synchronises except in moe_plan_read.
+ * moe_route_plan binds topk_idx and the workspace to the plan: both must stay
+ * alive and unmodified by anyone else until the last moe_dispatch /
+ * moe_combine / moe_plan_read using that routing has completed on the stream.
+ * Every call is asynchronous on the given stream (a hipStream_t; NULL = the
+ * null stream).  A plan is not thread-safe; calls on one workspace that
+ * overlap in time (different streams without ordering) race.
+ *
+ * Errors.  Host-detectable errors return before anything is launched.  Bad
+ * routing (an id outside [0, E) or repeated in a row) is found on the device:
+ * such slots are dropped (no row is written for them, they add nothing to the
+ * combine, their slot_of entry is -1), every access stays in bounds, and
+ * moe_plan_read(MOE_ITEM_STATUS) reports MOE_ERR_BAD_ROUTING.
+ */
+#ifndef MOE_SHUFFLE_H
+#define MOE_SHUFFLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* null, negative, misaligned or inconsistent arguments */
+  MOE_ERR_EXPERTS_LT_RANKS = 2, /* E < R: the split would leave ranks without experts  */
+  MOE_ERR_BAD_ROUTING = 3,      /* device found an id out of range or repeated in a row */
+  MOE_ERR_PLAN_NOT_ROUTED = 4,  /* dispatch/combine/read before moe_route_plan          */
+  MOE_ERR_HIP = 5,              /* a HIP runtime call or kernel launch failed           */
+  MOE_ERR_UNSUPPORTED = 6       /* sizes beyond the library's limits (below)            */
+} moe_status;
+
+/* Limits: E <= 1024, 1 <= k <= 16, k <= E, R <= E, R % G == 0, H % 8 == 0,
+ * T*k < 2^31, T*H < 2^31 * 8 (row indices are 32-bit, byte offsets 64-bit). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/* Node deduplication (one copy per (token, node), then intra-node fan-out).
+ * Requires N = R / G > 1. */
+#define MOE_FLAG_NODE_DEDUP 1u
+
+typedef struct moe_config {
+  int64_t num_tokens;     /* T >= 0 (0 is an empty batch: every call is a no-op) */
+  int32_t hidden;         /* H > 0, multiple of 8 (row = 2H bytes, 16-byte chunks) */
+  int32_t num_experts;    /* E, 1..MOE_MAX_EXPERTS                                 */
+  int32_t top_k;          /* k, 1..min(E, MOE_MAX_TOPK)                             */
+  int32_t num_ranks;      /* R, 1..E                                               */
+  int32_t ranks_per_node; /* G, divides R; N = R / G nodes                          */
+  uint32_t flags;         /* MOE_FLAG_*                                             */
+} moe_config;
+
+typedef struct moe_plan moe_plan; /* opaque, host-side */
+
+/* What moe_plan_read copies out (all int32 unless noted). */
+typedef enum moe_item {
+  MOE_ITEM_STATUS = 0,         /* 1 value: moe_status of the last route (MOE_OK or MOE_ERR_BAD_ROUTING) */
+  MOE_ITEM_COUNTS = 1,         /* [E]     rows per expert                                      */
+  MOE_ITEM_EXPERT_OFFSETS = 2, /* [E+1]   exclusive scan of counts                             */
+  MOE_ITEM_RANK_OFFSETS = 3,   /* [R+1]   first receive row of each rank                       */
+  MOE_ITEM_SLOT_OF = 4,        /* [T*k]   receive row of token slot (t, j), -1 if dropped       */
+  MOE_ITEM_ROW_SRC = 5,        /* [T*k]   source token of each receive row                     */
+  MOE_ITEM_NUM_STAGED = 6,     /* 1 value: D, staging rows used (dedup only)                    */
+  MOE_ITEM_STAGE_OFFSETS = 7,  /* [R+1]   first staging row of each forwarder (dedup only)      */
+  MOE_ITEM_STAGE_OF = 8,       /* [T*k]   staging row feeding token slot (t, j) (dedup only)    */
+  MOE_ITEM_STAGE_SRC = 9,      /* [Dmax]  source token of each staging row; first D valid       */
+  MOE_ITEM_SEND_ROWS = 10,     /* [R*R]   rows rank s sends to rank d (modelled link traffic)   */
+  MOE_ITEM_SEND_COPIES = 11,   /* [R*R]   distinct tokens rank s sends to rank d                */
+  MOE_ITEM_NODE_COPIES = 12    /* [R*N]   distinct tokens rank s sends to node n                */
+} moe_item;
+
+typedef enum moe_out_dtype { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
+
+/* Ceil/floor contiguous expert partition on the host: writes lo[0..R] with
+ * rank d holding experts [lo[d], lo[d+1]).  The device uses the same rule.
+ * lo_out: host array of R+1 int32, owned by the caller.
+ * Errors: MOE_ERR_INVALID_ARGUMENT (null, E <= 0, R <= 0),
+ *         MOE_ERR_EXPERTS_LT_RANKS (E < R). */
+moe_status moe_expert_partition(int32_t num_experts, int32_t num_ranks, int32_t* lo_out);
+
+/* Validates cfg and creates a plan.  Host only: makes no HIP call.
+ * Errors: INVALID_ARGUMENT, EXPERTS_LT_RANKS, UNSUPPORTED; *out untouched then. */
+moe_status moe_plan_create(const moe_config* cfg, moe_plan** out);
+void moe_plan_destroy(moe_plan* plan); /* NULL is a no-op */
+
+/* Device workspace the caller must provide to moe_route_plan (bytes, a
+ * multiple of 256; the buffer itself must be 256-byte aligned). */
+size_t moe_plan_workspace_bytes(const moe_plan* plan);
+int64_t moe_plan_recv_rows(const moe_plan* plan);         /* T*k                          */
+int64_t moe_plan_staging_rows_max(const moe_plan* plan);  /* T*min(k, N) with dedup, else 0 */
+
+/* Route plan: validates routing, builds the per-expert histogram, its
+ * exclusive scan and the segment descriptors (and, with dedup, the per-
+ * forwarder staging descriptors).  topk_idx: device [T, k] int32.
+ * workspace: device, moe_plan_workspace_bytes(plan) bytes.  Asynchronous.
+ * The first route into a given workspace address also initialises its
+ * control words.  Errors: INVALID_ARGUMENT, HIP. */
+moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspace, void* stream);
+
+/* Dispatch: recv[slot_of[t, j]] = x[t] for every valid slot.  x: device
+ * [T, H] bf16; recv: device [T*k, H] bf16.  staging: device
+ * [staging_rows_max, H] bf16 when the plan has MOE_FLAG_NODE_DEDUP, else
+ * ignored (may be NULL).  Asynchronous.
+ * Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
+moe_status moe_dispatch(const moe_plan* plan, const uint16_t* x, uint16_t* recv, uint16_t* staging,
+                        void* stream);
+
+/* Combine: out[t] = sum_{j=0..k-1} topk_w[t, j] * y[slot_of[t, j]], each term
+ * a float32 fused multiply-add in ascending j starting from 0, then rounded
+ * to bf16 (nearest even) or stored as float32.  y: device [T*k, H] bf16 in
+ * the receive layout; topk_w: device [T, k] float32; out: device [T, H] of
+ * out_dtype.  Asynchronous.  Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
+moe_status moe_combine(const moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
+                       int32_t out_dtype, void* stream);
+
+/* Copies one plan item to host memory (synchronises the stream).  bytes must
+ * be at least the item's size (see moe_item).  The traffic matrices
+ * (SEND_ROWS, SEND_COPIES, NODE_COPIES) are computed on demand by a small
+ * kernel from the workspace.  Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
+moe_status moe_plan_read(const moe_plan* plan, int32_t item, void* host_dst, size_t bytes,
+                         void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_str(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_SHUFFLE_H */

@@ -1,0 +1,112 @@
+"""The C ABI on the host (CPU, no GPU needed): the library loads, exports every
+function include/moe_shuffle.h declares, and rejects bad configurations before
+anything is launched."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from combine_shuffling_amd import _abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_shuffle.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _abi.lib()
+    names = declared_functions()
+    assert set(names) == set(_abi.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def make(T=128, H=256, E=8, k=2, R=2, G=None, flags=0):
+    cfg = _abi.MoeConfig(T, H, E, k, R, R if G is None else G, flags)
+    h = ctypes.c_void_p()
+    st = _abi.lib().moe_plan_create(ctypes.byref(cfg), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), _abi.OK),
+    (dict(T=0), _abi.OK),
+    (dict(T=-1), _abi.ERR_INVALID_ARGUMENT),
+    (dict(H=0), _abi.ERR_INVALID_ARGUMENT),
+    (dict(H=12), _abi.ERR_INVALID_ARGUMENT),          # row not a whole number of 16-byte chunks
+    (dict(E=0), _abi.ERR_INVALID_ARGUMENT),
+    (dict(k=0), _abi.ERR_INVALID_ARGUMENT),
+    (dict(k=9), _abi.ERR_INVALID_ARGUMENT),           # k > E
+    (dict(E=2, R=8), _abi.ERR_EXPERTS_LT_RANKS),      # zero-expert ranks
+    (dict(E=8, R=3, G=2), _abi.ERR_INVALID_ARGUMENT),  # G does not divide R
+    (dict(E=2048, k=2), _abi.ERR_UNSUPPORTED),
+    (dict(E=64, k=17, R=4), _abi.ERR_UNSUPPORTED),
+    (dict(flags=_abi.FLAG_NODE_DEDUP), _abi.ERR_INVALID_ARGUMENT),  # one node: nothing to dedup
+    (dict(R=2, G=1, flags=_abi.FLAG_NODE_DEDUP), _abi.OK),
+    (dict(flags=4), _abi.ERR_INVALID_ARGUMENT),
+    (dict(T=1 << 28, k=8), _abi.ERR_UNSUPPORTED),     # T*k past 32-bit row indices
+])
+def test_plan_create_status(kw, want):
+    st, h = make(**kw)
+    assert st == want, _abi.status_str(st)
+    if st == _abi.OK:
+        _abi.lib().moe_plan_destroy(h)
+
+
+def test_plan_sizes():
+    L = _abi.lib()
+    st, h = make(T=16384, H=7168, E=256, k=8, R=64, G=8, flags=_abi.FLAG_NODE_DEDUP)
+    assert st == _abi.OK
+    assert L.moe_plan_recv_rows(h) == 16384 * 8
+    assert L.moe_plan_staging_rows_max(h) == 16384 * 8   # min(k, N) = 8
+    ws = L.moe_plan_workspace_bytes(h)
+    assert ws % 256 == 0 and ws >= 4 * (3 * 16384 * 8)
+    L.moe_plan_destroy(h)
+    st, h = make(T=4096, H=2048, E=64, k=8, R=4)
+    assert L.moe_plan_staging_rows_max(h) == 0
+    L.moe_plan_destroy(h)
+    L.moe_plan_destroy(None)
+
+
+def test_calls_before_route_are_refused():
+    L = _abi.lib()
+    st, h = make()
+    buf = np.zeros(16, dtype=np.int32)
+    vp = ctypes.c_void_p
+    assert L.moe_dispatch(h, vp(16), vp(16), None, None) == _abi.ERR_PLAN_NOT_ROUTED
+    assert L.moe_combine(h, vp(16), vp(16), vp(16), 0, None) == _abi.ERR_PLAN_NOT_ROUTED
+    assert L.moe_plan_read(h, 0, buf.ctypes.data_as(vp), buf.nbytes, None) == \
+        _abi.ERR_PLAN_NOT_ROUTED
+    # null / misaligned workspace is refused before any launch
+    assert L.moe_route_plan(h, vp(256), None, None) == _abi.ERR_INVALID_ARGUMENT
+    assert L.moe_route_plan(h, vp(256), vp(1024 + 8), None) == _abi.ERR_INVALID_ARGUMENT
+    L.moe_plan_destroy(h)
+
+
+def test_expert_partition_matches_printed_and_oracle():
+    import oracle
+    from combine_shuffling_amd import expert_partition, MoeError
+
+    for E, R in [(256, 7), (100, 7), (384, 5), (384, 6), (384, 7), (8, 2), (1, 1), (1024, 1000)]:
+        assert expert_partition(E, R) == oracle.expert_partition(E, R).tolist()
+    assert np.diff(expert_partition(256, 7)).tolist() == [37, 37, 37, 37, 36, 36, 36]
+    assert np.diff(expert_partition(100, 7)).tolist() == [15, 15, 14, 14, 14, 14, 14]
+    with pytest.raises(MoeError) as ei:
+        expert_partition(2, 8)
+    assert ei.value.status == _abi.ERR_EXPERTS_LT_RANKS
+    with pytest.raises(MoeError):
+        expert_partition(0, 1)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert _abi.status_str(s)
+    assert "unknown" in _abi.status_str(99)

@@ -85,7 +85,7 @@ def test_plan_dispatch_combine_vs_brute(case):
     assert np.array_equal(oracle.dedup_stage_b(staging, p), recv)
     out = oracle.combine(recv, w, p)
     ref = brute.combine(recv.tolist(), w.tolist(), b)
-    assert np.array_equal(out, np.array(ref, dtype=np.float64).reshape(T, H))
+    assert np.array_equal(out, np.array(ref, dtype=np.float64).reshape(T, H), equal_nan=True)
 
 
 # ------------------------------------------------------------- invariants
