@@ -11,22 +11,36 @@ outputs), at least 2 GiB in all, so that a step never finds the previous
 step's data in the 256 MB last-level cache; within a step combine reads the
 rows dispatch has just written, as the path does.
 
-Prints one JSON line.  value = algorithmic payload bytes per step / wall time
-per step (bracketed by synchronize on both sides).  Algorithmic bytes:
+Prints one JSON line.
+  value       algorithmic payload bytes per step / wall time per step, over K
+              steps bracketed by synchronize on both sides, no events inside.
+  roofline    the dominant kernel: its algorithmic bytes per launch / its mean
+              duration, from HIP events on the launch stream bracketing a burst
+              of K back-to-back launches of it over the same buffer sets (an
+              event record adds a gap of about 2 us between kernels, so events
+              bracket bursts rather than single launches, and the value pass
+              has none).
+              traffic = HBM bytes per launch from the rocprofv3 FETCH_SIZE /
+              WRITE_SIZE summary under profiles/, scaled by the copy
+              calibration; null if the kernel sources changed since.
+Algorithmic bytes (payload rows only):
   dispatch single hop  (T + T*k) * 2H
   dispatch with dedup  (T + 2D + T*k) * 2H   (D staging rows, from the plan)
   combine              (T*k + T) * 2H
-roofline: the dominant kernel's algorithmic bytes per launch / its mean
-duration from HIP events recorded around its launch on the stream it runs on,
-against the 8 TB/s HBM peak.
+
+Helper modes (no GPU needed): --summarize-trace and --summarize-pmc turn
+rocprofv3 CSV output into the short summaries kept under profiles/.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -38,6 +52,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "dispatch+combine effective GB/s and % of HBM peak, 1 MI355X"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("combine_shuffling_amd/csrc/move.hip", "combine_shuffling_amd/csrc/moe_device.h",
+                  "combine_shuffling_amd/csrc/moe_internal.h")
 
 
 def parse():
@@ -50,7 +67,117 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) a few "
+                         "times, to scale hardware byte counters against a known size")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT"),
+                    help="write a kernel-duration summary of a rocprofv3 --stats CSV")
+    ap.add_argument("--summarize-pmc", nargs=5,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT"),
+                    help="write the per-launch HBM traffic summary of two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) scaled by the copy calibration runs")
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="size the copy calibration ran with (--copy-calibration MIB)")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(mib):
+    """torch.mul(a, 1, out=b) over MIB MiB of bf16: a plain copy kernel of known size."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 2
+    a = torch.randn(n, device=dev).to(torch.bfloat16)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"kernel": "torch elementwise mul (bf16)",
+                                           "read_bytes": n * 2, "write_bytes": n * 2,
+                                           "launches": 5}}), flush=True)
+
+
+def _pmc_means(path, counter):
+    """Mean counter value (KiB) per kernel name over its dispatches."""
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def _short(name):
+    m = re.search(r"(\w+_kernel)(<[^>]*>)?", name)
+    return m.group(1) + (m.group(2) or "") if m else name[:60]
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out, copy_mib, command):
+    """Per-launch HBM traffic of each kernel, scaled by the copy calibration."""
+    fetch = _pmc_means(fetch_csv, "FETCH_SIZE")
+    write = _pmc_means(write_csv, "WRITE_SIZE")
+    cf = _pmc_means(copy_fetch_csv, "FETCH_SIZE")
+    cw = _pmc_means(copy_write_csv, "WRITE_SIZE")
+    # The copy kernel is the bf16 elementwise mul of --copy-calibration; it is
+    # the one launched 5 times, reading and writing copy_mib MiB each time.
+    copy_name = max((k for k in cf if cf[k][1] == 5 and k in cw), key=lambda k: cw[k][0])
+    known_kib = copy_mib * 1024.0
+    f_fetch = known_kib / cf[copy_name][0]
+    f_write = known_kib / cw[copy_name][0]
+    kernels = {}
+    for name, (fk, n) in fetch.items():
+        if name not in write or not name.startswith("void moe::"):
+            continue
+        wk = write[name][0]
+        kernels[_short(name)] = {
+            "fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "dispatches": n,
+            "traffic_bytes": int(round((fk * f_fetch + wk * f_write) * 1024))}
+    summary = {"source_hash": kernel_source_hash(), "copy_kernel": copy_name[:80],
+               "copy_known_kib": known_kib, "copy_fetch_kib": round(cf[copy_name][0], 1),
+               "copy_write_kib": round(cw[copy_name][0], 1), "fetch_factor": round(f_fetch, 5),
+               "write_factor": round(f_write, 5), "kernels": kernels, "command": command}
+    with open(out, "w") as f:
+        f.write("# HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs,\n")
+        f.write("# each counter scaled by what it reads on a plain copy kernel of known size.\n")
+        f.write(json.dumps(summary, indent=1) + "\n")
+    print(out)
+
+
+def summarize_trace(stats_csv, out, command):
+    rows = list(csv.DictReader(open(stats_csv)))
+    with open(out, "w") as f:
+        f.write("# rocprofv3 --kernel-trace --stats summary\n# command: %s\n" % command)
+        f.write("%-60s %7s %12s %12s %12s\n" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
+        for r in rows:
+            f.write("%-60s %7s %12.2f %12.2f %12.2f\n" % (
+                r["Name"][:60], r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    print(out)
+
+
+def recorded_traffic(workload, kernel):
+    """Traffic per launch of `kernel` from the committed summary, if still current."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = "".join(ln for ln in open(path) if not ln.startswith("#"))
+    s = json.loads(text)
+    if s.get("source_hash") != kernel_source_hash():
+        return None
+    for name, v in s["kernels"].items():
+        if name.startswith(kernel):
+            return v["traffic_bytes"]
+    return None
 
 
 def algorithmic_bytes(wl, D):
@@ -90,6 +217,15 @@ def cpu_baseline(batch, seconds):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.command)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.copy_mib, args.command)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the expert-parallel ranks are virtual "
               f"partitions of a single MI355X's HBM; --gpus {args.gpus} is not supported.",
@@ -125,16 +261,10 @@ def main():
                  out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
         sets.append(s)
 
-    def step(s, ev=None):
+    def step(s):
         s["plan"].route(s["idx"])
-        if ev is not None:
-            ev[0].record()
         s["plan"].dispatch(s["x"], s["recv"], s["staging"])
-        if ev is not None:
-            ev[1].record()
         s["plan"].combine(s["recv"], s["w"], s["out"])
-        if ev is not None:
-            ev[2].record()
 
     for i in range(args.warmup):
         step(sets[i % n_sets])
@@ -142,27 +272,39 @@ def main():
     D = int(sets[0]["plan"].read("num_staged")[0]) if wl.node_dedup else 0
     disp_b, comb_b = algorithmic_bytes(wl, D)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Timed region: K steps, nothing else on the stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % n_sets], evs[i])
+        step(sets[i % n_sets])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    disp_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
     value = (disp_b + comb_b) / (ms_per_step * 1e-3) / 1e9
 
-    disp_gbs = disp_b / (disp_ms.mean() * 1e-3) / 1e9
-    comb_gbs = comb_b / (comb_ms.mean() * 1e-3) / 1e9
+    # Kernel pass: each phase as a burst of K back-to-back launches on the
+    # launch stream between one pair of events (per-launch event records
+    # would add their own gaps), cycling the same buffer sets.
+    def burst(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fn(sets[i % n_sets])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    disp_ms = burst(lambda s: s["plan"].dispatch(s["x"], s["recv"], s["staging"]))
+    comb_ms = burst(lambda s: s["plan"].combine(s["recv"], s["w"], s["out"]))
+    disp_gbs = disp_b / (disp_ms * 1e-3) / 1e9
+    comb_gbs = comb_b / (comb_ms * 1e-3) / 1e9
     if wl.node_dedup:
-        # two launches in dispatch: the dominant single kernel is combine
-        dom = ("combine_kernel", comb_b, comb_ms.mean(), comb_gbs)
+        # dispatch is two launches here; the dominant single launch timed is combine
+        dom = ("combine_kernel", comb_b, comb_ms, comb_gbs)
     else:
-        dom = max([("gather_kernel", disp_b, disp_ms.mean(), disp_gbs),
-                   ("combine_kernel", comb_b, comb_ms.mean(), comb_gbs)], key=lambda d: d[2])
+        dom = max([("gather_kernel", disp_b, disp_ms, disp_gbs),
+                   ("combine_kernel", comb_b, comb_ms, comb_gbs)], key=lambda d: d[2])
 
     result = {
         "metric": METRIC,
@@ -182,20 +324,14 @@ def main():
                    "staging_rows": D, "seed": wl.seed, "buffer_sets": n_sets},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "bytes_per_step": disp_b + comb_b,
-        "phases": {
-            "dispatch": {"bytes": disp_b, "ms_mean": round(float(disp_ms.mean()), 5),
-                         "ms_p10": round(float(np.percentile(disp_ms, 10)), 5),
-                         "ms_p90": round(float(np.percentile(disp_ms, 90)), 5),
-                         "GB/s": round(disp_gbs, 1)},
-            "combine": {"bytes": comb_b, "ms_mean": round(float(comb_ms.mean()), 5),
-                        "ms_p10": round(float(np.percentile(comb_ms, 10)), 5),
-                        "ms_p90": round(float(np.percentile(comb_ms, 90)), 5),
-                        "GB/s": round(comb_gbs, 1)},
-        },
+        "phases": {"dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),
+                                "GB/s": round(disp_gbs, 1), "launches": 2 if wl.node_dedup else 1},
+                   "combine": {"bytes": comb_b, "ms_per_launch": round(comb_ms, 5),
+                               "GB/s": round(comb_gbs, 1), "launches": 1}},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[3], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": dom[1],
-                     "ms_per_launch": round(float(dom[2]), 5)},
+                     "traffic": recorded_traffic(args.workload, dom[0]),
+                     "bytes_per_launch": dom[1], "ms_per_launch": round(float(dom[2]), 5)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

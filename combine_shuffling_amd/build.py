@@ -34,10 +34,15 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into LIB_PATH (always recompiles). Returns the path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
+def build(verbose: bool = False, extra_flags=(), out: str | None = None) -> str:
+    """Compile every source into ``out`` (default LIB_PATH; always recompiles).
+
+    extra_flags: more hipcc flags, e.g. the -D tunables of move.hip
+    (MOE_GATHER_U, MOE_COMBINE_U, MOE_MOVE_WAVES, MOE_NT_STORE).
+    """
+    out = LIB_PATH if out is None else out
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, f"-I{INCLUDE}", f"-I{CSRC}",
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -48,8 +53,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -20,17 +20,12 @@ struct moe_plan {
   const int32_t* idx;
   void* ws;
   moe::Work work;
-  bool routed;
+  bool routed;     // route_count has been launched for the bound routing
+  bool assigned;   // slot_of / row_src (and stage_of / stage_src) are final
 };
 
 namespace moe {
 namespace {
-
-int ceil_log2(int n) {
-  int b = 0;
-  while ((1 << b) < n) ++b;
-  return b;
-}
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -40,7 +35,7 @@ moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HI
 
 }  // namespace
 
-Layout make_layout(const Dims& d, int64_t staging_rows_max) {
+Layout make_layout(const Dims& d) {
   Layout l{};
   size_t at = 0;
   auto take = [&](size_t& field, int64_t ints) {
@@ -48,18 +43,24 @@ Layout make_layout(const Dims& d, int64_t staging_rows_max) {
     at = align_up(at + (size_t)std::max<int64_t>(ints, 1) * sizeof(int32_t), 256);
   };
   const int64_t tk = (int64_t)d.T * d.k;
-  take(l.ctrl, 64);
+  const int64_t fk = d.dedup ? tk : 1;
+  take(l.ctrl, kCtrlWords);
   take(l.tile_flags, d.nblk);
   take(l.tile_counts, (int64_t)d.nblk * d.E);
+  take(l.tile_base, (int64_t)d.nblk * d.E);
   take(l.counts, d.E);
   take(l.expert_off, d.E + 1);
   take(l.rank_off, d.R + 1);
+  take(l.lr, tk);
   take(l.slot_of, tk);
   take(l.row_src, tk);
   take(l.tile_fcounts, d.dedup ? (int64_t)d.nblk * d.R : 1);
+  take(l.tile_fbase, d.dedup ? (int64_t)d.nblk * d.R : 1);
   take(l.stage_off, d.dedup ? d.R + 1 : 1);
-  take(l.stage_of, d.dedup ? tk : 1);
-  take(l.stage_src, d.dedup ? staging_rows_max : 1);
+  take(l.fkey, fk);
+  take(l.flr, fk);
+  take(l.stage_of, fk);
+  take(l.stage_src, d.dedup ? d.smax : 1);
   take(l.send_rows, (int64_t)d.R * d.R);
   take(l.send_copies, (int64_t)d.R * d.R);
   take(l.node_copies, (int64_t)d.R * d.N);
@@ -74,19 +75,33 @@ Work bind_work(const Layout& l, void* base) {
   w.ctrl = p(l.ctrl);
   w.tile_flags = p(l.tile_flags);
   w.tile_counts = p(l.tile_counts);
+  w.tile_base = p(l.tile_base);
   w.counts = p(l.counts);
   w.expert_off = p(l.expert_off);
   w.rank_off = p(l.rank_off);
+  w.lr = p(l.lr);
   w.slot_of = p(l.slot_of);
   w.row_src = p(l.row_src);
   w.tile_fcounts = p(l.tile_fcounts);
+  w.tile_fbase = p(l.tile_fbase);
   w.stage_off = p(l.stage_off);
+  w.fkey = p(l.fkey);
+  w.flr = p(l.flr);
   w.stage_of = p(l.stage_of);
   w.stage_src = p(l.stage_src);
   w.send_rows = p(l.send_rows);
   w.send_copies = p(l.send_copies);
   w.node_copies = p(l.node_copies);
   return w;
+}
+
+// Makes slot_of / row_src (and the staging arrays) final when no dispatch
+// has done it since the last route.
+moe_status ensure_assigned(moe_plan* plan, hipStream_t s) {
+  if (plan->assigned) return MOE_OK;
+  if (launch_route_assign(plan->d, plan->idx, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
+  plan->assigned = true;
+  return MOE_OK;
 }
 
 }  // namespace moe
@@ -147,14 +162,16 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   d.erem = d.E % d.R;
   d.tbase = d.T / d.R;
   d.trem = d.T % d.R;
-  const int64_t per_tile_cap = (int64_t)moe::kPlanBlock * moe::kMaxPlanTiles;
+  // At most kMaxPlanTiles tiles, and few enough that the last block can scan
+  // the [tiles x experts] count matrix in LDS.
+  const int64_t max_tiles = std::min<int64_t>(moe::kMaxPlanTiles, moe::kScanLdsInts / d.E);
+  const int64_t per_tile_cap = (int64_t)moe::kPlanBlock * max_tiles;
   d.passes = (int32_t)std::max<int64_t>(1, (T + per_tile_cap - 1) / per_tile_cap);
-  const int64_t tile = (int64_t)moe::kPlanBlock * d.passes;
-  d.nblk = (int32_t)std::max<int64_t>(1, (T + tile - 1) / tile);
-  d.ebits = moe::ceil_log2(d.E);
-  d.fbits = moe::ceil_log2(d.R);
+  d.tile = moe::kPlanBlock * d.passes;
+  d.nblk = (int32_t)std::max<int64_t>(1, (T + d.tile - 1) / d.tile);
   d.dedup = dedup ? 1 : 0;
   d.chunks = (int32_t)chunks;
+  d.segs = (int32_t)((chunks + moe::kWave - 1) / moe::kWave);
   d.smax = (int32_t)staging_max;
 
   moe_plan* p = new (std::nothrow) moe_plan();
@@ -162,10 +179,11 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   p->cfg = c;
   p->d = d;
   p->staging_rows_max = staging_max;
-  p->layout = moe::make_layout(d, staging_max);
+  p->layout = moe::make_layout(d);
   p->idx = nullptr;
   p->ws = nullptr;
   p->routed = false;
+  p->assigned = false;
   *out = p;
   return MOE_OK;
 }
@@ -187,31 +205,36 @@ moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspa
   if (plan->d.T > 0 && (!topk_idx || !moe::aligned(topk_idx, 4))) return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   plan->routed = false;
+  plan->assigned = false;
   plan->idx = topk_idx;
   plan->ws = workspace;
   plan->work = moe::bind_work(plan->layout, workspace);
-  moe_status st = moe::from_hip(moe::launch_route_count(plan->d, topk_idx, plan->work, s));
-  if (st == MOE_OK) st = moe::from_hip(moe::launch_route_assign(plan->d, topk_idx, plan->work, s));
-  plan->routed = st == MOE_OK;
-  return st;
+  if (moe::launch_route_count(plan->d, topk_idx, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
+  plan->routed = true;
+  return MOE_OK;
 }
 
-moe_status moe_dispatch(const moe_plan* plan, const uint16_t* x, uint16_t* recv, uint16_t* staging,
+moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint16_t* staging,
                         void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARGUMENT;
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   if (plan->d.T == 0) return MOE_OK;
   if (!x || !recv || !moe::aligned(x, 16) || !moe::aligned(recv, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->d.dedup && (!staging || !moe::aligned(staging, 16))) return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!plan->d.dedup) return moe::from_hip(moe::launch_gather(plan->d, x, recv, plan->work, s));
-  if (!staging || !moe::aligned(staging, 16)) return MOE_ERR_INVALID_ARGUMENT;
-  moe_status st = moe::from_hip(moe::launch_stage_a(plan->d, x, staging, plan->work, plan->staging_rows_max, s));
-  if (st != MOE_OK) return st;
-  return moe::from_hip(
-      moe::launch_stage_b(plan->d, staging, recv, plan->work, plan->staging_rows_max, s));
+  if (!plan->d.dedup) {
+    if (moe::launch_gather(plan->d, plan->idx, x, recv, plan->work, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    plan->assigned = true;
+    return MOE_OK;
+  }
+  if (moe::launch_stage_a(plan->d, plan->idx, x, staging, plan->work, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  plan->assigned = true;
+  return moe::from_hip(moe::launch_stage_b(plan->d, staging, recv, plan->work, s));
 }
 
-moe_status moe_combine(const moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
+moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
                        int32_t out_dtype, void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARGUMENT;
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
@@ -220,28 +243,31 @@ moe_status moe_combine(const moe_plan* plan, const uint16_t* y, const float* top
   if (!y || !topk_w || !out || !moe::aligned(y, 16) || !moe::aligned(topk_w, 4) ||
       !moe::aligned(out, 16))
     return MOE_ERR_INVALID_ARGUMENT;
-  return moe::from_hip(moe::launch_combine(plan->d, y, topk_w, out, out_dtype == MOE_OUT_F32,
-                                           plan->work, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_status st = moe::ensure_assigned(plan, s);
+  if (st != MOE_OK) return st;
+  return moe::from_hip(
+      moe::launch_combine(plan->d, y, topk_w, out, out_dtype == MOE_OUT_F32, plan->work, s));
 }
 
-moe_status moe_plan_read(const moe_plan* plan, int32_t item, void* host_dst, size_t bytes,
+moe_status moe_plan_read(moe_plan* plan, int32_t item, void* host_dst, size_t bytes,
                          void* stream) {
   if (!plan || !host_dst) return MOE_ERR_INVALID_ARGUMENT;
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   const moe::Dims& d = plan->d;
-  const moe::Work& w = plan->work;
+  const moe::Work w = plan->work;
   const int64_t tk = (int64_t)d.T * d.k;
   const int32_t* src = nullptr;
   int64_t n = 0;
   bool traffic = false;
   switch (item) {
-    case MOE_ITEM_STATUS: src = w.ctrl; n = 1; break;
+    case MOE_ITEM_STATUS: src = w.ctrl + moe::kCtrlStatus; n = 1; break;
     case MOE_ITEM_COUNTS: src = w.counts; n = d.E; break;
     case MOE_ITEM_EXPERT_OFFSETS: src = w.expert_off; n = d.E + 1; break;
     case MOE_ITEM_RANK_OFFSETS: src = w.rank_off; n = d.R + 1; break;
     case MOE_ITEM_SLOT_OF: src = w.slot_of; n = tk; break;
     case MOE_ITEM_ROW_SRC: src = w.row_src; n = tk; break;
-    case MOE_ITEM_NUM_STAGED: src = w.ctrl + 1; n = 1; break;
+    case MOE_ITEM_NUM_STAGED: src = w.ctrl + moe::kCtrlStaged; n = 1; break;
     case MOE_ITEM_STAGE_OFFSETS: src = w.stage_off; n = d.R + 1; break;
     case MOE_ITEM_STAGE_OF: src = w.stage_of; n = tk; break;
     case MOE_ITEM_STAGE_SRC: src = w.stage_src; n = plan->staging_rows_max; break;
@@ -256,6 +282,12 @@ moe_status moe_plan_read(const moe_plan* plan, int32_t item, void* host_dst, siz
   const size_t need = (size_t)n * sizeof(int32_t);
   if (bytes < need) return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool per_slot = item == MOE_ITEM_SLOT_OF || item == MOE_ITEM_ROW_SRC ||
+                        item == MOE_ITEM_STAGE_OF || item == MOE_ITEM_STAGE_SRC || traffic;
+  if (per_slot) {
+    const moe_status st = moe::ensure_assigned(plan, s);
+    if (st != MOE_OK) return st;
+  }
   if (traffic) {
     const size_t mat = (size_t)d.R * d.R * sizeof(int32_t);
     hipError_t e = hipMemsetAsync(w.send_rows, 0, mat, s);

@@ -1,0 +1,60 @@
+// Device helpers shared by the route-plan and data-movement kernels.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// Part of element i under the contiguous ceil/floor split whose first `rem`
+// parts hold base + 1 elements (TensorRT-LLM PR #13888, "support non-divisible
+// EP in MoE alltoall", performance commit message: base and remainder are
+// computed once per kernel, and a zero remainder takes a single divide).
+__device__ __forceinline__ int split_part(int i, int base, int rem) {
+  if (rem == 0) return i / base;
+  const int cut = rem * (base + 1);
+  return i < cut ? i / (base + 1) : rem + (i - cut) / base;
+}
+
+// Receive row of every slot of token t: the row of (tile, expert) from the
+// scan plus the slot's rank inside the tile; -1 for a dropped slot.
+template <int KMAX>
+__device__ __forceinline__ void token_slots(const Dims& d, const Work& w,
+                                            const int32_t* __restrict__ idx, int t,
+                                            int (&slot)[KMAX]) {
+  const int64_t at = (int64_t)t * d.k;
+  const int b = t / d.tile;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    slot[j] = -1;
+    if (j < d.k) {
+      const int l = w.lr[at + j];
+      if (l >= 0) slot[j] = w.tile_base[b * d.E + idx[at + j]] + l;
+    }
+  }
+}
+
+// Staging row feeding every slot of token t (node deduplication): the first
+// slot of a node owns the row (tile base of its forwarder plus its rank),
+// later slots of the same node share it; -1 for a dropped slot.
+// `lead` gets bit j set when slot j is the first slot of its node.
+template <int KMAX>
+__device__ __forceinline__ void token_stages(const Dims& d, const Work& w, int t,
+                                             int (&p)[KMAX], uint32_t& lead) {
+  const int64_t at = (int64_t)t * d.k;
+  const int b = t / d.tile;
+  int key[KMAX];
+  lead = 0;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    key[j] = j < d.k ? w.fkey[at + j] : -1;
+    p[j] = key[j] >= 0 ? w.tile_fbase[b * d.R + key[j]] + w.flr[at + j] : -1;
+    if (key[j] >= 0) lead |= 1u << j;
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+    for (int jj = 0; jj < j; ++jj)
+      if (key[j] == -2 - jj) p[j] = p[jj];
+}
+
+}  // namespace moe

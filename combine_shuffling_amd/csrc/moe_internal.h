@@ -14,8 +14,13 @@ namespace moe {
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kPlanBlock = 256;    // threads per route-plan block = tokens per pass
 constexpr int kPlanWaves = kPlanBlock / kWave;
-constexpr int kMaxPlanTiles = 64;  // route-plan tiles (blocks); tiles grow past 64*256 tokens
-constexpr int kMoveBlock = 256;    // threads per data-movement block
+constexpr int kMaxPlanTiles = 64;  // route-plan tiles (blocks) at most
+constexpr int kScanLdsInts = 8192; // tile-count matrix the last block scans in LDS (32 KiB)
+
+// ctrl words at the start of the workspace.
+constexpr int kCtrlStatus = 0;     // moe_status of the last route
+constexpr int kCtrlStaged = 1;     // D, staging rows used
+constexpr int kCtrlWords = 64;
 
 // Sizes and the hoisted constants of the two ceil/floor splits.  Passed by
 // value to every kernel.
@@ -24,27 +29,34 @@ struct Dims {
   int32_t ebase, erem;    // experts: E / R, E % R
   int32_t tbase, trem;    // tokens:  T / R, T % R (owner ranks)
   int32_t passes;         // 256-token passes per plan tile
+  int32_t tile;           // tokens per plan tile = 256 * passes
   int32_t nblk;           // plan tiles
-  int32_t ebits, fbits;   // bits that tell expert ids / forwarder ids apart
   int32_t dedup;          // MOE_FLAG_NODE_DEDUP set
   int32_t chunks;         // 16-byte chunks per row = H / 8
+  int32_t segs;           // 64-chunk row segments per row = ceil(chunks / 64)
   int32_t smax;           // staging rows allocated (T * min(k, N) with dedup, else 0)
 };
 
-// Device pointers into the caller's workspace.  Sizes in int32 elements.
+// Device pointers into the caller's workspace (int32 arrays).
 struct Work {
-  int32_t* ctrl;          // [64]: [0] status of the last route, [1] D staging rows used
+  int32_t* ctrl;          // [kCtrlWords]
   int32_t* tile_flags;    // [nblk]      bad-routing flag per tile
   int32_t* tile_counts;   // [nblk * E]  rows per (tile, expert), tile-major
+  int32_t* tile_base;     // [nblk * E]  first receive row of (tile, expert)
   int32_t* counts;        // [E]
   int32_t* expert_off;    // [E + 1]
   int32_t* rank_off;      // [R + 1]
+  int32_t* lr;            // [T * k]     rank of slot (t, j) among its tile's slots of that expert; -1 dropped
   int32_t* slot_of;       // [T * k]     token slot -> receive row (-1: dropped)
   int32_t* row_src;       // [T * k]     receive row -> token
-  int32_t* tile_fcounts;  // [nblk * R]  staging rows per (tile, forwarder)       (dedup)
-  int32_t* stage_off;     // [R + 1]     first staging row of each forwarder       (dedup)
-  int32_t* stage_of;      // [T * k]     token slot -> staging row of its node     (dedup)
-  int32_t* stage_src;     // [Dmax]      staging row -> token                      (dedup)
+  int32_t* tile_fcounts;  // [nblk * R]  staging rows per (tile, forwarder)               (dedup)
+  int32_t* tile_fbase;    // [nblk * R]  first staging row of (tile, forwarder)           (dedup)
+  int32_t* stage_off;     // [R + 1]     first staging row of each forwarder               (dedup)
+  int32_t* fkey;          // [T * k]     forwarder of the node's first slot; -2-j on later
+                          //             slots of the node (j = its first slot); -1 dropped (dedup)
+  int32_t* flr;           // [T * k]     rank among the tile's staging rows of that forwarder (dedup)
+  int32_t* stage_of;      // [T * k]     token slot -> staging row of its node             (dedup)
+  int32_t* stage_src;     // [smax]      staging row -> token                              (dedup)
   int32_t* send_rows;     // [R * R]     modelled link traffic (filled on demand)
   int32_t* send_copies;   // [R * R]
   int32_t* node_copies;   // [R * N]
@@ -52,25 +64,28 @@ struct Work {
 
 // Byte offsets of each Work array from the workspace base, and the total.
 struct Layout {
-  size_t ctrl, tile_flags, tile_counts, counts, expert_off, rank_off, slot_of, row_src,
-      tile_fcounts, stage_off, stage_of, stage_src, send_rows, send_copies, node_copies, total;
+  size_t ctrl, tile_flags, tile_counts, tile_base, counts, expert_off, rank_off, lr, slot_of,
+      row_src, tile_fcounts, tile_fbase, stage_off, fkey, flr, stage_of, stage_src, send_rows,
+      send_copies, node_copies, total;
 };
 
-Layout make_layout(const Dims& d, int64_t staging_rows_max);
+Layout make_layout(const Dims& d);
 Work bind_work(const Layout& l, void* base);
 
 // Route plan (route_plan.hip).
+// route_count then route_scan.
 hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);
 hipError_t launch_route_assign(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);
 hipError_t launch_traffic(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);
 
-// Data movement (move.hip).
-hipError_t launch_gather(const Dims& d, const uint16_t* x, uint16_t* recv, const Work& w,
-                         hipStream_t s);
-hipError_t launch_stage_a(const Dims& d, const uint16_t* x, uint16_t* staging, const Work& w,
-                          int64_t staging_rows_max, hipStream_t s);
+// Data movement (move.hip).  gather and stage_a also finish the plan
+// (slot_of, row_src, stage_of, stage_src) from the in-tile ranks.
+hipError_t launch_gather(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
+                         const Work& w, hipStream_t s);
+hipError_t launch_stage_a(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* staging,
+                          const Work& w, hipStream_t s);
 hipError_t launch_stage_b(const Dims& d, const uint16_t* staging, uint16_t* recv, const Work& w,
-                          int64_t staging_rows_max, hipStream_t s);
+                          hipStream_t s);
 hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* wts, void* out,
                           bool out_f32, const Work& w, hipStream_t s);
 

@@ -1,28 +1,53 @@
 // Data movement on gfx950: dispatch (gather-send fused with scatter-recv),
 // the two hops of node-deduplicated dispatch, and the weighted combine.
 //
-// All four kernels stream whole rows of 2H bytes as 16-byte chunks.  The work
-// is the flat list of (row, chunk) items; 64 consecutive lanes cover 1 KiB of
-// consecutive chunks, so every load and store instruction of a wave touches
-// whole contiguous rows (coalesced, no LDS staging needed: source and
-// destination rows are both contiguous).  Each thread handles U items spaced
-// one block apart and issues all of their loads before any store, to keep
-// enough bytes in flight to cover HBM latency.
+// Work unit: a wave-item = one 64-chunk segment of one row (64 lanes x 16
+// bytes = 1 KiB of consecutive bytes; the last segment of a row may be
+// partial).  A row's token is wave-uniform, so every per-token value (expert
+// ids, in-tile ranks, slots, weights) is loaded once per wave through the
+// scalar unit and only the 16-byte row chunks use vector memory.  Each wave
+// takes U wave-items and issues all of its loads before any store, to keep
+// enough bytes in flight to cover HBM latency.  Source and destination rows
+// are contiguous, so the row copies need no LDS staging.
 //
 //  gather   dispatch, single hop: each source row x[t] is read once and
 //           written to its k receive rows (FUSCO article, "core innovation":
 //           no pack buffer before the send, no reorder after the receive).
+//           Also finishes slot_of / row_src from the in-tile ranks.
 //  stage_a  deduplicated dispatch, hop 1: x[t] is read once and written once
 //           per distinct destination node, to that node's forwarder staging
 //           row (FUSCO article, "load balancing and cross-node
-//           deduplication").
+//           deduplication").  Also finishes slot_of / row_src / stage_of /
+//           stage_src.
 //  stage_b  hop 2, intra-node fan-out: each staging row is read once and
 //           written to every receive row of its token on that node.
 //  combine  out[t] = sum_j w[t,j] * y[slot_of[t,j]]: k row loads, one fp32
 //           fused multiply-add per element and slot in ascending j starting
 //           from 0, then round-to-nearest-even bf16 (or fp32) out (INC-MoE
 //           abstract: combine back to each token's owner).
-#include "moe_internal.h"
+#include "moe_device.h"
+
+#ifndef MOE_GATHER_U
+#define MOE_GATHER_U 1
+#endif
+#ifndef MOE_STAGE_U
+#define MOE_STAGE_U 2
+#endif
+#ifndef MOE_COMBINE_U
+#define MOE_COMBINE_U 2
+#endif
+#ifndef MOE_NT_LOAD
+#define MOE_NT_LOAD 1
+#endif
+#ifndef MOE_NT_LOAD_X
+#define MOE_NT_LOAD_X 0
+#endif
+#ifndef MOE_MOVE_WAVES
+#define MOE_MOVE_WAVES 4
+#endif
+#ifndef MOE_NT_STORE
+#define MOE_NT_STORE 1
+#endif
 
 namespace moe {
 namespace {
@@ -30,114 +55,193 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGatherU = 4;   // items per thread, gather / stage kernels
-constexpr int kCombineU = 2;  // items per thread, combine
+constexpr int kWaves = MOE_MOVE_WAVES;   // waves per block
+constexpr int kBlock = kWaves * kWave;
+constexpr int kGatherU = MOE_GATHER_U;    // wave-items per wave: gather
+constexpr int kStageU = MOE_STAGE_U;      // wave-items per wave: stage_a, stage_b
+constexpr int kCombineU = MOE_COMBINE_U;  // wave-items per wave: combine
 
-__device__ __forceinline__ void store_row_chunk(u32x4* p, u32x4 v) {
+// Rows are touched once per call: stream them past the caches (measured
+// faster on gfx950 for both the row reads and the row writes).
+template <typename V>
+__device__ __forceinline__ void store_chunk(V* p, V v) {
+#if MOE_NT_STORE
   __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+__device__ __forceinline__ u32x4 load_chunk(const u32x4* p) {
+#if MOE_NT_LOAD
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+// Token rows of x (dispatch source): plain loads measured faster here.
+__device__ __forceinline__ u32x4 load_x_chunk(const u32x4* p) {
+#if MOE_NT_LOAD_X
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+// Wave-item u of this wave: token t, chunk c of the lane, and whether the
+// item exists / the lane's chunk is inside the row.
+struct Item {
+  int t, c;
+  bool live, ok;
+};
+
+template <int U>
+__device__ __forceinline__ Item wave_item(const Dims& d, int items, int u) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int g = __builtin_amdgcn_readfirstlane((blockIdx.x * U + u) * kWaves + wave);
+  Item it;
+  it.live = g < items;
+  it.t = it.live ? g / d.segs : 0;
+  const int seg = g - it.t * d.segs;
+  it.c = seg * kWave + lane;
+  it.ok = it.live && it.c < d.chunks;
+  return it;
+}
+
+// Lane j (< k) writes the token's entry j of a per-slot plan array.
+template <int KMAX>
+__device__ __forceinline__ int lane_pick(const int (&v)[KMAX], int lane) {
+  int r = -1;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) r = lane == j ? v[j] : r;
+  return r;
 }
 
 template <int KMAX, int U>
-__global__ __launch_bounds__(kMoveBlock) void gather_kernel(const u32x4* __restrict__ x,
-                                                            u32x4* __restrict__ recv,
-                                                            const int32_t* __restrict__ slot_of,
-                                                            int k, int chunks, int items,
-                                                            uint32_t rows) {
-  const int first = blockIdx.x * (kMoveBlock * U) + threadIdx.x;
+__global__ __launch_bounds__(kBlock) void gather_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                        const u32x4* __restrict__ x,
+                                                        u32x4* __restrict__ recv, Work w) {
+  const int items = d.T * d.segs, lane = threadIdx.x % kWave;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  Item it[U];
   int slot[U][KMAX];
-  int col[U];
   u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int i = first + u * kMoveBlock;
-    const bool ok = i < items;
-    const int t = ok ? i / chunks : 0;
-    col[u] = i - t * chunks;
+    it[u] = wave_item<U>(d, items, u);
+    if (it[u].live) {
+      token_slots<KMAX>(d, w, idx, it[u].t, slot[u]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) slot[u][j] = (ok && j < k) ? slot_of[t * k + j] : -1;
-    if (ok) v[u] = x[i];
+      for (int j = 0; j < KMAX; ++j) slot[u][j] = -1;
+    }
+    if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
   }
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
+    // The first segment of a row publishes the token's slots.
+    if (it[u].live && it[u].c == lane && lane < d.k) {
+      const int s = lane_pick<KMAX>(slot[u], lane);
+      w.slot_of[(int64_t)it[u].t * d.k + lane] = s;
+      if ((uint32_t)s < rows) w.row_src[s] = it[u].t;
+    }
+    if (it[u].ok) {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if ((uint32_t)slot[u][j] < rows)
-        store_row_chunk(&recv[(int64_t)slot[u][j] * chunks + col[u]], v[u]);
+      for (int j = 0; j < KMAX; ++j)
+        if ((uint32_t)slot[u][j] < rows)
+          store_chunk(&recv[(int64_t)slot[u][j] * d.chunks + it[u].c], v[u]);
+    }
+  }
 }
 
-// Hop 1: one write per distinct destination node (a node's first slot holds
-// the staging row; later slots of the same node repeat it).
 template <int KMAX, int U>
-__global__ __launch_bounds__(kMoveBlock) void stage_a_kernel(const u32x4* __restrict__ x,
-                                                             u32x4* __restrict__ staging,
-                                                             const int32_t* __restrict__ stage_of,
-                                                             int k, int chunks, int items,
-                                                             uint32_t rows) {
-  const int first = blockIdx.x * (kMoveBlock * U) + threadIdx.x;
-  int row[U][KMAX];
-  int col[U];
+__global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                         const u32x4* __restrict__ x,
+                                                         u32x4* __restrict__ staging, Work w) {
+  const int items = d.T * d.segs, lane = threadIdx.x % kWave;
+  const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
+  Item it[U];
+  int slot[U][KMAX], p[U][KMAX];
+  uint32_t lead[U];
   u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int i = first + u * kMoveBlock;
-    const bool ok = i < items;
-    const int t = ok ? i / chunks : 0;
-    col[u] = i - t * chunks;
+    it[u] = wave_item<U>(d, items, u);
+    lead[u] = 0;
+    if (it[u].live) {
+      token_slots<KMAX>(d, w, idx, it[u].t, slot[u]);
+      token_stages<KMAX>(d, w, it[u].t, p[u], lead[u]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) row[u][j] = (ok && j < k) ? stage_of[t * k + j] : -1;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-#pragma unroll
-      for (int jj = 0; jj < j; ++jj)
-        if (row[u][jj] == row[u][j]) row[u][j] = -1;
-    if (ok) v[u] = x[i];
+      for (int j = 0; j < KMAX; ++j) slot[u][j] = p[u][j] = -1;
+    }
+    if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
   }
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
+    if (it[u].live && it[u].c == lane && lane < d.k) {
+      const int64_t at = (int64_t)it[u].t * d.k + lane;
+      const int s = lane_pick<KMAX>(slot[u], lane);
+      const int q = lane_pick<KMAX>(p[u], lane);
+      w.slot_of[at] = s;
+      if ((uint32_t)s < rows) w.row_src[s] = it[u].t;
+      w.stage_of[at] = q;
+      if (((lead[u] >> lane) & 1u) && (uint32_t)q < srows) w.stage_src[q] = it[u].t;
+    }
+    if (it[u].ok) {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if ((uint32_t)row[u][j] < rows)
-        store_row_chunk(&staging[(int64_t)row[u][j] * chunks + col[u]], v[u]);
+      for (int j = 0; j < KMAX; ++j)
+        if (((lead[u] >> j) & 1u) && (uint32_t)p[u][j] < srows)
+          store_chunk(&staging[(int64_t)p[u][j] * d.chunks + it[u].c], v[u]);
+    }
+  }
 }
 
-// Hop 2: staging row p (token stage_src[p]) goes to every slot of that token
-// whose staging row is p.  Rows at or past D (ctrl[1]) are unused.
+// Hop 2, one token per wave-item: each of the token's staging rows (one per
+// destination node) is read once and written to the token's slots on that
+// node.
 template <int KMAX, int U>
-__global__ __launch_bounds__(kMoveBlock) void stage_b_kernel(const u32x4* __restrict__ staging,
-                                                             u32x4* __restrict__ recv,
-                                                             const int32_t* __restrict__ stage_src,
-                                                             const int32_t* __restrict__ stage_of,
-                                                             const int32_t* __restrict__ slot_of,
-                                                             const int32_t* __restrict__ ctrl, int k,
-                                                             int chunks, int items_max, int T,
-                                                             uint32_t rows) {
-  const int items = min(items_max, ctrl[1] * chunks);
-  const int first = blockIdx.x * (kMoveBlock * U) + threadIdx.x;
-  int dst[U][KMAX];
-  int col[U];
-  u32x4 v[U];
+__global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __restrict__ staging,
+                                                         u32x4* __restrict__ recv, Work w) {
+  const int items = d.T * d.segs;
+  const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
+  Item it[U];
+  int slot[U][KMAX], p[U][KMAX];
+  u32x4 v[U][KMAX];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int i = first + u * kMoveBlock;
-    const bool ok = i < items;
-    const int p = ok ? i / chunks : 0;
-    col[u] = i - p * chunks;
-    int t = ok ? stage_src[p] : 0;
-    const bool tok = ok && (uint32_t)t < (uint32_t)T;
-    t = tok ? t : 0;
+    it[u] = wave_item<U>(d, items, u);
+    const int64_t at = (int64_t)it[u].t * d.k;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      dst[u][j] = -1;
-      if (tok && j < k && stage_of[t * k + j] == p) dst[u][j] = slot_of[t * k + j];
+      const bool has = it[u].live && j < d.k;
+      slot[u][j] = has ? w.slot_of[at + j] : -1;
+      p[u][j] = has ? w.stage_of[at + j] : -1;
     }
-    if (ok) v[u] = staging[i];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      bool first = (uint32_t)p[u][j] < srows;
+#pragma unroll
+      for (int jj = 0; jj < j; ++jj) first = first && p[u][jj] != p[u][j];
+      if (first && it[u].ok) v[u][j] = load_chunk(&staging[(int64_t)p[u][j] * d.chunks + it[u].c]);
+      if (!first) p[u][j] = p[u][j] < 0 ? -1 : -2 - p[u][j];  // later slot of a node: -2-row
+    }
   }
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
+    if (!it[u].ok) continue;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if ((uint32_t)dst[u][j] < rows)
-        store_row_chunk(&recv[(int64_t)dst[u][j] * chunks + col[u]], v[u]);
+    for (int j = 0; j < KMAX; ++j) {
+      if (p[u][j] < 0) continue;  // j is the first slot of its node: write all of the node's slots
+#pragma unroll
+      for (int jj = j; jj < KMAX; ++jj) {
+        const bool same = jj == j || p[u][jj] == -2 - p[u][j];
+        if (same && (uint32_t)slot[u][jj] < rows)
+          store_chunk(&recv[(int64_t)slot[u][jj] * d.chunks + it[u].c], v[u][j]);
+      }
+    }
+  }
 }
 
 // float -> bf16 bits, round to nearest even; NaN becomes a quiet NaN.
@@ -148,35 +252,34 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 template <int KMAX, int U, bool F32OUT>
-__global__ __launch_bounds__(kMoveBlock) void combine_kernel(const u32x4* __restrict__ y,
-                                                             const float* __restrict__ wts,
-                                                             const int32_t* __restrict__ slot_of,
-                                                             void* __restrict__ out, int k,
-                                                             int chunks, int items, uint32_t rows) {
-  const int first = blockIdx.x * (kMoveBlock * U) + threadIdx.x;
+__global__ __launch_bounds__(kBlock) void combine_kernel(Dims d, const u32x4* __restrict__ y,
+                                                         const float* __restrict__ wts,
+                                                         const int32_t* __restrict__ slot_of,
+                                                         void* __restrict__ out) {
+  const int items = d.T * d.segs;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  Item it[U];
   int slot[U][KMAX];
   float wj[U][KMAX];
   u32x4 v[U][KMAX];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int i = first + u * kMoveBlock;
-    const bool ok = i < items;
-    const int t = ok ? i / chunks : 0;
-    const int c = i - t * chunks;
+    it[u] = wave_item<U>(d, items, u);
+    const int64_t at = (int64_t)it[u].t * d.k;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      slot[u][j] = (ok && j < k) ? slot_of[t * k + j] : -1;
+      const bool has = it[u].live && j < d.k;
+      slot[u][j] = has ? slot_of[at + j] : -1;
       if ((uint32_t)slot[u][j] >= rows) slot[u][j] = -1;
-      wj[u][j] = (ok && j < k) ? wts[t * k + j] : 0.0f;
+      wj[u][j] = has ? wts[at + j] : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (slot[u][j] >= 0) v[u][j] = y[(int64_t)slot[u][j] * chunks + c];
+      if (slot[u][j] >= 0 && it[u].ok) v[u][j] = load_chunk(&y[(int64_t)slot[u][j] * d.chunks + it[u].c]);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int i = first + u * kMoveBlock;
-    if (i >= items) continue;
+    if (!it[u].ok) continue;
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
@@ -191,23 +294,24 @@ __global__ __launch_bounds__(kMoveBlock) void combine_kernel(const u32x4* __rest
         acc[2 * q + 1] = __builtin_fmaf(wj[u][j], hi, acc[2 * q + 1]);
       }
     }
+    const int64_t i = (int64_t)it[u].t * d.chunks + it[u].c;
     if constexpr (F32OUT) {
-      f32x4* o = reinterpret_cast<f32x4*>(out) + (int64_t)i * 2;
+      f32x4* o = reinterpret_cast<f32x4*>(out) + i * 2;
       const f32x4 a = {acc[0], acc[1], acc[2], acc[3]};
       const f32x4 b = {acc[4], acc[5], acc[6], acc[7]};
-      __builtin_nontemporal_store(a, o);
-      __builtin_nontemporal_store(b, o + 1);
+      store_chunk(o, a);
+      store_chunk(o + 1, b);
     } else {
       u32x4 r;
 #pragma unroll
       for (int q = 0; q < 4; ++q) r[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
-      store_row_chunk(reinterpret_cast<u32x4*>(out) + i, r);
+      store_chunk(reinterpret_cast<u32x4*>(out) + i, r);
     }
   }
 }
 
-inline int blocks_for(int64_t items, int per_thread) {
-  const int64_t per_block = (int64_t)kMoveBlock * per_thread;
+inline int blocks_for(const Dims& d, int per_wave) {
+  const int64_t items = (int64_t)d.T * d.segs, per_block = (int64_t)kWaves * per_wave;
   return (int)((items + per_block - 1) / per_block);
 }
 
@@ -221,26 +325,22 @@ hipError_t by_topk(int k, A... a) {
 
 template <int KMAX>
 struct GatherLaunch {
-  static hipError_t run(const Dims& d, const uint16_t* x, uint16_t* recv, const Work& w,
-                        hipStream_t s) {
-    const int items = d.T * d.chunks;
-    hipLaunchKernelGGL((gather_kernel<KMAX, kGatherU>), dim3(blocks_for(items, kGatherU)),
-                       dim3(kMoveBlock), 0, s, reinterpret_cast<const u32x4*>(x),
-                       reinterpret_cast<u32x4*>(recv), w.slot_of, d.k, d.chunks, items,
-                       (uint32_t)(d.T * d.k));
+  static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
+                        const Work& w, hipStream_t s) {
+    hipLaunchKernelGGL((gather_kernel<KMAX, kGatherU>), dim3(blocks_for(d, kGatherU)),
+                       dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
+                       reinterpret_cast<u32x4*>(recv), w);
     return hipGetLastError();
   }
 };
 
 template <int KMAX>
 struct StageALaunch {
-  static hipError_t run(const Dims& d, const uint16_t* x, uint16_t* staging, const Work& w,
-                        int64_t rows_max, hipStream_t s) {
-    const int items = d.T * d.chunks;
-    hipLaunchKernelGGL((stage_a_kernel<KMAX, kGatherU>), dim3(blocks_for(items, kGatherU)),
-                       dim3(kMoveBlock), 0, s, reinterpret_cast<const u32x4*>(x),
-                       reinterpret_cast<u32x4*>(staging), w.stage_of, d.k, d.chunks, items,
-                       (uint32_t)rows_max);
+  static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* staging,
+                        const Work& w, hipStream_t s) {
+    hipLaunchKernelGGL((stage_a_kernel<KMAX, kStageU>), dim3(blocks_for(d, kStageU)),
+                       dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
+                       reinterpret_cast<u32x4*>(staging), w);
     return hipGetLastError();
   }
 };
@@ -248,12 +348,10 @@ struct StageALaunch {
 template <int KMAX>
 struct StageBLaunch {
   static hipError_t run(const Dims& d, const uint16_t* staging, uint16_t* recv, const Work& w,
-                        int64_t rows_max, hipStream_t s) {
-    const int items = (int)(rows_max * d.chunks);
-    hipLaunchKernelGGL((stage_b_kernel<KMAX, kGatherU>), dim3(blocks_for(items, kGatherU)),
-                       dim3(kMoveBlock), 0, s, reinterpret_cast<const u32x4*>(staging),
-                       reinterpret_cast<u32x4*>(recv), w.stage_src, w.stage_of, w.slot_of, w.ctrl,
-                       d.k, d.chunks, items, d.T, (uint32_t)(d.T * d.k));
+                        hipStream_t s) {
+    hipLaunchKernelGGL((stage_b_kernel<KMAX, kStageU>), dim3(blocks_for(d, kStageU)),
+                       dim3(kBlock), 0, s, d, reinterpret_cast<const u32x4*>(staging),
+                       reinterpret_cast<u32x4*>(recv), w);
     return hipGetLastError();
   }
 };
@@ -262,38 +360,35 @@ template <int KMAX>
 struct CombineLaunch {
   static hipError_t run(const Dims& d, const uint16_t* y, const float* wts, void* out, bool f32,
                         const Work& w, hipStream_t s) {
-    const int items = d.T * d.chunks;
-    const dim3 grid(blocks_for(items, kCombineU));
+    const dim3 grid(blocks_for(d, kCombineU));
     if (f32)
-      hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, true>), grid, dim3(kMoveBlock), 0, s,
-                         reinterpret_cast<const u32x4*>(y), wts, w.slot_of, out, d.k, d.chunks,
-                         items, (uint32_t)(d.T * d.k));
+      hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, true>), grid, dim3(kBlock), 0, s, d,
+                         reinterpret_cast<const u32x4*>(y), wts, w.slot_of, out);
     else
-      hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, false>), grid, dim3(kMoveBlock), 0, s,
-                         reinterpret_cast<const u32x4*>(y), wts, w.slot_of, out, d.k, d.chunks,
-                         items, (uint32_t)(d.T * d.k));
+      hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, false>), grid, dim3(kBlock), 0, s, d,
+                         reinterpret_cast<const u32x4*>(y), wts, w.slot_of, out);
     return hipGetLastError();
   }
 };
 
 }  // namespace
 
-hipError_t launch_gather(const Dims& d, const uint16_t* x, uint16_t* recv, const Work& w,
-                         hipStream_t s) {
+hipError_t launch_gather(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
+                         const Work& w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
-  return by_topk<GatherLaunch>(d.k, d, x, recv, w, s);
+  return by_topk<GatherLaunch>(d.k, d, idx, x, recv, w, s);
 }
 
-hipError_t launch_stage_a(const Dims& d, const uint16_t* x, uint16_t* staging, const Work& w,
-                          int64_t staging_rows_max, hipStream_t s) {
+hipError_t launch_stage_a(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* staging,
+                          const Work& w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
-  return by_topk<StageALaunch>(d.k, d, x, staging, w, staging_rows_max, s);
+  return by_topk<StageALaunch>(d.k, d, idx, x, staging, w, s);
 }
 
 hipError_t launch_stage_b(const Dims& d, const uint16_t* staging, uint16_t* recv, const Work& w,
-                          int64_t staging_rows_max, hipStream_t s) {
+                          hipStream_t s) {
   if (d.T == 0) return hipSuccess;
-  return by_topk<StageBLaunch>(d.k, d, staging, recv, w, staging_rows_max, s);
+  return by_topk<StageBLaunch>(d.k, d, staging, recv, w, s);
 }
 
 hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* wts, void* out,

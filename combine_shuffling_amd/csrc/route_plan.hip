@@ -2,75 +2,37 @@
 // descriptors for the gather-send / scatter-recv shuffle (FUSCO article,
 // "core innovation": the sender's reads are driven by segment descriptors).
 //
-// Two launches, no atomics, no grid-wide wait, deterministic:
+// route_count  one block per tile of tokens (256 tokens per pass, 4 waves,
+//              lane = token).  Each wave builds, for every expert, the 64-bit
+//              ballot of its lanes routed to that expert: a lane holds k
+//              experts, so the ballots are assembled in LDS with 64-bit OR
+//              atomics (order-free, hence deterministic).  A slot's rank
+//              inside the tile is the popcount of its expert's ballot below
+//              the lane, plus the popcounts of the earlier waves' ballots and
+//              of the earlier passes.  The tile's per-expert counts go to HBM.
+// route_scan   one block loads the [tiles x experts] count matrix into LDS,
+//              sums columns, scans the expert totals and writes every
+//              (tile, expert) base row, the expert and rank offsets and the
+//              status.  (Back-to-back kernels on one stream start with no gap
+//              on this GPU, so the kernel boundary is the cheapest grid-wide
+//              wait: cheaper than a last-arriving-block ticket with its
+//              release / acquire fences.)
 //
-//  route_count   one block per tile of tokens (256 tokens per pass, 4 waves,
-//                lane = token).  Validates the tile's routing, and gives every
-//                slot (t, j) its rank among the earlier slots of the tile that
-//                name the same expert.  Ranks come from a wavefront
-//                ballot-match: for slot position q the wave takes one ballot
-//                per bit of the expert id, and every lane rebuilds from those
-//                ballots the mask of lanes whose q-th expert equals its own;
-//                OR-ing over q gives all lanes that name the expert, its
-//                popcount below the lane is the in-wave rank, and the lowest
-//                such lane publishes the wave's count in LDS.  Earlier waves'
-//                counts (and earlier passes') are added from LDS.  Writes the
-//                tile's per-expert counts and the in-tile ranks.
+// With node deduplication the same is done a second time over the keys
+// "forwarder rank of (token, node)" of the first slot of each distinct
+// destination node of a token, which orders staging rows by (forwarder,
+// token) (FUSCO article, "load balancing and cross-node deduplication": one
+// copy per destination node through a forwarding GPU).
 //
-//  route_assign  one block per tile again.  Each block sums the tile counts
-//                over all tiles and over the tiles before its own (at most 64
-//                tiles, so one batch of loads per thread), scans the totals
-//                into expert offsets in LDS, and turns every in-tile rank into
-//                a receive row: row = expert_off[e] + rows of e in earlier
-//                tiles + in-tile rank.  That is the stable (expert, token)
-//                order.  Block 0 also publishes counts, offsets and status.
-//
-// With node deduplication the same machinery runs a second time over the keys
-// "forwarder rank of (token, node)" for the first slot of each distinct node
-// of a token, giving staging rows ordered by (forwarder, token) (FUSCO
-// article, "load balancing and cross-node deduplication": one copy per
-// destination node through a forwarding GPU).
-//
-// Expert -> rank and token -> owner use the contiguous ceil/floor split of
-// TensorRT-LLM PR #13888 ("support non-divisible EP in MoE alltoall",
-// performance commit message), with base and remainder hoisted into the
-// kernel arguments and a single divide when the remainder is zero.
-#include "moe_internal.h"
+// A slot's receive row is then tile_base[tile][expert] + its in-tile rank:
+// the stable (expert, token) order.  The data-movement kernels that run next
+// finish slot_of / row_src (and stage_of / stage_src) on the fly; the
+// per-token route_assign kernel does the same when a consumer needs the plan
+// without a dispatch.
+#include "moe_device.h"
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ int split_part(int i, int base, int rem) {
-  if (rem == 0) return i / base;
-  const int cut = rem * (base + 1);
-  return i < cut ? i / (base + 1) : rem + (i - cut) / base;
-}
-
-// For every j, m[j] = lanes holding v[j] (of the calling lane) in any of
-// their k positions.  Values < 0 are absent and match nothing; the mask of
-// an absent v[j] is meaningless.  Must be called by the whole wave.
-template <int KMAX>
-__device__ __forceinline__ void wave_match(const int (&v)[KMAX], int k, int nbits,
-                                           uint64_t (&m)[KMAX]) {
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) m[j] = 0;
-#pragma unroll
-  for (int q = 0; q < KMAX; ++q) {
-    if (q < k) {
-      uint64_t acc[KMAX];
-      const uint64_t present = __ballot(v[q] >= 0);
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) acc[j] = present;
-      for (int b = 0; b < nbits; ++b) {
-        const uint64_t ones = __ballot((v[q] >> b) & 1);
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) acc[j] &= ((v[j] >> b) & 1) ? ones : ~ones;
-      }
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) m[j] |= acc[j];
-    }
-  }
-}
 
 // In-place exclusive scan of a[0..n) (n <= 4 * kPlanBlock) by the whole
 // block; returns the total.  s_wsum: kPlanWaves ints of LDS.
@@ -109,41 +71,75 @@ __device__ int block_exclusive_scan(int* a, int n, int* s_wsum) {
   return total;
 }
 
+// Scan of a [nblk, W] tile-major count matrix: column totals (to `totals` if
+// given), exclusive offsets of the columns (to off[0..W]), and the first row
+// of every (tile, column) (to base).  Leaves the offsets in s_tot; returns the
+// grand total.  Needs W * nblk <= kScanLdsInts.
+__device__ int scan_tiles(const int32_t* src, int32_t* base, int32_t* totals, int32_t* off, int W,
+                          int nblk, int* s_mat, int* s_tot, int* s_wsum) {
+  const int tid = threadIdx.x, n = W * nblk;
+#pragma unroll 8
+  for (int i = tid; i < n; i += kPlanBlock) s_mat[i] = src[i];
+  __syncthreads();
+  for (int c = tid; c < W; c += kPlanBlock) {
+    int s = 0;
+    for (int b = 0; b < nblk; ++b) s += s_mat[b * W + c];
+    s_tot[c] = s;
+    if (totals) totals[c] = s;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_tot, W, s_wsum);
+  for (int c = tid; c < W; c += kPlanBlock) {
+    int run = s_tot[c];
+    off[c] = run;
+    for (int b = 0; b < nblk; ++b) {
+      base[b * W + c] = run;
+      run += s_mat[b * W + c];
+    }
+  }
+  if (tid == 0) off[W] = total;
+  __syncthreads();
+  return total;
+}
+
 template <int KMAX>
 __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
                                                                  const int32_t* __restrict__ idx,
                                                                  Work w) {
-  __shared__ int s_wc[kPlanWaves * MOE_MAX_EXPERTS];   // per-wave expert counts
-  __shared__ int s_run[MOE_MAX_EXPERTS];               // tile counts so far
-  __shared__ int s_fwc[kPlanWaves * MOE_MAX_EXPERTS];  // per-wave forwarder counts (R <= E)
-  __shared__ int s_frun[MOE_MAX_EXPERTS];
+  __shared__ unsigned long long s_mask[kPlanWaves * MOE_MAX_EXPERTS];  // per-wave ballots; 32 KiB
+  __shared__ int s_run[MOE_MAX_EXPERTS];   // tile's slots per expert so far
+  __shared__ int s_frun[MOE_MAX_EXPERTS];  // tile's staging rows per forwarder so far (R <= E)
+  __shared__ int s_node[MOE_MAX_EXPERTS];  // destination node of each expert (dedup)
   __shared__ int s_bad;
 
   const int tid = threadIdx.x, wv = tid / kWave, lane = tid % kWave;
-  const uint64_t below = (1ull << lane) - 1ull;
+  const unsigned long long bit = 1ull << lane, below = bit - 1ull;
   const int E = d.E, R = d.R, k = d.k;
 
-  for (int i = tid; i < E; i += kPlanBlock) s_run[i] = 0;
+  for (int i = tid; i < E; i += kPlanBlock) {
+    s_run[i] = 0;
+    if (d.dedup) s_node[i] = split_part(i, d.ebase, d.erem) / d.G;
+  }
   if (d.dedup)
     for (int i = tid; i < R; i += kPlanBlock) s_frun[i] = 0;
   if (tid == 0) s_bad = 0;
+  __syncthreads();
 
   for (int pass = 0; pass < d.passes; ++pass) {
-    const int t = (blockIdx.x * d.passes + pass) * kPlanBlock + tid;
+    const int t = blockIdx.x * d.tile + pass * kPlanBlock + tid;
     const bool live = t < d.T;
-    for (int i = tid; i < kPlanWaves * E; i += kPlanBlock) s_wc[i] = 0;
-    if (d.dedup)
-      for (int i = tid; i < kPlanWaves * R; i += kPlanBlock) s_fwc[i] = 0;
+    const int64_t at = (int64_t)t * k;
+    for (int i = tid; i < kPlanWaves * E; i += kPlanBlock) s_mask[i] = 0;
 
-    // Load and validate: an id outside [0, E) or repeated in the row is
-    // dropped (the first occurrence of a repeat stays).
+    // An id outside [0, E) or repeated in the row is dropped (the first
+    // occurrence of a repeat stays) and flags the routing as bad.
     int e[KMAX];
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       int v = -1;
       if (live && j < k) {
-        v = idx[(int64_t)t * k + j];
+        v = idx[at + j];
         if (v < 0 || v >= E) {
           bad = true;
           v = -1;
@@ -157,76 +153,65 @@ __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
       }
       e[j] = v;
     }
-    __syncthreads();  // LDS zeroed; previous pass finished with it
-
-    uint64_t m[KMAX];
-    wave_match<KMAX>(e, k, d.ebits, m);
-    int lr[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      lr[j] = -1;
-      if (e[j] >= 0) {
-        lr[j] = __popcll(m[j] & below);
-        if (lr[j] == 0) s_wc[wv * E + e[j]] = __popcll(m[j]);
-      }
-    }
-
-    int f[KMAX], flr[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) f[j] = flr[j] = -1;
-    if (d.dedup) {
-      // Key of the first slot of each distinct destination node: the
-      // forwarder rank n*G + owner(t) % G.
-      const int g = live ? split_part(t, d.tbase, d.trem) % d.G : 0;
-      int nd[KMAX];
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) nd[j] = e[j] >= 0 ? split_part(e[j], d.ebase, d.erem) / d.G : -1;
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        bool first = nd[j] >= 0;
-#pragma unroll
-        for (int jj = 0; jj < j; ++jj) first = first && nd[jj] != nd[j];
-        if (first) f[j] = nd[j] * d.G + g;
-      }
-      wave_match<KMAX>(f, k, d.fbits, m);
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (f[j] >= 0) {
-          flr[j] = __popcll(m[j] & below);
-          if (flr[j] == 0) s_fwc[wv * R + f[j]] = __popcll(m[j]);
-        }
-      }
-    }
     if (bad) s_bad = 1;
     __syncthreads();
-
-    if (live) {
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {
-          int r = -1;
-          if (e[j] >= 0) {
-            r = s_run[e[j]] + lr[j];
-            for (int w2 = 0; w2 < wv; ++w2) r += s_wc[w2 * E + e[j]];
-          }
-          w.slot_of[(int64_t)t * k + j] = r;
-          if (d.dedup) {
-            int u = -1;
-            if (f[j] >= 0) {
-              u = s_frun[f[j]] + flr[j];
-              for (int w2 = 0; w2 < wv; ++w2) u += s_fwc[w2 * R + f[j]];
-            }
-            w.stage_of[(int64_t)t * k + j] = u;
-          }
+    for (int j = 0; j < KMAX; ++j)
+      if (e[j] >= 0) atomicOr(&s_mask[wv * E + e[j]], bit);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (live && j < k) {
+        int r = -1;
+        if (e[j] >= 0) {
+          r = s_run[e[j]] + __popcll(s_mask[wv * E + e[j]] & below);
+          for (int w2 = 0; w2 < wv; ++w2) r += __popcll(s_mask[w2 * E + e[j]]);
         }
+        w.lr[at + j] = r;
       }
     }
     __syncthreads();
     for (int i = tid; i < E; i += kPlanBlock)
-      s_run[i] += s_wc[i] + s_wc[E + i] + s_wc[2 * E + i] + s_wc[3 * E + i];
-    if (d.dedup)
+      s_run[i] += __popcll(s_mask[i]) + __popcll(s_mask[E + i]) + __popcll(s_mask[2 * E + i]) +
+                  __popcll(s_mask[3 * E + i]);
+
+    if (d.dedup) {
+      __syncthreads();
+      for (int i = tid; i < kPlanWaves * R; i += kPlanBlock) s_mask[i] = 0;
+      // Key of the first slot of each distinct destination node: forwarder
+      // rank n*G + owner(t) % G.  Later slots of the node point back to it.
+      const int g = live ? split_part(t, d.tbase, d.trem) % d.G : 0;
+      int nd[KMAX], key[KMAX];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        nd[j] = e[j] >= 0 ? s_node[e[j]] : -1;
+        key[j] = nd[j] >= 0 ? nd[j] * d.G + g : -1;
+#pragma unroll
+        for (int jj = j - 1; jj >= 0; --jj)
+          if (nd[j] >= 0 && nd[jj] == nd[j]) key[j] = -2 - jj;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (key[j] >= 0) atomicOr(&s_mask[wv * R + key[j]], bit);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (live && j < k) {
+          int r = -1;
+          if (key[j] >= 0) {
+            r = s_frun[key[j]] + __popcll(s_mask[wv * R + key[j]] & below);
+            for (int w2 = 0; w2 < wv; ++w2) r += __popcll(s_mask[w2 * R + key[j]]);
+          }
+          w.fkey[at + j] = key[j];
+          w.flr[at + j] = r;
+        }
+      }
+      __syncthreads();
       for (int i = tid; i < R; i += kPlanBlock)
-        s_frun[i] += s_fwc[i] + s_fwc[R + i] + s_fwc[2 * R + i] + s_fwc[3 * R + i];
+        s_frun[i] += __popcll(s_mask[i]) + __popcll(s_mask[R + i]) + __popcll(s_mask[2 * R + i]) +
+                     __popcll(s_mask[3 * R + i]);
+    }
     __syncthreads();
   }
 
@@ -236,117 +221,62 @@ __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
   if (tid == 0) w.tile_flags[blockIdx.x] = s_bad;
 }
 
-// Sum column `col` of a [nblk, width] tile-major matrix over all tiles and
-// over the tiles before `blk`.
-__device__ __forceinline__ void column_sums(const int32_t* __restrict__ m, int width, int col,
-                                            int nblk, int blk, int& total, int& before) {
-  int tot = 0, pre = 0;
-#pragma unroll 16
-  for (int b = 0; b < nblk; ++b) {
-    const int c = m[b * width + col];
-    tot += c;
-    pre += b < blk ? c : 0;
+// One block: scans the [tiles x experts] count matrix (and, with dedup, the
+// [tiles x forwarders] one) into base rows, offsets and the status.
+__global__ __launch_bounds__(kPlanBlock) void route_scan_kernel(Dims d, Work w) {
+  __shared__ int s_mat[kScanLdsInts];
+  __shared__ int s_tot[MOE_MAX_EXPERTS];
+  __shared__ int s_wsum[kPlanWaves];
+  const int tid = threadIdx.x, E = d.E, R = d.R;
+  const int rows = scan_tiles(w.tile_counts, w.tile_base, w.counts, w.expert_off, E, d.nblk, s_mat,
+                              s_tot, s_wsum);
+  for (int r = tid; r <= R; r += kPlanBlock) {
+    const int first = r * d.ebase + min(r, d.erem);  // first expert of rank r
+    w.rank_off[r] = first < E ? s_tot[first] : rows;
   }
-  total = tot;
-  before = pre;
+  int staged = 0;
+  if (d.dedup) {
+    __syncthreads();
+    staged = scan_tiles(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, R, d.nblk, s_mat,
+                        s_tot, s_wsum);
+  }
+  int bad = 0;
+  for (int b = tid; b < d.nblk; b += kPlanBlock) bad |= w.tile_flags[b];
+  bad = __syncthreads_or(bad);
+  if (tid == 0) {
+    w.ctrl[kCtrlStatus] = bad ? MOE_ERR_BAD_ROUTING : MOE_OK;
+    w.ctrl[kCtrlStaged] = staged;
+  }
 }
 
+// Finishes the plan one token per thread (slot_of, row_src; with dedup
+// stage_of, stage_src) for consumers that run without a dispatch.
 template <int KMAX>
 __global__ __launch_bounds__(kPlanBlock) void route_assign_kernel(Dims d,
                                                                   const int32_t* __restrict__ idx,
                                                                   Work w) {
-  __shared__ int s_off[MOE_MAX_EXPERTS];   // expert_off[e]
-  __shared__ int s_pre[MOE_MAX_EXPERTS];   // rows of e in earlier tiles
-  __shared__ int s_foff[MOE_MAX_EXPERTS];  // stage_off[f]
-  __shared__ int s_fpre[MOE_MAX_EXPERTS];
-  __shared__ int s_wsum[kPlanWaves];
-  __shared__ int s_bad;
-
-  const int tid = threadIdx.x, blk = blockIdx.x;
-  const int E = d.E, R = d.R, k = d.k;
-
-  for (int e = tid; e < E; e += kPlanBlock)
-    column_sums(w.tile_counts, E, e, d.nblk, blk, s_off[e], s_pre[e]);
-  if (d.dedup)
-    for (int f = tid; f < R; f += kPlanBlock)
-      column_sums(w.tile_fcounts, R, f, d.nblk, blk, s_foff[f], s_fpre[f]);
-  if (blk == 0 && tid == 0) {
-    int bad = 0;
-    for (int b = 0; b < d.nblk; ++b) bad |= w.tile_flags[b];
-    s_bad = bad;
-  }
-  __syncthreads();
-
-  if (blk == 0)
-    for (int e = tid; e < E; e += kPlanBlock) w.counts[e] = s_off[e];
-  __syncthreads();  // the scan rewrites s_off in place
-  const int rows = block_exclusive_scan(s_off, E, s_wsum);
-  int staged = 0;
-  if (d.dedup) staged = block_exclusive_scan(s_foff, R, s_wsum);
-
-  if (blk == 0) {
-    for (int e = tid; e < E; e += kPlanBlock) w.expert_off[e] = s_off[e];
-    for (int r = tid; r <= R; r += kPlanBlock) {
-      const int first = r * d.ebase + min(r, d.erem);  // first expert of rank r
-      w.rank_off[r] = first < E ? s_off[first] : rows;
-      if (d.dedup) w.stage_off[r] = r < R ? s_foff[r] : staged;
-    }
-    if (tid == 0) {
-      w.expert_off[E] = rows;
-      w.ctrl[0] = s_bad ? MOE_ERR_BAD_ROUTING : MOE_OK;
-      w.ctrl[1] = staged;
+  const int t = blockIdx.x * kPlanBlock + threadIdx.x;
+  if (t >= d.T) return;
+  const int64_t at = (int64_t)t * d.k;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  int slot[KMAX];
+  token_slots<KMAX>(d, w, idx, t, slot);
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < d.k) {
+      w.slot_of[at + j] = slot[j];
+      if ((uint32_t)slot[j] < rows) w.row_src[slot[j]] = t;
     }
   }
-
-  for (int pass = 0; pass < d.passes; ++pass) {
-    const int t = (blk * d.passes + pass) * kPlanBlock + tid;
-    if (t >= d.T) continue;
-    const int64_t at = (int64_t)t * k;
-    int e[KMAX], lr[KMAX];
+  if (d.dedup) {
+    int p[KMAX];
+    uint32_t lead;
+    token_stages<KMAX>(d, w, t, p, lead);
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      lr[j] = j < k ? w.slot_of[at + j] : -1;
-      e[j] = lr[j] >= 0 ? idx[at + j] : -1;
-    }
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j < k) {
-        int row = -1;
-        if (lr[j] >= 0) {
-          row = s_off[e[j]] + s_pre[e[j]] + lr[j];
-          if ((uint32_t)row < (uint32_t)(d.T * k)) w.row_src[row] = t;
-        }
-        w.slot_of[at + j] = row;
-      }
-    }
-    if (d.dedup) {
-      int nd[KMAX], p[KMAX];
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        nd[j] = e[j] >= 0 ? split_part(e[j], d.ebase, d.erem) / d.G : -1;
-        p[j] = -1;
-      }
-      const int g = split_part(t, d.tbase, d.trem) % d.G;
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {
-          const int u = w.stage_of[at + j];  // in-tile rank, set on a node's first slot
-          if (u >= 0) {
-            const int f = nd[j] * d.G + g;
-            p[j] = s_foff[f] + s_fpre[f] + u;
-            if ((uint32_t)p[j] < (uint32_t)d.smax) w.stage_src[p[j]] = t;
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {
-          int q = p[j];
-#pragma unroll
-          for (int jj = 0; jj < j; ++jj)
-            if (q < 0 && nd[j] >= 0 && nd[jj] == nd[j] && p[jj] >= 0) q = p[jj];
-          w.stage_of[at + j] = q;
-        }
+      if (j < d.k) {
+        w.stage_of[at + j] = p[j];
+        if (((lead >> j) & 1u) && (uint32_t)p[j] < (uint32_t)d.smax) w.stage_src[p[j]] = t;
       }
     }
   }
@@ -403,7 +333,9 @@ struct CountLaunch {
 template <int KMAX>
 struct AssignLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
-    hipLaunchKernelGGL(route_assign_kernel<KMAX>, dim3(d.nblk), dim3(kPlanBlock), 0, s, d, idx, w);
+    const int blocks = (d.T + kPlanBlock - 1) / kPlanBlock;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(route_assign_kernel<KMAX>, dim3(blocks), dim3(kPlanBlock), 0, s, d, idx, w);
     return hipGetLastError();
   }
 };
@@ -421,7 +353,10 @@ struct TrafficLaunch {
 }  // namespace
 
 hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
-  return by_topk<CountLaunch>(d.k, d, idx, w, s);
+  const hipError_t e = by_topk<CountLaunch>(d.k, d, idx, w, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kPlanBlock), 0, s, d, w);
+  return hipGetLastError();
 }
 
 hipError_t launch_route_assign(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {

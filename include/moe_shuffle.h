@@ -139,9 +139,11 @@ int64_t moe_plan_staging_rows_max(const moe_plan* plan);  /* T*min(k, N) with de
 /* Route plan: validates routing, builds the per-expert histogram, its
  * exclusive scan and the segment descriptors (and, with dedup, the per-
  * forwarder staging descriptors).  topk_idx: device [T, k] int32.
- * workspace: device, moe_plan_workspace_bytes(plan) bytes.  Asynchronous.
- * The first route into a given workspace address also initialises its
- * control words.  Errors: INVALID_ARGUMENT, HIP. */
+ * workspace: device, moe_plan_workspace_bytes(plan) bytes, contents need
+ * no initialisation.  Asynchronous.  The slot arrays (slot_of, row_src and
+ * the staging ones) are finished by the next moe_dispatch, or by the next
+ * moe_combine / moe_plan_read if no dispatch comes first.
+ * Errors: INVALID_ARGUMENT, HIP. */
 moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspace, void* stream);
 
 /* Dispatch: recv[slot_of[t, j]] = x[t] for every valid slot.  x: device
@@ -149,7 +151,7 @@ moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspa
  * [staging_rows_max, H] bf16 when the plan has MOE_FLAG_NODE_DEDUP, else
  * ignored (may be NULL).  Asynchronous.
  * Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
-moe_status moe_dispatch(const moe_plan* plan, const uint16_t* x, uint16_t* recv, uint16_t* staging,
+moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint16_t* staging,
                         void* stream);
 
 /* Combine: out[t] = sum_{j=0..k-1} topk_w[t, j] * y[slot_of[t, j]], each term
@@ -157,14 +159,14 @@ moe_status moe_dispatch(const moe_plan* plan, const uint16_t* x, uint16_t* recv,
  * to bf16 (nearest even) or stored as float32.  y: device [T*k, H] bf16 in
  * the receive layout; topk_w: device [T, k] float32; out: device [T, H] of
  * out_dtype.  Asynchronous.  Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
-moe_status moe_combine(const moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
+moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
                        int32_t out_dtype, void* stream);
 
 /* Copies one plan item to host memory (synchronises the stream).  bytes must
  * be at least the item's size (see moe_item).  The traffic matrices
  * (SEND_ROWS, SEND_COPIES, NODE_COPIES) are computed on demand by a small
  * kernel from the workspace.  Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
-moe_status moe_plan_read(const moe_plan* plan, int32_t item, void* host_dst, size_t bytes,
+moe_status moe_plan_read(moe_plan* plan, int32_t item, void* host_dst, size_t bytes,
                          void* stream);
 
 /* Static text for a status code. */

@@ -200,3 +200,20 @@ def test_bad_routing_is_flagged_and_memory_safe(dev):
     good = gen.make_batch(gen.custom(1500, 64, 16, 4, 4, 2, seed=2))
     run = GpuRun(good, dev).route()
     assert run.plan.status() == 0
+
+
+def test_plan_reads_and_combine_without_dispatch(dev):
+    # With no dispatch since the route, plan reads and combine finish the plan
+    # themselves (one thread per token).
+    batch = gen.make_batch(gen.custom(2500, 64, 40, 6, 8, 2, seed=4))
+    p = oracle.route_plan(batch.topk_idx, 40, 8, 2)
+    y = oracle.dispatch(batch.x, p)
+    for dedup in (False, True):
+        run = GpuRun(batch, dev, node_dedup=dedup).route()
+        check_plan(run, p)
+        out = run.combine(y=to_dev(y, dev), out_dtype=torch.float32)
+        check_combine(out.cpu().numpy(), y, batch.topk_w, p["slot_of"], True, "no-dispatch")
+        # combine straight after a fresh route, no reads in between
+        run.route()
+        out = run.combine(y=to_dev(y, dev))
+        check_combine(bits(out), y, batch.topk_w, p["slot_of"], False, "no-dispatch-bf16")
