@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="olmoe",
                     help="tiny | olmoe | qwen3 | dsv3 | nondiv (default: olmoe, the OLMoE-like prefill)")
+    ap.add_argument("--payload", choices=("bf16", "fp8"), default="bf16",
+                    help="row payload: bf16, or fp8 (OCP E4M3 codes + one float32 scale per "
+                         "128-element block; single-hop workloads only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
@@ -180,38 +183,48 @@ def recorded_traffic(workload, kernel):
     return None
 
 
-def algorithmic_bytes(wl, D):
+def algorithmic_bytes(wl, D, payload="bf16"):
     row = 2 * wl.hidden
     T, k = wl.num_tokens, wl.top_k
+    if payload == "fp8":
+        # token rows are read (and combine results written) as bf16; the k
+        # receive rows carry one byte per element plus a float32 per 128 elements
+        row8 = wl.hidden + 4 * ((wl.hidden + 127) // 128)
+        return T * row + T * k * row8, T * k * row8 + T * row
     disp = (T + T * k) * row if not wl.node_dedup else (T + 2 * D + T * k) * row
     comb = (T * k + T) * row
     return disp, comb
 
 
-def cpu_baseline(batch, seconds):
+def cpu_baseline(batch, seconds, payload="bf16"):
     """The oracle (numpy, as it stands) timed on this host on the same batch."""
     import oracle
+    from oracle import fp8 as ofp8
 
     wl = batch.workload
     reps, t0 = 0, time.perf_counter()
     D = 0
     while True:
         p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node)
-        if wl.node_dedup:
-            recv = oracle.dedup_stage_b(oracle.dedup_stage_a(batch.x, p), p)
+        if payload == "fp8":
+            codes, exps = ofp8.dispatch_fp8(batch.x, p)
+            ofp8.combine_fp8(codes, exps, batch.topk_w, p)
         else:
-            recv = oracle.dispatch(batch.x, p)
-        oracle.combine(recv, batch.topk_w, p)
+            if wl.node_dedup:
+                recv = oracle.dedup_stage_b(oracle.dedup_stage_a(batch.x, p), p)
+            else:
+                recv = oracle.dispatch(batch.x, p)
+            oracle.combine(recv, batch.topk_w, p)
         D = p["num_staged"]
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    disp, comb = algorithmic_bytes(wl, D)
+    disp, comb = algorithmic_bytes(wl, D, payload)
     return {"value": round((disp + comb) * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{reps} full passes of the {wl.name} batch (route plan, dispatch, "
-                      f"combine in float64) in {el:.1f} s on 1 thread; "
+            "sample": f"{reps} full passes of the {wl.name} batch ({payload} payload: route "
+                      f"plan, dispatch, combine in float64) in {el:.1f} s on 1 thread; "
                       f"os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"}
 
 
@@ -240,6 +253,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     wl = gen.get(args.workload)
+    fp8 = args.payload == "fp8"
+    if fp8 and wl.node_dedup:
+        print("the fp8 payload is single-hop only; the workload uses node deduplication",
+              file=sys.stderr)
+        sys.exit(2)
     batch = gen.make_batch(wl)
     T, H, k = wl.num_tokens, wl.hidden, wl.top_k
 
@@ -249,7 +267,8 @@ def main():
 
     probe = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup)
     set_bytes = (x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4 + probe.workspace_bytes
-                 + probe.recv_rows * H * 2 + probe.staging_rows_max * H * 2 + T * H * 2)
+                 + probe.recv_rows * H * (1 if fp8 else 2) + probe.staging_rows_max * H * 2
+                 + T * H * 2)
     n_sets = args.sets or max(2, math.ceil((2 << 30) / set_bytes))
     sets = []
     for _ in range(n_sets):
@@ -259,18 +278,34 @@ def main():
                  staging=(torch.empty((plan.staging_rows_max, H), dtype=torch.int16, device=dev)
                           if wl.node_dedup else None),
                  out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+        if fp8:
+            s["recv"] = torch.empty((plan.recv_rows, H), dtype=torch.uint8, device=dev)
+            s["scale"] = torch.empty((plan.recv_rows, plan.scale_blocks), dtype=torch.float32,
+                                     device=dev)
         sets.append(s)
+
+    def do_dispatch(s):
+        if fp8:
+            s["plan"].dispatch_fp8(s["x"], s["recv"], s["scale"])
+        else:
+            s["plan"].dispatch(s["x"], s["recv"], s["staging"])
+
+    def do_combine(s):
+        if fp8:
+            s["plan"].combine_fp8(s["recv"], s["scale"], s["w"], s["out"])
+        else:
+            s["plan"].combine(s["recv"], s["w"], s["out"])
 
     def step(s):
         s["plan"].route(s["idx"])
-        s["plan"].dispatch(s["x"], s["recv"], s["staging"])
-        s["plan"].combine(s["recv"], s["w"], s["out"])
+        do_dispatch(s)
+        do_combine(s)
 
     for i in range(args.warmup):
         step(sets[i % n_sets])
     torch.cuda.synchronize()
     D = int(sets[0]["plan"].read("num_staged")[0]) if wl.node_dedup else 0
-    disp_b, comb_b = algorithmic_bytes(wl, D)
+    disp_b, comb_b = algorithmic_bytes(wl, D, args.payload)
 
     # Timed region: K steps, nothing else on the stream.
     torch.cuda.synchronize()
@@ -295,16 +330,17 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    disp_ms = burst(lambda s: s["plan"].dispatch(s["x"], s["recv"], s["staging"]))
-    comb_ms = burst(lambda s: s["plan"].combine(s["recv"], s["w"], s["out"]))
+    disp_ms = burst(do_dispatch)
+    comb_ms = burst(do_combine)
     disp_gbs = disp_b / (disp_ms * 1e-3) / 1e9
     comb_gbs = comb_b / (comb_ms * 1e-3) / 1e9
     if wl.node_dedup:
         # dispatch is two launches here; the dominant single launch timed is combine
         dom = ("combine_kernel", comb_b, comb_ms, comb_gbs)
     else:
-        dom = max([("gather_kernel", disp_b, disp_ms, disp_gbs),
-                   ("combine_kernel", comb_b, comb_ms, comb_gbs)], key=lambda d: d[2])
+        sfx = "_fp8" if fp8 else ""
+        dom = max([(f"gather{sfx}_kernel", disp_b, disp_ms, disp_gbs),
+                   (f"combine{sfx}_kernel", comb_b, comb_ms, comb_gbs)], key=lambda d: d[2])
 
     result = {
         "metric": METRIC,
@@ -317,11 +353,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.payload,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "E": wl.num_experts, "k": k,
                    "R": wl.num_ranks, "G": wl.ranks_per_node, "node_dedup": wl.node_dedup,
-                   "staging_rows": D, "seed": wl.seed, "buffer_sets": n_sets},
+                   "staging_rows": D, "seed": wl.seed, "buffer_sets": n_sets,
+                   "payload": args.payload},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "bytes_per_step": disp_b + comb_b,
         "phases": {"dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),
@@ -335,7 +372,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, args.payload)
     print(json.dumps(result), flush=True)
 
 

@@ -21,7 +21,8 @@ import torch
 from . import _abi
 from ._abi import MoeError, ITEM  # noqa: F401
 
-__all__ = ["Plan", "MoeError", "expert_partition", "route_plan", "dispatch", "combine"]
+__all__ = ["Plan", "MoeError", "expert_partition", "route_plan", "dispatch", "combine",
+           "dispatch_fp8", "combine_fp8"]
 
 
 def expert_partition(num_experts: int, num_ranks: int) -> list[int]:
@@ -75,6 +76,7 @@ class Plan:
         self.workspace_bytes = int(self._lib.moe_plan_workspace_bytes(h))
         self.recv_rows = int(self._lib.moe_plan_recv_rows(h))
         self.staging_rows_max = int(self._lib.moe_plan_staging_rows_max(h))
+        self.scale_blocks = int(self._lib.moe_plan_scale_blocks(h))
         self.workspace = None
         self.topk_idx = None
         self.device = None
@@ -136,6 +138,46 @@ class Plan:
                                          _stream_handle(dev, stream)), "moe_combine")
         return out
 
+    # -- moe_dispatch_fp8
+    def dispatch_fp8(self, x: torch.Tensor, recv8: torch.Tensor | None = None,
+                     recv_scale: torch.Tensor | None = None, stream=None):
+        """fp8 payload: returns (codes uint8 [T*k, H], block scales float32 [T*k, nb])."""
+        dev = self.device
+        if dev is None:
+            raise MoeError(_abi.ERR_PLAN_NOT_ROUTED, "dispatch_fp8")
+        _need(x, (self.T, self.H), _BF16_LIKE, "x", dev)
+        if recv8 is None:
+            recv8 = torch.empty((self.recv_rows, self.H), dtype=torch.uint8, device=dev)
+        if recv_scale is None:
+            recv_scale = torch.empty((self.recv_rows, self.scale_blocks), dtype=torch.float32,
+                                     device=dev)
+        _need(recv8, (self.recv_rows, self.H), (torch.uint8,), "recv8", dev)
+        _need(recv_scale, (self.recv_rows, self.scale_blocks), (torch.float32,), "recv_scale", dev)
+        _abi.check(self._lib.moe_dispatch_fp8(self._h, _ptr(x), _ptr(recv8), _ptr(recv_scale),
+                                              _stream_handle(dev, stream)), "moe_dispatch_fp8")
+        return recv8, recv_scale
+
+    # -- moe_combine_fp8
+    def combine_fp8(self, y8: torch.Tensor, y_scale: torch.Tensor, topk_w: torch.Tensor,
+                    out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+                    stream=None) -> torch.Tensor:
+        dev = self.device
+        if dev is None:
+            raise MoeError(_abi.ERR_PLAN_NOT_ROUTED, "combine_fp8")
+        _need(y8, (self.recv_rows, self.H), (torch.uint8,), "y8", dev)
+        _need(y_scale, (self.recv_rows, self.scale_blocks), (torch.float32,), "y_scale", dev)
+        _need(topk_w, (self.T, self.k), (torch.float32,), "topk_w", dev)
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+        if out is None:
+            out = torch.empty((self.T, self.H), dtype=out_dtype, device=dev)
+        _need(out, (self.T, self.H), (out_dtype,), "out", dev)
+        code = _abi.OUT_F32 if out_dtype == torch.float32 else _abi.OUT_BF16
+        _abi.check(self._lib.moe_combine_fp8(self._h, _ptr(y8), _ptr(y_scale), _ptr(topk_w),
+                                             _ptr(out), code, _stream_handle(dev, stream)),
+                   "moe_combine_fp8")
+        return out
+
     # -- moe_plan_read
     def read(self, item: str, stream=None) -> np.ndarray:
         n = {"status": 1, "num_staged": 1, "counts": self.E, "expert_offsets": self.E + 1,
@@ -174,3 +216,14 @@ def combine(plan: Plan, y: torch.Tensor, topk_w: torch.Tensor, out=None,
             out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
     """moe_combine: returns out [T, H] (bf16 or float32)."""
     return plan.combine(y, topk_w, out, out_dtype, stream)
+
+
+def dispatch_fp8(plan: Plan, x: torch.Tensor, recv8=None, recv_scale=None, stream=None):
+    """moe_dispatch_fp8: returns (codes [T*k, H] uint8, block scales [T*k, nb] float32)."""
+    return plan.dispatch_fp8(x, recv8, recv_scale, stream)
+
+
+def combine_fp8(plan: Plan, y8: torch.Tensor, y_scale: torch.Tensor, topk_w: torch.Tensor,
+                out=None, out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """moe_combine_fp8: returns out [T, H] (bf16 or float32)."""
+    return plan.combine_fp8(y8, y_scale, topk_w, out, out_dtype, stream)

@@ -48,7 +48,8 @@ class MoeConfig(ctypes.Structure):
 EXPORTS = (
     "moe_expert_partition", "moe_plan_create", "moe_plan_destroy", "moe_plan_workspace_bytes",
     "moe_plan_recv_rows", "moe_plan_staging_rows_max", "moe_route_plan", "moe_dispatch",
-    "moe_combine", "moe_plan_read", "moe_status_str",
+    "moe_combine", "moe_plan_read", "moe_status_str", "moe_plan_scale_blocks",
+    "moe_dispatch_fp8", "moe_combine_fp8",
 )
 
 
@@ -91,6 +92,12 @@ def lib() -> ctypes.CDLL:
     L.moe_combine.restype = i32
     L.moe_plan_read.argtypes = [vp, i32, vp, sz, vp]
     L.moe_plan_read.restype = i32
+    L.moe_plan_scale_blocks.argtypes = [vp]
+    L.moe_plan_scale_blocks.restype = i64
+    L.moe_dispatch_fp8.argtypes = [vp, vp, vp, vp, vp]
+    L.moe_dispatch_fp8.restype = i32
+    L.moe_combine_fp8.argtypes = [vp, vp, vp, vp, vp, i32, vp]
+    L.moe_combine_fp8.restype = i32
     L.moe_status_str.argtypes = [i32]
     L.moe_status_str.restype = ctypes.c_char_p
     _lib = L

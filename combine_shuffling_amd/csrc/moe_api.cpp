@@ -250,6 +250,43 @@ moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, v
       moe::launch_combine(plan->d, y, topk_w, out, out_dtype == MOE_OUT_F32, plan->work, s));
 }
 
+int64_t moe_plan_scale_blocks(const moe_plan* plan) {
+  return plan ? ((int64_t)plan->d.H + 127) / 128 : 0;
+}
+
+moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, float* recv_scale,
+                            void* stream) {
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
+  if (plan->d.dedup) return MOE_ERR_UNSUPPORTED;
+  if (plan->d.T == 0) return MOE_OK;
+  if (!x || !recv8 || !recv_scale || !moe::aligned(x, 16) || !moe::aligned(recv8, 8) ||
+      !moe::aligned(recv_scale, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (moe::launch_gather_fp8(plan->d, plan->idx, x, recv8, recv_scale, plan->work, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  plan->assigned = true;
+  return MOE_OK;
+}
+
+moe_status moe_combine_fp8(moe_plan* plan, const uint8_t* y8, const float* y_scale,
+                           const float* topk_w, void* out, int32_t out_dtype, void* stream) {
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->d.T == 0) return MOE_OK;
+  if (!y8 || !y_scale || !topk_w || !out || !moe::aligned(y8, 8) || !moe::aligned(y_scale, 4) ||
+      !moe::aligned(topk_w, 4) || !moe::aligned(out, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_status st = moe::ensure_assigned(plan, s);
+  if (st != MOE_OK) return st;
+  return moe::from_hip(moe::launch_combine_fp8(plan->d, y8, y_scale, topk_w, out,
+                                               out_dtype == MOE_OUT_F32, plan->work, s));
+}
+
 moe_status moe_plan_read(moe_plan* plan, int32_t item, void* host_dst, size_t bytes,
                          void* stream) {
   if (!plan || !host_dst) return MOE_ERR_INVALID_ARGUMENT;

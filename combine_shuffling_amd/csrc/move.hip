@@ -310,6 +310,172 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(Dims d, const u32x4* __
   }
 }
 
+// ---- fp8 payload -----------------------------------------------------------
+// OCP E4M3 codes; each row is cut into blocks of 128 elements (16 lanes x 8),
+// each block scaled by the smallest power of two 2^e with amax <= 448 * 2^e.
+// Scaling by a power of two is exact, so the only rounding is the code
+// choice: the gfx950 conversion instruction, round to nearest even.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kFp8BlockChunks = 16;  // 16-byte bf16 chunks per scale block
+
+__device__ __forceinline__ int fp8_block_exp(float amax) {
+  if (!(amax > 0.0f) || amax > 3.0e38f) return 0;
+  int p;
+  const float m = frexpf(amax, &p);  // amax = m * 2^p, m in [0.5, 1)
+  const int e = p - 9 + (m > 0.875f ? 1 : 0);
+  return min(max(e, -126), 127);
+}
+
+__device__ __forceinline__ void unpack_bf16(u32x4 v, float (&f)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __uint_as_float(v[q] << 16);
+    f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
+  }
+}
+
+// 8 floats (already scaled) -> 8 E4M3 codes, element i in byte i.
+__device__ __forceinline__ u32x2 encode_e4m3x8(const float (&f)[8]) {
+  u32x2 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * h], f[4 * h + 1], 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * h + 2], f[4 * h + 3], word, true);
+    r[h] = (uint32_t)word;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void decode_e4m3x8(u32x2 c, float (&f)[8]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], true);
+    f[4 * h] = lo[0];
+    f[4 * h + 1] = lo[1];
+    f[4 * h + 2] = hi[0];
+    f[4 * h + 3] = hi[1];
+  }
+}
+
+// Dispatch with an fp8 payload: each token row is read once, quantized once
+// (block amax by a 16-lane reduction) and its codes and block scales are
+// written to the token's k receive rows.
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                            const u32x4* __restrict__ x,
+                                                            u32x2* __restrict__ recv8,
+                                                            float* __restrict__ rscale, Work w) {
+  const int items = d.T * d.segs, lane = threadIdx.x % kWave;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
+  const Item it = wave_item<1>(d, items, 0);
+  int slot[KMAX];
+  if (it.live) {
+    token_slots<KMAX>(d, w, idx, it.t, slot);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) slot[j] = -1;
+  }
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (it.ok) v = load_x_chunk(&x[(int64_t)it.t * d.chunks + it.c]);
+  float f[8];
+  unpack_bf16(v, f);
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(f[q]));
+#pragma unroll
+  for (int o = kFp8BlockChunks / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kFp8BlockChunks));
+  const int e = fp8_block_exp(amax);
+  const float inv = ldexpf(1.0f, -e);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) f[q] *= inv;
+  const u32x2 code = encode_e4m3x8(f);
+  const float scale = ldexpf(1.0f, e);
+  const bool scale_lane = (lane % kFp8BlockChunks) == 0;
+  const int blk = it.c / kFp8BlockChunks;
+
+  if (it.live && it.c == lane && lane < d.k) {
+    const int s = lane_pick<KMAX>(slot, lane);
+    w.slot_of[(int64_t)it.t * d.k + lane] = s;
+    if ((uint32_t)s < rows) w.row_src[s] = it.t;
+  }
+  if (it.ok) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if ((uint32_t)slot[j] < rows) {
+        store_chunk(&recv8[(int64_t)slot[j] * d.chunks + it.c], code);
+        if (scale_lane) rscale[(int64_t)slot[j] * nb + blk] = scale;
+      }
+    }
+  }
+}
+
+// Combine of an fp8 payload: codes decoded and scaled (exact), then the same
+// fp32 fused multiply-add chain as the bf16 combine.
+template <int KMAX, int U, bool F32OUT>
+__global__ __launch_bounds__(kBlock) void combine_fp8_kernel(Dims d, const u32x2* __restrict__ y8,
+                                                             const float* __restrict__ yscale,
+                                                             const float* __restrict__ wts,
+                                                             const int32_t* __restrict__ slot_of,
+                                                             void* __restrict__ out) {
+  const int items = d.T * d.segs;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
+  Item it[U];
+  int slot[U][KMAX];
+  float wj[U][KMAX], sc[U][KMAX];
+  u32x2 v[U][KMAX];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    it[u] = wave_item<U>(d, items, u);
+    const int64_t at = (int64_t)it[u].t * d.k;
+    const int blk = it[u].c / kFp8BlockChunks;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const bool has = it[u].live && j < d.k;
+      slot[u][j] = has ? slot_of[at + j] : -1;
+      if ((uint32_t)slot[u][j] >= rows) slot[u][j] = -1;
+      wj[u][j] = has ? wts[at + j] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (slot[u][j] >= 0 && it[u].ok) {
+        v[u][j] = __builtin_nontemporal_load(&y8[(int64_t)slot[u][j] * d.chunks + it[u].c]);
+        sc[u][j] = yscale[(int64_t)slot[u][j] * nb + blk];
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!it[u].ok) continue;
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (slot[u][j] < 0) continue;
+      float f[8];
+      decode_e4m3x8(v[u][j], f);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj[u][j], f[q] * sc[u][j], acc[q]);
+    }
+    const int64_t i = (int64_t)it[u].t * d.chunks + it[u].c;
+    if constexpr (F32OUT) {
+      f32x4* o = reinterpret_cast<f32x4*>(out) + i * 2;
+      const f32x4 a = {acc[0], acc[1], acc[2], acc[3]};
+      const f32x4 b = {acc[4], acc[5], acc[6], acc[7]};
+      store_chunk(o, a);
+      store_chunk(o + 1, b);
+    } else {
+      u32x4 r;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
+      store_chunk(reinterpret_cast<u32x4*>(out) + i, r);
+    }
+  }
+}
+
 inline int blocks_for(const Dims& d, int per_wave) {
   const int64_t items = (int64_t)d.T * d.segs, per_block = (int64_t)kWaves * per_wave;
   return (int)((items + per_block - 1) / per_block);
@@ -371,7 +537,47 @@ struct CombineLaunch {
   }
 };
 
+template <int KMAX>
+struct GatherFp8Launch {
+  static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
+                        float* rscale, const Work& w, hipStream_t s) {
+    hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), dim3(blocks_for(d, 1)), dim3(kBlock), 0, s, d,
+                       idx, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x2*>(recv8),
+                       rscale, w);
+    return hipGetLastError();
+  }
+};
+
+template <int KMAX>
+struct CombineFp8Launch {
+  static hipError_t run(const Dims& d, const uint8_t* y8, const float* yscale, const float* wts,
+                        void* out, bool f32, const Work& w, hipStream_t s) {
+    const dim3 grid(blocks_for(d, kCombineU));
+    const u32x2* y = reinterpret_cast<const u32x2*>(y8);
+    if (f32)
+      hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombineU, true>), grid, dim3(kBlock), 0, s, d,
+                         y, yscale, wts, w.slot_of, out);
+    else
+      hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombineU, false>), grid, dim3(kBlock), 0, s, d,
+                         y, yscale, wts, w.slot_of, out);
+    return hipGetLastError();
+  }
+};
+
 }  // namespace
+
+hipError_t launch_gather_fp8(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
+                             float* rscale, const Work& w, hipStream_t s) {
+  if (d.T == 0) return hipSuccess;
+  return by_topk<GatherFp8Launch>(d.k, d, idx, x, recv8, rscale, w, s);
+}
+
+hipError_t launch_combine_fp8(const Dims& d, const uint8_t* y8, const float* yscale,
+                              const float* wts, void* out, bool out_f32, const Work& w,
+                              hipStream_t s) {
+  if (d.T == 0) return hipSuccess;
+  return by_topk<CombineFp8Launch>(d.k, d, y8, yscale, wts, out, out_f32, w, s);
+}
 
 hipError_t launch_gather(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
                          const Work& w, hipStream_t s) {

@@ -162,6 +162,35 @@ moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint1
 moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
                        int32_t out_dtype, void* stream);
 
+/* ---- fp8 payload ----------------------------------------------------------
+ * Low-precision payload for dispatch and combine (TensorRT-LLM PR #13888,
+ * opt-in gate commit message: an fp8 low-precision combine is among the
+ * checked cases; the pages fix no format, so this is a reading).  Codes are
+ * OCP E4M3 (bias 7, largest finite 448, no infinities).  Every row is cut
+ * into blocks of 128 elements (the last may be shorter); each block carries
+ * one float32 scale 2^e, the smallest power of two with amax(|block|) <=
+ * 448 * 2^e (1 for an all-zero block), and code = E4M3(value / 2^e) rounded
+ * to nearest even.  Non-finite inputs give unspecified codes.
+ * Layouts: codes [rows, H] uint8 (8-byte aligned), scales [rows, nb] float32
+ * with nb = moe_plan_scale_blocks(plan) = ceil(H / 128). */
+int64_t moe_plan_scale_blocks(const moe_plan* plan);
+
+/* fp8 dispatch: each token row of x (bf16 [T, H]) is quantized once and its
+ * codes and block scales are written to its receive rows: recv8 [T*k, H]
+ * uint8, recv_scale [T*k, nb] float32.  Plans with MOE_FLAG_NODE_DEDUP are
+ * not supported (MOE_ERR_UNSUPPORTED).  Asynchronous.
+ * Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, UNSUPPORTED, HIP. */
+moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, float* recv_scale,
+                            void* stream);
+
+/* fp8 combine: out[t] = sum_j topk_w[t, j] * decode(y8, y_scale)[slot_of[t, j]]
+ * with the decode exact (code value times its block scale) and the same
+ * float32 fused multiply-add chain and output rounding as moe_combine.
+ * y8 [T*k, H] uint8 and y_scale [T*k, nb] float32 in the receive layout.
+ * Asynchronous.  Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
+moe_status moe_combine_fp8(moe_plan* plan, const uint8_t* y8, const float* y_scale,
+                           const float* topk_w, void* out, int32_t out_dtype, void* stream);
+
 /* Copies one plan item to host memory (synchronises the stream).  bytes must
  * be at least the item's size (see moe_item).  The traffic matrices
  * (SEND_ROWS, SEND_COPIES, NODE_COPIES) are computed on demand by a small

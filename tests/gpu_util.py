@@ -54,10 +54,19 @@ def ulp_bf16(ref: np.ndarray) -> np.ndarray:
 
 def check_combine(out: np.ndarray, y: np.ndarray, w: np.ndarray, slot_of: np.ndarray,
                   out_f32: bool, what: str) -> dict:
-    """out: gpu result for the tokens of slot_of (float32 or bf16 bits)."""
+    """out: gpu result for the tokens of slot_of (float32 or bf16 bits); y: bf16 rows."""
     k = slot_of.shape[1]
     ref = oracle.combine(y, w, {"slot_of": slot_of})
-    acc_err = k * U32 * abs_scale(y, w, slot_of) * (1 + 1e-3)
+    yv = oracle.bf16_to_f32(y).astype(np.float64)
+    return check_combine_values(out, ref, yv, w, slot_of, out_f32, what)
+
+
+def check_combine_values(out, ref, yv, w, slot_of, out_f32, what) -> dict:
+    """Same bars with the receive rows given as their (exact) float64 values yv."""
+    k = slot_of.shape[1]
+    wa = np.abs(np.asarray(w, dtype=np.float64))
+    scale = sum(wa[:, j:j + 1] * np.abs(yv[slot_of[:, j]]) for j in range(k))
+    acc_err = k * U32 * scale * (1 + 1e-3)
     if out_f32:
         got = out.astype(np.float64)
         bound = 1e-3 * np.abs(ref) + acc_err

@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -110,3 +110,13 @@ def test_status_strings():
     for s in range(7):
         assert _abi.status_str(s)
     assert "unknown" in _abi.status_str(99)
+
+
+def test_fp8_entry_points_on_host():
+    L = _abi.lib()
+    st, h = make(T=64, H=200)
+    assert L.moe_plan_scale_blocks(h) == 2          # ceil(200 / 128)
+    vp = ctypes.c_void_p
+    assert L.moe_dispatch_fp8(h, vp(16), vp(16), vp(16), None) == _abi.ERR_PLAN_NOT_ROUTED
+    assert L.moe_combine_fp8(h, vp(16), vp(16), vp(16), vp(16), 0, None) == _abi.ERR_PLAN_NOT_ROUTED
+    L.moe_plan_destroy(h)

@@ -1,0 +1,130 @@
+"""GPU parity of the fp8 payload (OCP E4M3, 1x128 power-of-two block scales).
+
+Bars: codes and block scales bit-exact against the oracle's quantization;
+combine of an fp8 payload within the same tolerance as the bf16 combine,
+taken against the oracle's float64 sum of the decoded values.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+from workloads import gen
+
+from gpu_util import check_combine_values, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def run_fp8(batch, dev, x_bits=None):
+    import combine_shuffling_amd as cs
+
+    wl = batch.workload
+    x = batch.x if x_bits is None else x_bits
+    plan = cs.Plan(wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks)
+    plan.route(to_dev(batch.topk_idx, dev))
+    rows = plan.recv_rows
+    codes_full = torch.full((rows + 2, wl.hidden), 0x55, dtype=torch.uint8, device=dev)
+    scale_full = torch.full((rows + 2, plan.scale_blocks), -1.0, dtype=torch.float32, device=dev)
+    plan.dispatch_fp8(to_dev(x, dev), codes_full[:rows], scale_full[:rows])
+    torch.cuda.synchronize()
+    assert bool((codes_full[rows:] == 0x55).all()) and bool((scale_full[rows:] == -1.0).all())
+    return plan, codes_full[:rows], scale_full[:rows]
+
+
+def check_fp8(batch, dev, x_bits=None, tokens=None):
+    wl = batch.workload
+    say(f"[fp8] {wl.describe()}")
+    x = batch.x if x_bits is None else x_bits
+    p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks)
+    plan, codes, scales = run_fp8(batch, dev, x)
+    want_c, want_e = fp8.dispatch_fp8(x, p)
+    got_c = codes.cpu().numpy()
+    got_s = scales.cpu().numpy().astype(np.float64)
+    bad = np.argwhere(got_c != want_c)
+    assert bad.size == 0, f"codes differ at {bad[:3].tolist()}: {got_c[tuple(bad[0])]:#x} vs {want_c[tuple(bad[0])]:#x}"
+    assert np.array_equal(got_s, np.ldexp(1.0, want_e)), "block scales differ"
+    assert np.array_equal(plan.read("slot_of").reshape(p["slot_of"].shape), p["slot_of"])
+    tok = np.arange(wl.num_tokens) if tokens is None else tokens
+    so = p["slot_of"][tok]
+    ref = fp8.combine_fp8(want_c, want_e, batch.topk_w[tok], {"slot_of": so})
+    yv = fp8.dequantize_rows(want_c, want_e)
+    w = to_dev(batch.topk_w, dev)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out = plan.combine_fp8(codes, scales, w, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy() if out_dtype == torch.float32 else \
+            out.cpu().view(torch.int16).numpy().view(np.uint16)
+        check_combine_values(o[tok], ref, yv, batch.topk_w[tok], so, out_dtype == torch.float32,
+                             wl.name + " fp8")
+
+
+@pytest.mark.parametrize("case", [
+    (1, 8, 1, 1, 1), (300, 200, 8, 2, 2), (1000, 136, 24, 5, 7), (2049, 256, 64, 8, 4),
+    (777, 1024, 100, 6, 7), (513, 72, 13, 13, 13)],
+    ids=lambda c: "T{}-H{}-E{}-k{}-R{}".format(*c))
+def test_fp8_small_shapes(case, dev):
+    T, H, E, k, R = case
+    check_fp8(gen.make_batch(gen.custom(T, H, E, k, R, seed=T + H)), dev)
+
+
+@pytest.mark.parametrize("name", ["tiny", "olmoe", "qwen3", "nondiv"])
+def test_fp8_workloads_full_size(name, dev):
+    batch = gen.make_batch(gen.get(name))
+    T = batch.workload.num_tokens
+    rng = np.random.default_rng(7)
+    tok = None if T <= 4096 else np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 512)]))
+    check_fp8(batch, dev, tokens=tok)
+
+
+def test_fp8_zero_rows_and_tiny_values(dev):
+    batch = gen.make_batch(gen.custom(400, 256, 16, 4, 4, seed=3))
+    x = batch.x.copy()
+    x[:50] = 0                                   # all-zero rows: scale 1, codes 0
+    x[50:100] = x[50:100] & np.uint16(0x807F)    # tiny bf16 values (exponent 0): subnormal range
+    x[100:150, :128] = 0                         # one zero block, one normal block
+    check_fp8(batch, dev, x_bits=x)
+
+
+def test_fp8_one_hot_combine_is_exact_decode(dev):
+    batch = gen.make_batch(gen.custom(1000, 512, 32, 4, 4, seed=8))
+    T, k = batch.topk_idx.shape
+    p = oracle.route_plan(batch.topk_idx, 32, 4)
+    plan, codes, scales = run_fp8(batch, dev)
+    pick = np.random.default_rng(1).integers(0, k, T)
+    w = np.zeros((T, k), dtype=np.float32)
+    w[np.arange(T), pick] = 1.0
+    out = plan.combine_fp8(codes, scales, to_dev(w, dev), out_dtype=torch.float32).cpu().numpy()
+    c, e = fp8.dispatch_fp8(batch.x, p)
+    rows = p["slot_of"][np.arange(T), pick]
+    assert np.array_equal(out.astype(np.float64), fp8.dequantize_rows(c[rows], e[rows]))
+
+
+def test_fp8_refuses_dedup_and_combines_without_dispatch(dev):
+    import combine_shuffling_amd as cs
+    from combine_shuffling_amd import _abi
+
+    batch = gen.make_batch(gen.custom(600, 128, 16, 4, 4, 2, seed=4))
+    idx = to_dev(batch.topk_idx, dev)
+    plan = cs.Plan(600, 128, 16, 4, 4, 2, node_dedup=True)
+    plan.route(idx)
+    with pytest.raises(cs.MoeError) as ei:
+        plan.dispatch_fp8(to_dev(batch.x, dev))
+    assert ei.value.status == _abi.ERR_UNSUPPORTED
+    # combine of a host-made fp8 payload straight after the route
+    p = oracle.route_plan(batch.topk_idx, 16, 4, 2)
+    c, e = fp8.dispatch_fp8(batch.x, p)
+    out = plan.combine_fp8(to_dev(c, dev), to_dev(np.ldexp(1.0, e).astype(np.float32), dev),
+                           to_dev(batch.topk_w, dev), out_dtype=torch.float32)
+    ref = fp8.combine_fp8(c, e, batch.topk_w, p)
+    check_combine_values(out.cpu().numpy(), ref, fp8.dequantize_rows(c, e), batch.topk_w,
+                         p["slot_of"], True, "fp8 no-dispatch")
