@@ -260,7 +260,7 @@ moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, f
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   if (plan->d.dedup) return MOE_ERR_UNSUPPORTED;
   if (plan->d.T == 0) return MOE_OK;
-  if (!x || !recv8 || !recv_scale || !moe::aligned(x, 16) || !moe::aligned(recv8, 8) ||
+  if (!x || !recv8 || !recv_scale || !moe::aligned(x, 16) || !moe::aligned(recv8, 16) ||
       !moe::aligned(recv_scale, 4))
     return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -277,7 +277,7 @@ moe_status moe_combine_fp8(moe_plan* plan, const uint8_t* y8, const float* y_sca
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARGUMENT;
   if (plan->d.T == 0) return MOE_OK;
-  if (!y8 || !y_scale || !topk_w || !out || !moe::aligned(y8, 8) || !moe::aligned(y_scale, 4) ||
+  if (!y8 || !y_scale || !topk_w || !out || !moe::aligned(y8, 16) || !moe::aligned(y_scale, 4) ||
       !moe::aligned(topk_w, 4) || !moe::aligned(out, 16))
     return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -39,6 +39,9 @@
 #ifndef MOE_NT_LOAD
 #define MOE_NT_LOAD 1
 #endif
+#ifndef MOE_COMBINE8_U
+#define MOE_COMBINE8_U 2
+#endif
 #ifndef MOE_NT_LOAD_X
 #define MOE_NT_LOAD_X 0
 #endif
@@ -60,6 +63,7 @@ constexpr int kBlock = kWaves * kWave;
 constexpr int kGatherU = MOE_GATHER_U;    // wave-items per wave: gather
 constexpr int kStageU = MOE_STAGE_U;      // wave-items per wave: stage_a, stage_b
 constexpr int kCombineU = MOE_COMBINE_U;  // wave-items per wave: combine
+constexpr int kCombine8U = MOE_COMBINE8_U; // wave-items per wave: combine of an fp8 payload
 
 // Rows are touched once per call: stream them past the caches (measured
 // faster on gfx950 for both the row reads and the row writes).
@@ -358,18 +362,60 @@ __device__ __forceinline__ void decode_e4m3x8(u32x2 c, float (&f)[8]) {
   }
 }
 
+// fp8 dispatch wave-items: each lane takes two 16-byte bf16 chunks (16
+// elements), so a wave covers 128 chunks of a row and writes 16 bytes of codes
+// per lane; a 128-element scale block is 8 lanes.  (The fp8 combine keeps one
+// chunk per lane: twice the waves in flight measured faster there.)
+constexpr int kFp8ItemChunks = 2 * kWave;
+constexpr int kFp8BlockLanes = kFp8BlockChunks / 2;
+
+struct Item8 {
+  int t, c0;         // token, first of the lane's two chunks
+  bool live, ok0, ok1;
+};
+
+template <int U>
+__device__ __forceinline__ Item8 wave_item8(const Dims& d, int segs8, int items, int u) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int g = __builtin_amdgcn_readfirstlane((blockIdx.x * U + u) * kWaves + wave);
+  Item8 it;
+  it.live = g < items;
+  it.t = it.live ? g / segs8 : 0;
+  const int seg = g - it.t * segs8;
+  it.c0 = seg * kFp8ItemChunks + 2 * lane;
+  it.ok0 = it.live && it.c0 < d.chunks;
+  it.ok1 = it.live && it.c0 + 1 < d.chunks;
+  return it;
+}
+
+// 16 codes of a lane at byte offset (row * H + c0 * 8): one 16-byte store when
+// rows are 16-byte multiples (H % 16 == 0), else two 8-byte stores.
+__device__ __forceinline__ void store_codes(uint8_t* base, int64_t row, const Dims& d,
+                                            const Item8& it, u32x2 a, u32x2 b) {
+  uint8_t* p = base + row * d.H + (int64_t)it.c0 * 8;
+  if ((d.H & 15) == 0) {
+    const u32x4 v = {a[0], a[1], b[0], b[1]};
+    store_chunk(reinterpret_cast<u32x4*>(p), v);
+  } else {
+    if (it.ok0) store_chunk(reinterpret_cast<u32x2*>(p), a);
+    if (it.ok1) store_chunk(reinterpret_cast<u32x2*>(p + 8), b);
+  }
+}
+
 // Dispatch with an fp8 payload: each token row is read once, quantized once
-// (block amax by a 16-lane reduction) and its codes and block scales are
+// (block amax by an 8-lane reduction) and its codes and block scales are
 // written to the token's k receive rows.
 template <int KMAX>
 __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
                                                             const u32x4* __restrict__ x,
-                                                            u32x2* __restrict__ recv8,
+                                                            uint8_t* __restrict__ recv8,
                                                             float* __restrict__ rscale, Work w) {
-  const int items = d.T * d.segs, lane = threadIdx.x % kWave;
+  const int lane = threadIdx.x % kWave;
+  const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
+  const int items = d.T * segs8;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  const Item it = wave_item<1>(d, items, 0);
+  const Item8 it = wave_item8<1>(d, segs8, items, 0);
   int slot[KMAX];
   if (it.live) {
     token_slots<KMAX>(d, w, idx, it.t, slot);
@@ -377,34 +423,41 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) slot[j] = -1;
   }
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (it.ok) v = load_x_chunk(&x[(int64_t)it.t * d.chunks + it.c]);
-  float f[8];
-  unpack_bf16(v, f);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int64_t xrow = (int64_t)it.t * d.chunks;
+  const u32x4 v0 = it.ok0 ? load_x_chunk(&x[xrow + it.c0]) : zero;
+  const u32x4 v1 = it.ok1 ? load_x_chunk(&x[xrow + it.c0 + 1]) : zero;
+  float f0[8], f1[8];
+  unpack_bf16(v0, f0);
+  unpack_bf16(v1, f1);
   float amax = 0.0f;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(f[q]));
+  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fmaxf(fabsf(f0[q]), fabsf(f1[q])));
 #pragma unroll
-  for (int o = kFp8BlockChunks / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kFp8BlockChunks));
+  for (int o = kFp8BlockLanes / 2; o > 0; o >>= 1)
+    amax = fmaxf(amax, __shfl_xor(amax, o, kFp8BlockLanes));
   const int e = fp8_block_exp(amax);
   const float inv = ldexpf(1.0f, -e);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) f[q] *= inv;
-  const u32x2 code = encode_e4m3x8(f);
+  for (int q = 0; q < 8; ++q) {
+    f0[q] *= inv;
+    f1[q] *= inv;
+  }
+  const u32x2 ca = encode_e4m3x8(f0), cb = encode_e4m3x8(f1);
   const float scale = ldexpf(1.0f, e);
-  const bool scale_lane = (lane % kFp8BlockChunks) == 0;
-  const int blk = it.c / kFp8BlockChunks;
+  const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
+  const int blk = it.c0 / kFp8BlockChunks;
 
-  if (it.live && it.c == lane && lane < d.k) {
+  if (it.live && it.c0 == 2 * lane && lane < d.k) {  // first segment publishes the slots
     const int s = lane_pick<KMAX>(slot, lane);
     w.slot_of[(int64_t)it.t * d.k + lane] = s;
     if ((uint32_t)s < rows) w.row_src[s] = it.t;
   }
-  if (it.ok) {
+  if (it.ok0) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if ((uint32_t)slot[j] < rows) {
-        store_chunk(&recv8[(int64_t)slot[j] * d.chunks + it.c], code);
+        store_codes(recv8, slot[j], d, it, ca, cb);
         if (scale_lane) rscale[(int64_t)slot[j] * nb + blk] = scale;
       }
     }
@@ -476,6 +529,12 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_kernel(Dims d, const u32x2
   }
 }
 
+inline int blocks_for8(const Dims& d, int per_wave) {
+  const int64_t segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
+  const int64_t items = (int64_t)d.T * segs8, per_block = (int64_t)kWaves * per_wave;
+  return (int)((items + per_block - 1) / per_block);
+}
+
 inline int blocks_for(const Dims& d, int per_wave) {
   const int64_t items = (int64_t)d.T * d.segs, per_block = (int64_t)kWaves * per_wave;
   return (int)((items + per_block - 1) / per_block);
@@ -541,9 +600,8 @@ template <int KMAX>
 struct GatherFp8Launch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
                         float* rscale, const Work& w, hipStream_t s) {
-    hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), dim3(blocks_for(d, 1)), dim3(kBlock), 0, s, d,
-                       idx, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x2*>(recv8),
-                       rscale, w);
+    hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s, d,
+                       idx, reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
     return hipGetLastError();
   }
 };
@@ -552,14 +610,14 @@ template <int KMAX>
 struct CombineFp8Launch {
   static hipError_t run(const Dims& d, const uint8_t* y8, const float* yscale, const float* wts,
                         void* out, bool f32, const Work& w, hipStream_t s) {
-    const dim3 grid(blocks_for(d, kCombineU));
+    const dim3 grid(blocks_for(d, kCombine8U));
     const u32x2* y = reinterpret_cast<const u32x2*>(y8);
     if (f32)
-      hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombineU, true>), grid, dim3(kBlock), 0, s, d,
+      hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, true>), grid, dim3(kBlock), 0, s, d,
                          y, yscale, wts, w.slot_of, out);
     else
-      hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombineU, false>), grid, dim3(kBlock), 0, s, d,
-                         y, yscale, wts, w.slot_of, out);
+      hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, false>), grid, dim3(kBlock), 0, s,
+                         d, y, yscale, wts, w.slot_of, out);
     return hipGetLastError();
   }
 };

@@ -171,7 +171,7 @@ moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, v
  * one float32 scale 2^e, the smallest power of two with amax(|block|) <=
  * 448 * 2^e (1 for an all-zero block), and code = E4M3(value / 2^e) rounded
  * to nearest even.  Non-finite inputs give unspecified codes.
- * Layouts: codes [rows, H] uint8 (8-byte aligned), scales [rows, nb] float32
+ * Layouts: codes [rows, H] uint8 (16-byte aligned), scales [rows, nb] float32
  * with nb = moe_plan_scale_blocks(plan) = ceil(H / 128). */
 int64_t moe_plan_scale_blocks(const moe_plan* plan);
 
