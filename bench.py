@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--payload", choices=("bf16", "fp8"), default="bf16",
                     help="row payload: bf16, or fp8 (OCP E4M3 codes + one float32 scale per "
                          "128-element block; single-hop workloads only)")
+    ap.add_argument("--load-aware-forwarders", action="store_true",
+                    help="node-deduplicated workloads: choose forwarders by load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
@@ -265,14 +267,15 @@ def main():
     idx0 = torch.from_numpy(batch.topk_idx).to(dev)
     w0 = torch.from_numpy(batch.topk_w).to(dev)
 
-    probe = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup)
+    la = args.load_aware_forwarders and wl.node_dedup
+    probe = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la)
     set_bytes = (x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4 + probe.workspace_bytes
                  + probe.recv_rows * H * (1 if fp8 else 2) + probe.staging_rows_max * H * 2
                  + T * H * 2)
     n_sets = args.sets or max(2, math.ceil((2 << 30) / set_bytes))
     sets = []
     for _ in range(n_sets):
-        plan = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup)
+        plan = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la)
         s = dict(plan=plan, x=x0.clone(), idx=idx0.clone(), w=w0.clone(),
                  recv=torch.empty((plan.recv_rows, H), dtype=torch.int16, device=dev),
                  staging=(torch.empty((plan.staging_rows_max, H), dtype=torch.int16, device=dev)
@@ -305,6 +308,12 @@ def main():
         step(sets[i % n_sets])
     torch.cuda.synchronize()
     D = int(sets[0]["plan"].read("num_staged")[0]) if wl.node_dedup else 0
+    fwd_rows = None
+    if wl.node_dedup:
+        per = np.diff(sets[0]["plan"].read("stage_offsets"))
+        fwd_rows = {"rule": "load_aware" if la else "static", "max": int(per.max()),
+                    "mean": round(float(per.mean()), 1),
+                    "max_over_mean": round(float(per.max() / max(per.mean(), 1e-9)), 4)}
     disp_b, comb_b = algorithmic_bytes(wl, D, args.payload)
 
     # Timed region: K steps, nothing else on the stream.
@@ -358,7 +367,7 @@ def main():
         "config": {"workload": wl.name, "T": T, "H": H, "E": wl.num_experts, "k": k,
                    "R": wl.num_ranks, "G": wl.ranks_per_node, "node_dedup": wl.node_dedup,
                    "staging_rows": D, "seed": wl.seed, "buffer_sets": n_sets,
-                   "payload": args.payload},
+                   "payload": args.payload, "forwarder_rows": fwd_rows},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "bytes_per_step": disp_b + comb_b,
         "phases": {"dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),

@@ -61,10 +61,12 @@ class Plan:
     """Owns one moe_plan (host) and, once routed, its device workspace tensor."""
 
     def __init__(self, num_tokens: int, hidden: int, num_experts: int, top_k: int,
-                 num_ranks: int, ranks_per_node: int | None = None, node_dedup: bool = False):
+                 num_ranks: int, ranks_per_node: int | None = None, node_dedup: bool = False,
+                 load_aware_forwarders: bool = False):
         G = num_ranks if ranks_per_node is None else ranks_per_node
-        self.cfg = _abi.MoeConfig(num_tokens, hidden, num_experts, top_k, num_ranks, G,
-                                  _abi.FLAG_NODE_DEDUP if node_dedup else 0)
+        flags = (_abi.FLAG_NODE_DEDUP if node_dedup else 0) | \
+            (_abi.FLAG_LOAD_AWARE_FORWARDERS if load_aware_forwarders else 0)
+        self.cfg = _abi.MoeConfig(num_tokens, hidden, num_experts, top_k, num_ranks, G, flags)
         self._lib = _abi.lib()
         h = ctypes.c_void_p()
         _abi.check(self._lib.moe_plan_create(ctypes.byref(self.cfg), ctypes.byref(h)),
@@ -184,7 +186,8 @@ class Plan:
              "rank_offsets": self.R + 1, "slot_of": self.T * self.k, "row_src": self.T * self.k,
              "stage_offsets": self.R + 1, "stage_of": self.T * self.k,
              "stage_src": self.staging_rows_max, "send_rows": self.R * self.R,
-             "send_copies": self.R * self.R, "node_copies": self.R * self.N}[item]
+             "send_copies": self.R * self.R, "node_copies": self.R * self.N,
+             "forwarders": self.R * self.N}[item]
         buf = np.zeros(max(n, 1), dtype=np.int32)
         dev = self.device
         if dev is None:
@@ -200,10 +203,12 @@ class Plan:
 
 def route_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, hidden: int,
                ranks_per_node: int | None = None, node_dedup: bool = False,
-               workspace: torch.Tensor | None = None, stream=None) -> Plan:
+               load_aware_forwarders: bool = False, workspace: torch.Tensor | None = None,
+               stream=None) -> Plan:
     """moe_plan_create + moe_route_plan for a [T, k] int32 routing on the GPU."""
     T, k = topk_idx.shape
-    plan = Plan(T, hidden, num_experts, k, num_ranks, ranks_per_node, node_dedup)
+    plan = Plan(T, hidden, num_experts, k, num_ranks, ranks_per_node, node_dedup,
+                load_aware_forwarders)
     return plan.route(topk_idx, workspace, stream)
 
 

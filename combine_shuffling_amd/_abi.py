@@ -21,6 +21,7 @@ ERR_HIP = 5
 ERR_UNSUPPORTED = 6
 
 FLAG_NODE_DEDUP = 1
+FLAG_LOAD_AWARE_FORWARDERS = 2
 MAX_EXPERTS = 1024
 MAX_TOPK = 16
 
@@ -30,7 +31,7 @@ OUT_F32 = 1
 # moe_item
 ITEM = dict(status=0, counts=1, expert_offsets=2, rank_offsets=3, slot_of=4, row_src=5,
             num_staged=6, stage_offsets=7, stage_of=8, stage_src=9, send_rows=10,
-            send_copies=11, node_copies=12)
+            send_copies=11, node_copies=12, forwarders=13)
 
 
 class MoeConfig(ctypes.Structure):

@@ -54,8 +54,9 @@ Layout make_layout(const Dims& d) {
   take(l.lr, tk);
   take(l.slot_of, tk);
   take(l.row_src, tk);
-  take(l.tile_fcounts, d.dedup ? (int64_t)d.nblk * d.R : 1);
-  take(l.tile_fbase, d.dedup ? (int64_t)d.nblk * d.R : 1);
+  take(l.tile_fcounts, d.dedup ? (int64_t)d.nblk * d.fkeys : 1);
+  take(l.tile_fbase, d.dedup ? (int64_t)d.nblk * d.fkeys : 1);
+  take(l.fwd, d.dedup ? (int64_t)d.R * d.N : 1);
   take(l.stage_off, d.dedup ? d.R + 1 : 1);
   take(l.fkey, fk);
   take(l.flr, fk);
@@ -84,6 +85,7 @@ Work bind_work(const Layout& l, void* base) {
   w.row_src = p(l.row_src);
   w.tile_fcounts = p(l.tile_fcounts);
   w.tile_fbase = p(l.tile_fbase);
+  w.fwd = p(l.fwd);
   w.stage_off = p(l.stage_off);
   w.fkey = p(l.fkey);
   w.flr = p(l.flr);
@@ -135,14 +137,18 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   if (c.num_tokens < 0 || c.hidden <= 0 || c.hidden % 8 || c.num_experts <= 0 || c.top_k <= 0 ||
       c.num_ranks <= 0 || c.ranks_per_node <= 0)
     return MOE_ERR_INVALID_ARGUMENT;
-  if (c.flags & ~MOE_FLAG_NODE_DEDUP) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.flags & ~(MOE_FLAG_NODE_DEDUP | MOE_FLAG_LOAD_AWARE_FORWARDERS))
+    return MOE_ERR_INVALID_ARGUMENT;
   if (c.num_experts > MOE_MAX_EXPERTS || c.top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (c.top_k > c.num_experts) return MOE_ERR_INVALID_ARGUMENT;
   if (c.num_experts < c.num_ranks) return MOE_ERR_EXPERTS_LT_RANKS;
   if (c.num_ranks % c.ranks_per_node) return MOE_ERR_INVALID_ARGUMENT;
   const int32_t nodes = c.num_ranks / c.ranks_per_node;
   const bool dedup = (c.flags & MOE_FLAG_NODE_DEDUP) != 0;
+  const bool load_aware = (c.flags & MOE_FLAG_LOAD_AWARE_FORWARDERS) != 0;
   if (dedup && nodes < 2) return MOE_ERR_INVALID_ARGUMENT;
+  if (load_aware && !dedup) return MOE_ERR_INVALID_ARGUMENT;
+  if (load_aware && (int64_t)c.num_ranks * nodes > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
 
   const int64_t T = c.num_tokens, chunks = c.hidden / 8;
   const int64_t staging_max = dedup ? T * std::min<int64_t>(c.top_k, nodes) : 0;
@@ -162,14 +168,17 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   d.erem = d.E % d.R;
   d.tbase = d.T / d.R;
   d.trem = d.T % d.R;
-  // At most kMaxPlanTiles tiles, and few enough that the last block can scan
-  // the [tiles x experts] count matrix in LDS.
-  const int64_t max_tiles = std::min<int64_t>(moe::kMaxPlanTiles, moe::kScanLdsInts / d.E);
+  d.dedup = dedup ? 1 : 0;
+  d.load_aware = load_aware ? 1 : 0;
+  d.fkeys = load_aware ? d.R * d.N : d.R;
+  // At most kMaxPlanTiles tiles, and few enough that the scan kernel holds
+  // the [tiles x experts] (and [tiles x staging keys]) count matrix in LDS.
+  const int64_t widest = std::max<int64_t>(d.E, dedup ? d.fkeys : 1);
+  const int64_t max_tiles = std::min<int64_t>(moe::kMaxPlanTiles, moe::kScanLdsInts / widest);
   const int64_t per_tile_cap = (int64_t)moe::kPlanBlock * max_tiles;
   d.passes = (int32_t)std::max<int64_t>(1, (T + per_tile_cap - 1) / per_tile_cap);
   d.tile = moe::kPlanBlock * d.passes;
   d.nblk = (int32_t)std::max<int64_t>(1, (T + d.tile - 1) / d.tile);
-  d.dedup = dedup ? 1 : 0;
   d.chunks = (int32_t)chunks;
   d.segs = (int32_t)((chunks + moe::kWave - 1) / moe::kWave);
   d.smax = (int32_t)staging_max;
@@ -311,10 +320,12 @@ moe_status moe_plan_read(moe_plan* plan, int32_t item, void* host_dst, size_t by
     case MOE_ITEM_SEND_ROWS: src = w.send_rows; n = (int64_t)d.R * d.R; traffic = true; break;
     case MOE_ITEM_SEND_COPIES: src = w.send_copies; n = (int64_t)d.R * d.R; traffic = true; break;
     case MOE_ITEM_NODE_COPIES: src = w.node_copies; n = (int64_t)d.R * d.N; traffic = true; break;
+    case MOE_ITEM_FORWARDERS: src = w.fwd; n = (int64_t)d.R * d.N; break;
     default: return MOE_ERR_INVALID_ARGUMENT;
   }
   const bool dedup_item = item == MOE_ITEM_NUM_STAGED || item == MOE_ITEM_STAGE_OFFSETS ||
-                          item == MOE_ITEM_STAGE_OF || item == MOE_ITEM_STAGE_SRC;
+                          item == MOE_ITEM_STAGE_OF || item == MOE_ITEM_STAGE_SRC ||
+                          item == MOE_ITEM_FORWARDERS;
   if (dedup_item && !d.dedup) return MOE_ERR_INVALID_ARGUMENT;
   const size_t need = (size_t)n * sizeof(int32_t);
   if (bytes < need) return MOE_ERR_INVALID_ARGUMENT;

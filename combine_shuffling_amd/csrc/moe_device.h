@@ -47,7 +47,7 @@ __device__ __forceinline__ void token_stages(const Dims& d, const Work& w, int t
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     key[j] = j < d.k ? w.fkey[at + j] : -1;
-    p[j] = key[j] >= 0 ? w.tile_fbase[b * d.R + key[j]] + w.flr[at + j] : -1;
+    p[j] = key[j] >= 0 ? w.tile_fbase[b * d.fkeys + key[j]] + w.flr[at + j] : -1;
     if (key[j] >= 0) lead |= 1u << j;
   }
 #pragma unroll

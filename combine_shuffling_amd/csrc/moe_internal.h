@@ -32,6 +32,8 @@ struct Dims {
   int32_t tile;           // tokens per plan tile = 256 * passes
   int32_t nblk;           // plan tiles
   int32_t dedup;          // MOE_FLAG_NODE_DEDUP set
+  int32_t load_aware;     // MOE_FLAG_LOAD_AWARE_FORWARDERS set
+  int32_t fkeys;          // staging keys: forwarders (R), or (owner, node) pairs (R * N)
   int32_t chunks;         // 16-byte chunks per row = H / 8
   int32_t segs;           // 64-chunk row segments per row = ceil(chunks / 64)
   int32_t smax;           // staging rows allocated (T * min(k, N) with dedup, else 0)
@@ -49,10 +51,11 @@ struct Work {
   int32_t* lr;            // [T * k]     rank of slot (t, j) among its tile's slots of that expert; -1 dropped
   int32_t* slot_of;       // [T * k]     token slot -> receive row (-1: dropped)
   int32_t* row_src;       // [T * k]     receive row -> token
-  int32_t* tile_fcounts;  // [nblk * R]  staging rows per (tile, forwarder)               (dedup)
-  int32_t* tile_fbase;    // [nblk * R]  first staging row of (tile, forwarder)           (dedup)
+  int32_t* tile_fcounts;  // [nblk * fkeys] staging rows per (tile, key)                 (dedup)
+  int32_t* tile_fbase;    // [nblk * fkeys] first staging row of (tile, key)              (dedup)
+  int32_t* fwd;           // [R * N]     forwarder of (owner s, node n) at s * N + n      (dedup)
   int32_t* stage_off;     // [R + 1]     first staging row of each forwarder               (dedup)
-  int32_t* fkey;          // [T * k]     forwarder of the node's first slot; -2-j on later
+  int32_t* fkey;          // [T * k]     staging key of the node's first slot; -2-j on later
                           //             slots of the node (j = its first slot); -1 dropped (dedup)
   int32_t* flr;           // [T * k]     rank among the tile's staging rows of that forwarder (dedup)
   int32_t* stage_of;      // [T * k]     token slot -> staging row of its node             (dedup)
@@ -65,7 +68,7 @@ struct Work {
 // Byte offsets of each Work array from the workspace base, and the total.
 struct Layout {
   size_t ctrl, tile_flags, tile_counts, tile_base, counts, expert_off, rank_off, lr, slot_of,
-      row_src, tile_fcounts, tile_fbase, stage_off, fkey, flr, stage_of, stage_src, send_rows,
+      row_src, tile_fcounts, tile_fbase, fwd, stage_off, fkey, flr, stage_of, stage_src, send_rows,
       send_copies, node_copies, total;
 };
 

@@ -120,8 +120,9 @@ __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
     s_run[i] = 0;
     if (d.dedup) s_node[i] = split_part(i, d.ebase, d.erem) / d.G;
   }
+  const int K = d.fkeys;
   if (d.dedup)
-    for (int i = tid; i < R; i += kPlanBlock) s_frun[i] = 0;
+    for (int i = tid; i < K; i += kPlanBlock) s_frun[i] = 0;
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
@@ -177,15 +178,17 @@ __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
 
     if (d.dedup) {
       __syncthreads();
-      for (int i = tid; i < kPlanWaves * R; i += kPlanBlock) s_mask[i] = 0;
-      // Key of the first slot of each distinct destination node: forwarder
-      // rank n*G + owner(t) % G.  Later slots of the node point back to it.
-      const int g = live ? split_part(t, d.tbase, d.trem) % d.G : 0;
+      for (int i = tid; i < kPlanWaves * K; i += kPlanBlock) s_mask[i] = 0;
+      // Key of the first slot of each distinct destination node: the
+      // forwarder rank n*G + owner(t) % G, or with load-aware forwarders the
+      // (owner, node) pair owner*N + n (its forwarder is chosen by the scan).
+      // Later slots of the node point back to the first.
+      const int owner = live ? split_part(t, d.tbase, d.trem) : 0;
       int nd[KMAX], key[KMAX];
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         nd[j] = e[j] >= 0 ? s_node[e[j]] : -1;
-        key[j] = nd[j] >= 0 ? nd[j] * d.G + g : -1;
+        key[j] = nd[j] < 0 ? -1 : d.load_aware ? owner * d.N + nd[j] : nd[j] * d.G + owner % d.G;
 #pragma unroll
         for (int jj = j - 1; jj >= 0; --jj)
           if (nd[j] >= 0 && nd[jj] == nd[j]) key[j] = -2 - jj;
@@ -193,32 +196,89 @@ __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (key[j] >= 0) atomicOr(&s_mask[wv * R + key[j]], bit);
+        if (key[j] >= 0) atomicOr(&s_mask[wv * K + key[j]], bit);
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (live && j < k) {
           int r = -1;
           if (key[j] >= 0) {
-            r = s_frun[key[j]] + __popcll(s_mask[wv * R + key[j]] & below);
-            for (int w2 = 0; w2 < wv; ++w2) r += __popcll(s_mask[w2 * R + key[j]]);
+            r = s_frun[key[j]] + __popcll(s_mask[wv * K + key[j]] & below);
+            for (int w2 = 0; w2 < wv; ++w2) r += __popcll(s_mask[w2 * K + key[j]]);
           }
           w.fkey[at + j] = key[j];
           w.flr[at + j] = r;
         }
       }
       __syncthreads();
-      for (int i = tid; i < R; i += kPlanBlock)
-        s_frun[i] += __popcll(s_mask[i]) + __popcll(s_mask[R + i]) + __popcll(s_mask[2 * R + i]) +
-                     __popcll(s_mask[3 * R + i]);
+      for (int i = tid; i < K; i += kPlanBlock)
+        s_frun[i] += __popcll(s_mask[i]) + __popcll(s_mask[K + i]) + __popcll(s_mask[2 * K + i]) +
+                     __popcll(s_mask[3 * K + i]);
     }
     __syncthreads();
   }
 
   for (int i = tid; i < E; i += kPlanBlock) w.tile_counts[blockIdx.x * E + i] = s_run[i];
   if (d.dedup)
-    for (int i = tid; i < R; i += kPlanBlock) w.tile_fcounts[blockIdx.x * R + i] = s_frun[i];
+    for (int i = tid; i < K; i += kPlanBlock) w.tile_fcounts[blockIdx.x * K + i] = s_frun[i];
   if (tid == 0) w.tile_flags[blockIdx.x] = s_bad;
+}
+
+// Load-aware forwarders (FUSCO article, "load balancing and cross-node
+// deduplication": forwarding follows the load and is spread evenly over a
+// node's GPUs).  Keys are (owner s, node n) pairs; the load of a pair is its
+// staging rows.  In each node the owners are ranked by load (more first, ties
+// to the lower owner) and dealt to the node's G ranks in snake order.  Staging
+// rows stay ordered by (forwarder, token); owners hold ascending token ranges,
+// so inside a forwarder that is (owner, token).  Writes the forwarder table,
+// stage_off and the (tile, pair) bases; returns D.  Needs R*N <= 1024 and
+// nblk * R * N <= kScanLdsInts.
+__device__ int scan_load_aware(const Dims& d, const Work& w, int* s_mat, int* s_tot, int* s_wsum) {
+  __shared__ int s_load[MOE_MAX_EXPERTS];  // per pair
+  __shared__ int s_fwd[MOE_MAX_EXPERTS];   // per pair
+  const int tid = threadIdx.x, R = d.R, N = d.N, G = d.G, K = d.fkeys, nblk = d.nblk;
+#pragma unroll 8
+  for (int i = tid; i < K * nblk; i += kPlanBlock) s_mat[i] = w.tile_fcounts[i];
+  __syncthreads();
+  for (int c = tid; c < K; c += kPlanBlock) {
+    int l = 0;
+    for (int b = 0; b < nblk; ++b) l += s_mat[b * K + c];
+    s_load[c] = l;
+  }
+  __syncthreads();
+  for (int c = tid; c < K; c += kPlanBlock) {
+    const int s = c / N, n = c % N, l = s_load[c];
+    int rank = 0;
+    for (int s2 = 0; s2 < R; ++s2) {
+      const int l2 = s_load[s2 * N + n];
+      rank += (l2 > l || (l2 == l && s2 < s)) ? 1 : 0;
+    }
+    const int lap = rank / G, pos = rank % G;
+    const int f = n * G + ((lap & 1) ? G - 1 - pos : pos);
+    s_fwd[c] = f;
+    w.fwd[c] = f;
+  }
+  __syncthreads();
+  for (int f = tid; f < R; f += kPlanBlock) {  // rows each forwarder stages
+    const int n = f / G;
+    int tot = 0;
+    for (int s = 0; s < R; ++s) tot += s_fwd[s * N + n] == f ? s_load[s * N + n] : 0;
+    s_tot[f] = tot;
+  }
+  __syncthreads();
+  const int staged = block_exclusive_scan(s_tot, R, s_wsum);
+  for (int f = tid; f <= R; f += kPlanBlock) w.stage_off[f] = f < R ? s_tot[f] : staged;
+  for (int c = tid; c < K; c += kPlanBlock) {
+    const int s = c / N, n = c % N, f = s_fwd[c];
+    int run = s_tot[f];
+    for (int s2 = 0; s2 < s; ++s2) run += s_fwd[s2 * N + n] == f ? s_load[s2 * N + n] : 0;
+    for (int b = 0; b < nblk; ++b) {
+      w.tile_fbase[b * K + c] = run;
+      run += s_mat[b * K + c];
+    }
+  }
+  __syncthreads();
+  return staged;
 }
 
 // One block: scans the [tiles x experts] count matrix (and, with dedup, the
@@ -237,8 +297,14 @@ __global__ __launch_bounds__(kPlanBlock) void route_scan_kernel(Dims d, Work w) 
   int staged = 0;
   if (d.dedup) {
     __syncthreads();
-    staged = scan_tiles(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, R, d.nblk, s_mat,
-                        s_tot, s_wsum);
+    if (d.load_aware) {
+      staged = scan_load_aware(d, w, s_mat, s_tot, s_wsum);
+    } else {
+      staged = scan_tiles(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, R, d.nblk, s_mat,
+                          s_tot, s_wsum);
+      for (int c = tid; c < R * d.N; c += kPlanBlock)
+        w.fwd[c] = (c % d.N) * d.G + (c / d.N) % d.G;
+    }
   }
   int bad = 0;
   for (int b = tid; b < d.nblk; b += kPlanBlock) bad |= w.tile_flags[b];

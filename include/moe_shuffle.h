@@ -38,8 +38,9 @@
  *                        tokens ascending inside an expert;
  *   staging  [Dmax, H]   bf16, rows ordered by (forwarder rank, token); the
  *                        forwarder of (token t, node n) is rank
- *                        n*G + owner(t) % G, owner(t) being the contiguous
- *                        ceil/floor split of the T tokens over the R ranks;
+ *                        n*G + owner(t) % G (or the load-aware choice, see
+ *                        MOE_FLAG_LOAD_AWARE_FORWARDERS), owner(t) being the
+ *                        contiguous ceil/floor split of the T tokens over R;
  *   out      [T, H]      bf16 (round to nearest even) or float32.
  *
  * Ownership.  The caller owns every device buffer (inputs, outputs and the
@@ -86,6 +87,14 @@ typedef enum moe_status {
 /* Node deduplication (one copy per (token, node), then intra-node fan-out).
  * Requires N = R / G > 1. */
 #define MOE_FLAG_NODE_DEDUP 1u
+/* With MOE_FLAG_NODE_DEDUP: choose each (owner rank s, node n)'s forwarder by
+ * load instead of the static n*G + s % G (FUSCO article, "load balancing and
+ * cross-node deduplication": forwarding follows the load and is spread evenly
+ * over the node's GPUs; the rule is a reading).  In each node the owners are
+ * ranked by the rows they stage for it (more first, ties to the lower owner)
+ * and dealt to the node's G ranks in snake order 0..G-1, G-1..0, ...
+ * Requires R * N <= MOE_MAX_EXPERTS. */
+#define MOE_FLAG_LOAD_AWARE_FORWARDERS 2u
 
 typedef struct moe_config {
   int64_t num_tokens;     /* T >= 0 (0 is an empty batch: every call is a no-op) */
@@ -113,7 +122,8 @@ typedef enum moe_item {
   MOE_ITEM_STAGE_SRC = 9,      /* [Dmax]  source token of each staging row; first D valid       */
   MOE_ITEM_SEND_ROWS = 10,     /* [R*R]   rows rank s sends to rank d (modelled link traffic)   */
   MOE_ITEM_SEND_COPIES = 11,   /* [R*R]   distinct tokens rank s sends to rank d                */
-  MOE_ITEM_NODE_COPIES = 12    /* [R*N]   distinct tokens rank s sends to node n                */
+  MOE_ITEM_NODE_COPIES = 12,   /* [R*N]   distinct tokens rank s sends to node n                */
+  MOE_ITEM_FORWARDERS = 13     /* [R*N]   forwarder rank of (owner s, node n) (dedup only)      */
 } moe_item;
 
 typedef enum moe_out_dtype { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;

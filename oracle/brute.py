@@ -23,7 +23,7 @@ def _part_starts(n: int, parts: int) -> list[int]:
     return starts
 
 
-def plan(idx: list[list[int]], E: int, R: int, G: int) -> dict:
+def plan(idx: list[list[int]], E: int, R: int, G: int, forwarders: str = "static") -> dict:
     T = len(idx)
     k = len(idx[0]) if T else 0
     estarts = _part_starts(E, R)
@@ -77,13 +77,31 @@ def plan(idx: list[list[int]], E: int, R: int, G: int) -> dict:
         for n in nodes:
             node_copies[s][n] += 1
 
+    # Forwarder of each (source, node): static same-local-index, or the
+    # load-aware snake deal of sources ranked by load.
+    fwd = [[n * G + s % G for n in range(N)] for s in range(R)]
+    if forwarders == "load_aware":
+        for n in range(N):
+            ranked = []
+            for s in range(R):
+                # insert s after every source with more load, or equal load and lower id
+                at = 0
+                while at < len(ranked) and (node_copies[ranked[at]][n] > node_copies[s][n] or
+                                            (node_copies[ranked[at]][n] == node_copies[s][n]
+                                             and ranked[at] < s)):
+                    at += 1
+                ranked.insert(at, s)
+            for i, s in enumerate(ranked):
+                lap, posn = i // G, i % G
+                fwd[s][n] = n * G + (posn if lap % 2 == 0 else G - 1 - posn)
+
     # Forwarder staging: walk forwarders in order, then tokens.
     stage_src, stage_node, stage_offsets = [], [], [0]
     pos = {}
     for f in range(R):
-        n, g = f // G, f % G
+        n = f // G
         for t in range(T):
-            if owner(t) % G != g:
+            if fwd[owner(t)][n] != f:
                 continue
             if any(rank_of(idx[t][j]) // G == n for j in range(k)):
                 pos[(t, n)] = len(stage_src)
@@ -97,7 +115,7 @@ def plan(idx: list[list[int]], E: int, R: int, G: int) -> dict:
                 send_copies=send_copies, node_copies=node_copies,
                 stage_src=stage_src, stage_node=stage_node,
                 stage_offsets=stage_offsets, stage_of=stage_of,
-                num_staged=len(stage_src))
+                num_staged=len(stage_src), forwarders=fwd)
 
 
 def dispatch(x: list[list[int]], p: dict) -> list[list[int]]:

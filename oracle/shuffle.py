@@ -52,8 +52,29 @@ def expert_counts(idx: np.ndarray, num_experts: int) -> np.ndarray:
     return np.bincount(a.ravel(), minlength=num_experts).astype(np.int64)
 
 
+def load_aware_forwarders(node_copies: np.ndarray, G: int) -> np.ndarray:
+    """fwd[s, n]: the rank of node n that forwards source s's copies for node n.
+
+    FUSCO article, "load balancing and cross-node deduplication": forwarding
+    follows the load and is spread evenly over the node's GPUs.  The pages
+    give no rule; the reading taken: in each node, the sources are ranked by
+    their load (copies bound for the node; more first, ties to the lower
+    source) and dealt to the node's G ranks in snake order (0, 1, .., G-1,
+    G-1, .., 0, 0, 1, ..).
+    """
+    R, N = node_copies.shape
+    fwd = np.zeros((R, N), dtype=np.int64)
+    for n in range(N):
+        order = sorted(range(R), key=lambda s: (-int(node_copies[s, n]), s))
+        for i, s in enumerate(order):
+            lap, pos = divmod(i, G)
+            g = pos if lap % 2 == 0 else G - 1 - pos
+            fwd[s, n] = n * G + g
+    return fwd
+
+
 def route_plan(idx: np.ndarray, num_experts: int, num_ranks: int,
-               ranks_per_node: int | None = None) -> dict:
+               ranks_per_node: int | None = None, forwarders: str = "static") -> dict:
     """Segment descriptors for gather-send / scatter-recv.
 
     FUSCO article, "core innovation": the sender reads scattered source rows
@@ -111,10 +132,17 @@ def route_plan(idx: np.ndarray, num_experts: int, num_ranks: int,
                 node_copies=node_copies)
 
     # Forwarding-GPU deduplication: one staging row per distinct
-    # (token, destination node); the forwarder of (t, n) is rank
-    # n*G + owner(t) % G; rows are ordered by (forwarder, token).
+    # (token, destination node); rows are ordered by (forwarder, token).  The
+    # forwarder of (t, n) is rank n*G + owner(t) % G ("static"), or the
+    # load-aware choice per (owner, node) above ("load_aware").
+    if forwarders == "static":
+        fwd_table = np.array([[n * G + s % G for n in range(N)] for s in range(R)], dtype=np.int64)
+    elif forwarders == "load_aware":
+        fwd_table = load_aware_forwarders(node_copies, G)
+    else:
+        raise ValueError(f"unknown forwarder rule {forwarders!r}")
     pt, pn = np.nonzero(present_node)      # pairs in (token, node) order
-    fwd = pn * G + owner[pt] % G
+    fwd = fwd_table[owner[pt], pn] if pt.size else np.zeros(0, dtype=np.int64)
     so = np.argsort(fwd, kind="stable")    # keeps token order inside a forwarder
     stage_src = pt[so]
     stage_node = pn[so]
@@ -125,7 +153,7 @@ def route_plan(idx: np.ndarray, num_experts: int, num_ranks: int,
     pos[stage_src, stage_node] = np.arange(D, dtype=np.int64)
     stage_of = pos[np.repeat(np.arange(T), k).reshape(T, k), node]
     plan.update(num_staged=D, stage_src=stage_src, stage_node=stage_node,
-                stage_offsets=stage_offsets, stage_of=stage_of)
+                stage_offsets=stage_offsets, stage_of=stage_of, forwarders=fwd_table)
     return plan
 
 

@@ -93,7 +93,7 @@ def check_combine_values(out, ref, yv, w, slot_of, out_f32, what) -> dict:
 class GpuRun:
     """One route plan + dispatch (+ combine) on the GPU through the C ABI."""
 
-    def __init__(self, batch, dev, node_dedup=None, poison=True):
+    def __init__(self, batch, dev, node_dedup=None, load_aware=False):
         wl = batch.workload
         self.wl, self.batch, self.dev = wl, batch, dev
         self.dedup = wl.node_dedup if node_dedup is None else node_dedup
@@ -101,7 +101,7 @@ class GpuRun:
         self.idx = to_dev(batch.topk_idx, dev)
         self.w = to_dev(batch.topk_w, dev)
         self.plan = cs.Plan(wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
-                            wl.ranks_per_node, self.dedup)
+                            wl.ranks_per_node, self.dedup, load_aware)
         p = self.plan
         # Guard rows after every output; poisoned so unwritten rows show.
         self.recv_full = torch.full((p.recv_rows + 4, wl.hidden), -1, dtype=torch.int16, device=dev)

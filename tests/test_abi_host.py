@@ -52,6 +52,10 @@ def make(T=128, H=256, E=8, k=2, R=2, G=None, flags=0):
     (dict(flags=_abi.FLAG_NODE_DEDUP), _abi.ERR_INVALID_ARGUMENT),  # one node: nothing to dedup
     (dict(R=2, G=1, flags=_abi.FLAG_NODE_DEDUP), _abi.OK),
     (dict(flags=4), _abi.ERR_INVALID_ARGUMENT),
+    (dict(R=2, G=1, flags=_abi.FLAG_LOAD_AWARE_FORWARDERS), _abi.ERR_INVALID_ARGUMENT),  # needs dedup
+    (dict(R=2, G=1, flags=_abi.FLAG_NODE_DEDUP | _abi.FLAG_LOAD_AWARE_FORWARDERS), _abi.OK),
+    (dict(E=1024, R=1024, G=1, flags=_abi.FLAG_NODE_DEDUP | _abi.FLAG_LOAD_AWARE_FORWARDERS),
+     _abi.ERR_UNSUPPORTED),                            # R*N past the key space
     (dict(T=1 << 28, k=8), _abi.ERR_UNSUPPORTED),     # T*k past 32-bit row indices
 ])
 def test_plan_create_status(kw, want):

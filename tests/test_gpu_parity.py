@@ -40,13 +40,15 @@ def check_plan(run: GpuRun, p: dict):
         assert np.array_equal(r.read("stage_offsets"), p["stage_offsets"])
         assert np.array_equal(r.read("stage_of").reshape(T, k), p["stage_of"])
         assert np.array_equal(r.read("stage_src")[:D], p["stage_src"])
+        assert np.array_equal(r.read("forwarders").reshape(wl.num_ranks, -1), p["forwarders"])
 
 
-def full_check(batch, dev, dedup=None, combine_tokens=None, traffic=False):
+def full_check(batch, dev, dedup=None, combine_tokens=None, traffic=False, load_aware=False):
     wl = batch.workload
-    say(f"[parity] {wl.describe()} dedup={dedup}")
-    p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node)
-    run = GpuRun(batch, dev, node_dedup=dedup).route().dispatch()
+    say(f"[parity] {wl.describe()} dedup={dedup} load_aware={load_aware}")
+    p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node,
+                          forwarders="load_aware" if load_aware else "static")
+    run = GpuRun(batch, dev, node_dedup=dedup, load_aware=load_aware).route().dispatch()
     torch.cuda.synchronize()
     check_plan(run, p)
     assert run.guards_intact()
@@ -217,3 +219,19 @@ def test_plan_reads_and_combine_without_dispatch(dev):
         run.route()
         out = run.combine(y=to_dev(y, dev))
         check_combine(bits(out), y, batch.topk_w, p["slot_of"], False, "no-dispatch-bf16")
+
+
+@pytest.mark.parametrize("case", [
+    (2048, 64, 64, 4, 16, 4), (3001, 40, 30, 5, 6, 2), (777, 24, 1024, 16, 32, 8), (20000, 16, 64, 8, 32, 4)],
+    ids=lambda c: "T{}-H{}-E{}-k{}-R{}-G{}".format(*c))
+def test_load_aware_forwarders(case, dev):
+    T, H, E, k, R, G = case
+    batch = gen.make_batch(gen.custom(T, H, E, k, R, G, seed=T))
+    full_check(batch, dev, dedup=True, load_aware=True)
+
+
+def test_load_aware_forwarders_dsv3(dev):
+    batch = gen.make_batch(gen.get("dsv3"))
+    T = batch.workload.num_tokens
+    sample = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(5).integers(0, T, 256)]))
+    full_check(batch, dev, combine_tokens=sample, load_aware=True)

@@ -66,12 +66,13 @@ def tiny_cases(draw):
     return E, R, G, k, T, H, idx, x, w
 
 
-@given(tiny_cases())
+@given(tiny_cases(), st.sampled_from(["static", "load_aware"]))
 @settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
-def test_plan_dispatch_combine_vs_brute(case):
+def test_plan_dispatch_combine_vs_brute(case, fwd_rule):
     E, R, G, k, T, H, idx, x, w = case
-    p = oracle.route_plan(idx, E, R, G)
-    b = brute.plan(idx.tolist(), E, R, G)
+    p = oracle.route_plan(idx, E, R, G, forwarders=fwd_rule)
+    b = brute.plan(idx.tolist(), E, R, G, forwarders=fwd_rule)
+    assert p["forwarders"].tolist() == b["forwarders"]
     for key in ("counts", "expert_offsets", "rank_offsets", "row_src", "send_rows",
                 "send_copies", "node_copies", "stage_src", "stage_node", "stage_offsets",
                 "num_staged"):
@@ -130,7 +131,7 @@ def check_plan_invariants(idx, p):
     for f in range(R):
         a, b = p["stage_offsets"][f], p["stage_offsets"][f + 1]
         assert np.all(p["stage_node"][a:b] == f // G)
-        assert np.all(owner[p["stage_src"][a:b]] % G == f % G)
+        assert np.all(p["forwarders"][owner[p["stage_src"][a:b]], f // G] == f)
         assert np.all(np.diff(p["stage_src"][a:b]) > 0)
     st_ = p["stage_of"]
     assert np.array_equal(p["stage_src"][st_], np.repeat(np.arange(T), k).reshape(T, k))
@@ -254,3 +255,52 @@ def test_combine_linear_in_weights():
     mag = _abs_scale(y, np.abs(w1) + np.abs(w2), p)
     k = b.topk_idx.shape[1]
     assert np.all(np.abs(lhs - rhs) <= (2.0 ** -24 + 4 * k * 2.0 ** -53) * mag)
+
+
+# ------------------------------------------------------------- load-aware forwarders
+
+def test_load_aware_hand_example():
+    # Node 0 loads (worked by hand): s0=5, s1=1, s2=3, s3=3 with G=2.  Ranked by
+    # load, ties to the lower source: s0, s2, s3, s1; snake deal 0,1,1,0 gives
+    # forwarder loads 5+1=6 and 3+3=6.
+    loads = np.array([[5], [1], [3], [3]])
+    fwd = oracle.shuffle.load_aware_forwarders(loads, 2)
+    assert fwd[:, 0].tolist() == [0, 0, 1, 1]
+    # the static rule would give (s % 2): loads 5+3=8 and 1+3=4
+    per = np.bincount(fwd[:, 0], weights=loads[:, 0], minlength=2)
+    assert per.tolist() == [6, 6]
+
+
+def _skewed_routing(T=2048, R=16, G=4, E=64, k=4, seed=0):
+    # Each quarter of the token range prefers one node: sources' loads per node
+    # differ a lot, which the static same-local-index rule cannot see.
+    rng = np.random.default_rng(seed)
+    N = R // G
+    per_node = E // N
+    band = np.arange(T) * 4 // T
+    idx = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        fav = int(band[t]) % N
+        heavy = rng.random() < 0.8
+        pool = np.arange(fav * per_node, (fav + 1) * per_node) if heavy else np.arange(E)
+        idx[t] = rng.permutation(pool)[:k]
+    return idx, E, R, G
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_load_aware_balances_forwarders(seed):
+    idx, E, R, G = _skewed_routing(seed=seed)
+    st_ = oracle.route_plan(idx, E, R, G, forwarders="static")
+    la = oracle.route_plan(idx, E, R, G, forwarders="load_aware")
+    check_plan_invariants(idx.astype(np.int64), la)
+    # same pairs staged either way, only their forwarders differ
+    assert la["num_staged"] == st_["num_staged"]
+    assert np.array_equal(la["node_copies"], st_["node_copies"])
+    loads = lambda p: np.diff(p["stage_offsets"]).reshape(R // G, G)
+    l_la, l_st = loads(la), loads(st_)
+    # per node: the snake deal keeps forwarders within one source's load of each other
+    biggest = la["node_copies"].max(axis=0)
+    assert np.all(l_la.max(axis=1) - l_la.min(axis=1) <= biggest)
+    assert l_la.max() <= l_st.max()
+    # each forwarder sits on its node, and every source sends a node's copies to one forwarder
+    assert np.all(la["forwarders"] // G == np.arange(R // G)[None, :])
