@@ -69,6 +69,9 @@ def parse():
                          "128-element block; single-hop workloads only)")
     ap.add_argument("--load-aware-forwarders", action="store_true",
                     help="node-deduplicated workloads: choose forwarders by load")
+    ap.add_argument("--hier-combine", action="store_true",
+                    help="node-deduplicated workloads: two-hop combine (fp32 partial per staging "
+                         "row, then the sum over the token's nodes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
@@ -185,9 +188,12 @@ def recorded_traffic(workload, kernel):
     return None
 
 
-def algorithmic_bytes(wl, D, payload="bf16"):
+def algorithmic_bytes(wl, D, payload="bf16", hier=False):
     row = 2 * wl.hidden
     T, k = wl.num_tokens, wl.top_k
+    if hier:
+        # hop 1 reads T*k rows and writes D fp32 partials; hop 2 reads them back
+        return (T + 2 * D + T * k) * row, (T * k + T) * row + 2 * D * 2 * row
     if payload == "fp8":
         # token rows are read (and combine results written) as bf16; the k
         # receive rows carry one byte per element plus a float32 per 128 elements
@@ -268,6 +274,7 @@ def main():
     w0 = torch.from_numpy(batch.topk_w).to(dev)
 
     la = args.load_aware_forwarders and wl.node_dedup
+    hier = args.hier_combine and wl.node_dedup
     probe = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la)
     set_bytes = (x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4 + probe.workspace_bytes
                  + probe.recv_rows * H * (1 if fp8 else 2) + probe.staging_rows_max * H * 2
@@ -281,6 +288,8 @@ def main():
                  staging=(torch.empty((plan.staging_rows_max, H), dtype=torch.int16, device=dev)
                           if wl.node_dedup else None),
                  out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+        if hier:
+            s["part"] = torch.empty((plan.staging_rows_max, H), dtype=torch.float32, device=dev)
         if fp8:
             s["recv"] = torch.empty((plan.recv_rows, H), dtype=torch.uint8, device=dev)
             s["scale"] = torch.empty((plan.recv_rows, plan.scale_blocks), dtype=torch.float32,
@@ -294,7 +303,9 @@ def main():
             s["plan"].dispatch(s["x"], s["recv"], s["staging"])
 
     def do_combine(s):
-        if fp8:
+        if hier:
+            s["plan"].combine_hier(s["recv"], s["w"], s["part"], s["out"])
+        elif fp8:
             s["plan"].combine_fp8(s["recv"], s["scale"], s["w"], s["out"])
         else:
             s["plan"].combine(s["recv"], s["w"], s["out"])
@@ -314,7 +325,7 @@ def main():
         fwd_rows = {"rule": "load_aware" if la else "static", "max": int(per.max()),
                     "mean": round(float(per.mean()), 1),
                     "max_over_mean": round(float(per.max() / max(per.mean(), 1e-9)), 4)}
-    disp_b, comb_b = algorithmic_bytes(wl, D, args.payload)
+    disp_b, comb_b = algorithmic_bytes(wl, D, args.payload, hier)
 
     # Timed region: K steps, nothing else on the stream.
     torch.cuda.synchronize()
@@ -343,7 +354,10 @@ def main():
     comb_ms = burst(do_combine)
     disp_gbs = disp_b / (disp_ms * 1e-3) / 1e9
     comb_gbs = comb_b / (comb_ms * 1e-3) / 1e9
-    if wl.node_dedup:
+    if hier:
+        # both phases are two launches here; report the combine phase
+        dom = ("combine_part_kernel+combine_nodes_kernel", comb_b, comb_ms, comb_gbs)
+    elif wl.node_dedup:
         # dispatch is two launches here; the dominant single launch timed is combine
         dom = ("combine_kernel", comb_b, comb_ms, comb_gbs)
     else:
@@ -367,13 +381,14 @@ def main():
         "config": {"workload": wl.name, "T": T, "H": H, "E": wl.num_experts, "k": k,
                    "R": wl.num_ranks, "G": wl.ranks_per_node, "node_dedup": wl.node_dedup,
                    "staging_rows": D, "seed": wl.seed, "buffer_sets": n_sets,
-                   "payload": args.payload, "forwarder_rows": fwd_rows},
+                   "payload": args.payload, "forwarder_rows": fwd_rows,
+                   "combine": "hierarchical" if hier else "direct"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "bytes_per_step": disp_b + comb_b,
         "phases": {"dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),
                                 "GB/s": round(disp_gbs, 1), "launches": 2 if wl.node_dedup else 1},
                    "combine": {"bytes": comb_b, "ms_per_launch": round(comb_ms, 5),
-                               "GB/s": round(comb_gbs, 1), "launches": 1}},
+                               "GB/s": round(comb_gbs, 1), "launches": 2 if hier else 1}},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[3], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(args.workload, dom[0]),

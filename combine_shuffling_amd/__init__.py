@@ -22,7 +22,7 @@ from . import _abi
 from ._abi import MoeError, ITEM  # noqa: F401
 
 __all__ = ["Plan", "MoeError", "expert_partition", "route_plan", "dispatch", "combine",
-           "dispatch_fp8", "combine_fp8"]
+           "dispatch_fp8", "combine_fp8", "combine_hier"]
 
 
 def expert_partition(num_experts: int, num_ranks: int) -> list[int]:
@@ -140,6 +140,30 @@ class Plan:
                                          _stream_handle(dev, stream)), "moe_combine")
         return out
 
+    # -- moe_combine_hier
+    def combine_hier(self, y: torch.Tensor, topk_w: torch.Tensor,
+                     partials: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                     out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+        """Two-hop combine of a node-deduplicated plan (fp32 partial per staging row)."""
+        dev = self.device
+        if dev is None:
+            raise MoeError(_abi.ERR_PLAN_NOT_ROUTED, "combine_hier")
+        _need(y, (self.recv_rows, self.H), _BF16_LIKE, "y", dev)
+        _need(topk_w, (self.T, self.k), (torch.float32,), "topk_w", dev)
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+        if partials is None:
+            partials = torch.empty((self.staging_rows_max, self.H), dtype=torch.float32, device=dev)
+        _need(partials, (self.staging_rows_max, self.H), (torch.float32,), "partials", dev)
+        if out is None:
+            out = torch.empty((self.T, self.H), dtype=out_dtype, device=dev)
+        _need(out, (self.T, self.H), (out_dtype,), "out", dev)
+        code = _abi.OUT_F32 if out_dtype == torch.float32 else _abi.OUT_BF16
+        _abi.check(self._lib.moe_combine_hier(self._h, _ptr(y), _ptr(topk_w), _ptr(partials),
+                                              _ptr(out), code, _stream_handle(dev, stream)),
+                   "moe_combine_hier")
+        return out
+
     # -- moe_dispatch_fp8
     def dispatch_fp8(self, x: torch.Tensor, recv8: torch.Tensor | None = None,
                      recv_scale: torch.Tensor | None = None, stream=None):
@@ -232,3 +256,9 @@ def combine_fp8(plan: Plan, y8: torch.Tensor, y_scale: torch.Tensor, topk_w: tor
                 out=None, out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
     """moe_combine_fp8: returns out [T, H] (bf16 or float32)."""
     return plan.combine_fp8(y8, y_scale, topk_w, out, out_dtype, stream)
+
+
+def combine_hier(plan: Plan, y: torch.Tensor, topk_w: torch.Tensor, partials=None, out=None,
+                 out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """moe_combine_hier: two-hop combine of a node-deduplicated plan."""
+    return plan.combine_hier(y, topk_w, partials, out, out_dtype, stream)

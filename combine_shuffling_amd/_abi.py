@@ -50,7 +50,7 @@ EXPORTS = (
     "moe_expert_partition", "moe_plan_create", "moe_plan_destroy", "moe_plan_workspace_bytes",
     "moe_plan_recv_rows", "moe_plan_staging_rows_max", "moe_route_plan", "moe_dispatch",
     "moe_combine", "moe_plan_read", "moe_status_str", "moe_plan_scale_blocks",
-    "moe_dispatch_fp8", "moe_combine_fp8",
+    "moe_dispatch_fp8", "moe_combine_fp8", "moe_combine_hier",
 )
 
 
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
     L.moe_dispatch_fp8.restype = i32
     L.moe_combine_fp8.argtypes = [vp, vp, vp, vp, vp, i32, vp]
     L.moe_combine_fp8.restype = i32
+    L.moe_combine_hier.argtypes = [vp, vp, vp, vp, vp, i32, vp]
+    L.moe_combine_hier.restype = i32
     L.moe_status_str.argtypes = [i32]
     L.moe_status_str.restype = ctypes.c_char_p
     _lib = L

@@ -259,6 +259,23 @@ moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, v
       moe::launch_combine(plan->d, y, topk_w, out, out_dtype == MOE_OUT_F32, plan->work, s));
 }
 
+moe_status moe_combine_hier(moe_plan* plan, const uint16_t* y, const float* topk_w,
+                            float* partials, void* out, int32_t out_dtype, void* stream) {
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
+  if (!plan->d.dedup) return MOE_ERR_INVALID_ARGUMENT;
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->d.T == 0) return MOE_OK;
+  if (!y || !topk_w || !partials || !out || !moe::aligned(y, 16) || !moe::aligned(topk_w, 4) ||
+      !moe::aligned(partials, 16) || !moe::aligned(out, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_status st = moe::ensure_assigned(plan, s);
+  if (st != MOE_OK) return st;
+  return moe::from_hip(moe::launch_combine_hier(plan->d, plan->idx, y, topk_w, partials, out,
+                                                out_dtype == MOE_OUT_F32, plan->work, s));
+}
+
 int64_t moe_plan_scale_blocks(const moe_plan* plan) {
   return plan ? ((int64_t)plan->d.H + 127) / 128 : 0;
 }

@@ -91,6 +91,11 @@ hipError_t launch_stage_b(const Dims& d, const uint16_t* staging, uint16_t* recv
                           hipStream_t s);
 hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* wts, void* out,
                           bool out_f32, const Work& w, hipStream_t s);
+// Two-hop combine of a node-deduplicated plan: fp32 partial per staging row,
+// then the sum over the token's nodes.  part: [smax, H] float32.
+hipError_t launch_combine_hier(const Dims& d, const int32_t* idx, const uint16_t* y,
+                               const float* wts, float* part, void* out, bool out_f32,
+                               const Work& w, hipStream_t s);
 // fp8 payload (OCP E4M3 codes, one power-of-two scale per 128-element block).
 hipError_t launch_gather_fp8(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
                              float* rscale, const Work& w, hipStream_t s);

@@ -248,6 +248,14 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
   }
 }
 
+__device__ __forceinline__ void unpack_bf16(u32x4 v, float (&f)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __uint_as_float(v[q] << 16);
+    f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
+  }
+}
+
 // float -> bf16 bits, round to nearest even; NaN becomes a quiet NaN.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -314,6 +322,115 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(Dims d, const u32x4* __
   }
 }
 
+// ---- hierarchical combine over the deduplication's staging rows ------------
+// Hop 1 (at the forwarder): one fp32 partial per staging row p = (token t,
+// node n), the fused multiply-add chain over t's slots on n in ascending j.
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void combine_part_kernel(Dims d, const u32x4* __restrict__ y,
+                                                              const float* __restrict__ wts,
+                                                              f32x4* __restrict__ part, Work w) {
+  const int staged = min(w.ctrl[kCtrlStaged], d.smax);
+  const int items = staged * d.segs;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  const Item it = wave_item<1>(d, items, 0);  // it.t is the staging row here
+  const int p = it.t;
+  const int t = it.live ? w.stage_src[p] : -1;
+  const bool tok = (uint32_t)t < (uint32_t)d.T;
+  const int64_t at = (int64_t)(tok ? t : 0) * d.k;
+  int slot[KMAX];
+  float wj[KMAX];
+  u32x4 v[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool mine = tok && j < d.k && w.stage_of[at + j] == p;
+    slot[j] = mine ? w.slot_of[at + j] : -1;
+    if ((uint32_t)slot[j] >= rows) slot[j] = -1;
+    wj[j] = mine ? wts[at + j] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (slot[j] >= 0 && it.ok) v[j] = load_chunk(&y[(int64_t)slot[j] * d.chunks + it.c]);
+  if (!it.ok) return;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (slot[j] < 0) continue;
+    float f[8];
+    unpack_bf16(v[j], f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj[j], f[q], acc[q]);
+  }
+  f32x4* o = part + ((int64_t)p * d.chunks + it.c) * 2;
+  store_chunk(o, f32x4{acc[0], acc[1], acc[2], acc[3]});
+  store_chunk(o + 1, f32x4{acc[4], acc[5], acc[6], acc[7]});
+}
+
+// Hop 2 (at the owner): out[t] = sum of t's partials in ascending node order
+// (one partial per node the token reached), then bf16 (nearest even) or fp32.
+template <int KMAX, bool F32OUT>
+__global__ __launch_bounds__(kBlock) void combine_nodes_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                               const f32x4* __restrict__ part,
+                                                               Work w, void* __restrict__ out) {
+  const int items = d.T * d.segs;
+  const uint32_t srows = (uint32_t)d.smax;
+  const Item it = wave_item<1>(d, items, 0);
+  const int64_t at = (int64_t)it.t * d.k;
+  int p[KMAX], node[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool has = it.live && j < d.k;
+    p[j] = has ? w.stage_of[at + j] : -1;
+    if ((uint32_t)p[j] >= srows) p[j] = -1;
+#pragma unroll
+    for (int jj = 0; jj < j; ++jj)
+      if (p[jj] == p[j]) p[j] = -1;  // a later slot of an already seen node
+    node[j] = p[j] >= 0 ? split_part(idx[at + j], d.ebase, d.erem) / d.G : 0x7fffffff;
+  }
+  f32x4 a[KMAX], b[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (p[j] >= 0 && it.ok) {
+      const f32x4* src = part + ((int64_t)p[j] * d.chunks + it.c) * 2;
+      a[j] = __builtin_nontemporal_load(src);
+      b[j] = __builtin_nontemporal_load(src + 1);
+    }
+  }
+  if (!it.ok) return;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+  // Add the partials in ascending node order (nodes of distinct rows differ).
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (p[j] < 0) continue;
+      int rank = 0;
+#pragma unroll
+      for (int jj = 0; jj < KMAX; ++jj) rank += (p[jj] >= 0 && node[jj] < node[j]) ? 1 : 0;
+      if (rank != r) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q] += a[j][q];
+        acc[4 + q] += b[j][q];
+      }
+    }
+  }
+  const int64_t i = (int64_t)it.t * d.chunks + it.c;
+  if constexpr (F32OUT) {
+    f32x4* o = reinterpret_cast<f32x4*>(out) + i * 2;
+    store_chunk(o, f32x4{acc[0], acc[1], acc[2], acc[3]});
+    store_chunk(o + 1, f32x4{acc[4], acc[5], acc[6], acc[7]});
+  } else {
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
+    store_chunk(reinterpret_cast<u32x4*>(out) + i, r);
+  }
+}
+
 // ---- fp8 payload -----------------------------------------------------------
 // OCP E4M3 codes; each row is cut into blocks of 128 elements (16 lanes x 8),
 // each block scaled by the smallest power of two 2^e with amax <= 448 * 2^e.
@@ -328,14 +445,6 @@ __device__ __forceinline__ int fp8_block_exp(float amax) {
   const float m = frexpf(amax, &p);  // amax = m * 2^p, m in [0.5, 1)
   const int e = p - 9 + (m > 0.875f ? 1 : 0);
   return min(max(e, -126), 127);
-}
-
-__device__ __forceinline__ void unpack_bf16(u32x4 v, float (&f)[8]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f[2 * q] = __uint_as_float(v[q] << 16);
-    f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
-  }
 }
 
 // 8 floats (already scaled) -> 8 E4M3 codes, element i in byte i.
@@ -622,7 +731,37 @@ struct CombineFp8Launch {
   }
 };
 
+template <int KMAX>
+struct CombineHierLaunch {
+  static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* y, const float* wts,
+                        float* part, void* out, bool f32, const Work& w, hipStream_t s) {
+    const int64_t part_items = (int64_t)d.smax * d.segs;
+    const int part_blocks = (int)((part_items + kWaves - 1) / kWaves);
+    if (part_blocks > 0)
+      hipLaunchKernelGGL((combine_part_kernel<KMAX>), dim3(part_blocks), dim3(kBlock), 0, s, d,
+                         reinterpret_cast<const u32x4*>(y), wts, reinterpret_cast<f32x4*>(part),
+                         w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const f32x4* pp = reinterpret_cast<const f32x4*>(part);
+    if (f32)
+      hipLaunchKernelGGL((combine_nodes_kernel<KMAX, true>), dim3(blocks_for(d, 1)), dim3(kBlock),
+                         0, s, d, idx, pp, w, out);
+    else
+      hipLaunchKernelGGL((combine_nodes_kernel<KMAX, false>), dim3(blocks_for(d, 1)), dim3(kBlock),
+                         0, s, d, idx, pp, w, out);
+    return hipGetLastError();
+  }
+};
+
 }  // namespace
+
+hipError_t launch_combine_hier(const Dims& d, const int32_t* idx, const uint16_t* y,
+                               const float* wts, float* part, void* out, bool out_f32,
+                               const Work& w, hipStream_t s) {
+  if (d.T == 0) return hipSuccess;
+  return by_topk<CombineHierLaunch>(d.k, d, idx, y, wts, part, out, out_f32, w, s);
+}
 
 hipError_t launch_gather_fp8(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
                              float* rscale, const Work& w, hipStream_t s) {

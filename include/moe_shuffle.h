@@ -172,6 +172,20 @@ moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint1
 moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
                        int32_t out_dtype, void* stream);
 
+/* Hierarchical combine for plans with MOE_FLAG_NODE_DEDUP: the return path
+ * of the forwarding GPU (FUSCO article, "load balancing and cross-node
+ * deduplication") with the reduction done where the data meets (INC-MoE
+ * abstract, ReduceScatter combine).  Hop 1, at the forwarder: one float32
+ * partial per staging row (token t, node n), the fused multiply-add chain of
+ * topk_w[t, j] * y[slot_of[t, j]] over t's slots on n in ascending j; hop 2,
+ * at the owner: out[t] = sum of t's partials in ascending node order, then
+ * bf16 (nearest even) or float32.  partials: device [staging_rows_max, H]
+ * float32 scratch owned by the caller (first D rows written).  Two launches;
+ * asynchronous.  Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT (not a dedup
+ * plan, bad pointers), HIP. */
+moe_status moe_combine_hier(moe_plan* plan, const uint16_t* y, const float* topk_w,
+                            float* partials, void* out, int32_t out_dtype, void* stream);
+
 /* ---- fp8 payload ----------------------------------------------------------
  * Low-precision payload for dispatch and combine (TensorRT-LLM PR #13888,
  * opt-in gate commit message: an fp8 low-precision combine is among the

@@ -43,5 +43,7 @@ from .shuffle import (  # noqa: F401
     dedup_stage_b,
     combine,
     combine_by_rank_partials,
+    combine_hierarchical,
+    load_aware_forwarders,
     roundtrip,
 )

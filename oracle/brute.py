@@ -146,3 +146,25 @@ def combine(y: list[list[int]], w: list[list[float]], p: dict) -> list[list[floa
             row.append(acc)
         out.append(row)
     return out
+
+
+def combine_hierarchical(y: list[list[int]], w: list[list[float]], p: dict) -> list[list[float]]:
+    """Partials per (token, node), then the sum over the token's nodes in node order."""
+    T = len(p["slot_of"])
+    k = len(p["slot_of"][0]) if T else 0
+    H = len(y[0]) if y else 0
+    out = []
+    for t in range(T):
+        nodes = sorted(set(p["stage_node"][p["stage_of"][t][j]] for j in range(k)))
+        row = []
+        for h in range(H):
+            acc = 0.0
+            for n in nodes:
+                part = 0.0
+                for j in range(k):
+                    if p["stage_node"][p["stage_of"][t][j]] == n:
+                        part += float(w[t][j]) * bf16_value(y[p["slot_of"][t][j]][h])
+                acc += part
+            row.append(acc)
+        out.append(row)
+    return out

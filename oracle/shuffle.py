@@ -243,6 +243,33 @@ def combine_by_rank_partials(y: np.ndarray, w: np.ndarray, plan: dict) -> np.nda
     return total
 
 
+def combine_hierarchical(y: np.ndarray, w: np.ndarray, plan: dict):
+    """Two-hop combine over the deduplication's staging rows (float64).
+
+    The return path of the forwarding GPU (FUSCO article, "load balancing
+    and cross-node deduplication") with the ReduceScatter-style reduction of
+    the INC-MoE abstract: at the forwarder, one partial per staging row
+    p = (token t, node n), part[p] = sum over t's slots on n (ascending j) of
+    w[t, j] * y[slot_of[t, j]]; at the owner, out[t] = sum of t's partials in
+    ascending node order.  Returns (out [T, H], part [D, H]).
+    """
+    ya = np.asarray(y, dtype=np.uint16)
+    wa = np.asarray(w, dtype=np.float32).astype(np.float64)
+    slot_of, stage_of = plan["slot_of"], plan["stage_of"]
+    T, k = slot_of.shape
+    H = ya.shape[1] if ya.ndim == 2 else 0
+    D = plan["num_staged"]
+    part = np.zeros((D, H), dtype=np.float64)
+    for j in range(k):
+        rows = bf16_to_f32(ya[slot_of[:, j]]).astype(np.float64)
+        np.add.at(part, stage_of[:, j], wa[:, j:j + 1] * rows)
+    out = np.zeros((T, H), dtype=np.float64)
+    node_order = np.argsort(plan["stage_node"], kind="stable")
+    for p in node_order:                    # ascending node; each token has one row per node
+        out[plan["stage_src"][p]] += part[p]
+    return out, part
+
+
 def roundtrip(x: np.ndarray, w: np.ndarray, plan: dict) -> np.ndarray:
     """Dispatch, identity expert, combine: float64 [T, H]."""
     return combine(dispatch(x, plan), w, plan)

@@ -61,12 +61,16 @@ def check_combine(out: np.ndarray, y: np.ndarray, w: np.ndarray, slot_of: np.nda
     return check_combine_values(out, ref, yv, w, slot_of, out_f32, what)
 
 
-def check_combine_values(out, ref, yv, w, slot_of, out_f32, what) -> dict:
-    """Same bars with the receive rows given as their (exact) float64 values yv."""
+def check_combine_values(out, ref, yv, w, slot_of, out_f32, what, roundings=None) -> dict:
+    """Same bars with the receive rows given as their (exact) float64 values yv.
+
+    roundings: float32 roundings on the way to each output (default k: the
+    FMA chain; the two-hop combine adds one per extra node).
+    """
     k = slot_of.shape[1]
     wa = np.abs(np.asarray(w, dtype=np.float64))
     scale = sum(wa[:, j:j + 1] * np.abs(yv[slot_of[:, j]]) for j in range(k))
-    acc_err = k * U32 * scale * (1 + 1e-3)
+    acc_err = (k if roundings is None else roundings) * U32 * scale * (1 + 1e-3)
     if out_f32:
         got = out.astype(np.float64)
         bound = 1e-3 * np.abs(ref) + acc_err

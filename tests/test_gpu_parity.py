@@ -12,7 +12,7 @@ import torch
 import oracle
 from workloads import gen
 
-from gpu_util import GpuRun, bits, check_combine, say, to_dev
+from gpu_util import GpuRun, bits, check_combine, check_combine_values, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -235,3 +235,75 @@ def test_load_aware_forwarders_dsv3(dev):
     T = batch.workload.num_tokens
     sample = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(5).integers(0, T, 256)]))
     full_check(batch, dev, combine_tokens=sample, load_aware=True)
+
+
+def hier_check(batch, dev, load_aware, tokens=None):
+    wl = batch.workload
+    say(f"[hier] {wl.describe()} load_aware={load_aware}")
+    p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node,
+                          forwarders="load_aware" if load_aware else "static")
+    run = GpuRun(batch, dev, node_dedup=True, load_aware=load_aware).route().dispatch()
+    y = bits(run.recv)
+    tok = np.arange(wl.num_tokens) if tokens is None else np.asarray(tokens)
+    # The plan restricted to the checked tokens and their staging rows, renumbered.
+    rows = np.unique(p["stage_of"][tok])
+    sub = dict(slot_of=p["slot_of"][tok], stage_of=np.searchsorted(rows, p["stage_of"][tok]),
+               stage_src=np.searchsorted(tok, p["stage_src"][rows]),
+               stage_node=p["stage_node"][rows], num_staged=len(rows))
+    w = batch.topk_w[tok]
+    ref, ref_part = oracle.combine_hierarchical(y, w, sub)
+    yv = oracle.bf16_to_f32(y).astype(np.float64)
+    k, N = wl.top_k, wl.num_ranks // wl.ranks_per_node
+    # a partial is an FMA chain over at most k slots
+    part_scale = np.zeros_like(ref_part)
+    for j in range(k):
+        np.add.at(part_scale, sub["stage_of"][:, j], np.abs(w[:, j:j + 1]) * np.abs(yv[sub["slot_of"][:, j]]))
+    D = p["num_staged"]
+    for out_dtype in (torch.float32, torch.bfloat16):
+        part = torch.full((run.plan.staging_rows_max, wl.hidden), float("nan"),
+                          dtype=torch.float32, device=dev)
+        out = run.plan.combine_hier(run.recv, run.w, partials=part, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert not torch.isnan(part[:D]).any(), "a staging row's partial was not written"
+        gp = part[torch.as_tensor(rows, device=dev)].cpu().numpy().astype(np.float64)
+        perr = np.abs(gp - ref_part)
+        assert np.all(perr <= k * 2.0 ** -24 * part_scale * 1.001), float(perr.max())
+        o = out.cpu().numpy() if out_dtype == torch.float32 else bits(out)
+        check_combine_values(o[tok], ref, yv, w, sub["slot_of"], out_dtype == torch.float32,
+                             wl.name + " hier", roundings=k + N)
+
+
+@pytest.mark.parametrize("load_aware", [False, True])
+@pytest.mark.parametrize("case", [
+    (1000, 64, 32, 4, 8, 2), (3001, 40, 30, 5, 6, 2), (777, 24, 1024, 16, 32, 8),
+    (2048, 256, 256, 8, 64, 8)], ids=lambda c: "T{}-H{}-E{}-k{}-R{}-G{}".format(*c))
+def test_hierarchical_combine(case, load_aware, dev):
+    T, H, E, k, R, G = case
+    hier_check(gen.make_batch(gen.custom(T, H, E, k, R, G, seed=T + k)), dev, load_aware)
+
+
+def test_hierarchical_combine_dsv3(dev):
+    batch = gen.make_batch(gen.get("dsv3"))
+    T = batch.workload.num_tokens
+    tok = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(9).integers(0, T, 512)]))
+    hier_check(batch, dev, False, tokens=tok)
+
+
+def test_hierarchical_combine_without_dispatch(dev):
+    # Route, then combine rows that were placed by someone else: the plan fills
+    # its per-slot tables itself.
+    import combine_shuffling_amd as cs
+
+    batch = gen.make_batch(gen.custom(900, 32, 64, 6, 16, 4, seed=17))
+    wl = batch.workload
+    p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node)
+    y = oracle.dispatch(batch.x, p)
+    plan = cs.Plan(wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
+                   wl.ranks_per_node, True)
+    plan.route(to_dev(batch.topk_idx, dev))
+    out = plan.combine_hier(to_dev(y, dev), to_dev(batch.topk_w, dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, _ = oracle.combine_hierarchical(y, batch.topk_w, p)
+    yv = oracle.bf16_to_f32(y).astype(np.float64)
+    check_combine_values(out.cpu().numpy(), ref, yv, batch.topk_w, p["slot_of"], True,
+                         "hier without dispatch", roundings=wl.top_k + 4)

@@ -304,3 +304,34 @@ def test_load_aware_balances_forwarders(seed):
     assert l_la.max() <= l_st.max()
     # each forwarder sits on its node, and every source sends a node's copies to one forwarder
     assert np.all(la["forwarders"] // G == np.arange(R // G)[None, :])
+
+
+# ------------------------------------------------------------- hierarchical combine
+
+@given(tiny_cases(), st.sampled_from(["static", "load_aware"]))
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+def test_hierarchical_combine_vs_brute(case, fwd_rule):
+    E, R, G, k, T, H, idx, x, w = case
+    p = oracle.route_plan(idx, E, R, G, forwarders=fwd_rule)
+    b = brute.plan(idx.tolist(), E, R, G, forwarders=fwd_rule)
+    y = oracle.dispatch(x, p)
+    out, part = oracle.combine_hierarchical(y, w, p)
+    ref = brute.combine_hierarchical(y.tolist(), w.tolist(), b)
+    assert np.array_equal(out, np.array(ref, dtype=np.float64).reshape(T, H), equal_nan=True)
+    assert part.shape == (p["num_staged"], H)
+
+
+def test_hierarchical_combine_equals_direct():
+    b = gen.make_batch(gen.custom(700, 64, 256, 8, 64, 8, routing="node_limited",
+                                  nodes_per_token=4, node_score_topn=2, seed=3))
+    p = oracle.route_plan(b.topk_idx, 256, 64, 8)
+    y = oracle.dispatch(b.x, p)
+    h, part = oracle.combine_hierarchical(y, b.topk_w, p)
+    d = oracle.combine(y, b.topk_w, p)
+    k, N = 8, 8
+    assert np.all(np.abs(h - d) <= (k + N) * 2.0 ** -53 * 2 * _abs_scale(y, b.topk_w, p))
+    # partials of one token add up, node by node, to the token's output
+    t = 5
+    rows = [q for q in range(p["num_staged"]) if p["stage_src"][q] == t]
+    assert len(rows) == len(set(p["stage_node"][rows]))
+    assert np.allclose(part[rows].sum(axis=0), d[t], rtol=0, atol=1e-12)
