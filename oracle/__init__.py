@@ -22,6 +22,9 @@ pure-Python loops for tiny inputs.  Sources, by page title and section:
   * INC-MoE abstract (weekinpapers 2610.36339): dispatch sends tokens to the
     ranks holding their experts, combine returns expert outputs to each
     token's owner; the AllGather / ReduceScatter formulation;
+  * INC-MoE abstract: tokens partitioned into bands that pass through the
+    dispatch / expert / combine pipeline one after another
+    (``route_plan_banded``: each band routed as its own batch);
   * TensorRT-LLM PR #13888 ("support non-divisible EP in MoE alltoall"):
     the ceil/floor contiguous expert-to-rank partition, its printed cases,
     and the rejection of fewer experts than ranks.
@@ -38,6 +41,7 @@ from .shuffle import (  # noqa: F401
     validate_routing,
     expert_counts,
     route_plan,
+    route_plan_banded,
     dispatch,
     dedup_stage_a,
     dedup_stage_b,

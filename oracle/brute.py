@@ -168,3 +168,34 @@ def combine_hierarchical(y: list[list[int]], w: list[list[float]], p: dict) -> l
             row.append(acc)
         out.append(row)
     return out
+
+
+def plan_banded(idx: list[list[int]], E: int, R: int, band: int) -> dict:
+    """Each band of `band` consecutive tokens routed on its own, rows numbered on from t0*k."""
+    T = len(idx)
+    k = len(idx[0]) if T else 0
+    estarts = _part_starts(E, R)
+    nb = max(1, (T + band - 1) // band)
+    slot_of = [[None] * k for _ in range(T)]
+    row_src = [None] * (T * k)
+    counts, eoff, roff = [], [], []
+    for b in range(nb):
+        t0, t1 = b * band, min((b + 1) * band, T)
+        nxt = t0 * k
+        c = [0] * E
+        offs = []
+        for e in range(E):
+            offs.append(nxt)
+            for t in range(t0, t1):
+                for j in range(k):
+                    if idx[t][j] == e:
+                        slot_of[t][j] = nxt
+                        row_src[nxt] = t
+                        nxt += 1
+                        c[e] += 1
+        offs.append(nxt)
+        counts.append(c)
+        eoff.append(offs)
+        roff.append([offs[estarts[d]] for d in range(R + 1)])
+    return dict(slot_of=slot_of, row_src=row_src, counts=counts, expert_offsets=eoff,
+                rank_offsets=roff, num_bands=nb)

@@ -157,6 +157,45 @@ def route_plan(idx: np.ndarray, num_experts: int, num_ranks: int,
     return plan
 
 
+def route_plan_banded(idx: np.ndarray, num_experts: int, num_ranks: int, band: int) -> dict:
+    """Route plan of a batch cut into bands of `band` consecutive tokens.
+
+    INC-MoE abstract: the tokens are partitioned into bands that pass through
+    the dispatch, expert and combine stages one after another.  The reading
+    taken: each band is routed as a batch of its own.  Band b holds tokens
+    [t0, t1) = [b*band, min((b+1)*band, T)) and owns receive rows
+    [t0*k, t1*k), laid out inside like a whole batch's receive buffer (ranks,
+    then experts, then tokens ascending).  Returns slot_of [T, k] and
+    row_src [T*k] as global rows, and per band counts [nb, E],
+    expert_offsets [nb, E+1] and rank_offsets [nb, R+1] (global rows), with
+    nb = max(1, ceil(T / band)).  The modelled link traffic and the token
+    owners do not depend on the layout: they are the whole batch's.
+    """
+    if band <= 0:
+        raise ValueError("band must be positive")
+    a = validate_routing(idx, num_experts)
+    T, k = a.shape
+    nb = max(1, -(-T // band))
+    plan = route_plan(a, num_experts, num_ranks)
+    slot_of = np.empty((T, k), dtype=np.int64)
+    row_src = np.empty(T * k, dtype=np.int64)
+    counts, eoff, roff = [], [], []
+    for b in range(nb):
+        t0, t1 = b * band, min((b + 1) * band, T)
+        p = route_plan(a[t0:t1], num_experts, num_ranks)
+        base = t0 * k
+        slot_of[t0:t1] = p["slot_of"] + base
+        row_src[base:t1 * k] = p["row_src"] + t0
+        counts.append(p["counts"])
+        eoff.append(p["expert_offsets"] + base)
+        roff.append(p["rank_offsets"] + base)
+    plan.update(band=band, num_bands=nb, slot_of=slot_of, row_src=row_src,
+                counts=np.array(counts, dtype=np.int64),
+                expert_offsets=np.array(eoff, dtype=np.int64),
+                rank_offsets=np.array(roff, dtype=np.int64))
+    return plan
+
+
 def dispatch(x: np.ndarray, plan: dict) -> np.ndarray:
     """Single-hop dispatch: recv[r] = x[row_src[r]], a bit copy of each row.
 

@@ -335,3 +335,56 @@ def test_hierarchical_combine_equals_direct():
     rows = [q for q in range(p["num_staged"]) if p["stage_src"][q] == t]
     assert len(rows) == len(set(p["stage_node"][rows]))
     assert np.allclose(part[rows].sum(axis=0), d[t], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------- banded route plan
+
+def test_banded_hand_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "banded_example.json")))
+    idx = np.array(g["topk_idx"], dtype=np.int32)
+    p = oracle.route_plan_banded(idx, g["E"], g["R"], g["band"])
+    for key in ("slot_of", "row_src", "counts", "expert_offsets", "rank_offsets"):
+        assert np.asarray(p[key]).tolist() == g["expected"][key], key
+    assert oracle.route_plan(idx, g["E"], g["R"])["slot_of"].tolist() == \
+        g["expected"]["unbanded_slot_of"]
+
+
+@given(tiny_cases(), st.integers(1, 7))
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+def test_banded_plan_vs_brute(case, band):
+    E, R, G, k, T, H, idx, x, w = case
+    p = oracle.route_plan_banded(idx, E, R, band)
+    b = brute.plan_banded(idx.tolist(), E, R, band)
+    assert p["num_bands"] == b["num_bands"]
+    for key in ("slot_of", "row_src", "counts", "expert_offsets", "rank_offsets"):
+        assert np.asarray(p[key]).tolist() == b[key], key
+
+
+@pytest.mark.parametrize("band", [256, 1000, 4096, 5000])
+def test_banded_plan_invariants(band):
+    batch = gen.make_batch(gen.custom(4096, 16, 64, 8, 4, 4, seed=2))
+    idx, w = batch.topk_idx, batch.topk_w
+    T, k = idx.shape
+    p = oracle.route_plan_banded(idx, 64, 4, band)
+    whole = oracle.route_plan(idx, 64, 4)
+    if band >= T:       # one band is the unbanded plan
+        for key in ("slot_of", "row_src", "counts", "expert_offsets", "rank_offsets"):
+            assert np.array_equal(np.asarray(p[key]).reshape(np.asarray(whole[key]).shape), whole[key])
+    assert np.array_equal(np.sort(p["slot_of"].ravel()), np.arange(T * k))
+    assert np.array_equal(p["row_src"][p["slot_of"]], np.repeat(np.arange(T), k).reshape(T, k))
+    assert np.array_equal(p["counts"].sum(axis=0), oracle.expert_counts(idx, 64))
+    for b in range(p["num_bands"]):
+        t0, t1 = b * band, min((b + 1) * band, T)
+        rows = p["slot_of"][t0:t1]
+        assert rows.min() >= t0 * k and rows.max() < t1 * k
+        # inside a band: experts ascending, tokens ascending inside an expert
+        e_of_row = np.empty(T * k, dtype=np.int64)
+        e_of_row[p["slot_of"].ravel()] = idx.ravel()
+        seg = slice(t0 * k, t1 * k)
+        key = e_of_row[seg] * T + p["row_src"][seg]
+        assert np.all(np.diff(key) > 0)
+        assert p["expert_offsets"][b][0] == t0 * k and p["expert_offsets"][b][-1] == t1 * k
+    # the combine of a token does not depend on where its rows sit
+    y = oracle.dispatch(batch.x, p)
+    assert np.array_equal(oracle.combine(y, w, p), oracle.combine(oracle.dispatch(batch.x, whole), w, whole))
+    assert np.array_equal(p["send_rows"], whole["send_rows"])
