@@ -53,7 +53,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "dispatch+combine effective GB/s and % of HBM peak, 1 MI355X"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("combine_shuffling_amd/csrc/move.hip", "combine_shuffling_amd/csrc/moe_device.h",
+KERNEL_SOURCES = ("combine_shuffling_amd/csrc/move.hip", "combine_shuffling_amd/csrc/move_body.h",
+                  "combine_shuffling_amd/csrc/pipeline.hip", "combine_shuffling_amd/csrc/plan_body.h",
+                  "combine_shuffling_amd/csrc/moe_device.h",
                   "combine_shuffling_amd/csrc/moe_internal.h")
 
 
@@ -72,6 +74,11 @@ def parse():
     ap.add_argument("--hier-combine", action="store_true",
                     help="node-deduplicated workloads: two-hop combine (fp32 partial per staging "
                          "row, then the sum over the token's nodes)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="single-hop workloads: route, dispatch and combine of every band of "
+                         "tokens in one persistent launch (banded plan)")
+    ap.add_argument("--band-tokens", type=int, default=2048,
+                    help="tokens per band with --pipeline (a multiple of 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
@@ -204,7 +211,7 @@ def algorithmic_bytes(wl, D, payload="bf16", hier=False):
     return disp, comb
 
 
-def cpu_baseline(batch, seconds, payload="bf16"):
+def cpu_baseline(batch, seconds, payload="bf16", band=0):
     """The oracle (numpy, as it stands) timed on this host on the same batch."""
     import oracle
     from oracle import fp8 as ofp8
@@ -213,7 +220,10 @@ def cpu_baseline(batch, seconds, payload="bf16"):
     reps, t0 = 0, time.perf_counter()
     D = 0
     while True:
-        p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node)
+        if band:
+            p = oracle.route_plan_banded(batch.topk_idx, wl.num_experts, wl.num_ranks, band)
+        else:
+            p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node)
         if payload == "fp8":
             codes, exps = ofp8.dispatch_fp8(batch.x, p)
             ofp8.combine_fp8(codes, exps, batch.topk_w, p)
@@ -223,7 +233,7 @@ def cpu_baseline(batch, seconds, payload="bf16"):
             else:
                 recv = oracle.dispatch(batch.x, p)
             oracle.combine(recv, batch.topk_w, p)
-        D = p["num_staged"]
+        D = p.get("num_staged", 0)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -231,8 +241,9 @@ def cpu_baseline(batch, seconds, payload="bf16"):
     disp, comb = algorithmic_bytes(wl, D, payload)
     return {"value": round((disp + comb) * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{reps} full passes of the {wl.name} batch ({payload} payload: route "
-                      f"plan, dispatch, combine in float64) in {el:.1f} s on 1 thread; "
+            "sample": f"{reps} full passes of the {wl.name} batch ({payload} payload: "
+                      f"{'banded ' if band else ''}route plan, dispatch, combine in float64) "
+                      f"in {el:.1f} s on 1 thread; "
                       f"os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"}
 
 
@@ -275,14 +286,22 @@ def main():
 
     la = args.load_aware_forwarders and wl.node_dedup
     hier = args.hier_combine and wl.node_dedup
-    probe = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la)
+    pipe = args.pipeline
+    if pipe and (wl.node_dedup or fp8):
+        print("the banded pipeline runs single-hop workloads with the bf16 payload",
+              file=sys.stderr)
+        sys.exit(2)
+    band = args.band_tokens if pipe else 0
+    probe = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la,
+                    band)
     set_bytes = (x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4 + probe.workspace_bytes
                  + probe.recv_rows * H * (1 if fp8 else 2) + probe.staging_rows_max * H * 2
                  + T * H * 2)
     n_sets = args.sets or max(2, math.ceil((2 << 30) / set_bytes))
     sets = []
     for _ in range(n_sets):
-        plan = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la)
+        plan = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la,
+                       band)
         s = dict(plan=plan, x=x0.clone(), idx=idx0.clone(), w=w0.clone(),
                  recv=torch.empty((plan.recv_rows, H), dtype=torch.int16, device=dev),
                  staging=(torch.empty((plan.staging_rows_max, H), dtype=torch.int16, device=dev)
@@ -311,6 +330,9 @@ def main():
             s["plan"].combine(s["recv"], s["w"], s["out"])
 
     def step(s):
+        if pipe:
+            s["plan"].pipeline(s["idx"], s["x"], s["w"], s["recv"], s["out"])
+            return
         s["plan"].route(s["idx"])
         do_dispatch(s)
         do_combine(s)
@@ -350,11 +372,20 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    disp_ms = burst(do_dispatch)
-    comb_ms = burst(do_combine)
-    disp_gbs = disp_b / (disp_ms * 1e-3) / 1e9
-    comb_gbs = comb_b / (comb_ms * 1e-3) / 1e9
-    if hier:
+    if pipe:
+        # one launch per step does everything; the bursts of the separate
+        # kernels do not exist here
+        pipe_ms = burst(step)
+        disp_ms = comb_ms = pipe_ms
+        disp_gbs = comb_gbs = (disp_b + comb_b) / (pipe_ms * 1e-3) / 1e9
+    else:
+        disp_ms = burst(do_dispatch)
+        comb_ms = burst(do_combine)
+        disp_gbs = disp_b / (disp_ms * 1e-3) / 1e9
+        comb_gbs = comb_b / (comb_ms * 1e-3) / 1e9
+    if pipe:
+        dom = ("pipeline_kernel", disp_b + comb_b, pipe_ms, disp_gbs)
+    elif hier:
         # both phases are two launches here; report the combine phase
         dom = ("combine_part_kernel+combine_nodes_kernel", comb_b, comb_ms, comb_gbs)
     elif wl.node_dedup:
@@ -382,13 +413,16 @@ def main():
                    "R": wl.num_ranks, "G": wl.ranks_per_node, "node_dedup": wl.node_dedup,
                    "staging_rows": D, "seed": wl.seed, "buffer_sets": n_sets,
                    "payload": args.payload, "forwarder_rows": fwd_rows,
-                   "combine": "hierarchical" if hier else "direct"},
+                   "combine": "hierarchical" if hier else "direct",
+                   "path": f"pipeline, bands of {band} tokens" if pipe else "separate launches"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "bytes_per_step": disp_b + comb_b,
-        "phases": {"dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),
-                                "GB/s": round(disp_gbs, 1), "launches": 2 if wl.node_dedup else 1},
-                   "combine": {"bytes": comb_b, "ms_per_launch": round(comb_ms, 5),
-                               "GB/s": round(comb_gbs, 1), "launches": 2 if hier else 1}},
+        "phases": ({"pipeline": {"bytes": disp_b + comb_b, "ms_per_launch": round(pipe_ms, 5),
+                                 "GB/s": round(disp_gbs, 1), "launches": 1}} if pipe else
+                   {"dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),
+                                 "GB/s": round(disp_gbs, 1), "launches": 2 if wl.node_dedup else 1},
+                    "combine": {"bytes": comb_b, "ms_per_launch": round(comb_ms, 5),
+                                "GB/s": round(comb_gbs, 1), "launches": 2 if hier else 1}}),
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[3], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(args.workload, dom[0]),
@@ -396,7 +430,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, args.payload)
+        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, args.payload, band)
     print(json.dumps(result), flush=True)
 
 

@@ -9,6 +9,10 @@ module only checks shapes and passes pointers.
                       ranks_per_node=G, node_dedup=False)
     recv, staging = dispatch(plan, x)           # x: [T, H] bf16 on the GPU
     out = combine(plan, y, topk_w)              # y: [T*k, H] bf16, receive layout
+
+Banded plans (band_tokens > 0) route each band of consecutive tokens as its
+own batch; ``Plan.pipeline`` runs route, dispatch and combine of every band
+in one persistent launch.
 """
 
 from __future__ import annotations
@@ -22,7 +26,7 @@ from . import _abi
 from ._abi import MoeError, ITEM  # noqa: F401
 
 __all__ = ["Plan", "MoeError", "expert_partition", "route_plan", "dispatch", "combine",
-           "dispatch_fp8", "combine_fp8", "combine_hier"]
+           "dispatch_fp8", "combine_fp8", "combine_hier", "pipeline"]
 
 
 def expert_partition(num_experts: int, num_ranks: int) -> list[int]:
@@ -62,11 +66,12 @@ class Plan:
 
     def __init__(self, num_tokens: int, hidden: int, num_experts: int, top_k: int,
                  num_ranks: int, ranks_per_node: int | None = None, node_dedup: bool = False,
-                 load_aware_forwarders: bool = False):
+                 load_aware_forwarders: bool = False, band_tokens: int = 0):
         G = num_ranks if ranks_per_node is None else ranks_per_node
         flags = (_abi.FLAG_NODE_DEDUP if node_dedup else 0) | \
             (_abi.FLAG_LOAD_AWARE_FORWARDERS if load_aware_forwarders else 0)
-        self.cfg = _abi.MoeConfig(num_tokens, hidden, num_experts, top_k, num_ranks, G, flags)
+        self.cfg = _abi.MoeConfig(num_tokens, hidden, num_experts, top_k, num_ranks, G, flags,
+                                  band_tokens)
         self._lib = _abi.lib()
         h = ctypes.c_void_p()
         _abi.check(self._lib.moe_plan_create(ctypes.byref(self.cfg), ctypes.byref(h)),
@@ -79,6 +84,7 @@ class Plan:
         self.recv_rows = int(self._lib.moe_plan_recv_rows(h))
         self.staging_rows_max = int(self._lib.moe_plan_staging_rows_max(h))
         self.scale_blocks = int(self._lib.moe_plan_scale_blocks(h))
+        self.bands = int(self._lib.moe_plan_bands(h))
         self.workspace = None
         self.topk_idx = None
         self.device = None
@@ -103,6 +109,39 @@ class Plan:
         _abi.check(self._lib.moe_route_plan(self._h, _ptr(topk_idx), _ptr(workspace),
                                             _stream_handle(dev, stream)), "moe_route_plan")
         return self
+
+    # -- moe_pipeline
+    def pipeline(self, topk_idx: torch.Tensor, x: torch.Tensor, topk_w: torch.Tensor,
+                 recv: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 out_dtype: torch.dtype = torch.bfloat16, workspace: torch.Tensor | None = None,
+                 stream=None):
+        """Route, dispatch and combine (identity expert) of every band in one launch.
+
+        Returns (recv [T*k, H], out [T, H]); the plan is routed afterwards."""
+        dev = topk_idx.device
+        _need(topk_idx, (self.T, self.k), (torch.int32,), "topk_idx", dev)
+        _need(x, (self.T, self.H), _BF16_LIKE, "x", dev)
+        _need(topk_w, (self.T, self.k), (torch.float32,), "topk_w", dev)
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+        if recv is None:
+            recv = torch.empty((self.recv_rows, self.H), dtype=x.dtype, device=dev)
+        _need(recv, (self.recv_rows, self.H), _BF16_LIKE, "recv", dev)
+        if out is None:
+            out = torch.empty((self.T, self.H), dtype=out_dtype, device=dev)
+        _need(out, (self.T, self.H), (out_dtype,), "out", dev)
+        if workspace is None:
+            if self.workspace is None or self.workspace.device != dev:
+                self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=dev)
+            workspace = self.workspace
+        elif workspace.numel() * workspace.element_size() < self.workspace_bytes:
+            raise ValueError("workspace too small")
+        self.workspace, self.topk_idx, self.device = workspace, topk_idx, dev
+        code = _abi.OUT_F32 if out_dtype == torch.float32 else _abi.OUT_BF16
+        _abi.check(self._lib.moe_pipeline(self._h, _ptr(topk_idx), _ptr(workspace), _ptr(x),
+                                          _ptr(recv), _ptr(topk_w), _ptr(out), code,
+                                          _stream_handle(dev, stream)), "moe_pipeline")
+        return recv, out
 
     # -- moe_dispatch
     def dispatch(self, x: torch.Tensor, recv: torch.Tensor | None = None,
@@ -206,8 +245,10 @@ class Plan:
 
     # -- moe_plan_read
     def read(self, item: str, stream=None) -> np.ndarray:
-        n = {"status": 1, "num_staged": 1, "counts": self.E, "expert_offsets": self.E + 1,
-             "rank_offsets": self.R + 1, "slot_of": self.T * self.k, "row_src": self.T * self.k,
+        nb = self.bands
+        n = {"status": 1, "num_staged": 1, "counts": nb * self.E,
+             "expert_offsets": nb * (self.E + 1), "rank_offsets": nb * (self.R + 1),
+             "slot_of": self.T * self.k, "row_src": self.T * self.k,
              "stage_offsets": self.R + 1, "stage_of": self.T * self.k,
              "stage_src": self.staging_rows_max, "send_rows": self.R * self.R,
              "send_copies": self.R * self.R, "node_copies": self.R * self.N,
@@ -262,3 +303,9 @@ def combine_hier(plan: Plan, y: torch.Tensor, topk_w: torch.Tensor, partials=Non
                  out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
     """moe_combine_hier: two-hop combine of a node-deduplicated plan."""
     return plan.combine_hier(y, topk_w, partials, out, out_dtype, stream)
+
+
+def pipeline(plan: Plan, topk_idx: torch.Tensor, x: torch.Tensor, topk_w: torch.Tensor,
+             recv=None, out=None, out_dtype: torch.dtype = torch.bfloat16, stream=None):
+    """moe_pipeline: returns (recv [T*k, H], out [T, H])."""
+    return plan.pipeline(topk_idx, x, topk_w, recv, out, out_dtype, stream=stream)

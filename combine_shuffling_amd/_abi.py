@@ -19,6 +19,7 @@ ERR_BAD_ROUTING = 3
 ERR_PLAN_NOT_ROUTED = 4
 ERR_HIP = 5
 ERR_UNSUPPORTED = 6
+ERR_PIPELINE_STALL = 7
 
 FLAG_NODE_DEDUP = 1
 FLAG_LOAD_AWARE_FORWARDERS = 2
@@ -43,6 +44,7 @@ class MoeConfig(ctypes.Structure):
         ("num_ranks", ctypes.c_int32),
         ("ranks_per_node", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("band_tokens", ctypes.c_int32),
     ]
 
 
@@ -50,7 +52,7 @@ EXPORTS = (
     "moe_expert_partition", "moe_plan_create", "moe_plan_destroy", "moe_plan_workspace_bytes",
     "moe_plan_recv_rows", "moe_plan_staging_rows_max", "moe_route_plan", "moe_dispatch",
     "moe_combine", "moe_plan_read", "moe_status_str", "moe_plan_scale_blocks",
-    "moe_dispatch_fp8", "moe_combine_fp8", "moe_combine_hier",
+    "moe_dispatch_fp8", "moe_combine_fp8", "moe_combine_hier", "moe_plan_bands", "moe_pipeline",
 )
 
 
@@ -101,6 +103,10 @@ def lib() -> ctypes.CDLL:
     L.moe_combine_fp8.restype = i32
     L.moe_combine_hier.argtypes = [vp, vp, vp, vp, vp, i32, vp]
     L.moe_combine_hier.restype = i32
+    L.moe_plan_bands.argtypes = [vp]
+    L.moe_plan_bands.restype = i64
+    L.moe_pipeline.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]
+    L.moe_pipeline.restype = i32
     L.moe_status_str.argtypes = [i32]
     L.moe_status_str.restype = ctypes.c_char_p
     _lib = L

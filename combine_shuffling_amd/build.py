@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoeshuffle.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ("route_plan.hip", "move.hip", "moe_api.cpp")
+SOURCES = ("route_plan.hip", "move.hip", "pipeline.hip", "moe_api.cpp")
 
 # -packed-fp32-ops: no packed fp32 instructions in device code.
 HIP_FLAGS = [

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "moe_internal.h"
 
@@ -22,6 +23,7 @@ struct moe_plan {
   moe::Work work;
   bool routed;     // route_count has been launched for the bound routing
   bool assigned;   // slot_of / row_src (and stage_of / stage_src) are final
+  void* pipe_ws;   // workspace whose pipeline counters are known to be clear
 };
 
 namespace moe {
@@ -45,12 +47,14 @@ Layout make_layout(const Dims& d) {
   const int64_t tk = (int64_t)d.T * d.k;
   const int64_t fk = d.dedup ? tk : 1;
   take(l.ctrl, kCtrlWords);
+  take(l.band_status, d.nbands);
+  take(l.pipe, (kPipeHead + 3 * (int64_t)d.nbands) * kPipeSlot);
   take(l.tile_flags, d.nblk);
   take(l.tile_counts, (int64_t)d.nblk * d.E);
   take(l.tile_base, (int64_t)d.nblk * d.E);
-  take(l.counts, d.E);
-  take(l.expert_off, d.E + 1);
-  take(l.rank_off, d.R + 1);
+  take(l.counts, (int64_t)d.nbands * d.E);
+  take(l.expert_off, (int64_t)d.nbands * (d.E + 1));
+  take(l.rank_off, (int64_t)d.nbands * (d.R + 1));
   take(l.lr, tk);
   take(l.slot_of, tk);
   take(l.row_src, tk);
@@ -74,6 +78,8 @@ Work bind_work(const Layout& l, void* base) {
   auto p = [&](size_t off) { return reinterpret_cast<int32_t*>(b + off); };
   Work w{};
   w.ctrl = p(l.ctrl);
+  w.band_status = p(l.band_status);
+  w.pipe = p(l.pipe);
   w.tile_flags = p(l.tile_flags);
   w.tile_counts = p(l.tile_counts);
   w.tile_base = p(l.tile_base);
@@ -119,6 +125,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_PLAN_NOT_ROUTED: return "plan has not been routed (call moe_route_plan first)";
     case MOE_ERR_HIP: return "HIP runtime error";
     case MOE_ERR_UNSUPPORTED: return "sizes beyond the library's limits";
+    case MOE_ERR_PIPELINE_STALL: return "a banded-pipeline wait gave up; outputs are unspecified";
   }
   return "unknown status";
 }
@@ -150,7 +157,10 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   if (load_aware && !dedup) return MOE_ERR_INVALID_ARGUMENT;
   if (load_aware && (int64_t)c.num_ranks * nodes > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
 
+  if (c.band_tokens < 0 || c.band_tokens % moe::kPlanBlock) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t T = c.num_tokens, chunks = c.hidden / 8;
+  const bool banded = c.band_tokens > 0 && c.band_tokens < T;
+  if (banded && dedup) return MOE_ERR_UNSUPPORTED;
   const int64_t staging_max = dedup ? T * std::min<int64_t>(c.top_k, nodes) : 0;
   const int64_t lim = INT32_MAX;
   if (T * c.top_k >= lim || T * chunks >= lim || staging_max * chunks >= lim)
@@ -171,14 +181,29 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   d.dedup = dedup ? 1 : 0;
   d.load_aware = load_aware ? 1 : 0;
   d.fkeys = load_aware ? d.R * d.N : d.R;
-  // At most kMaxPlanTiles tiles, and few enough that the scan kernel holds
-  // the [tiles x experts] (and [tiles x staging keys]) count matrix in LDS.
   const int64_t widest = std::max<int64_t>(d.E, dedup ? d.fkeys : 1);
-  const int64_t max_tiles = std::min<int64_t>(moe::kMaxPlanTiles, moe::kScanLdsInts / widest);
-  const int64_t per_tile_cap = (int64_t)moe::kPlanBlock * max_tiles;
-  d.passes = (int32_t)std::max<int64_t>(1, (T + per_tile_cap - 1) / per_tile_cap);
-  d.tile = moe::kPlanBlock * d.passes;
-  d.nblk = (int32_t)std::max<int64_t>(1, (T + d.tile - 1) / d.tile);
+  if (banded) {
+    // One 256-token tile per pass; a band's tile-count matrix must fit the
+    // scan's LDS, and the pipeline's schedule holds at most 192 bands.
+    d.passes = 1;
+    d.tile = moe::kPlanBlock;
+    d.nblk = (int32_t)((T + d.tile - 1) / d.tile);
+    d.band = c.band_tokens;
+    d.tpb = d.band / d.tile;
+    d.nbands = (int32_t)((T + d.band - 1) / d.band);
+    if ((int64_t)d.tpb * d.E > moe::kScanLdsInts || d.nbands > 192) return MOE_ERR_UNSUPPORTED;
+  } else {
+    // At most kMaxPlanTiles tiles, and few enough that the scan kernel holds
+    // the [tiles x experts] (and [tiles x staging keys]) count matrix in LDS.
+    const int64_t max_tiles = std::min<int64_t>(moe::kMaxPlanTiles, moe::kScanLdsInts / widest);
+    const int64_t per_tile_cap = (int64_t)moe::kPlanBlock * max_tiles;
+    d.passes = (int32_t)std::max<int64_t>(1, (T + per_tile_cap - 1) / per_tile_cap);
+    d.tile = moe::kPlanBlock * d.passes;
+    d.nblk = (int32_t)std::max<int64_t>(1, (T + d.tile - 1) / d.tile);
+    d.band = d.nblk * d.tile;
+    d.tpb = d.nblk;
+    d.nbands = 1;
+  }
   d.chunks = (int32_t)chunks;
   d.segs = (int32_t)((chunks + moe::kWave - 1) / moe::kWave);
   d.smax = (int32_t)staging_max;
@@ -193,6 +218,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   p->ws = nullptr;
   p->routed = false;
   p->assigned = false;
+  p->pipe_ws = nullptr;
   *out = p;
   return MOE_OK;
 }
@@ -209,6 +235,8 @@ int64_t moe_plan_staging_rows_max(const moe_plan* plan) {
   return plan ? plan->staging_rows_max : 0;
 }
 
+int64_t moe_plan_bands(const moe_plan* plan) { return plan ? plan->d.nbands : 0; }
+
 moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspace, void* stream) {
   if (!plan || !workspace || !moe::aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   if (plan->d.T > 0 && (!topk_idx || !moe::aligned(topk_idx, 4))) return MOE_ERR_INVALID_ARGUMENT;
@@ -220,6 +248,36 @@ moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspa
   plan->work = moe::bind_work(plan->layout, workspace);
   if (moe::launch_route_count(plan->d, topk_idx, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
   plan->routed = true;
+  return MOE_OK;
+}
+
+moe_status moe_pipeline(moe_plan* plan, const int32_t* topk_idx, void* workspace,
+                        const uint16_t* x, uint16_t* recv, const float* topk_w, void* out,
+                        int32_t out_dtype, void* stream) {
+  if (!plan || !workspace || !moe::aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->d.dedup || plan->d.H % 64) return MOE_ERR_UNSUPPORTED;
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->d.T > 0 &&
+      (!topk_idx || !x || !recv || !topk_w || !out || !moe::aligned(topk_idx, 4) ||
+       !moe::aligned(x, 16) || !moe::aligned(recv, 128) || !moe::aligned(topk_w, 4) ||
+       !moe::aligned(out, 16)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->d.T == 0) return moe_route_plan(plan, topk_idx, workspace, stream);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  plan->routed = false;
+  plan->assigned = false;
+  plan->idx = topk_idx;
+  plan->ws = workspace;
+  plan->work = moe::bind_work(plan->layout, workspace);
+  if (plan->pipe_ws != workspace) {
+    if (moe::launch_pipe_clear(plan->d, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
+    plan->pipe_ws = workspace;
+  }
+  if (moe::launch_pipeline(plan->d, topk_idx, x, recv, topk_w, out, out_dtype == MOE_OUT_F32,
+                           plan->work, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  plan->routed = true;
+  plan->assigned = true;
   return MOE_OK;
 }
 
@@ -324,10 +382,10 @@ moe_status moe_plan_read(moe_plan* plan, int32_t item, void* host_dst, size_t by
   int64_t n = 0;
   bool traffic = false;
   switch (item) {
-    case MOE_ITEM_STATUS: src = w.ctrl + moe::kCtrlStatus; n = 1; break;
-    case MOE_ITEM_COUNTS: src = w.counts; n = d.E; break;
-    case MOE_ITEM_EXPERT_OFFSETS: src = w.expert_off; n = d.E + 1; break;
-    case MOE_ITEM_RANK_OFFSETS: src = w.rank_off; n = d.R + 1; break;
+    case MOE_ITEM_STATUS: src = w.band_status; n = 1; break;
+    case MOE_ITEM_COUNTS: src = w.counts; n = (int64_t)d.nbands * d.E; break;
+    case MOE_ITEM_EXPERT_OFFSETS: src = w.expert_off; n = (int64_t)d.nbands * (d.E + 1); break;
+    case MOE_ITEM_RANK_OFFSETS: src = w.rank_off; n = (int64_t)d.nbands * (d.R + 1); break;
     case MOE_ITEM_SLOT_OF: src = w.slot_of; n = tk; break;
     case MOE_ITEM_ROW_SRC: src = w.row_src; n = tk; break;
     case MOE_ITEM_NUM_STAGED: src = w.ctrl + moe::kCtrlStaged; n = 1; break;
@@ -360,6 +418,19 @@ moe_status moe_plan_read(moe_plan* plan, int32_t item, void* host_dst, size_t by
     if (e == hipSuccess) e = hipMemsetAsync(w.node_copies, 0, (size_t)d.R * d.N * sizeof(int32_t), s);
     if (e == hipSuccess && d.T > 0) e = moe::launch_traffic(d, plan->idx, w, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (item == MOE_ITEM_STATUS) {
+    // One status per band: report the first that is not MOE_OK.
+    std::vector<int32_t> st(d.nbands, 0);
+    if (hipMemcpyAsync(st.data(), w.band_status, st.size() * sizeof(int32_t),
+                       hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return MOE_ERR_HIP;
+    int32_t worst = MOE_OK;
+    for (int32_t v : st)
+      if (v != MOE_OK && worst == MOE_OK) worst = v;
+    std::memcpy(host_dst, &worst, sizeof worst);
+    return MOE_OK;
   }
   if (need > 0) {
     if (hipMemcpyAsync(host_dst, src, need, hipMemcpyDeviceToHost, s) != hipSuccess)

@@ -15,9 +15,31 @@ __device__ __forceinline__ int split_part(int i, int base, int rem) {
   return i < cut ? i / (base + 1) : rem + (i - cut) / base;
 }
 
+// Plan-array accesses.  COH = false: plain loads and stores (one kernel per
+// step; the kernel boundary publishes everything).  COH = true: device-scope
+// (sc1) accesses, for arrays one block writes and a block on another XCD
+// reads inside the same launch (the banded pipeline): they go past the
+// per-XCD L2 to the coherence point, so no cache-wide write-back or
+// invalidate is needed to hand them over.
+template <bool COH>
+__device__ __forceinline__ int32_t ld_plan(const int32_t* p) {
+  if constexpr (COH)
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
+template <bool COH>
+__device__ __forceinline__ void st_plan(int32_t* p, int32_t v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 // Receive row of every slot of token t: the row of (tile, expert) from the
 // scan plus the slot's rank inside the tile; -1 for a dropped slot.
-template <int KMAX>
+template <int KMAX, bool COH = false>
 __device__ __forceinline__ void token_slots(const Dims& d, const Work& w,
                                             const int32_t* __restrict__ idx, int t,
                                             int (&slot)[KMAX]) {
@@ -27,8 +49,8 @@ __device__ __forceinline__ void token_slots(const Dims& d, const Work& w,
   for (int j = 0; j < KMAX; ++j) {
     slot[j] = -1;
     if (j < d.k) {
-      const int l = w.lr[at + j];
-      if (l >= 0) slot[j] = w.tile_base[b * d.E + idx[at + j]] + l;
+      const int l = ld_plan<COH>(&w.lr[at + j]);
+      if (l >= 0) slot[j] = ld_plan<COH>(&w.tile_base[b * d.E + idx[at + j]]) + l;
     }
   }
 }

@@ -18,9 +18,20 @@ constexpr int kMaxPlanTiles = 64;  // route-plan tiles (blocks) at most
 constexpr int kScanLdsInts = 8192; // tile-count matrix the last block scans in LDS (32 KiB)
 
 // ctrl words at the start of the workspace.
-constexpr int kCtrlStatus = 0;     // moe_status of the last route
 constexpr int kCtrlStaged = 1;     // D, staging rows used
 constexpr int kCtrlWords = 64;
+
+// Banded pipeline: counters in Work::pipe, each in a slot of its own
+// (kPipeSlot ints, so polls of one counter do not contend with updates of
+// another): the head slots, then three per band (count tiles done, scan
+// done, gather tickets done).  All zero between launches: the last block of
+// every launch clears them.
+constexpr int kPipeSlot = 64;      // ints per counter slot (256 bytes)
+constexpr int kPipeTicket = 0;     // next ticket to hand out
+constexpr int kPipeExit = 1;       // blocks that have left the ticket loop
+constexpr int kPipeStall = 2;      // set when a bounded wait gave up
+constexpr int kPipeHead = 4;       // head slots
+constexpr int kPipeMaxSteps = 256; // schedule steps (bands + stage lags) at most
 
 // Sizes and the hoisted constants of the two ceil/floor splits.  Passed by
 // value to every kernel.
@@ -31,6 +42,9 @@ struct Dims {
   int32_t passes;         // 256-token passes per plan tile
   int32_t tile;           // tokens per plan tile = 256 * passes
   int32_t nblk;           // plan tiles
+  int32_t band;           // tokens per band (a multiple of tile; >= T with one band)
+  int32_t nbands;         // bands, each routed as a batch of its own
+  int32_t tpb;            // plan tiles per band
   int32_t dedup;          // MOE_FLAG_NODE_DEDUP set
   int32_t load_aware;     // MOE_FLAG_LOAD_AWARE_FORWARDERS set
   int32_t fkeys;          // staging keys: forwarders (R), or (owner, node) pairs (R * N)
@@ -42,12 +56,14 @@ struct Dims {
 // Device pointers into the caller's workspace (int32 arrays).
 struct Work {
   int32_t* ctrl;          // [kCtrlWords]
+  int32_t* band_status;   // [nbands]    moe_status of each band's route
+  int32_t* pipe;          // [(kPipeHead + 3 * nbands) * kPipeSlot] banded-pipeline counters
   int32_t* tile_flags;    // [nblk]      bad-routing flag per tile
   int32_t* tile_counts;   // [nblk * E]  rows per (tile, expert), tile-major
   int32_t* tile_base;     // [nblk * E]  first receive row of (tile, expert)
-  int32_t* counts;        // [E]
-  int32_t* expert_off;    // [E + 1]
-  int32_t* rank_off;      // [R + 1]
+  int32_t* counts;        // [nbands * E]
+  int32_t* expert_off;    // [nbands * (E + 1)]  global receive rows
+  int32_t* rank_off;      // [nbands * (R + 1)]
   int32_t* lr;            // [T * k]     rank of slot (t, j) among its tile's slots of that expert; -1 dropped
   int32_t* slot_of;       // [T * k]     token slot -> receive row (-1: dropped)
   int32_t* row_src;       // [T * k]     receive row -> token
@@ -67,7 +83,7 @@ struct Work {
 
 // Byte offsets of each Work array from the workspace base, and the total.
 struct Layout {
-  size_t ctrl, tile_flags, tile_counts, tile_base, counts, expert_off, rank_off, lr, slot_of,
+  size_t ctrl, band_status, pipe, tile_flags, tile_counts, tile_base, counts, expert_off, rank_off, lr, slot_of,
       row_src, tile_fcounts, tile_fbase, fwd, stage_off, fkey, flr, stage_of, stage_src, send_rows,
       send_copies, node_copies, total;
 };
@@ -76,7 +92,7 @@ Layout make_layout(const Dims& d);
 Work bind_work(const Layout& l, void* base);
 
 // Route plan (route_plan.hip).
-// route_count then route_scan.
+// route_count then route_scan (one block per band).
 hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);
 hipError_t launch_route_assign(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);
 hipError_t launch_traffic(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);
@@ -96,6 +112,12 @@ hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* wts, vo
 hipError_t launch_combine_hier(const Dims& d, const int32_t* idx, const uint16_t* y,
                                const float* wts, float* part, void* out, bool out_f32,
                                const Work& w, hipStream_t s);
+// Banded pipeline: route, dispatch and combine (identity expert) of every
+// band in one persistent launch (pipeline.hip).  Work::pipe must be zero.
+hipError_t launch_pipeline(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
+                           const float* wts, void* out, bool out_f32, const Work& w,
+                           hipStream_t s);
+hipError_t launch_pipe_clear(const Dims& d, const Work& w, hipStream_t s);
 // fp8 payload (OCP E4M3 codes, one power-of-two scale per 128-element block).
 hipError_t launch_gather_fp8(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
                              float* rscale, const Work& w, hipStream_t s);

@@ -25,139 +25,10 @@
 //           fused multiply-add per element and slot in ascending j starting
 //           from 0, then round-to-nearest-even bf16 (or fp32) out (INC-MoE
 //           abstract: combine back to each token's owner).
-#include "moe_device.h"
-
-#ifndef MOE_GATHER_U
-#define MOE_GATHER_U 1
-#endif
-#ifndef MOE_STAGE_U
-#define MOE_STAGE_U 2
-#endif
-#ifndef MOE_COMBINE_U
-#define MOE_COMBINE_U 2
-#endif
-#ifndef MOE_NT_LOAD
-#define MOE_NT_LOAD 1
-#endif
-#ifndef MOE_COMBINE8_U
-#define MOE_COMBINE8_U 2
-#endif
-#ifndef MOE_NT_LOAD_X
-#define MOE_NT_LOAD_X 0
-#endif
-#ifndef MOE_MOVE_WAVES
-#define MOE_MOVE_WAVES 4
-#endif
-#ifndef MOE_NT_STORE
-#define MOE_NT_STORE 1
-#endif
+#include "move_body.h"
 
 namespace moe {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = MOE_MOVE_WAVES;   // waves per block
-constexpr int kBlock = kWaves * kWave;
-constexpr int kGatherU = MOE_GATHER_U;    // wave-items per wave: gather
-constexpr int kStageU = MOE_STAGE_U;      // wave-items per wave: stage_a, stage_b
-constexpr int kCombineU = MOE_COMBINE_U;  // wave-items per wave: combine
-constexpr int kCombine8U = MOE_COMBINE8_U; // wave-items per wave: combine of an fp8 payload
-
-// Rows are touched once per call: stream them past the caches (measured
-// faster on gfx950 for both the row reads and the row writes).
-template <typename V>
-__device__ __forceinline__ void store_chunk(V* p, V v) {
-#if MOE_NT_STORE
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
-}
-
-__device__ __forceinline__ u32x4 load_chunk(const u32x4* p) {
-#if MOE_NT_LOAD
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-
-// Token rows of x (dispatch source): plain loads measured faster here.
-__device__ __forceinline__ u32x4 load_x_chunk(const u32x4* p) {
-#if MOE_NT_LOAD_X
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-
-// Wave-item u of this wave: token t, chunk c of the lane, and whether the
-// item exists / the lane's chunk is inside the row.
-struct Item {
-  int t, c;
-  bool live, ok;
-};
-
-template <int U>
-__device__ __forceinline__ Item wave_item(const Dims& d, int items, int u) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int g = __builtin_amdgcn_readfirstlane((blockIdx.x * U + u) * kWaves + wave);
-  Item it;
-  it.live = g < items;
-  it.t = it.live ? g / d.segs : 0;
-  const int seg = g - it.t * d.segs;
-  it.c = seg * kWave + lane;
-  it.ok = it.live && it.c < d.chunks;
-  return it;
-}
-
-// Lane j (< k) writes the token's entry j of a per-slot plan array.
-template <int KMAX>
-__device__ __forceinline__ int lane_pick(const int (&v)[KMAX], int lane) {
-  int r = -1;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) r = lane == j ? v[j] : r;
-  return r;
-}
-
-template <int KMAX, int U>
-__global__ __launch_bounds__(kBlock) void gather_kernel(Dims d, const int32_t* __restrict__ idx,
-                                                        const u32x4* __restrict__ x,
-                                                        u32x4* __restrict__ recv, Work w) {
-  const int items = d.T * d.segs, lane = threadIdx.x % kWave;
-  const uint32_t rows = (uint32_t)(d.T * d.k);
-  Item it[U];
-  int slot[U][KMAX];
-  u32x4 v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, items, u);
-    if (it[u].live) {
-      token_slots<KMAX>(d, w, idx, it[u].t, slot[u]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) slot[u][j] = -1;
-    }
-    if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    // The first segment of a row publishes the token's slots.
-    if (it[u].live && it[u].c == lane && lane < d.k) {
-      const int s = lane_pick<KMAX>(slot[u], lane);
-      w.slot_of[(int64_t)it[u].t * d.k + lane] = s;
-      if ((uint32_t)s < rows) w.row_src[s] = it[u].t;
-    }
-    if (it[u].ok) {
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if ((uint32_t)slot[u][j] < rows)
-          store_chunk(&recv[(int64_t)slot[u][j] * d.chunks + it[u].c], v[u]);
-    }
-  }
-}
 
 template <int KMAX, int U>
 __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* __restrict__ idx,
@@ -244,80 +115,6 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
         if (same && (uint32_t)slot[u][jj] < rows)
           store_chunk(&recv[(int64_t)slot[u][jj] * d.chunks + it[u].c], v[u][j]);
       }
-    }
-  }
-}
-
-__device__ __forceinline__ void unpack_bf16(u32x4 v, float (&f)[8]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f[2 * q] = __uint_as_float(v[q] << 16);
-    f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
-  }
-}
-
-// float -> bf16 bits, round to nearest even; NaN becomes a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-template <int KMAX, int U, bool F32OUT>
-__global__ __launch_bounds__(kBlock) void combine_kernel(Dims d, const u32x4* __restrict__ y,
-                                                         const float* __restrict__ wts,
-                                                         const int32_t* __restrict__ slot_of,
-                                                         void* __restrict__ out) {
-  const int items = d.T * d.segs;
-  const uint32_t rows = (uint32_t)(d.T * d.k);
-  Item it[U];
-  int slot[U][KMAX];
-  float wj[U][KMAX];
-  u32x4 v[U][KMAX];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, items, u);
-    const int64_t at = (int64_t)it[u].t * d.k;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      const bool has = it[u].live && j < d.k;
-      slot[u][j] = has ? slot_of[at + j] : -1;
-      if ((uint32_t)slot[u][j] >= rows) slot[u][j] = -1;
-      wj[u][j] = has ? wts[at + j] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (slot[u][j] >= 0 && it[u].ok) v[u][j] = load_chunk(&y[(int64_t)slot[u][j] * d.chunks + it[u].c]);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (!it[u].ok) continue;
-    float acc[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (slot[u][j] < 0) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = __uint_as_float(v[u][j][q] << 16);
-        const float hi = __uint_as_float(v[u][j][q] & 0xffff0000u);
-        acc[2 * q] = __builtin_fmaf(wj[u][j], lo, acc[2 * q]);
-        acc[2 * q + 1] = __builtin_fmaf(wj[u][j], hi, acc[2 * q + 1]);
-      }
-    }
-    const int64_t i = (int64_t)it[u].t * d.chunks + it[u].c;
-    if constexpr (F32OUT) {
-      f32x4* o = reinterpret_cast<f32x4*>(out) + i * 2;
-      const f32x4 a = {acc[0], acc[1], acc[2], acc[3]};
-      const f32x4 b = {acc[4], acc[5], acc[6], acc[7]};
-      store_chunk(o, a);
-      store_chunk(o + 1, b);
-    } else {
-      u32x4 r;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) r[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
-      store_chunk(reinterpret_cast<u32x4*>(out) + i, r);
     }
   }
 }

@@ -53,6 +53,16 @@
  * null stream).  A plan is not thread-safe; calls on one workspace that
  * overlap in time (different streams without ordering) race.
  *
+ * Bands.  With band_tokens = B > 0 and B < T the batch is cut into
+ * nb = ceil(T / B) bands; band b holds tokens [b*B, min((b+1)*B, T)) and owns
+ * receive rows [b*B*k, min((b+1)*B, T)*k), laid out inside like a whole
+ * batch's receive buffer (INC-MoE abstract: tokens are partitioned into bands
+ * that go through dispatch, expert and combine one after another).  Every
+ * call works on banded plans; COUNTS, EXPERT_OFFSETS and RANK_OFFSETS then
+ * hold one row per band (global receive rows), and moe_pipeline runs the
+ * whole path band by band in one launch.  Limits: B * E <= 2^21 (a band's
+ * tile-count matrix fits the scan's LDS), nb <= 192.
+ *
  * Errors.  Host-detectable errors return before anything is launched.  Bad
  * routing (an id outside [0, E) or repeated in a row) is found on the device:
  * such slots are dropped (no row is written for them, they add nothing to the
@@ -76,7 +86,8 @@ typedef enum moe_status {
   MOE_ERR_BAD_ROUTING = 3,      /* device found an id out of range or repeated in a row */
   MOE_ERR_PLAN_NOT_ROUTED = 4,  /* dispatch/combine/read before moe_route_plan          */
   MOE_ERR_HIP = 5,              /* a HIP runtime call or kernel launch failed           */
-  MOE_ERR_UNSUPPORTED = 6       /* sizes beyond the library's limits (below)            */
+  MOE_ERR_UNSUPPORTED = 6,      /* sizes beyond the library's limits (below)            */
+  MOE_ERR_PIPELINE_STALL = 7    /* a banded-pipeline wait gave up (moe_pipeline)         */
 } moe_status;
 
 /* Limits: E <= 1024, 1 <= k <= 16, k <= E, R <= E, R % G == 0, H % 8 == 0,
@@ -104,16 +115,21 @@ typedef struct moe_config {
   int32_t num_ranks;      /* R, 1..E                                               */
   int32_t ranks_per_node; /* G, divides R; N = R / G nodes                          */
   uint32_t flags;         /* MOE_FLAG_*                                             */
+  int32_t band_tokens;    /* 0: one band.  Else a multiple of 256: the tokens are cut
+                             into bands of band_tokens consecutive tokens (the last
+                             may be shorter), each routed as a batch of its own (see
+                             "Bands" below).  Not with MOE_FLAG_NODE_DEDUP.          */
 } moe_config;
 
 typedef struct moe_plan moe_plan; /* opaque, host-side */
 
 /* What moe_plan_read copies out (all int32 unless noted). */
 typedef enum moe_item {
-  MOE_ITEM_STATUS = 0,         /* 1 value: moe_status of the last route (MOE_OK or MOE_ERR_BAD_ROUTING) */
-  MOE_ITEM_COUNTS = 1,         /* [E]     rows per expert                                      */
-  MOE_ITEM_EXPERT_OFFSETS = 2, /* [E+1]   exclusive scan of counts                             */
-  MOE_ITEM_RANK_OFFSETS = 3,   /* [R+1]   first receive row of each rank                       */
+  MOE_ITEM_STATUS = 0,         /* 1 value: moe_status of the last route (MOE_OK, MOE_ERR_BAD_ROUTING,
+                                  or MOE_ERR_PIPELINE_STALL after a moe_pipeline that gave up) */
+  MOE_ITEM_COUNTS = 1,         /* [nb*E]     rows per (band, expert)                           */
+  MOE_ITEM_EXPERT_OFFSETS = 2, /* [nb*(E+1)] first receive row of each expert, per band         */
+  MOE_ITEM_RANK_OFFSETS = 3,   /* [nb*(R+1)] first receive row of each rank, per band           */
   MOE_ITEM_SLOT_OF = 4,        /* [T*k]   receive row of token slot (t, j), -1 if dropped       */
   MOE_ITEM_ROW_SRC = 5,        /* [T*k]   source token of each receive row                     */
   MOE_ITEM_NUM_STAGED = 6,     /* 1 value: D, staging rows used (dedup only)                    */
@@ -145,6 +161,7 @@ void moe_plan_destroy(moe_plan* plan); /* NULL is a no-op */
 size_t moe_plan_workspace_bytes(const moe_plan* plan);
 int64_t moe_plan_recv_rows(const moe_plan* plan);         /* T*k                          */
 int64_t moe_plan_staging_rows_max(const moe_plan* plan);  /* T*min(k, N) with dedup, else 0 */
+int64_t moe_plan_bands(const moe_plan* plan);             /* nb (1 without bands)          */
 
 /* Route plan: validates routing, builds the per-expert histogram, its
  * exclusive scan and the segment descriptors (and, with dedup, the per-
@@ -214,6 +231,30 @@ moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, f
  * Asynchronous.  Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
 moe_status moe_combine_fp8(moe_plan* plan, const uint8_t* y8, const float* y_scale,
                            const float* topk_w, void* out, int32_t out_dtype, void* stream);
+
+/* Banded pipeline: route plan, dispatch and combine of every band in ONE
+ * persistent launch, with the identity as the expert (y = recv).  INC-MoE
+ * abstract: bands pass a dispatch -> expert -> combine pipeline inside a
+ * single persistent kernel, role-specialised thread blocks working on
+ * different bands at once and handing them on with device-side
+ * synchronisation.  Per band, in order: count (its plan tiles), scan (its
+ * segment descriptors), gather (recv rows, as moe_dispatch), combine (out,
+ * as moe_combine over recv).  Results equal moe_route_plan + moe_dispatch +
+ * moe_combine(y = recv) on the same plan, bit for bit.
+ * Arguments as for those calls; the routing and the workspace are bound to
+ * the plan as by moe_route_plan, and the plan is routed afterwards.  Needs
+ * H % 64 == 0 (rows of whole 128-byte lines) and recv 128-byte aligned, so
+ * that no cache line holds bytes of two bands.  The
+ * workspace also holds the pipeline's counters: the first moe_pipeline of a
+ * plan on a workspace clears them (one small extra launch) and every launch
+ * leaves them clear, so a workspace used with moe_pipeline must not be
+ * written by anyone else while the plan uses it.  Every wait inside the
+ * launch is bounded; a wait that gives up makes moe_plan_read(STATUS) report
+ * MOE_ERR_PIPELINE_STALL (the outputs are then unspecified).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (MOE_FLAG_NODE_DEDUP, H % 64 != 0), HIP. */
+moe_status moe_pipeline(moe_plan* plan, const int32_t* topk_idx, void* workspace,
+                        const uint16_t* x, uint16_t* recv, const float* topk_w, void* out,
+                        int32_t out_dtype, void* stream);
 
 /* Copies one plan item to host memory (synchronises the stream).  bytes must
  * be at least the item's size (see moe_item).  The traffic matrices

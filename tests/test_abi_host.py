@@ -29,8 +29,8 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
-def make(T=128, H=256, E=8, k=2, R=2, G=None, flags=0):
-    cfg = _abi.MoeConfig(T, H, E, k, R, R if G is None else G, flags)
+def make(T=128, H=256, E=8, k=2, R=2, G=None, flags=0, band=0):
+    cfg = _abi.MoeConfig(T, H, E, k, R, R if G is None else G, flags, band)
     h = ctypes.c_void_p()
     st = _abi.lib().moe_plan_create(ctypes.byref(cfg), ctypes.byref(h))
     return st, h
@@ -57,6 +57,13 @@ def make(T=128, H=256, E=8, k=2, R=2, G=None, flags=0):
     (dict(E=1024, R=1024, G=1, flags=_abi.FLAG_NODE_DEDUP | _abi.FLAG_LOAD_AWARE_FORWARDERS),
      _abi.ERR_UNSUPPORTED),                            # R*N past the key space
     (dict(T=1 << 28, k=8), _abi.ERR_UNSUPPORTED),     # T*k past 32-bit row indices
+    (dict(T=4096, band=512), _abi.OK),
+    (dict(T=4096, band=100), _abi.ERR_INVALID_ARGUMENT),   # not a multiple of 256
+    (dict(T=4096, band=-256), _abi.ERR_INVALID_ARGUMENT),
+    (dict(T=4096, band=8192), _abi.OK),                   # one band
+    (dict(T=4096, E=1024, k=2, band=4096 - 256), _abi.ERR_UNSUPPORTED),  # 15 tiles x 1024 > LDS
+    (dict(T=256 * 193, band=256), _abi.ERR_UNSUPPORTED),  # more than 192 bands
+    (dict(T=4096, R=4, G=2, flags=_abi.FLAG_NODE_DEDUP, band=512), _abi.ERR_UNSUPPORTED),
 ])
 def test_plan_create_status(kw, want):
     st, h = make(**kw)
@@ -110,8 +117,41 @@ def test_expert_partition_matches_printed_and_oracle():
         expert_partition(0, 1)
 
 
+def test_band_counts():
+    L = _abi.lib()
+    for T, band, nb in [(4096, 512, 8), (4000, 512, 8), (4096, 0, 1), (4096, 8192, 1), (0, 256, 1),
+                        (257, 256, 2)]:
+        st, h = make(T=T, band=band)
+        assert st == _abi.OK
+        assert L.moe_plan_bands(h) == nb, (T, band)
+        L.moe_plan_destroy(h)
+
+
+def test_pipeline_refused_on_host():
+    L = _abi.lib()
+    vp = ctypes.c_void_p
+    st, h = make(T=64)
+    assert L.moe_pipeline(h, vp(16), None, vp(16), vp(16), vp(16), vp(16), 0, None) == \
+        _abi.ERR_INVALID_ARGUMENT                       # no workspace
+    assert L.moe_pipeline(h, vp(16), vp(1024), vp(16), vp(16), vp(16), vp(16), 7, None) == \
+        _abi.ERR_INVALID_ARGUMENT                       # bad out dtype
+    assert L.moe_pipeline(h, vp(18), vp(1024), vp(16), vp(16), vp(16), vp(16), 0, None) == \
+        _abi.ERR_INVALID_ARGUMENT                       # misaligned routing
+    assert L.moe_pipeline(h, vp(16), vp(1024), vp(16), vp(16 + 64), vp(16), vp(16), 0, None) == \
+        _abi.ERR_INVALID_ARGUMENT                       # recv not 128-byte aligned
+    L.moe_plan_destroy(h)
+    st, h = make(T=64, H=200)                           # rows not whole 128-byte lines
+    assert L.moe_pipeline(h, vp(16), vp(1024), vp(16), vp(16), vp(16), vp(16), 0, None) == \
+        _abi.ERR_UNSUPPORTED
+    L.moe_plan_destroy(h)
+    st, h = make(T=64, R=2, G=1, flags=_abi.FLAG_NODE_DEDUP)
+    assert L.moe_pipeline(h, vp(16), vp(1024), vp(16), vp(16), vp(16), vp(16), 0, None) == \
+        _abi.ERR_UNSUPPORTED
+    L.moe_plan_destroy(h)
+
+
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert _abi.status_str(s)
     assert "unknown" in _abi.status_str(99)
 
