@@ -396,6 +396,8 @@ def main():
         dom = max([(f"gather{sfx}_kernel", disp_b, disp_ms, disp_gbs),
                    (f"combine{sfx}_kernel", comb_b, comb_ms, comb_gbs)], key=lambda d: d[2])
 
+    # which committed traffic summary covers this run
+    variant = "_pipeline" if pipe else "_fp8" if fp8 else "_hier" if hier else ""
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -425,7 +427,7 @@ def main():
                                 "GB/s": round(comb_gbs, 1), "launches": 2 if hier else 1}}),
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[3], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(args.workload, dom[0]),
+                     "traffic": recorded_traffic(args.workload + variant, dom[0]),
                      "bytes_per_launch": dom[1], "ms_per_launch": round(float(dom[2]), 5)},
         "cpu_baseline": None,
     }
