@@ -139,7 +139,8 @@ __global__ __launch_bounds__(kBlock) void pipeline_kernel(Dims d, const int32_t*
   // Count and scan share the dynamic LDS (never both in one ticket).
   int* s_ints = reinterpret_cast<int*>(s_dyn);
   const CountLds cl{reinterpret_cast<unsigned long long*>(s_dyn),
-                    reinterpret_cast<int*>(s_dyn) + lds_count_run, nullptr, nullptr, &s_bad};
+                    s_ints + lds_count_run - kPlanWaves * d.E, s_ints + lds_count_run, nullptr,
+                    nullptr, &s_bad};
   const ScanLds sl{s_ints, s_ints + d.tpb * d.E, s_ints + d.tpb * d.E + d.E};
 
   // The next ticket is claimed while the current one runs (thread 0 keeps
@@ -229,9 +230,10 @@ template <int KMAX>
 struct PipelineLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
                         const float* wts, void* out, bool out_f32, const Work& w, hipStream_t s) {
-    // Dynamic LDS: count needs kPlanWaves * E ballots and E running counts;
-    // scan needs the band's tpb * E count matrix, E totals and kPlanWaves sums.
-    const int count_run = kPlanWaves * d.E * 2;  // in ints, after the ballots
+    // Dynamic LDS: count needs kPlanWaves * E ballots (64-bit), a
+    // kPlanWaves * E prefix table and E running counts; scan needs the band's
+    // tpb * E count matrix, E totals and kPlanWaves sums.
+    const int count_run = kPlanWaves * d.E * 3;  // in ints: ballots, then the prefix table
     const size_t count_bytes = sizeof(int) * ((size_t)count_run + d.E);
     const size_t scan_bytes = sizeof(int) * ((size_t)d.tpb * d.E + d.E + kPlanWaves);
     const size_t lds = (std::max(count_bytes, scan_bytes) + 15) / 16 * 16;

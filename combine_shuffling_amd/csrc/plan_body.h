@@ -81,12 +81,25 @@ __device__ int scan_tiles(const int32_t* src, int32_t* base, int32_t* totals, in
 // LDS of one count tile: per-wave ballots [kPlanWaves * max(E, fkeys)] and
 // running counts.  s_frun / s_node are used with node deduplication only.
 struct CountLds {
-  unsigned long long* mask;  // per-wave ballots
+  unsigned long long* mask;  // per-wave ballots                      [kPlanWaves * max(E, fkeys)]
+  int* pre;                  // slots before each (wave, key) so far   [kPlanWaves * max(E, fkeys)]
   int* run;                  // tile's slots per expert so far        [E]
   int* frun;                 // tile's staging rows per key so far    [fkeys]
   int* node;                 // destination node of each expert       [E]
   int* bad;                  // [1]
 };
+
+// s_pre[w * W + c] = run[c] + the ballots of waves before w for key c: the
+// number of the tile's slots with key c that come before wave w's tokens.
+__device__ __forceinline__ void prefix_table(const unsigned long long* s_mask, int* s_pre,
+                                             const int* s_run, int W) {
+  for (int i = threadIdx.x; i < kPlanWaves * W; i += kPlanBlock) {
+    const int wv = i / W, c = i - wv * W;
+    int n = s_run[c];
+    for (int q = 0; q < wv; ++q) n += __popcll(s_mask[q * W + c]);
+    s_pre[i] = n;
+  }
+}
 
 // One plan tile (tokens [tile * d.tile, (tile + 1) * d.tile)) by the whole
 // block: in-tile ranks of every slot, the tile's per-expert counts and its
@@ -95,6 +108,7 @@ template <int KMAX, bool COH = false>
 __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, const Work& w,
                                            int tile, const CountLds& L) {
   unsigned long long* s_mask = L.mask;
+  int* s_pre = L.pre;
   int* s_run = L.run;
   int* s_frun = L.frun;
   int* s_node = L.node;
@@ -148,21 +162,17 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
     for (int j = 0; j < KMAX; ++j)
       if (e[j] >= 0) atomicOr(&s_mask[wv * E + e[j]], bit);
     __syncthreads();
+    prefix_table(s_mask, s_pre, s_run, E);
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (live && j < k) {
-        int r = -1;
-        if (e[j] >= 0) {
-          r = s_run[e[j]] + __popcll(s_mask[wv * E + e[j]] & below);
-          for (int w2 = 0; w2 < wv; ++w2) r += __popcll(s_mask[w2 * E + e[j]]);
-        }
+        const int r = e[j] >= 0 ? s_pre[wv * E + e[j]] + __popcll(s_mask[wv * E + e[j]] & below) : -1;
         st_plan<COH>(&w.lr[at + j], r);
       }
     }
-    __syncthreads();
     for (int i = tid; i < E; i += kPlanBlock)
-      s_run[i] += __popcll(s_mask[i]) + __popcll(s_mask[E + i]) + __popcll(s_mask[2 * E + i]) +
-                  __popcll(s_mask[3 * E + i]);
+      s_run[i] = s_pre[(kPlanWaves - 1) * E + i] + __popcll(s_mask[(kPlanWaves - 1) * E + i]);
 
     if (d.dedup) {
       __syncthreads();
@@ -186,22 +196,19 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
       for (int j = 0; j < KMAX; ++j)
         if (key[j] >= 0) atomicOr(&s_mask[wv * K + key[j]], bit);
       __syncthreads();
+      prefix_table(s_mask, s_pre, s_frun, K);
+      __syncthreads();
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (live && j < k) {
-          int r = -1;
-          if (key[j] >= 0) {
-            r = s_frun[key[j]] + __popcll(s_mask[wv * K + key[j]] & below);
-            for (int w2 = 0; w2 < wv; ++w2) r += __popcll(s_mask[w2 * K + key[j]]);
-          }
+          const int r =
+              key[j] >= 0 ? s_pre[wv * K + key[j]] + __popcll(s_mask[wv * K + key[j]] & below) : -1;
           w.fkey[at + j] = key[j];
           w.flr[at + j] = r;
         }
       }
-      __syncthreads();
       for (int i = tid; i < K; i += kPlanBlock)
-        s_frun[i] += __popcll(s_mask[i]) + __popcll(s_mask[K + i]) + __popcll(s_mask[2 * K + i]) +
-                     __popcll(s_mask[3 * K + i]);
+        s_frun[i] = s_pre[(kPlanWaves - 1) * K + i] + __popcll(s_mask[(kPlanWaves - 1) * K + i]);
     }
     __syncthreads();
   }

@@ -39,11 +39,12 @@ __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
                                                                  const int32_t* __restrict__ idx,
                                                                  Work w) {
   __shared__ unsigned long long s_mask[kPlanWaves * MOE_MAX_EXPERTS];  // per-wave ballots; 32 KiB
+  __shared__ int s_pre[kPlanWaves * MOE_MAX_EXPERTS];  // slots before each (wave, key); 16 KiB
   __shared__ int s_run[MOE_MAX_EXPERTS];   // tile's slots per expert so far
-  __shared__ int s_frun[MOE_MAX_EXPERTS];  // tile's staging rows per forwarder so far (R <= E)
+  __shared__ int s_frun[MOE_MAX_EXPERTS];  // tile's staging rows per key so far (fkeys <= 1024)
   __shared__ int s_node[MOE_MAX_EXPERTS];  // destination node of each expert (dedup)
   __shared__ int s_bad;
-  count_tile<KMAX>(d, idx, w, blockIdx.x, CountLds{s_mask, s_run, s_frun, s_node, &s_bad});
+  count_tile<KMAX>(d, idx, w, blockIdx.x, CountLds{s_mask, s_pre, s_run, s_frun, s_node, &s_bad});
 }
 
 // One block per band.
