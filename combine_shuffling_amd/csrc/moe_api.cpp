@@ -23,7 +23,7 @@ struct moe_plan {
   moe::Work work;
   bool routed;     // route_count has been launched for the bound routing
   bool assigned;   // slot_of / row_src (and stage_of / stage_src) are final
-  void* pipe_ws;   // workspace whose pipeline counters are known to be clear
+  void* clean_ws;  // workspace whose pipeline counters are known to be zero
 };
 
 namespace moe {
@@ -101,6 +101,15 @@ Work bind_work(const Layout& l, void* base) {
   w.send_copies = p(l.send_copies);
   w.node_copies = p(l.node_copies);
   return w;
+}
+
+// The first pipeline launch of a plan on a workspace zeroes its counters;
+// every pipeline launch leaves them at zero.
+moe_status ensure_counters_clear(moe_plan* plan, hipStream_t s) {
+  if (plan->clean_ws == plan->ws) return MOE_OK;
+  if (launch_counters_clear(plan->d, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
+  plan->clean_ws = plan->ws;
+  return MOE_OK;
 }
 
 // Makes slot_of / row_src (and the staging arrays) final when no dispatch
@@ -218,7 +227,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   p->ws = nullptr;
   p->routed = false;
   p->assigned = false;
-  p->pipe_ws = nullptr;
+  p->clean_ws = nullptr;
   *out = p;
   return MOE_OK;
 }
@@ -269,10 +278,7 @@ moe_status moe_pipeline(moe_plan* plan, const int32_t* topk_idx, void* workspace
   plan->idx = topk_idx;
   plan->ws = workspace;
   plan->work = moe::bind_work(plan->layout, workspace);
-  if (plan->pipe_ws != workspace) {
-    if (moe::launch_pipe_clear(plan->d, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
-    plan->pipe_ws = workspace;
-  }
+  if (moe::ensure_counters_clear(plan, s) != MOE_OK) return MOE_ERR_HIP;
   if (moe::launch_pipeline(plan->d, topk_idx, x, recv, topk_w, out, out_dtype == MOE_OUT_F32,
                            plan->work, s) != hipSuccess)
     return MOE_ERR_HIP;

@@ -117,7 +117,8 @@ hipError_t launch_combine_hier(const Dims& d, const int32_t* idx, const uint16_t
 hipError_t launch_pipeline(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
                            const float* wts, void* out, bool out_f32, const Work& w,
                            hipStream_t s);
-hipError_t launch_pipe_clear(const Dims& d, const Work& w, hipStream_t s);
+// Zeroes the pipeline's counters in a workspace.
+hipError_t launch_counters_clear(const Dims& d, const Work& w, hipStream_t s);
 // fp8 payload (OCP E4M3 codes, one power-of-two scale per 128-element block).
 hipError_t launch_gather_fp8(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
                              float* rscale, const Work& w, hipStream_t s);

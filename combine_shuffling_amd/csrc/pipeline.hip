@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kBlock) void pipeline_kernel(Dims d, const int32_t*
   }
 }
 
-__global__ void pipe_clear_kernel(int32_t* pipe, int n) {
+__global__ void counters_clear_kernel(int32_t* pipe, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) pipe[i] = 0;
 }
 
@@ -296,8 +296,8 @@ hipError_t launch_pipeline(const Dims& d, const int32_t* idx, const uint16_t* x,
   return by_topk<PipelineLaunch>(d.k, d, idx, x, recv, wts, out, out_f32, w, s);
 }
 
-hipError_t launch_pipe_clear(const Dims& d, const Work& w, hipStream_t s) {
-  hipLaunchKernelGGL(pipe_clear_kernel, dim3(1), dim3(kBlock), 0, s, w.pipe,
+hipError_t launch_counters_clear(const Dims& d, const Work& w, hipStream_t s) {
+  hipLaunchKernelGGL(counters_clear_kernel, dim3(1), dim3(kBlock), 0, s, w.pipe,
                      (kPipeHead + 3 * d.nbands) * kPipeSlot);
   return hipGetLastError();
 }

@@ -104,6 +104,8 @@ __device__ __forceinline__ void prefix_table(const unsigned long long* s_mask, i
 // One plan tile (tokens [tile * d.tile, (tile + 1) * d.tile)) by the whole
 // block: in-tile ranks of every slot, the tile's per-expert counts and its
 // bad-routing flag.
+// COH: ranks, counts and flags are device-scope stores (read by other blocks
+// of the same launch).
 template <int KMAX, bool COH = false>
 __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, const Work& w,
                                            int tile, const CountLds& L) {
@@ -215,7 +217,7 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
 
   for (int i = tid; i < E; i += kPlanBlock) st_plan<COH>(&w.tile_counts[tile * E + i], s_run[i]);
   if (d.dedup)
-    for (int i = tid; i < K; i += kPlanBlock) w.tile_fcounts[tile * K + i] = s_frun[i];
+    for (int i = tid; i < K; i += kPlanBlock) st_plan<COH>(&w.tile_fcounts[tile * K + i], s_frun[i]);
   if (tid == 0) st_plan<COH>(&w.tile_flags[tile], s_bad);
 }
 
@@ -228,12 +230,13 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
 // so inside a forwarder that is (owner, token).  Writes the forwarder table,
 // stage_off and the (tile, pair) bases; returns D.  Needs R*N <= 1024 and
 // nblk * R * N <= kScanLdsInts.
+template <bool COH = false>
 __device__ int scan_load_aware(const Dims& d, const Work& w, int* s_mat, int* s_tot, int* s_wsum) {
   __shared__ int s_load[MOE_MAX_EXPERTS];  // per pair
   __shared__ int s_fwd[MOE_MAX_EXPERTS];   // per pair
   const int tid = threadIdx.x, R = d.R, N = d.N, G = d.G, K = d.fkeys, nblk = d.nblk;
 #pragma unroll 8
-  for (int i = tid; i < K * nblk; i += kPlanBlock) s_mat[i] = w.tile_fcounts[i];
+  for (int i = tid; i < K * nblk; i += kPlanBlock) s_mat[i] = ld_plan<COH>(&w.tile_fcounts[i]);
   __syncthreads();
   for (int c = tid; c < K; c += kPlanBlock) {
     int l = 0;
@@ -308,10 +311,10 @@ __device__ __forceinline__ void scan_band(const Dims& d, const Work& w, int band
   if (DEDUP && d.dedup) {
     __syncthreads();
     if (d.load_aware) {
-      staged = scan_load_aware(d, w, s_mat, s_tot, s_wsum);
+      staged = scan_load_aware<COH>(d, w, s_mat, s_tot, s_wsum);
     } else {
-      staged = scan_tiles(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, R, d.nblk, 0, s_mat,
-                          s_tot, s_wsum);
+      staged = scan_tiles<COH>(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, R, d.nblk, 0,
+                               s_mat, s_tot, s_wsum);
       for (int c = tid; c < R * d.N; c += kPlanBlock)
         w.fwd[c] = (c % d.N) * d.G + (c / d.N) % d.G;
     }

@@ -167,7 +167,7 @@ int64_t moe_plan_bands(const moe_plan* plan);             /* nb (1 without bands
  * exclusive scan and the segment descriptors (and, with dedup, the per-
  * forwarder staging descriptors).  topk_idx: device [T, k] int32.
  * workspace: device, moe_plan_workspace_bytes(plan) bytes, contents need
- * no initialisation.  Asynchronous.  The slot arrays (slot_of, row_src and
+ * no initialisation (but see moe_pipeline).  Asynchronous.  The slot arrays (slot_of, row_src and
  * the staging ones) are finished by the next moe_dispatch, or by the next
  * moe_combine / moe_plan_read if no dispatch comes first.
  * Errors: INVALID_ARGUMENT, HIP. */
@@ -244,11 +244,11 @@ moe_status moe_combine_fp8(moe_plan* plan, const uint8_t* y8, const float* y_sca
  * Arguments as for those calls; the routing and the workspace are bound to
  * the plan as by moe_route_plan, and the plan is routed afterwards.  Needs
  * H % 64 == 0 (rows of whole 128-byte lines) and recv 128-byte aligned, so
- * that no cache line holds bytes of two bands.  The
- * workspace also holds the pipeline's counters: the first moe_pipeline of a
- * plan on a workspace clears them (one small extra launch) and every launch
- * leaves them clear, so a workspace used with moe_pipeline must not be
- * written by anyone else while the plan uses it.  Every wait inside the
+ * that no cache line holds bytes of two bands.  The workspace also holds the
+ * pipeline's counters: the first moe_pipeline of a plan on a workspace zeroes
+ * them (one small extra launch) and every launch leaves them at zero, so a
+ * workspace used with moe_pipeline must not be written by anyone else, nor
+ * shared with another plan, while the plan uses it.  Every wait inside the
  * launch is bounded; a wait that gives up makes moe_plan_read(STATUS) report
  * MOE_ERR_PIPELINE_STALL (the outputs are then unspecified).
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (MOE_FLAG_NODE_DEDUP, H % 64 != 0), HIP. */
