@@ -15,8 +15,10 @@ The pages fix no format or scale convention; the reading taken here:
   * code choice: round to the nearest representable E4M3 value, ties to the
     even code (last mantissa bit 0), saturating at +-448; NaN stays NaN;
   * dispatch quantizes each token row once and sends the codes and block
-    scales to its k receive rows; combine decodes (code value * 2^e, exact),
-    and forms the same weighted sum as the bf16 combine.
+    scales to its k receive rows (with node deduplication: once per
+    destination node to a staging row, then fanned out); combine decodes
+    (code value * 2^e, exact), and forms the same weighted sum as the bf16
+    combine.
 """
 
 from __future__ import annotations
@@ -105,6 +107,26 @@ def dispatch_fp8(x_bits: np.ndarray, plan: dict):
     """fp8 dispatch: (codes [T*k, H], block exponents [T*k, nb]) of recv rows."""
     codes, exps = quantize_rows(x_bits)
     return codes[plan["row_src"]], exps[plan["row_src"]]
+
+
+def dedup_dispatch_fp8(x_bits: np.ndarray, plan: dict):
+    """Node-deduplicated fp8 dispatch (FUSCO article, "load balancing and
+    cross-node deduplication", with the fp8 payload above): each token is
+    quantized once; hop 1 writes one staging row of codes and block exponents
+    per distinct (token, node), hop 2 fans each staging row out to the
+    token's receive rows on that node.
+
+    Returns (staging codes [D, H], staging exponents [D, nb], receive codes
+    [T*k, H], receive exponents [T*k, nb]).
+    """
+    codes, exps = quantize_rows(x_bits)
+    sc, se = codes[plan["stage_src"]], exps[plan["stage_src"]]
+    slots, stages = plan["slot_of"].ravel(), plan["stage_of"].ravel()
+    rc = np.empty((slots.size, codes.shape[1]), dtype=np.uint8)
+    re = np.empty((slots.size, exps.shape[1]), dtype=np.int64)
+    rc[slots] = sc[stages]
+    re[slots] = se[stages]
+    return sc, se, rc, re
 
 
 def combine_fp8(codes: np.ndarray, exps: np.ndarray, w: np.ndarray, plan: dict,

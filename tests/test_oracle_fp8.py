@@ -120,3 +120,22 @@ def test_fp8_combine_within_quantization_bound():
     bound = sum(w[:, j:j + 1] * (2.0 ** -4 * np.abs(y[so[:, j]]) + 2.0 ** -10 * scale[so[:, j]])
                 for j in range(so.shape[1]))
     assert np.all(np.abs(q - ref) <= bound * (1 + 1e-9))
+
+
+@pytest.mark.parametrize("fwd", ["static", "load_aware"])
+def test_dedup_fp8_fan_out_equals_single_hop(fwd):
+    # The staging hop carries each (token, node) once; after the fan-out every
+    # receive row holds exactly the single-hop payload.
+    b = gen.make_batch(gen.custom(900, 200, 64, 8, 16, 4, routing="node_limited",
+                                  nodes_per_token=2, node_score_topn=2, seed=6))
+    p = oracle.route_plan(b.topk_idx, 64, 16, 4, forwarders=fwd)
+    sc, se, rc, re = fp8.dedup_dispatch_fp8(b.x, p)
+    c1, e1 = fp8.dispatch_fp8(b.x, p)
+    assert np.array_equal(rc, c1) and np.array_equal(re, e1)
+    assert sc.shape == (p["num_staged"], 200) and se.shape == (p["num_staged"], 2)
+    # each staging row decodes to its token within half an E4M3 step
+    x = oracle.bf16_to_f32(b.x).astype(np.float64)[p["stage_src"]]
+    scale = np.repeat(np.ldexp(1.0, se), 128, axis=1)[:, :200]
+    assert np.all(np.abs(fp8.dequantize_rows(sc, se) - x) <= 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * scale)
+    # fewer staged rows than receive rows: the hop saves payload
+    assert p["num_staged"] < rc.shape[0]
