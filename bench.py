@@ -203,9 +203,10 @@ def algorithmic_bytes(wl, D, payload="bf16", hier=False):
         return (T + 2 * D + T * k) * row, (T * k + T) * row + 2 * D * 2 * row
     if payload == "fp8":
         # token rows are read (and combine results written) as bf16; the k
-        # receive rows carry one byte per element plus a float32 per 128 elements
+        # receive rows (and the D staging rows, written once and read once)
+        # carry one byte per element plus a float32 per 128 elements
         row8 = wl.hidden + 4 * ((wl.hidden + 127) // 128)
-        return T * row + T * k * row8, T * k * row8 + T * row
+        return T * row + (2 * D + T * k) * row8, T * k * row8 + T * row
     disp = (T + T * k) * row if not wl.node_dedup else (T + 2 * D + T * k) * row
     comb = (T * k + T) * row
     return disp, comb
@@ -225,7 +226,10 @@ def cpu_baseline(batch, seconds, payload="bf16", band=0):
         else:
             p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node)
         if payload == "fp8":
-            codes, exps = ofp8.dispatch_fp8(batch.x, p)
+            if wl.node_dedup:
+                _, _, codes, exps = ofp8.dedup_dispatch_fp8(batch.x, p)
+            else:
+                codes, exps = ofp8.dispatch_fp8(batch.x, p)
             ofp8.combine_fp8(codes, exps, batch.topk_w, p)
         else:
             if wl.node_dedup:
@@ -273,10 +277,6 @@ def main():
     dev = torch.device("cuda:0")
     wl = gen.get(args.workload)
     fp8 = args.payload == "fp8"
-    if fp8 and wl.node_dedup:
-        print("the fp8 payload is single-hop only; the workload uses node deduplication",
-              file=sys.stderr)
-        sys.exit(2)
     batch = gen.make_batch(wl)
     T, H, k = wl.num_tokens, wl.hidden, wl.top_k
 
@@ -286,6 +286,9 @@ def main():
 
     la = args.load_aware_forwarders and wl.node_dedup
     hier = args.hier_combine and wl.node_dedup
+    if hier and fp8:
+        print("the hierarchical combine takes the bf16 payload", file=sys.stderr)
+        sys.exit(2)
     pipe = args.pipeline
     if pipe and (wl.node_dedup or fp8):
         print("the banded pipeline runs single-hop workloads with the bf16 payload",
@@ -313,11 +316,15 @@ def main():
             s["recv"] = torch.empty((plan.recv_rows, H), dtype=torch.uint8, device=dev)
             s["scale"] = torch.empty((plan.recv_rows, plan.scale_blocks), dtype=torch.float32,
                                      device=dev)
+            if wl.node_dedup:
+                s["staging"] = torch.empty((plan.staging_rows_max, H), dtype=torch.uint8, device=dev)
+                s["sscale"] = torch.empty((plan.staging_rows_max, plan.scale_blocks),
+                                          dtype=torch.float32, device=dev)
         sets.append(s)
 
     def do_dispatch(s):
         if fp8:
-            s["plan"].dispatch_fp8(s["x"], s["recv"], s["scale"])
+            s["plan"].dispatch_fp8(s["x"], s["recv"], s["scale"], s["staging"], s.get("sscale"))
         else:
             s["plan"].dispatch(s["x"], s["recv"], s["staging"])
 
@@ -390,7 +397,7 @@ def main():
         dom = ("combine_part_kernel+combine_nodes_kernel", comb_b, comb_ms, comb_gbs)
     elif wl.node_dedup:
         # dispatch is two launches here; the dominant single launch timed is combine
-        dom = ("combine_kernel", comb_b, comb_ms, comb_gbs)
+        dom = ("combine_fp8_kernel" if fp8 else "combine_kernel", comb_b, comb_ms, comb_gbs)
     else:
         sfx = "_fp8" if fp8 else ""
         dom = max([(f"gather{sfx}_kernel", disp_b, disp_ms, disp_gbs),

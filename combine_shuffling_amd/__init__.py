@@ -205,8 +205,12 @@ class Plan:
 
     # -- moe_dispatch_fp8
     def dispatch_fp8(self, x: torch.Tensor, recv8: torch.Tensor | None = None,
-                     recv_scale: torch.Tensor | None = None, stream=None):
-        """fp8 payload: returns (codes uint8 [T*k, H], block scales float32 [T*k, nb])."""
+                     recv_scale: torch.Tensor | None = None, staging8: torch.Tensor | None = None,
+                     staging_scale: torch.Tensor | None = None, stream=None):
+        """fp8 payload: returns (codes uint8 [T*k, H], block scales float32 [T*k, nb]).
+
+        With node deduplication the codes and scales pass through staging rows
+        (staging8 [staging_rows_max, H] uint8, staging_scale [.., nb] float32)."""
         dev = self.device
         if dev is None:
             raise MoeError(_abi.ERR_PLAN_NOT_ROUTED, "dispatch_fp8")
@@ -218,7 +222,16 @@ class Plan:
                                      device=dev)
         _need(recv8, (self.recv_rows, self.H), (torch.uint8,), "recv8", dev)
         _need(recv_scale, (self.recv_rows, self.scale_blocks), (torch.float32,), "recv_scale", dev)
+        if self.node_dedup:
+            D = self.staging_rows_max
+            if staging8 is None:
+                staging8 = torch.empty((D, self.H), dtype=torch.uint8, device=dev)
+            if staging_scale is None:
+                staging_scale = torch.empty((D, self.scale_blocks), dtype=torch.float32, device=dev)
+            _need(staging8, (D, self.H), (torch.uint8,), "staging8", dev)
+            _need(staging_scale, (D, self.scale_blocks), (torch.float32,), "staging_scale", dev)
         _abi.check(self._lib.moe_dispatch_fp8(self._h, _ptr(x), _ptr(recv8), _ptr(recv_scale),
+                                              _ptr(staging8), _ptr(staging_scale),
                                               _stream_handle(dev, stream)), "moe_dispatch_fp8")
         return recv8, recv_scale
 
@@ -288,9 +301,10 @@ def combine(plan: Plan, y: torch.Tensor, topk_w: torch.Tensor, out=None,
     return plan.combine(y, topk_w, out, out_dtype, stream)
 
 
-def dispatch_fp8(plan: Plan, x: torch.Tensor, recv8=None, recv_scale=None, stream=None):
+def dispatch_fp8(plan: Plan, x: torch.Tensor, recv8=None, recv_scale=None, staging8=None,
+                 staging_scale=None, stream=None):
     """moe_dispatch_fp8: returns (codes [T*k, H] uint8, block scales [T*k, nb] float32)."""
-    return plan.dispatch_fp8(x, recv8, recv_scale, stream)
+    return plan.dispatch_fp8(x, recv8, recv_scale, staging8, staging_scale, stream)
 
 
 def combine_fp8(plan: Plan, y8: torch.Tensor, y_scale: torch.Tensor, topk_w: torch.Tensor,

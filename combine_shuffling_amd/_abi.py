@@ -97,7 +97,7 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_read.restype = i32
     L.moe_plan_scale_blocks.argtypes = [vp]
     L.moe_plan_scale_blocks.restype = i64
-    L.moe_dispatch_fp8.argtypes = [vp, vp, vp, vp, vp]
+    L.moe_dispatch_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.moe_dispatch_fp8.restype = i32
     L.moe_combine_fp8.argtypes = [vp, vp, vp, vp, vp, i32, vp]
     L.moe_combine_fp8.restype = i32

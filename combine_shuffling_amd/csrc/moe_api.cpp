@@ -345,18 +345,22 @@ int64_t moe_plan_scale_blocks(const moe_plan* plan) {
 }
 
 moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, float* recv_scale,
-                            void* stream) {
+                            uint8_t* staging8, float* staging_scale, void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARGUMENT;
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
-  if (plan->d.dedup) return MOE_ERR_UNSUPPORTED;
   if (plan->d.T == 0) return MOE_OK;
   if (!x || !recv8 || !recv_scale || !moe::aligned(x, 16) || !moe::aligned(recv8, 16) ||
       !moe::aligned(recv_scale, 4))
     return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->d.dedup && (!staging8 || !staging_scale || !moe::aligned(staging8, 16) ||
+                        !moe::aligned(staging_scale, 4)))
+    return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (moe::launch_gather_fp8(plan->d, plan->idx, x, recv8, recv_scale, plan->work, s) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
+  const hipError_t e =
+      plan->d.dedup ? moe::launch_stage_fp8(plan->d, plan->idx, x, staging8, staging_scale, recv8,
+                                            recv_scale, plan->work, s)
+                    : moe::launch_gather_fp8(plan->d, plan->idx, x, recv8, recv_scale, plan->work, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
   plan->assigned = true;
   return MOE_OK;
 }

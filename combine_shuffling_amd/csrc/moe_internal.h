@@ -122,6 +122,11 @@ hipError_t launch_counters_clear(const Dims& d, const Work& w, hipStream_t s);
 // fp8 payload (OCP E4M3 codes, one power-of-two scale per 128-element block).
 hipError_t launch_gather_fp8(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
                              float* rscale, const Work& w, hipStream_t s);
+// Node-deduplicated fp8 dispatch: stage_a_fp8 then stage_b_fp8.  Also
+// finishes slot_of / row_src / stage_of / stage_src.
+hipError_t launch_stage_fp8(const Dims& d, const int32_t* idx, const uint16_t* x,
+                            uint8_t* stage8, float* sscale, uint8_t* recv8, float* rscale,
+                            const Work& w, hipStream_t s);
 hipError_t launch_combine_fp8(const Dims& d, const uint8_t* y8, const float* yscale,
                               const float* wts, void* out, bool out_f32, const Work& w,
                               hipStream_t s);

@@ -308,27 +308,16 @@ __device__ __forceinline__ void store_codes(uint8_t* base, int64_t row, const Di
   }
 }
 
-// Dispatch with an fp8 payload: each token row is read once, quantized once
-// (block amax by an 8-lane reduction) and its codes and block scales are
-// written to the token's k receive rows.
-template <int KMAX>
-__global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
-                                                            const u32x4* __restrict__ x,
-                                                            uint8_t* __restrict__ recv8,
-                                                            float* __restrict__ rscale, Work w) {
-  const int lane = threadIdx.x % kWave;
-  const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
-  const int items = d.T * segs8;
-  const uint32_t rows = (uint32_t)(d.T * d.k);
-  const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  const Item8 it = wave_item8<1>(d, segs8, items, 0);
-  int slot[KMAX];
-  if (it.live) {
-    token_slots<KMAX>(d, w, idx, it.t, slot);
-  } else {
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) slot[j] = -1;
-  }
+// The lane's 16 codes of its two chunks of token row it.t and its scale
+// block's scale 2^e (block amax by an 8-lane reduction; every lane of the
+// wave must call it).
+struct Fp8Piece {
+  u32x2 a, b;
+  float scale;
+};
+
+__device__ __forceinline__ Fp8Piece quantize_piece(const Dims& d, const Item8& it,
+                                                   const u32x4* __restrict__ x) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
   const int64_t xrow = (int64_t)it.t * d.chunks;
   const u32x4 v0 = it.ok0 ? load_x_chunk(&x[xrow + it.c0]) : zero;
@@ -349,8 +338,48 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
     f0[q] *= inv;
     f1[q] *= inv;
   }
-  const u32x2 ca = encode_e4m3x8(f0), cb = encode_e4m3x8(f1);
-  const float scale = ldexpf(1.0f, e);
+  return Fp8Piece{encode_e4m3x8(f0), encode_e4m3x8(f1), ldexpf(1.0f, e)};
+}
+
+// 16 codes of a lane from byte offset (row * H + c0 * 8), the inverse of
+// store_codes.
+__device__ __forceinline__ void load_codes(const uint8_t* base, int64_t row, const Dims& d,
+                                           const Item8& it, u32x2& a, u32x2& b) {
+  const uint8_t* p = base + row * d.H + (int64_t)it.c0 * 8;
+  if ((d.H & 15) == 0) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    a = u32x2{v[0], v[1]};
+    b = u32x2{v[2], v[3]};
+  } else {
+    const u32x2 zero = {0u, 0u};
+    a = it.ok0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)) : zero;
+    b = it.ok1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + 8)) : zero;
+  }
+}
+
+// Dispatch with an fp8 payload: each token row is read once, quantized once
+// and its codes and block scales are written to the token's k receive rows.
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                            const u32x4* __restrict__ x,
+                                                            uint8_t* __restrict__ recv8,
+                                                            float* __restrict__ rscale, Work w) {
+  const int lane = threadIdx.x % kWave;
+  const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
+  const int items = d.T * segs8;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
+  const Item8 it = wave_item8<1>(d, segs8, items, 0);
+  int slot[KMAX];
+  if (it.live) {
+    token_slots<KMAX>(d, w, idx, it.t, slot);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) slot[j] = -1;
+  }
+  const Fp8Piece q = quantize_piece(d, it, x);
+  const u32x2 ca = q.a, cb = q.b;
+  const float scale = q.scale;
   const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
   const int blk = it.c0 / kFp8BlockChunks;
 
@@ -365,6 +394,104 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
       if ((uint32_t)slot[j] < rows) {
         store_codes(recv8, slot[j], d, it, ca, cb);
         if (scale_lane) rscale[(int64_t)slot[j] * nb + blk] = scale;
+      }
+    }
+  }
+}
+
+// Node-deduplicated dispatch with an fp8 payload, hop 1: each token row is
+// read and quantized once, and its codes and block scales go to one staging
+// row per destination node.  Also finishes slot_of / row_src / stage_of /
+// stage_src.
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void stage_a_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                             const u32x4* __restrict__ x,
+                                                             uint8_t* __restrict__ stage8,
+                                                             float* __restrict__ sscale, Work w) {
+  const int lane = threadIdx.x % kWave;
+  const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
+  const int items = d.T * segs8;
+  const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
+  const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
+  const Item8 it = wave_item8<1>(d, segs8, items, 0);
+  int slot[KMAX], p[KMAX];
+  uint32_t lead = 0;
+  if (it.live) {
+    token_slots<KMAX>(d, w, idx, it.t, slot);
+    token_stages<KMAX>(d, w, it.t, p, lead);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) slot[j] = p[j] = -1;
+  }
+  const Fp8Piece q = quantize_piece(d, it, x);
+  const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
+  const int blk = it.c0 / kFp8BlockChunks;
+  if (it.live && it.c0 == 2 * lane && lane < d.k) {  // first segment publishes the plan
+    const int64_t at = (int64_t)it.t * d.k + lane;
+    const int s = lane_pick<KMAX>(slot, lane);
+    const int r = lane_pick<KMAX>(p, lane);
+    w.slot_of[at] = s;
+    if ((uint32_t)s < rows) w.row_src[s] = it.t;
+    w.stage_of[at] = r;
+    if (((lead >> lane) & 1u) && (uint32_t)r < srows) w.stage_src[r] = it.t;
+  }
+  if (it.ok0) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (((lead >> j) & 1u) && (uint32_t)p[j] < srows) {
+        store_codes(stage8, p[j], d, it, q.a, q.b);
+        if (scale_lane) sscale[(int64_t)p[j] * nb + blk] = q.scale;
+      }
+    }
+  }
+}
+
+// Hop 2, one token per wave-item: each of the token's staging rows (codes and
+// scales) is read once and written to the token's slots on that node.
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void stage_b_fp8_kernel(Dims d, const uint8_t* __restrict__ stage8,
+                                                             const float* __restrict__ sscale,
+                                                             uint8_t* __restrict__ recv8,
+                                                             float* __restrict__ rscale, Work w) {
+  const int lane = threadIdx.x % kWave;
+  const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
+  const int items = d.T * segs8;
+  const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
+  const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
+  const Item8 it = wave_item8<1>(d, segs8, items, 0);
+  const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
+  const int blk = it.c0 / kFp8BlockChunks;
+  const int64_t at = (int64_t)it.t * d.k;
+  int slot[KMAX], p[KMAX];
+  u32x2 a[KMAX], b[KMAX];
+  float sc[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool has = it.live && j < d.k;
+    slot[j] = has ? w.slot_of[at + j] : -1;
+    p[j] = has ? w.stage_of[at + j] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    bool first = (uint32_t)p[j] < srows;
+#pragma unroll
+    for (int jj = 0; jj < j; ++jj) first = first && p[jj] != p[j];
+    if (first && it.ok0) {
+      load_codes(stage8, p[j], d, it, a[j], b[j]);
+      if (scale_lane) sc[j] = sscale[(int64_t)p[j] * nb + blk];
+    }
+    if (!first) p[j] = p[j] < 0 ? -1 : -2 - p[j];  // later slot of a node: -2-row
+  }
+  if (!it.ok0) return;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (p[j] < 0) continue;  // j is the first slot of its node: write all of the node's slots
+#pragma unroll
+    for (int jj = j; jj < KMAX; ++jj) {
+      const bool same = jj == j || p[jj] == -2 - p[j];
+      if (same && (uint32_t)slot[jj] < rows) {
+        store_codes(recv8, slot[jj], d, it, a[j], b[j]);
+        if (scale_lane) rscale[(int64_t)slot[jj] * nb + blk] = sc[j];
       }
     }
   }
@@ -513,6 +640,26 @@ struct GatherFp8Launch {
 };
 
 template <int KMAX>
+struct StageAFp8Launch {
+  static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* stage8,
+                        float* sscale, const Work& w, hipStream_t s) {
+    hipLaunchKernelGGL((stage_a_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s, d,
+                       idx, reinterpret_cast<const u32x4*>(x), stage8, sscale, w);
+    return hipGetLastError();
+  }
+};
+
+template <int KMAX>
+struct StageBFp8Launch {
+  static hipError_t run(const Dims& d, const uint8_t* stage8, const float* sscale, uint8_t* recv8,
+                        float* rscale, const Work& w, hipStream_t s) {
+    hipLaunchKernelGGL((stage_b_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s, d,
+                       stage8, sscale, recv8, rscale, w);
+    return hipGetLastError();
+  }
+};
+
+template <int KMAX>
 struct CombineFp8Launch {
   static hipError_t run(const Dims& d, const uint8_t* y8, const float* yscale, const float* wts,
                         void* out, bool f32, const Work& w, hipStream_t s) {
@@ -564,6 +711,16 @@ hipError_t launch_gather_fp8(const Dims& d, const int32_t* idx, const uint16_t* 
                              float* rscale, const Work& w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
   return by_topk<GatherFp8Launch>(d.k, d, idx, x, recv8, rscale, w, s);
+}
+
+hipError_t launch_stage_fp8(const Dims& d, const int32_t* idx, const uint16_t* x,
+                            uint8_t* stage8, float* sscale, uint8_t* recv8, float* rscale,
+                            const Work& w, hipStream_t s) {
+  if (d.T == 0) return hipSuccess;
+  const hipError_t e = by_topk<StageAFp8Launch>(d.k, d, idx, x, stage8, sscale, w, s);
+  if (e != hipSuccess) return e;
+  return by_topk<StageBFp8Launch>(d.k, d, stage8, static_cast<const float*>(sscale), recv8, rscale,
+                                  w, s);
 }
 
 hipError_t launch_combine_fp8(const Dims& d, const uint8_t* y8, const float* yscale,

@@ -218,11 +218,15 @@ int64_t moe_plan_scale_blocks(const moe_plan* plan);
 
 /* fp8 dispatch: each token row of x (bf16 [T, H]) is quantized once and its
  * codes and block scales are written to its receive rows: recv8 [T*k, H]
- * uint8, recv_scale [T*k, nb] float32.  Plans with MOE_FLAG_NODE_DEDUP are
- * not supported (MOE_ERR_UNSUPPORTED).  Asynchronous.
- * Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, UNSUPPORTED, HIP. */
+ * uint8, recv_scale [T*k, nb] float32.  With MOE_FLAG_NODE_DEDUP the codes
+ * and scales go first to one staging row per (token, node) -- staging8
+ * [staging_rows_max, H] uint8 and staging_scale [staging_rows_max, nb]
+ * float32, caller-owned, first D rows written -- and are then fanned out
+ * inside the node (the same hops as moe_dispatch); without it staging8 and
+ * staging_scale are ignored (may be NULL).  The receive rows are the same
+ * either way.  Asynchronous.  Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
 moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, float* recv_scale,
-                            void* stream);
+                            uint8_t* staging8, float* staging_scale, void* stream);
 
 /* fp8 combine: out[t] = sum_j topk_w[t, j] * decode(y8, y_scale)[slot_of[t, j]]
  * with the decode exact (code value times its block scale) and the same

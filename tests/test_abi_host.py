@@ -161,6 +161,6 @@ def test_fp8_entry_points_on_host():
     st, h = make(T=64, H=200)
     assert L.moe_plan_scale_blocks(h) == 2          # ceil(200 / 128)
     vp = ctypes.c_void_p
-    assert L.moe_dispatch_fp8(h, vp(16), vp(16), vp(16), None) == _abi.ERR_PLAN_NOT_ROUTED
+    assert L.moe_dispatch_fp8(h, vp(16), vp(16), vp(16), None, None, None) == _abi.ERR_PLAN_NOT_ROUTED
     assert L.moe_combine_fp8(h, vp(16), vp(16), vp(16), vp(16), 0, None) == _abi.ERR_PLAN_NOT_ROUTED
     L.moe_plan_destroy(h)

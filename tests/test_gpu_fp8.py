@@ -109,17 +109,71 @@ def test_fp8_one_hot_combine_is_exact_decode(dev):
     assert np.array_equal(out.astype(np.float64), fp8.dequantize_rows(c[rows], e[rows]))
 
 
-def test_fp8_refuses_dedup_and_combines_without_dispatch(dev):
+def check_fp8_dedup(batch, dev, load_aware=False, tokens=None):
     import combine_shuffling_amd as cs
-    from combine_shuffling_amd import _abi
+
+    wl = batch.workload
+    T, H, k = wl.num_tokens, wl.hidden, wl.top_k
+    say(f"[fp8 dedup] {wl.describe()} load_aware={load_aware}")
+    p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node,
+                          forwarders="load_aware" if load_aware else "static")
+    sc, se, rc, re = fp8.dedup_dispatch_fp8(batch.x, p)
+    plan = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, True, load_aware)
+    plan.route(to_dev(batch.topk_idx, dev))
+    rows, smax, nb = plan.recv_rows, plan.staging_rows_max, plan.scale_blocks
+    codes_full = torch.full((rows + 2, H), 0x55, dtype=torch.uint8, device=dev)
+    scale_full = torch.full((rows + 2, nb), -1.0, dtype=torch.float32, device=dev)
+    st8_full = torch.full((smax + 2, H), 0x55, dtype=torch.uint8, device=dev)
+    sts_full = torch.full((smax + 2, nb), -1.0, dtype=torch.float32, device=dev)
+    plan.dispatch_fp8(to_dev(batch.x, dev), codes_full[:rows], scale_full[:rows], st8_full[:smax],
+                      sts_full[:smax])
+    torch.cuda.synchronize()
+    for full, n, fill in ((codes_full, rows, 0x55), (scale_full, rows, -1.0), (st8_full, smax, 0x55),
+                          (sts_full, smax, -1.0)):
+        assert bool((full[n:] == fill).all()), "fp8 dedup dispatch wrote past a buffer"
+    D = p["num_staged"]
+    assert np.array_equal(st8_full[:D].cpu().numpy(), sc), "staging codes differ"
+    assert np.array_equal(sts_full[:D].cpu().numpy().astype(np.float64), np.ldexp(1.0, se))
+    got_c = codes_full[:rows].cpu().numpy()
+    assert np.array_equal(got_c, rc), "receive codes differ"
+    assert np.array_equal(scale_full[:rows].cpu().numpy().astype(np.float64), np.ldexp(1.0, re))
+    assert np.array_equal(plan.read("stage_of").reshape(T, k), p["stage_of"])
+    assert np.array_equal(plan.read("stage_src")[:D], p["stage_src"])
+    tok = np.arange(T) if tokens is None else tokens
+    so = p["slot_of"][tok]
+    ref = fp8.combine_fp8(rc, re, batch.topk_w[tok], {"slot_of": so})
+    out = plan.combine_fp8(codes_full[:rows], scale_full[:rows], to_dev(batch.topk_w, dev),
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_combine_values(out.cpu().numpy()[tok], ref, fp8.dequantize_rows(rc, re),
+                         batch.topk_w[tok], so, True, wl.name + " fp8 dedup")
+
+
+@pytest.mark.parametrize("load_aware", [False, True])
+@pytest.mark.parametrize("case", [
+    (600, 128, 16, 4, 4, 2), (1000, 200, 64, 8, 16, 4), (777, 24, 1024, 16, 32, 8),
+    (2048, 512, 256, 8, 64, 8)], ids=lambda c: "T{}-H{}-E{}-k{}-R{}-G{}".format(*c))
+def test_fp8_dedup_small(case, load_aware, dev):
+    T, H, E, k, R, G = case
+    check_fp8_dedup(gen.make_batch(gen.custom(T, H, E, k, R, G, routing="node_limited",
+                                              nodes_per_token=min(4, R // G), node_score_topn=2,
+                                              seed=T + H)), dev, load_aware)
+
+
+def test_fp8_dedup_dsv3(dev):
+    batch = gen.make_batch(gen.get("dsv3"))
+    T = batch.workload.num_tokens
+    tok = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(11).integers(0, T, 384)]))
+    check_fp8_dedup(batch, dev, tokens=tok)
+
+
+def test_fp8_combines_without_dispatch(dev):
+    import combine_shuffling_amd as cs
 
     batch = gen.make_batch(gen.custom(600, 128, 16, 4, 4, 2, seed=4))
     idx = to_dev(batch.topk_idx, dev)
     plan = cs.Plan(600, 128, 16, 4, 4, 2, node_dedup=True)
     plan.route(idx)
-    with pytest.raises(cs.MoeError) as ei:
-        plan.dispatch_fp8(to_dev(batch.x, dev))
-    assert ei.value.status == _abi.ERR_UNSUPPORTED
     # combine of a host-made fp8 payload straight after the route
     p = oracle.route_plan(batch.topk_idx, 16, 4, 2)
     c, e = fp8.dispatch_fp8(batch.x, p)
