@@ -27,6 +27,10 @@
 //           abstract: combine back to each token's owner).
 #include "move_body.h"
 
+#ifndef MOE_HIER_PART_U
+#define MOE_HIER_PART_U 4  // wave-items per wave: hop 1 of the hierarchical combine (1: 1403 us, 2: 1340, 4: 1322 on dsv3)
+#endif
+
 namespace moe {
 namespace {
 
@@ -122,46 +126,53 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
 // ---- hierarchical combine over the deduplication's staging rows ------------
 // Hop 1 (at the forwarder): one fp32 partial per staging row p = (token t,
 // node n), the fused multiply-add chain over t's slots on n in ascending j.
-template <int KMAX>
+template <int KMAX, int U>
 __global__ __launch_bounds__(kBlock) void combine_part_kernel(Dims d, const u32x4* __restrict__ y,
                                                               const float* __restrict__ wts,
                                                               f32x4* __restrict__ part, Work w) {
   const int staged = min(w.ctrl[kCtrlStaged], d.smax);
   const int items = staged * d.segs;
   const uint32_t rows = (uint32_t)(d.T * d.k);
-  const Item it = wave_item<1>(d, items, 0);  // it.t is the staging row here
-  const int p = it.t;
-  const int t = it.live ? w.stage_src[p] : -1;
-  const bool tok = (uint32_t)t < (uint32_t)d.T;
-  const int64_t at = (int64_t)(tok ? t : 0) * d.k;
-  int slot[KMAX];
-  float wj[KMAX];
-  u32x4 v[KMAX];
+  Item it[U];  // it[u].t is the staging row here
+  int slot[U][KMAX];
+  float wj[U][KMAX];
+  u32x4 v[U][KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    const bool mine = tok && j < d.k && w.stage_of[at + j] == p;
-    slot[j] = mine ? w.slot_of[at + j] : -1;
-    if ((uint32_t)slot[j] >= rows) slot[j] = -1;
-    wj[j] = mine ? wts[at + j] : 0.0f;
+  for (int u = 0; u < U; ++u) {
+    it[u] = wave_item<U>(d, items, u);
+    const int p = it[u].t;
+    const int t = it[u].live ? w.stage_src[p] : -1;
+    const bool tok = (uint32_t)t < (uint32_t)d.T;
+    const int64_t at = (int64_t)(tok ? t : 0) * d.k;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const bool mine = tok && j < d.k && w.stage_of[at + j] == p;
+      slot[u][j] = mine ? w.slot_of[at + j] : -1;
+      if ((uint32_t)slot[u][j] >= rows) slot[u][j] = -1;
+      wj[u][j] = mine ? wts[at + j] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (slot[u][j] >= 0 && it[u].ok) v[u][j] = load_chunk(&y[(int64_t)slot[u][j] * d.chunks + it[u].c]);
   }
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j)
-    if (slot[j] >= 0 && it.ok) v[j] = load_chunk(&y[(int64_t)slot[j] * d.chunks + it.c]);
-  if (!it.ok) return;
-  float acc[8];
+  for (int u = 0; u < U; ++u) {
+    if (!it[u].ok) continue;
+    float acc[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (slot[j] < 0) continue;
-    float f[8];
-    unpack_bf16(v[j], f);
+    for (int j = 0; j < KMAX; ++j) {
+      if (slot[u][j] < 0) continue;
+      float f[8];
+      unpack_bf16(v[u][j], f);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj[j], f[q], acc[q]);
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj[u][j], f[q], acc[q]);
+    }
+    f32x4* o = part + ((int64_t)it[u].t * d.chunks + it[u].c) * 2;
+    store_chunk(o, f32x4{acc[0], acc[1], acc[2], acc[3]});
+    store_chunk(o + 1, f32x4{acc[4], acc[5], acc[6], acc[7]});
   }
-  f32x4* o = part + ((int64_t)p * d.chunks + it.c) * 2;
-  store_chunk(o, f32x4{acc[0], acc[1], acc[2], acc[3]});
-  store_chunk(o + 1, f32x4{acc[4], acc[5], acc[6], acc[7]});
 }
 
 // Hop 2 (at the owner): out[t] = sum of t's partials in ascending node order
@@ -679,10 +690,11 @@ template <int KMAX>
 struct CombineHierLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* y, const float* wts,
                         float* part, void* out, bool f32, const Work& w, hipStream_t s) {
+    constexpr int PU = MOE_HIER_PART_U;
     const int64_t part_items = (int64_t)d.smax * d.segs;
-    const int part_blocks = (int)((part_items + kWaves - 1) / kWaves);
+    const int part_blocks = (int)((part_items + kWaves * PU - 1) / (kWaves * PU));
     if (part_blocks > 0)
-      hipLaunchKernelGGL((combine_part_kernel<KMAX>), dim3(part_blocks), dim3(kBlock), 0, s, d,
+      hipLaunchKernelGGL((combine_part_kernel<KMAX, PU>), dim3(part_blocks), dim3(kBlock), 0, s, d,
                          reinterpret_cast<const u32x4*>(y), wts, reinterpret_cast<f32x4*>(part),
                          w);
     hipError_t e = hipGetLastError();
