@@ -87,6 +87,8 @@ SMALL = [
     (600, 64, 128, 8, 8, 8, "zipf"),
     (20000, 16, 30, 4, 6, 3, "uniform"),       # two 256-token passes per tile
     (40000, 8, 256, 8, 64, 8, "uniform"),     # three passes per tile
+    (1500, 64, 1024, 16, 1024, 1, "uniform"),  # most experts and ranks: 1024 one-rank nodes
+    (1, 64, 1024, 16, 64, 8, "uniform"),       # one token, dedup
 ]
 
 
@@ -222,7 +224,8 @@ def test_plan_reads_and_combine_without_dispatch(dev):
 
 
 @pytest.mark.parametrize("case", [
-    (2048, 64, 64, 4, 16, 4), (3001, 40, 30, 5, 6, 2), (777, 24, 1024, 16, 32, 8), (20000, 16, 64, 8, 32, 4)],
+    (2048, 64, 64, 4, 16, 4), (3001, 40, 30, 5, 6, 2), (777, 24, 1024, 16, 32, 8), (20000, 16, 64, 8, 32, 4),
+    (1800, 32, 64, 16, 32, 1)],   # R * N = 1024 owner-node pairs, the most the scan holds
     ids=lambda c: "T{}-H{}-E{}-k{}-R{}-G{}".format(*c))
 def test_load_aware_forwarders(case, dev):
     T, H, E, k, R, G = case
