@@ -57,5 +57,33 @@ def build(verbose: bool = False, extra_flags=(), out: str | None = None) -> str:
     return out
 
 
+C_TESTS = os.path.join(ROOT, "tests", "c")
+
+
+def build_c_tests() -> list:
+    """Compile the plain-C users of the ABI (tests/c/*.c) against the built
+    library with gcc, into tests/c/build/.  abi_gpu also links the HIP C
+    runtime.  The binaries find the library through an $ORIGIN-relative
+    rpath, so the tree can move."""
+    out_dir = os.path.join(C_TESTS, "build")
+    os.makedirs(out_dir, exist_ok=True)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    rpath = "-Wl,-rpath,$ORIGIN/../../../combine_shuffling_amd"
+    common = ["gcc", "-O2", "-std=c11", "-Wall", "-Werror", f"-I{INCLUDE}"]
+    link = [f"-L{PKG}", "-lmoeshuffle", rpath]
+    built = []
+    for name, extra in (("abi_host", []),
+                        ("abi_gpu", ["-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+                                     f"-L{rocm}/lib", "-lamdhip64", f"-Wl,-rpath,{rocm}/lib"])):
+        dst = os.path.join(out_dir, name)
+        cmd = [*common, os.path.join(C_TESTS, name + ".c"), "-o", dst, *link, *extra]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"gcc failed for {name}:\n{res.stdout}{res.stderr}")
+        built.append(dst)
+    return built
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print("\n".join(build_c_tests()))
