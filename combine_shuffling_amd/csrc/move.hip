@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* 
     it[u] = wave_item<U>(d, items, u);
     lead[u] = 0;
     if (it[u].live) {
-      token_slots<KMAX>(d, w, idx, it[u].t, slot[u]);
+      token_slots_serial<KMAX>(d, w, idx, it[u].t, slot[u]);
       token_stages<KMAX>(d, w, it[u].t, p[u], lead[u]);
     } else {
 #pragma unroll
@@ -92,11 +92,18 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
   for (int u = 0; u < U; ++u) {
     it[u] = wave_item<U>(d, items, u);
     const int64_t at = (int64_t)it[u].t * d.k;
+    int sj[KMAX], pj[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {  // no branch between the loads: they issue together
+      const int64_t a = slot_index(at, j, d.k);
+      sj[j] = w.slot_of[a];
+      pj[j] = w.stage_of[a];
+    }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const bool has = it[u].live && j < d.k;
-      slot[u][j] = has ? w.slot_of[at + j] : -1;
-      p[u][j] = has ? w.stage_of[at + j] : -1;
+      slot[u][j] = has ? sj[j] : -1;
+      p[u][j] = has ? pj[j] : -1;
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
@@ -428,7 +435,7 @@ __global__ __launch_bounds__(kBlock) void stage_a_fp8_kernel(Dims d, const int32
   int slot[KMAX], p[KMAX];
   uint32_t lead = 0;
   if (it.live) {
-    token_slots<KMAX>(d, w, idx, it.t, slot);
+    token_slots_serial<KMAX>(d, w, idx, it.t, slot);
     token_stages<KMAX>(d, w, it.t, p, lead);
   } else {
 #pragma unroll
@@ -476,11 +483,18 @@ __global__ __launch_bounds__(kBlock) void stage_b_fp8_kernel(Dims d, const uint8
   int slot[KMAX], p[KMAX];
   u32x2 a[KMAX], b[KMAX];
   float sc[KMAX];
+  int sj[KMAX], pj[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {  // no branch between the loads: they issue together
+    const int64_t a = slot_index(at, j, d.k);
+    sj[j] = w.slot_of[a];
+    pj[j] = w.stage_of[a];
+  }
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     const bool has = it.live && j < d.k;
-    slot[j] = has ? w.slot_of[at + j] : -1;
-    p[j] = has ? w.stage_of[at + j] : -1;
+    slot[j] = has ? sj[j] : -1;
+    p[j] = has ? pj[j] : -1;
   }
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
@@ -528,12 +542,19 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_kernel(Dims d, const u32x2
     it[u] = wave_item<U>(d, items, u);
     const int64_t at = (int64_t)it[u].t * d.k;
     const int blk = it[u].c / kFp8BlockChunks;
+    int sj[KMAX];
+    float wt[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {  // no branch between the loads: they issue together
+      const int64_t a = slot_index(at, j, d.k);
+      sj[j] = slot_of[a];
+      wt[j] = wts[a];
+    }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const bool has = it[u].live && j < d.k;
-      slot[u][j] = has ? slot_of[at + j] : -1;
-      if ((uint32_t)slot[u][j] >= rows) slot[u][j] = -1;
-      wj[u][j] = has ? wts[at + j] : 0.0f;
+      slot[u][j] = has && (uint32_t)sj[j] < rows ? sj[j] : -1;
+      wj[u][j] = has ? wt[j] : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {

@@ -194,12 +194,19 @@ __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, con
   for (int u = 0; u < U; ++u) {
     it[u] = wave_item<U>(d, blk, base, limit, u);
     const int64_t at = (int64_t)it[u].t * d.k;
+    int sj[KMAX];
+    float wt[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {  // no branch between the loads: they issue together
+      const int64_t a = slot_index(at, j, d.k);
+      sj[j] = ld_plan<COH>(&slot_of[a]);
+      wt[j] = wts[a];
+    }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const bool has = it[u].live && j < d.k;
-      slot[u][j] = has ? ld_plan<COH>(&slot_of[at + j]) : -1;
-      if ((uint32_t)slot[u][j] >= rows) slot[u][j] = -1;
-      wj[u][j] = has ? wts[at + j] : 0.0f;
+      slot[u][j] = has && (uint32_t)sj[j] < rows ? sj[j] : -1;
+      wj[u][j] = has ? wt[j] : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
