@@ -22,6 +22,7 @@ struct moe_plan {
   void* ws;
   moe::Work work;
   bool routed;     // route_count has been launched for the bound routing
+  bool scanned;    // route_scan has been launched for it (tile bases, offsets, status)
   bool assigned;   // slot_of / row_src (and stage_of / stage_src) are final
   void* clean_ws;  // workspace whose pipeline counters are known to be zero
 };
@@ -112,10 +113,19 @@ moe_status ensure_counters_clear(moe_plan* plan, hipStream_t s) {
   return MOE_OK;
 }
 
+// Launches the plan's scan if the route left it to the gather (small plans).
+moe_status ensure_scanned(moe_plan* plan, hipStream_t s) {
+  if (plan->scanned) return MOE_OK;
+  if (launch_route_scan(plan->d, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
+  plan->scanned = true;
+  return MOE_OK;
+}
+
 // Makes slot_of / row_src (and the staging arrays) final when no dispatch
 // has done it since the last route.
 moe_status ensure_assigned(moe_plan* plan, hipStream_t s) {
   if (plan->assigned) return MOE_OK;
+  if (ensure_scanned(plan, s) != MOE_OK) return MOE_ERR_HIP;
   if (launch_route_assign(plan->d, plan->idx, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
   plan->assigned = true;
   return MOE_OK;
@@ -213,6 +223,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
     d.tpb = d.nblk;
     d.nbands = 1;
   }
+  // Small single-hop plans: the gather scans the tile counts itself.
+  d.fused_scan = (!dedup && d.nbands == 1 && (int64_t)d.nblk * d.E <= moe::kFusedScanInts) ? 1 : 0;
   d.chunks = (int32_t)chunks;
   d.segs = (int32_t)((chunks + moe::kWave - 1) / moe::kWave);
   d.smax = (int32_t)staging_max;
@@ -226,6 +238,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   p->idx = nullptr;
   p->ws = nullptr;
   p->routed = false;
+  p->scanned = false;
   p->assigned = false;
   p->clean_ws = nullptr;
   *out = p;
@@ -255,8 +268,12 @@ moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspa
   plan->idx = topk_idx;
   plan->ws = workspace;
   plan->work = moe::bind_work(plan->layout, workspace);
+  plan->scanned = false;
   if (moe::launch_route_count(plan->d, topk_idx, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
   plan->routed = true;
+  // Small single-hop plans leave the scan to the gather (and to whoever reads
+  // the plan arrays before it).
+  if (!plan->d.fused_scan && moe::ensure_scanned(plan, s) != MOE_OK) return MOE_ERR_HIP;
   return MOE_OK;
 }
 
@@ -283,6 +300,7 @@ moe_status moe_pipeline(moe_plan* plan, const int32_t* topk_idx, void* workspace
                            plan->work, s) != hipSuccess)
     return MOE_ERR_HIP;
   plan->routed = true;
+  plan->scanned = true;
   plan->assigned = true;
   return MOE_OK;
 }
@@ -301,6 +319,7 @@ moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint1
     plan->assigned = true;
     return MOE_OK;
   }
+  if (moe::ensure_scanned(plan, s) != MOE_OK) return MOE_ERR_HIP;
   if (moe::launch_stage_a(plan->d, plan->idx, x, staging, plan->work, s) != hipSuccess)
     return MOE_ERR_HIP;
   plan->assigned = true;
@@ -356,6 +375,7 @@ moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, f
                         !moe::aligned(staging_scale, 4)))
     return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (moe::ensure_scanned(plan, s) != MOE_OK) return MOE_ERR_HIP;
   const hipError_t e =
       plan->d.dedup ? moe::launch_stage_fp8(plan->d, plan->idx, x, staging8, staging_scale, recv8,
                                             recv_scale, plan->work, s)
@@ -415,6 +435,7 @@ moe_status moe_plan_read(moe_plan* plan, int32_t item, void* host_dst, size_t by
   const size_t need = (size_t)n * sizeof(int32_t);
   if (bytes < need) return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (moe::ensure_scanned(plan, s) != MOE_OK) return MOE_ERR_HIP;
   const bool per_slot = item == MOE_ITEM_SLOT_OF || item == MOE_ITEM_ROW_SRC ||
                         item == MOE_ITEM_STAGE_OF || item == MOE_ITEM_STAGE_SRC || traffic;
   if (per_slot) {

@@ -16,6 +16,7 @@ constexpr int kPlanBlock = 256;    // threads per route-plan block = tokens per 
 constexpr int kPlanWaves = kPlanBlock / kWave;
 constexpr int kMaxPlanTiles = 64;  // route-plan tiles (blocks) at most
 constexpr int kScanLdsInts = 8192; // tile-count matrix the last block scans in LDS (32 KiB)
+constexpr int kFusedScanInts = 2048; // tile-count matrices up to this size are scanned in the gather
 
 // ctrl words at the start of the workspace.
 constexpr int kCtrlStaged = 1;     // D, staging rows used
@@ -45,6 +46,7 @@ struct Dims {
   int32_t band;           // tokens per band (a multiple of tile; >= T with one band)
   int32_t nbands;         // bands, each routed as a batch of its own
   int32_t tpb;            // plan tiles per band
+  int32_t fused_scan;     // the single-hop gather scans the tile counts itself (small plans)
   int32_t dedup;          // MOE_FLAG_NODE_DEDUP set
   int32_t load_aware;     // MOE_FLAG_LOAD_AWARE_FORWARDERS set
   int32_t fkeys;          // staging keys: forwarders (R), or (owner, node) pairs (R * N)
@@ -92,13 +94,15 @@ Layout make_layout(const Dims& d);
 Work bind_work(const Layout& l, void* base);
 
 // Route plan (route_plan.hip).
-// route_count then route_scan (one block per band).
+// route_count, and route_scan (one block per band).
 hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);
+hipError_t launch_route_scan(const Dims& d, const Work& w, hipStream_t s);
 hipError_t launch_route_assign(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);
 hipError_t launch_traffic(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);
 
 // Data movement (move.hip).  gather and stage_a also finish the plan
-// (slot_of, row_src, stage_of, stage_src) from the in-tile ranks.
+// (slot_of, row_src, stage_of, stage_src) from the in-tile ranks.  With
+// d.fused_scan the gather reads the raw tile counts and needs no route_scan.
 hipError_t launch_gather(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
                          const Work& w, hipStream_t s);
 hipError_t launch_stage_a(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* staging,

@@ -26,6 +26,7 @@
 //           from 0, then round-to-nearest-even bf16 (or fp32) out (INC-MoE
 //           abstract: combine back to each token's owner).
 #include "move_body.h"
+#include "plan_body.h"
 
 #ifndef MOE_HIER_PART_U
 #define MOE_HIER_PART_U 4  // wave-items per wave: hop 1 of the hierarchical combine (1: 1403 us, 2: 1340, 4: 1322 on dsv3)
@@ -33,6 +34,64 @@
 
 namespace moe {
 namespace {
+
+// Gather for plans whose tile-count matrix is small (nblk * E <=
+// kFusedScanInts): every block first issues its row loads, then scans the raw
+// tile counts in LDS (column totals, their exclusive scan over the experts,
+// and the prefix over earlier tiles for the experts its tokens use) while
+// those loads are in flight.  The plan's separate scan launch then leaves the
+// critical path (it still runs, lazily, for anything that reads the plan
+// arrays).  Same receive rows as gather_kernel.
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void gather_scan_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                             const u32x4* __restrict__ x,
+                                                             u32x4* __restrict__ recv, Work w) {
+  __shared__ int s_mat[kFusedScanInts];   // tile counts [nblk][E]
+  __shared__ int s_off[MOE_MAX_EXPERTS];  // first receive row of each expert
+  __shared__ int s_wsum[kPlanWaves];
+  const int items = d.T * d.segs, lane = threadIdx.x % kWave, tid = threadIdx.x;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  const Item it = wave_item<1>(d, items, 0);
+  u32x4 v;
+  if (it.ok) v = load_x_chunk(&x[(int64_t)it.t * d.chunks + it.c]);
+
+  const int E = d.E, n = d.nblk * E;
+  for (int i = tid; i < n; i += kBlock) s_mat[i] = w.tile_counts[i];
+  __syncthreads();
+  for (int e = tid; e < E; e += kBlock) {
+    int sum = 0;
+    for (int b = 0; b < d.nblk; ++b) sum += s_mat[b * E + e];
+    s_off[e] = sum;
+  }
+  __syncthreads();
+  block_exclusive_scan(s_off, E, s_wsum);
+
+  // Lane j < k of each wave resolves slot j of the wave's token.
+  int mine = -1;
+  if (it.live && lane < d.k) {
+    const int64_t at = (int64_t)it.t * d.k + lane;
+    const int l = w.lr[at];
+    const int e = min(max(idx[at], 0), E - 1);
+    if (l >= 0) {
+      int base = s_off[e];
+      for (int b = 0; b < it.t / d.tile; ++b) base += s_mat[b * E + e];
+      mine = base + l;
+    }
+  }
+  int slot[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
+
+  if (it.live && it.c == lane && lane < d.k) {  // the first segment publishes the slots
+    w.slot_of[(int64_t)it.t * d.k + lane] = mine;
+    if ((uint32_t)mine < rows) w.row_src[mine] = it.t;
+  }
+  if (it.ok) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if ((uint32_t)slot[j] < rows) store_chunk(&recv[(int64_t)slot[j] * d.chunks + it.c], v);
+  }
+}
 
 template <int KMAX, int U>
 __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* __restrict__ idx,
@@ -617,9 +676,13 @@ template <int KMAX>
 struct GatherLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
                         const Work& w, hipStream_t s) {
-    hipLaunchKernelGGL((gather_kernel<KMAX, kGatherU>), dim3(blocks_for(d, kGatherU)),
-                       dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
-                       reinterpret_cast<u32x4*>(recv), w);
+    if (d.fused_scan)
+      hipLaunchKernelGGL((gather_scan_kernel<KMAX>), dim3(blocks_for(d, 1)), dim3(kBlock), 0, s, d,
+                         idx, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), w);
+    else
+      hipLaunchKernelGGL((gather_kernel<KMAX, kGatherU>), dim3(blocks_for(d, kGatherU)),
+                         dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
+                         reinterpret_cast<u32x4*>(recv), w);
     return hipGetLastError();
   }
 };

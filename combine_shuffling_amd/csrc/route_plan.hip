@@ -159,8 +159,10 @@ struct TrafficLaunch {
 }  // namespace
 
 hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
-  const hipError_t e = by_topk<CountLaunch>(d.k, d, idx, w, s);
-  if (e != hipSuccess) return e;
+  return by_topk<CountLaunch>(d.k, d, idx, w, s);
+}
+
+hipError_t launch_route_scan(const Dims& d, const Work& w, hipStream_t s) {
   hipLaunchKernelGGL(route_scan_kernel, dim3(d.nbands), dim3(kPlanBlock), 0, s, d, w);
   return hipGetLastError();
 }
