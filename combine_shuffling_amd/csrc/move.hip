@@ -58,13 +58,39 @@ __global__ __launch_bounds__(kBlock) void gather_scan_kernel(Dims d, const int32
   const int E = d.E, n = d.nblk * E;
   for (int i = tid; i < n; i += kBlock) s_mat[i] = w.tile_counts[i];
   __syncthreads();
-  for (int e = tid; e < E; e += kBlock) {
-    int sum = 0;
-    for (int b = 0; b < d.nblk; ++b) sum += s_mat[b * E + e];
-    s_off[e] = sum;
+  if (E <= kWave) {
+    // Up to 64 experts: kBlock / E threads per expert sum parts of its
+    // column, then one wave adds the parts and scans with lane shuffles.
+    const int parts = min(kBlock / E, d.nblk);
+    if (tid < parts * E) {
+      const int q = tid / E, e = tid - q * E;
+      int sum = 0;
+      for (int b = q * d.nblk / parts; b < (q + 1) * d.nblk / parts; ++b) sum += s_mat[b * E + e];
+      s_off[tid] = sum;
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      int tot = 0;
+      if (tid < E)
+        for (int q = 0; q < parts; ++q) tot += s_off[q * E + tid];
+      int incl = tot;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (tid >= o) incl += y;
+      }
+      if (tid < E) s_off[tid] = incl - tot;  // parts are all read: each lane read only its column
+    }
+    __syncthreads();
+  } else {
+    for (int e = tid; e < E; e += kBlock) {
+      int sum = 0;
+      for (int b = 0; b < d.nblk; ++b) sum += s_mat[b * E + e];
+      s_off[e] = sum;
+    }
+    __syncthreads();
+    block_exclusive_scan(s_off, E, s_wsum);
   }
-  __syncthreads();
-  block_exclusive_scan(s_off, E, s_wsum);
 
   // Lane j < k of each wave resolves slot j of the wave's token.
   int mine = -1;
