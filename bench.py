@@ -180,19 +180,21 @@ def summarize_trace(stats_csv, out, command):
     print(out)
 
 
-def recorded_traffic(workload, kernel):
-    """Traffic per launch of `kernel` from the committed summary, if still current."""
+def recorded_traffic(workload, kernels):
+    """(kernel, traffic per launch) of the first of `kernels` (names separated by
+    '|') in the committed summary, if the summary is still current."""
     path = os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
     if not os.path.exists(path):
-        return None
+        return None, None
     text = "".join(ln for ln in open(path) if not ln.startswith("#"))
     s = json.loads(text)
     if s.get("source_hash") != kernel_source_hash():
-        return None
-    for name, v in s["kernels"].items():
-        if name.startswith(kernel):
-            return v["traffic_bytes"]
-    return None
+        return None, None
+    for kernel in kernels.split("|"):
+        for name, v in s["kernels"].items():
+            if name.split("<")[0] == kernel:
+                return name, v["traffic_bytes"]
+    return None, None
 
 
 def algorithmic_bytes(wl, D, payload="bf16", hier=False):
@@ -400,11 +402,14 @@ def main():
         dom = ("combine_fp8_kernel" if fp8 else "combine_kernel", comb_b, comb_ms, comb_gbs)
     else:
         sfx = "_fp8" if fp8 else ""
-        dom = max([(f"gather{sfx}_kernel", disp_b, disp_ms, disp_gbs),
+        # small single-hop plans scan inside the gather (gather_scan_kernel)
+        gname = "gather_fp8_kernel" if fp8 else "gather_scan_kernel|gather_kernel"
+        dom = max([(gname, disp_b, disp_ms, disp_gbs),
                    (f"combine{sfx}_kernel", comb_b, comb_ms, comb_gbs)], key=lambda d: d[2])
 
     # which committed traffic summary covers this run
     variant = "_pipeline" if pipe else "_fp8" if fp8 else "_hier" if hier else ""
+    traffic_kernel, traffic = recorded_traffic(args.workload + variant, dom[0])
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -432,9 +437,9 @@ def main():
                                  "GB/s": round(disp_gbs, 1), "launches": 2 if wl.node_dedup else 1},
                     "combine": {"bytes": comb_b, "ms_per_launch": round(comb_ms, 5),
                                 "GB/s": round(comb_gbs, 1), "launches": 2 if hier else 1}}),
-        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[3], 1),
+        "roofline": {"bound": "hbm", "kernel": traffic_kernel or dom[0], "achieved": round(dom[3], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(args.workload + variant, dom[0]),
+                     "traffic": traffic,
                      "bytes_per_launch": dom[1], "ms_per_launch": round(float(dom[2]), 5)},
         "cpu_baseline": None,
     }
