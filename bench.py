@@ -5,11 +5,17 @@ scan, segment descriptors), moe_dispatch (single hop, or the two hops of node
 deduplication for the DeepSeek-V3-like workload) and moe_combine (bf16 out),
 with the identity expert between dispatch and combine.
 
-Inputs are resident in HBM before timing starts.  Consecutive steps cycle
-through several independent copies of every buffer (inputs, plan workspace,
-outputs), at least 2 GiB in all, so that a step never finds the previous
-step's data in the 256 MB last-level cache; within a step combine reads the
-rows dispatch has just written, as the path does.
+Inputs are resident in HBM before timing starts, and no step finds them in
+a cache.  Consecutive steps cycle through independent copies of every buffer
+(inputs, plan workspace, receive and staging rows, outputs).  The rows are
+streamed with non-temporal accesses, which leave the 256 MB last-level cache
+(MALL) to what is read with plain loads, the token rows x above all; so the
+copies of the inputs total at least four times the MALL (and the copies of
+everything at least 2 GiB), and each step reads its x from HBM.  With fewer
+copies the MALL keeps x between steps: on the non-divisible workload, x
+cycled over 2 copies (268 MB) gives a 164 us dispatch, over 4 copies 183 us,
+and one copy reused 151 us.  Within a step combine reads the rows dispatch
+has just written, as the path does.
 
 Prints one JSON line.
   value       algorithmic payload bytes per step / wall time per step, over K
@@ -51,6 +57,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20   # MI355X last-level cache (AMD Infinity Cache)
+MAX_SETS = 256
 METRIC = "dispatch+combine effective GB/s and % of HBM peak, 1 MI355X"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("combine_shuffling_amd/csrc/move.hip", "combine_shuffling_amd/csrc/move_body.h",
@@ -82,6 +90,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
+    ap.add_argument("--inflight", type=int, default=2,
+                    help="batches in flight: consecutive steps go round-robin to this many HIP "
+                         "streams, each stream running its steps in order (1: one stream, every "
+                         "step after the previous one)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) a few "
                          "times, to scale hardware byte counters against a known size")
@@ -302,7 +314,12 @@ def main():
     set_bytes = (x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4 + probe.workspace_bytes
                  + probe.recv_rows * H * (1 if fp8 else 2) + probe.staging_rows_max * H * 2
                  + T * H * 2)
-    n_sets = args.sets or max(2, math.ceil((2 << 30) / set_bytes))
+    in_bytes = x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4
+    inflight = 1 if pipe else max(1, args.inflight)
+    n_sets = args.sets or min(MAX_SETS, max(2, math.ceil((2 << 30) / set_bytes),
+                                            math.ceil(4 * MALL_BYTES / in_bytes)))
+    # a set always runs on the same stream, so its reuse is ordered after its last use
+    n_sets = -(-n_sets // inflight) * inflight
     sets = []
     for _ in range(n_sets):
         plan = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la,
@@ -324,30 +341,44 @@ def main():
                                           dtype=torch.float32, device=dev)
         sets.append(s)
 
-    def do_dispatch(s):
+    # Stream 0 is torch's current stream; the others are plain streams of the
+    # default priority.
+    streams = [torch.cuda.current_stream(dev)] + [torch.cuda.Stream(dev) for _ in range(inflight - 1)]
+
+    def do_dispatch(s, st=None):
         if fp8:
-            s["plan"].dispatch_fp8(s["x"], s["recv"], s["scale"], s["staging"], s.get("sscale"))
+            s["plan"].dispatch_fp8(s["x"], s["recv"], s["scale"], s["staging"], s.get("sscale"),
+                                   stream=st)
         else:
-            s["plan"].dispatch(s["x"], s["recv"], s["staging"])
+            s["plan"].dispatch(s["x"], s["recv"], s["staging"], stream=st)
 
-    def do_combine(s):
+    def do_combine(s, st=None):
         if hier:
-            s["plan"].combine_hier(s["recv"], s["w"], s["part"], s["out"])
+            s["plan"].combine_hier(s["recv"], s["w"], s["part"], s["out"], stream=st)
         elif fp8:
-            s["plan"].combine_fp8(s["recv"], s["scale"], s["w"], s["out"])
+            s["plan"].combine_fp8(s["recv"], s["scale"], s["w"], s["out"], stream=st)
         else:
-            s["plan"].combine(s["recv"], s["w"], s["out"])
+            s["plan"].combine(s["recv"], s["w"], s["out"], stream=st)
 
-    def step(s):
+    def step(s, st=None):
         if pipe:
-            s["plan"].pipeline(s["idx"], s["x"], s["w"], s["recv"], s["out"])
+            s["plan"].pipeline(s["idx"], s["x"], s["w"], s["recv"], s["out"], stream=st)
             return
-        s["plan"].route(s["idx"])
-        do_dispatch(s)
-        do_combine(s)
+        s["plan"].route(s["idx"], stream=st)
+        do_dispatch(s, st)
+        do_combine(s, st)
+
+    def timed_steps(n_streams):
+        """Wall time per step of K steps; step i on stream i % n_streams."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(sets[i % n_sets], streams[i % n_streams])
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
 
     for i in range(args.warmup):
-        step(sets[i % n_sets])
+        step(sets[i % n_sets], streams[i % inflight])
     torch.cuda.synchronize()
     D = int(sets[0]["plan"].read("num_staged")[0]) if wl.node_dedup else 0
     fwd_rows = None
@@ -358,15 +389,12 @@ def main():
                     "max_over_mean": round(float(per.max() / max(per.mean(), 1e-9)), 4)}
     disp_b, comb_b = algorithmic_bytes(wl, D, args.payload, hier)
 
-    # Timed region: K steps, nothing else on the stream.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % n_sets])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    # Timed region: K steps and nothing else, with `inflight` batches in
+    # flight; then the same K steps one after another on one stream.
+    ms_per_step = timed_steps(inflight)
     value = (disp_b + comb_b) / (ms_per_step * 1e-3) / 1e9
+    serial_ms = timed_steps(1) if inflight > 1 else ms_per_step
+    serial_value = (disp_b + comb_b) / (serial_ms * 1e-3) / 1e9
 
     # Kernel pass: each phase as a burst of K back-to-back launches on the
     # launch stream between one pair of events (per-launch event records
@@ -428,7 +456,10 @@ def main():
                    "staging_rows": D, "seed": wl.seed, "buffer_sets": n_sets,
                    "payload": args.payload, "forwarder_rows": fwd_rows,
                    "combine": "hierarchical" if hier else "direct",
-                   "path": f"pipeline, bands of {band} tokens" if pipe else "separate launches"},
+                   "path": f"pipeline, bands of {band} tokens" if pipe else "separate launches",
+                   "batches_in_flight": inflight},
+        "serial": {"ms_per_step": round(serial_ms, 5), "value": round(serial_value, 2),
+                   "pct_of_hbm_peak": round(100.0 * serial_value / HBM_PEAK_GBS, 2)},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "bytes_per_step": disp_b + comb_b,
         "phases": ({"pipeline": {"bytes": disp_b + comb_b, "ms_per_launch": round(pipe_ms, 5),

@@ -224,7 +224,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
     d.nbands = 1;
   }
   // Small single-hop plans: the gather scans the tile counts itself.
-  d.fused_scan = (!dedup && d.nbands == 1 && (int64_t)d.nblk * d.E <= moe::kFusedScanInts) ? 1 : 0;
+  d.fused_scan = (MOE_FUSED_SCAN && !dedup && d.nbands == 1 &&
+                  (int64_t)d.nblk * d.E <= moe::kFusedScanInts) ? 1 : 0;
   d.chunks = (int32_t)chunks;
   d.segs = (int32_t)((chunks + moe::kWave - 1) / moe::kWave);
   d.smax = (int32_t)staging_max;

@@ -20,6 +20,9 @@ constexpr int kScanLdsInts = 8192; // tile-count matrix the last block scans in 
 // olmoe 16 x 64 gains 2 us per step; qwen3's 32 x 128 loses 6 us, as every
 // gather block then redoes a 4096-entry scan).
 constexpr int kFusedScanInts = 2048;
+#ifndef MOE_FUSED_SCAN
+#define MOE_FUSED_SCAN 1  // 0: always launch the scan in the route plan
+#endif
 
 // ctrl words at the start of the workspace.
 constexpr int kCtrlStaged = 1;     // D, staging rows used
