@@ -140,7 +140,9 @@ __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* 
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) slot[u][j] = p[u][j] = -1;
     }
-    if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
+    // non-temporal here (measured: DeepSeek-V3-like dispatch 826 -> 794 us
+    // with x read from HBM); the single-hop gather keeps plain loads
+    if (it[u].ok) v[u] = load_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
