@@ -76,7 +76,7 @@ def parse():
                     help="tiny | olmoe | qwen3 | dsv3 | nondiv (default: olmoe, the OLMoE-like prefill)")
     ap.add_argument("--payload", choices=("bf16", "fp8"), default="bf16",
                     help="row payload: bf16, or fp8 (OCP E4M3 codes + one float32 scale per "
-                         "128-element block; single-hop workloads only)")
+                         "128-element block; with node dedup, the staging rows are fp8 too)")
     ap.add_argument("--load-aware-forwarders", action="store_true",
                     help="node-deduplicated workloads: choose forwarders by load")
     ap.add_argument("--hier-combine", action="store_true",
