@@ -58,6 +58,7 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
   __shared__ int s_wsum[GW];
   const int items = d.T * d.segs, lane = threadIdx.x % kWave, tid = threadIdx.x;
   const uint32_t rows = (uint32_t)(d.T * d.k);
+  const bool keep = keep_rows(rows, 2 * d.H);
   // wave-item g = block * GW + wave (one per wave)
   Item it;
   {
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
   if (it.ok) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if ((uint32_t)slot[j] < rows) store_chunk(&recv[(int64_t)slot[j] * d.chunks + it.c], v);
+      if ((uint32_t)slot[j] < rows) store_row(&recv[(int64_t)slot[j] * d.chunks + it.c], v, keep);
   }
 }
 
@@ -142,6 +143,7 @@ __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* 
                                                          u32x4* __restrict__ staging, Work w) {
   const int items = d.T * d.segs, lane = threadIdx.x % kWave;
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
+  const bool keep = keep_rows(srows, 2 * d.H);
   Item it[U];
   int slot[U][KMAX], p[U][KMAX];
   uint32_t lead[U];
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* 
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
         if (((lead[u] >> j) & 1u) && (uint32_t)p[u][j] < srows)
-          store_chunk(&staging[(int64_t)p[u][j] * d.chunks + it[u].c], v[u]);
+          store_row(&staging[(int64_t)p[u][j] * d.chunks + it[u].c], v[u], keep);
     }
   }
 }
@@ -189,6 +191,7 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
                                                          u32x4* __restrict__ recv, Work w) {
   const int items = d.T * d.segs;
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
+  const bool keep = keep_rows(rows, 2 * d.H);
   Item it[U];
   int slot[U][KMAX], p[U][KMAX];
   u32x4 v[U][KMAX];
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
       for (int jj = j; jj < KMAX; ++jj) {
         const bool same = jj == j || p[u][jj] == -2 - p[u][j];
         if (same && (uint32_t)slot[u][jj] < rows)
-          store_chunk(&recv[(int64_t)slot[u][jj] * d.chunks + it[u].c], v[u][j]);
+          store_row(&recv[(int64_t)slot[u][jj] * d.chunks + it[u].c], v[u][j], keep);
       }
     }
   }
@@ -419,14 +422,14 @@ __device__ __forceinline__ Item8 wave_item8(const Dims& d, int segs8, int items,
 // 16 codes of a lane at byte offset (row * H + c0 * 8): one 16-byte store when
 // rows are 16-byte multiples (H % 16 == 0), else two 8-byte stores.
 __device__ __forceinline__ void store_codes(uint8_t* base, int64_t row, const Dims& d,
-                                            const Item8& it, u32x2 a, u32x2 b) {
+                                            const Item8& it, u32x2 a, u32x2 b, bool keep) {
   uint8_t* p = base + row * d.H + (int64_t)it.c0 * 8;
   if ((d.H & 15) == 0) {
     const u32x4 v = {a[0], a[1], b[0], b[1]};
-    store_chunk(reinterpret_cast<u32x4*>(p), v);
+    store_row(reinterpret_cast<u32x4*>(p), v, keep);
   } else {
-    if (it.ok0) store_chunk(reinterpret_cast<u32x2*>(p), a);
-    if (it.ok1) store_chunk(reinterpret_cast<u32x2*>(p + 8), b);
+    if (it.ok0) store_row(reinterpret_cast<u32x2*>(p), a, keep);
+    if (it.ok1) store_row(reinterpret_cast<u32x2*>(p + 8), b, keep);
   }
 }
 
@@ -514,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if ((uint32_t)slot[j] < rows) {
-        store_codes(recv8, slot[j], d, it, ca, cb);
+        store_codes(recv8, slot[j], d, it, ca, cb, keep_rows((int64_t)d.T * d.k, d.H));
         if (scale_lane) rscale[(int64_t)slot[j] * nb + blk] = scale;
       }
     }
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(kBlock) void stage_a_fp8_kernel(Dims d, const int32
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (((lead >> j) & 1u) && (uint32_t)p[j] < srows) {
-        store_codes(stage8, p[j], d, it, q.a, q.b);
+        store_codes(stage8, p[j], d, it, q.a, q.b, keep_rows(d.smax, d.H));
         if (scale_lane) sscale[(int64_t)p[j] * nb + blk] = q.scale;
       }
     }
@@ -619,7 +622,7 @@ __global__ __launch_bounds__(kBlock) void stage_b_fp8_kernel(Dims d, const uint8
     for (int jj = j; jj < KMAX; ++jj) {
       const bool same = jj == j || p[jj] == -2 - p[j];
       if (same && (uint32_t)slot[jj] < rows) {
-        store_codes(recv8, slot[jj], d, it, a[j], b[j]);
+        store_codes(recv8, slot[jj], d, it, a[j], b[j], keep_rows((int64_t)d.T * d.k, d.H));
         if (scale_lane) rscale[(int64_t)slot[jj] * nb + blk] = sc[j];
       }
     }
