@@ -20,12 +20,19 @@ has just written, as the path does.
 Prints one JSON line.
   value       algorithmic payload bytes per step / wall time per step, over K
               steps bracketed by synchronize on both sides, no events inside.
+  phases      route plan, dispatch and combine timed inside K more steps
+              run one after another on one stream, with HIP events on that
+              stream between the phases.  Inside a step, the non-temporal
+              writes a kernel leaves behind drain while the next kernel runs,
+              so each phase is timed in the order the step runs it (timed
+              alone, back to back, the same kernels measured the other way
+              round: qwen3 gather 117 us alone vs 93 us in a step, combine
+              104 vs 116 us).  An event exposes one kernel-launch latency
+              (about 2.5 us) that back-to-back kernels hide: the phase times
+              have it subtracted, estimated as (sum of the phase intervals -
+              the serial step time) / 3.  The value pass has no events.
   roofline    the dominant kernel: its algorithmic bytes per launch / its mean
-              duration, from HIP events on the launch stream bracketing a burst
-              of K back-to-back launches of it over the same buffer sets (an
-              event record adds a gap of about 2 us between kernels, so events
-              bracket bursts rather than single launches, and the value pass
-              has none).
+              duration from the phase pass.
               traffic = HBM bytes per launch from the rocprofv3 FETCH_SIZE /
               WRITE_SIZE summary under profiles/, scaled by the copy
               calibration; null if the kernel sources changed since.
@@ -396,28 +403,47 @@ def main():
     serial_ms = timed_steps(1) if inflight > 1 else ms_per_step
     serial_value = (disp_b + comb_b) / (serial_ms * 1e-3) / 1e9
 
-    # Kernel pass: each phase as a burst of K back-to-back launches on the
-    # launch stream between one pair of events (per-launch event records
-    # would add their own gaps), cycling the same buffer sets.
-    def burst(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Phase pass: K more steps one after another on stream 0, with events
+    # between the phases (route plan | dispatch | combine).
+    def phase_pass():
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
         torch.cuda.synchronize()
-        e0.record()
         for i in range(args.steps):
-            fn(sets[i % n_sets])
-        e1.record()
+            s, ev = sets[i % n_sets], evs[i]
+            ev[0].record()
+            if pipe:
+                step(s)
+                ev[1].record()
+                ev[2].record()
+            else:
+                s["plan"].route(s["idx"])
+                ev[1].record()
+                do_dispatch(s)
+                ev[2].record()
+                do_combine(s)
+            ev[3].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        t = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                      for e in evs])
+        return t.mean(axis=0)
 
+    route_ms, disp_ms, comb_ms = (float(v) for v in phase_pass())
+    # An event makes the GPU finish the kernel before it and only then launch
+    # the next one, so each interval also holds one kernel-launch latency
+    # that back-to-back kernels hide.  The same steps without events (the
+    # serial timing above) give it: (sum of intervals - step) / intervals.
+    intervals = 1 if pipe else 3
+    event_gap_ms = max(0.0, ((route_ms + disp_ms + comb_ms) if not pipe else route_ms) - serial_ms)
+    event_gap_ms /= intervals
+    route_ms -= event_gap_ms
+    disp_ms -= event_gap_ms
+    comb_ms -= event_gap_ms
     if pipe:
-        # one launch per step does everything; the bursts of the separate
-        # kernels do not exist here
-        pipe_ms = burst(step)
+        # one launch per step does everything
+        pipe_ms = route_ms
         disp_ms = comb_ms = pipe_ms
         disp_gbs = comb_gbs = (disp_b + comb_b) / (pipe_ms * 1e-3) / 1e9
     else:
-        disp_ms = burst(do_dispatch)
-        comb_ms = burst(do_combine)
         disp_gbs = disp_b / (disp_ms * 1e-3) / 1e9
         comb_gbs = comb_b / (comb_ms * 1e-3) / 1e9
     if pipe:
@@ -464,14 +490,16 @@ def main():
         "bytes_per_step": disp_b + comb_b,
         "phases": ({"pipeline": {"bytes": disp_b + comb_b, "ms_per_launch": round(pipe_ms, 5),
                                  "GB/s": round(disp_gbs, 1), "launches": 1}} if pipe else
-                   {"dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),
+                   {"route": {"ms_per_step": round(route_ms, 5)},
+                    "dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),
                                  "GB/s": round(disp_gbs, 1), "launches": 2 if wl.node_dedup else 1},
                     "combine": {"bytes": comb_b, "ms_per_launch": round(comb_ms, 5),
                                 "GB/s": round(comb_gbs, 1), "launches": 2 if hier else 1}}),
         "roofline": {"bound": "hbm", "kernel": traffic_kernel or dom[0], "achieved": round(dom[3], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "bytes_per_launch": dom[1], "ms_per_launch": round(float(dom[2]), 5)},
+                     "bytes_per_launch": dom[1], "ms_per_launch": round(float(dom[2]), 5),
+                     "event_gap_ms": round(event_gap_ms, 5)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
