@@ -111,10 +111,8 @@ hipError_t launch_traffic(const Dims& d, const int32_t* idx, const Work& w, hipS
 // d.fused_scan the gather reads the raw tile counts and needs no route_scan.
 hipError_t launch_gather(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
                          const Work& w, hipStream_t s);
-hipError_t launch_stage_a(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* staging,
-                          const Work& w, hipStream_t s);
-hipError_t launch_stage_b(const Dims& d, const uint16_t* staging, uint16_t* recv, const Work& w,
-                          hipStream_t s);
+hipError_t launch_dedup_dispatch(const Dims& d, const int32_t* idx, const uint16_t* x,
+                                 uint16_t* staging, uint16_t* recv, const Work& w, hipStream_t s);
 hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* wts, void* out,
                           bool out_f32, const Work& w, hipStream_t s);
 // Two-hop combine of a node-deduplicated plan: fp32 partial per staging row,

@@ -32,6 +32,15 @@
 #define MOE_HIER_PART_U 4  // wave-items per wave: hop 1 of the hierarchical combine (1: 1403 us, 2: 1340, 4: 1322 on dsv3)
 #endif
 
+#ifndef MOE_STAGE_CHUNK
+#define MOE_STAGE_CHUNK 0
+#endif
+#ifndef MOE_STAGE_CHUNK_MIB
+// DeepSeek-V3-like dispatch, us with two batches in flight / one stream:
+// no chunks 1217 / 1217, 512 MiB 1228 / 1187, 256 MiB 1178 / 1180,
+// 224 MiB (8 chunks) 1142 / 1181, 128 MiB 1107 / 1265
+#define MOE_STAGE_CHUNK_MIB 224
+#endif
 #ifndef MOE_GSCAN_WAVES
 #define MOE_GSCAN_WAVES 8  // olmoe dispatch: 4 -> 32.2 us, 8 -> 30.9, 16 -> 31.4
 #endif
@@ -40,6 +49,8 @@ namespace moe {
 namespace {
 
 constexpr int kGatherScanWaves = MOE_GSCAN_WAVES;  // waves per gather_scan block when E <= 64
+constexpr int kStageChunkTokens = MOE_STAGE_CHUNK;  // tokens per hop-1/hop-2 chunk (0: by bytes)
+constexpr int64_t kChunkBytes = (int64_t)MOE_STAGE_CHUNK_MIB << 20;  // staging bytes per chunk, at most
 
 // Gather for plans whose tile-count matrix is small (nblk * E <=
 // kFusedScanInts): every block first issues its row loads, then scans the raw
@@ -138,19 +149,19 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
 }
 
 template <int KMAX, int U>
-__global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* __restrict__ idx,
-                                                         const u32x4* __restrict__ x,
-                                                         u32x4* __restrict__ staging, Work w) {
-  const int items = d.T * d.segs, lane = threadIdx.x % kWave;
+__device__ __forceinline__ void stage_a_body(const Dims& d, const int32_t* __restrict__ idx,
+                                             const u32x4* __restrict__ x,
+                                             u32x4* __restrict__ staging, const Work& w, int blk,
+                                             int item0, int item_end, int keep) {
+  const int lane = threadIdx.x % kWave;
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
-  const bool keep = keep_rows(srows, 2 * d.H);
   Item it[U];
   int slot[U][KMAX], p[U][KMAX];
   uint32_t lead[U];
   u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, items, u);
+    it[u] = wave_item<U>(d, blk, item0, item_end, u);
     lead[u] = 0;
     if (it[u].live) {
       token_slots_serial<KMAX>(d, w, idx, it[u].t, slot[u]);
@@ -187,9 +198,9 @@ __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* 
 // destination node) is read once and written to the token's slots on that
 // node.
 template <int KMAX, int U>
-__global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __restrict__ staging,
-                                                         u32x4* __restrict__ recv, Work w) {
-  const int items = d.T * d.segs;
+__device__ __forceinline__ void stage_b_body(const Dims& d, const u32x4* __restrict__ staging,
+                                             u32x4* __restrict__ recv, const Work& w, int blk,
+                                             int item0, int item_end) {
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   const bool keep = keep_rows(rows, 2 * d.H);
   Item it[U];
@@ -197,7 +208,7 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
   u32x4 v[U][KMAX];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, items, u);
+    it[u] = wave_item<U>(d, blk, item0, item_end, u);
     const int64_t at = (int64_t)it[u].t * d.k;
     int sj[KMAX], pj[KMAX];
 #pragma unroll
@@ -235,6 +246,21 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
       }
     }
   }
+}
+
+template <int KMAX, int U>
+__global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                         const u32x4* __restrict__ x,
+                                                         u32x4* __restrict__ staging, Work w,
+                                                         int item0, int item_end, int keep) {
+  stage_a_body<KMAX, U>(d, idx, x, staging, w, blockIdx.x, item0, item_end, keep);
+}
+
+template <int KMAX, int U>
+__global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __restrict__ staging,
+                                                         u32x4* __restrict__ recv, Work w,
+                                                         int item0, int item_end) {
+  stage_b_body<KMAX, U>(d, staging, recv, w, blockIdx.x, item0, item_end);
 }
 
 // ---- hierarchical combine over the deduplication's staging rows ------------
@@ -406,11 +432,11 @@ struct Item8 {
 };
 
 template <int U>
-__device__ __forceinline__ Item8 wave_item8(const Dims& d, int segs8, int items, int u) {
+__device__ __forceinline__ Item8 wave_item8(const Dims& d, int segs8, int base, int limit, int u) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int g = __builtin_amdgcn_readfirstlane((blockIdx.x * U + u) * kWaves + wave);
+  const int g = __builtin_amdgcn_readfirstlane(base + (blockIdx.x * U + u) * kWaves + wave);
   Item8 it;
-  it.live = g < items;
+  it.live = g < limit;
   it.t = it.live ? g / segs8 : 0;
   const int seg = g - it.t * segs8;
   it.c0 = seg * kFp8ItemChunks + 2 * lane;
@@ -494,7 +520,7 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
   const int items = d.T * segs8;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  const Item8 it = wave_item8<1>(d, segs8, items, 0);
+  const Item8 it = wave_item8<1>(d, segs8, 0, items, 0);
   int slot[KMAX];
   if (it.live) {
     token_slots<KMAX>(d, w, idx, it.t, slot);
@@ -532,13 +558,13 @@ template <int KMAX>
 __global__ __launch_bounds__(kBlock) void stage_a_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
                                                              const u32x4* __restrict__ x,
                                                              uint8_t* __restrict__ stage8,
-                                                             float* __restrict__ sscale, Work w) {
+                                                             float* __restrict__ sscale, Work w,
+                                                             int item0, int item_end, int keep) {
   const int lane = threadIdx.x % kWave;
   const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
-  const int items = d.T * segs8;
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  const Item8 it = wave_item8<1>(d, segs8, items, 0);
+  const Item8 it = wave_item8<1>(d, segs8, item0, item_end, 0);
   int slot[KMAX], p[KMAX];
   uint32_t lead = 0;
   if (it.live) {
@@ -564,7 +590,7 @@ __global__ __launch_bounds__(kBlock) void stage_a_fp8_kernel(Dims d, const int32
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (((lead >> j) & 1u) && (uint32_t)p[j] < srows) {
-        store_codes(stage8, p[j], d, it, q.a, q.b, keep_rows(d.smax, d.H));
+        store_codes(stage8, p[j], d, it, q.a, q.b, keep);
         if (scale_lane) sscale[(int64_t)p[j] * nb + blk] = q.scale;
       }
     }
@@ -577,13 +603,13 @@ template <int KMAX>
 __global__ __launch_bounds__(kBlock) void stage_b_fp8_kernel(Dims d, const uint8_t* __restrict__ stage8,
                                                              const float* __restrict__ sscale,
                                                              uint8_t* __restrict__ recv8,
-                                                             float* __restrict__ rscale, Work w) {
+                                                             float* __restrict__ rscale, Work w,
+                                                             int item0, int item_end) {
   const int lane = threadIdx.x % kWave;
   const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
-  const int items = d.T * segs8;
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  const Item8 it = wave_item8<1>(d, segs8, items, 0);
+  const Item8 it = wave_item8<1>(d, segs8, item0, item_end, 0);
   const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
   const int blk = it.c0 / kFp8BlockChunks;
   const int64_t at = (int64_t)it.t * d.k;
@@ -744,25 +770,44 @@ struct GatherLaunch {
   }
 };
 
-template <int KMAX>
-struct StageALaunch {
-  static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* staging,
-                        const Work& w, hipStream_t s) {
-    hipLaunchKernelGGL((stage_a_kernel<KMAX, kStageU>), dim3(blocks_for(d, kStageU)),
-                       dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
-                       reinterpret_cast<u32x4*>(staging), w);
-    return hipGetLastError();
-  }
-};
+// Tokens per chunk of the deduplicated dispatch: even chunks, each with at
+// most kChunkBytes of staging rows (row_bound bytes a token, at most).
+inline int stage_chunk_tokens(const Dims& d, int64_t row_bound) {
+  if (kStageChunkTokens > 0) return kStageChunkTokens;
+  const int64_t n = std::max<int64_t>(1, ((int64_t)d.T * row_bound + kChunkBytes - 1) / kChunkBytes);
+  return (int)(((int64_t)d.T + n - 1) / n);
+}
 
+// Deduplicated dispatch over chunks of consecutive tokens: hop 1, then hop
+// 2, of each chunk before the next chunk.  A chunk's staging rows (at most
+// tokens * min(k, N) rows) fit in the 256 MB MALL, so hop 2 reads rows
+// hop 1 has just written (DeepSeek-V3-like, 8 chunks: dispatch 799 -> 756
+// us on one stream; one launch holding both hops cost occupancy and was
+// slower).  The rows, and the plan arrays hop 1 finishes, of one chunk are
+// disjoint from every other chunk's.
 template <int KMAX>
-struct StageBLaunch {
-  static hipError_t run(const Dims& d, const uint16_t* staging, uint16_t* recv, const Work& w,
-                        hipStream_t s) {
-    hipLaunchKernelGGL((stage_b_kernel<KMAX, kStageU>), dim3(blocks_for(d, kStageU)),
-                       dim3(kBlock), 0, s, d, reinterpret_cast<const u32x4*>(staging),
-                       reinterpret_cast<u32x4*>(recv), w);
-    return hipGetLastError();
+struct DedupLaunch {
+  static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* staging,
+                        uint16_t* recv, const Work& w, hipStream_t s) {
+    const int64_t row_bound = (int64_t)min(d.k, d.N) * 2 * d.H;  // staging bytes per token, at most
+    const int chunk = stage_chunk_tokens(d, row_bound);
+    const int per_block = kWaves * kStageU;
+    const int keep = (int64_t)chunk * row_bound <= kKeepBytes;
+    for (int t0 = 0; t0 < d.T; t0 += chunk) {
+      const int item0 = t0 * d.segs, item_end = min(d.T, t0 + chunk) * d.segs;
+      const int blocks = (item_end - item0 + per_block - 1) / per_block;
+      hipLaunchKernelGGL((stage_a_kernel<KMAX, kStageU>), dim3(blocks), dim3(kBlock), 0, s, d,
+                         idx, reinterpret_cast<const u32x4*>(x),
+                         reinterpret_cast<u32x4*>(staging), w, item0, item_end, keep);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((stage_b_kernel<KMAX, kStageU>), dim3(blocks), dim3(kBlock), 0, s, d,
+                         reinterpret_cast<const u32x4*>(staging), reinterpret_cast<u32x4*>(recv), w,
+                         item0, item_end);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
 };
 
@@ -791,23 +836,31 @@ struct GatherFp8Launch {
   }
 };
 
+// The deduplicated fp8 dispatch in chunks of tokens, as DedupLaunch.
 template <int KMAX>
-struct StageAFp8Launch {
+struct DedupFp8Launch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* stage8,
-                        float* sscale, const Work& w, hipStream_t s) {
-    hipLaunchKernelGGL((stage_a_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s, d,
-                       idx, reinterpret_cast<const u32x4*>(x), stage8, sscale, w);
-    return hipGetLastError();
-  }
-};
-
-template <int KMAX>
-struct StageBFp8Launch {
-  static hipError_t run(const Dims& d, const uint8_t* stage8, const float* sscale, uint8_t* recv8,
-                        float* rscale, const Work& w, hipStream_t s) {
-    hipLaunchKernelGGL((stage_b_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s, d,
-                       stage8, sscale, recv8, rscale, w);
-    return hipGetLastError();
+                        float* sscale, uint8_t* recv8, float* rscale, const Work& w,
+                        hipStream_t s) {
+    const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
+    const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
+    const int64_t row_bound = (int64_t)min(d.k, d.N) * (d.H + 4 * nb);  // codes + scales
+    const int chunk = stage_chunk_tokens(d, row_bound);
+    const int keep = (int64_t)chunk * row_bound <= kKeepBytes;
+    for (int t0 = 0; t0 < d.T; t0 += chunk) {
+      const int item0 = t0 * segs8, item_end = min(d.T, t0 + chunk) * segs8;
+      const int blocks = (item_end - item0 + kWaves - 1) / kWaves;
+      hipLaunchKernelGGL((stage_a_fp8_kernel<KMAX>), dim3(blocks), dim3(kBlock), 0, s, d, idx,
+                         reinterpret_cast<const u32x4*>(x), stage8, sscale, w, item0, item_end,
+                         keep);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((stage_b_fp8_kernel<KMAX>), dim3(blocks), dim3(kBlock), 0, s, d, stage8,
+                         static_cast<const float*>(sscale), recv8, rscale, w, item0, item_end);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
 };
 
@@ -870,10 +923,7 @@ hipError_t launch_stage_fp8(const Dims& d, const int32_t* idx, const uint16_t* x
                             uint8_t* stage8, float* sscale, uint8_t* recv8, float* rscale,
                             const Work& w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
-  const hipError_t e = by_topk<StageAFp8Launch>(d.k, d, idx, x, stage8, sscale, w, s);
-  if (e != hipSuccess) return e;
-  return by_topk<StageBFp8Launch>(d.k, d, stage8, static_cast<const float*>(sscale), recv8, rscale,
-                                  w, s);
+  return by_topk<DedupFp8Launch>(d.k, d, idx, x, stage8, sscale, recv8, rscale, w, s);
 }
 
 hipError_t launch_combine_fp8(const Dims& d, const uint8_t* y8, const float* yscale,
@@ -889,16 +939,10 @@ hipError_t launch_gather(const Dims& d, const int32_t* idx, const uint16_t* x, u
   return by_topk<GatherLaunch>(d.k, d, idx, x, recv, w, s);
 }
 
-hipError_t launch_stage_a(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* staging,
-                          const Work& w, hipStream_t s) {
+hipError_t launch_dedup_dispatch(const Dims& d, const int32_t* idx, const uint16_t* x,
+                                 uint16_t* staging, uint16_t* recv, const Work& w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
-  return by_topk<StageALaunch>(d.k, d, idx, x, staging, w, s);
-}
-
-hipError_t launch_stage_b(const Dims& d, const uint16_t* staging, uint16_t* recv, const Work& w,
-                          hipStream_t s) {
-  if (d.T == 0) return hipSuccess;
-  return by_topk<StageBLaunch>(d.k, d, staging, recv, w, s);
+  return by_topk<DedupLaunch>(d.k, d, idx, x, staging, recv, w, s);
 }
 
 hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* wts, void* out,

@@ -167,6 +167,15 @@ def test_fp8_dedup_dsv3(dev):
     check_fp8_dedup(batch, dev, tokens=tok)
 
 
+def test_fp8_dedup_in_chunks(dev):
+    # 8999 tokens of 8 staging rows of 7168 codes + 56 scales at most: the
+    # fp8 dispatch runs hop 1 and hop 2 in 3 chunks, the last ragged.
+    batch = gen.make_batch(gen.custom(8999, 7168, 32, 8, 8, 1, seed=9))
+    T = batch.workload.num_tokens
+    tok = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(12).integers(0, T, 256)]))
+    check_fp8_dedup(batch, dev, tokens=tok)
+
+
 def test_fp8_combines_without_dispatch(dev):
     import combine_shuffling_amd as cs
 

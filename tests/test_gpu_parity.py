@@ -113,6 +113,21 @@ def test_workload_full_size(name, dev):
     full_check(batch, dev, combine_tokens=None if T <= 4096 else sample, traffic=True)
 
 
+@pytest.mark.parametrize("case", [
+    # T,    H,   E,   k,  R,  G  -- staging rows past one 224 MiB chunk
+    (2500, 7168, 64, 8, 16, 2),   # 2 chunks (the bound counts min(k, N) = 8 rows a token)
+    (4999, 7168, 32, 8, 8, 1),    # 3 chunks of 1667 tokens, the last ragged; 8 nodes
+])
+def test_dedup_dispatch_in_chunks(case, dev):
+    # Hop 1 and hop 2 run chunk by chunk over consecutive tokens; the rows
+    # must be those of the whole-batch oracle.
+    T, H, E, k, R, G = case
+    batch = gen.make_batch(gen.custom(T, H, E, k, R, G, seed=T))
+    rng = np.random.default_rng(7)
+    sample = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 512)]))
+    full_check(batch, dev, combine_tokens=sample)
+
+
 def test_dedup_workload_single_hop_too(dev):
     # The DeepSeek-V3-like routing through the single-hop path gives the same rows.
     batch = gen.make_batch(gen.get("dsv3"))
