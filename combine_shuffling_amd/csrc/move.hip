@@ -28,8 +28,10 @@
 #include "move_body.h"
 #include "plan_body.h"
 
-#ifndef MOE_HIER_PART_U
-#define MOE_HIER_PART_U 4  // wave-items per wave: hop 1 of the hierarchical combine (1: 1403 us, 2: 1340, 4: 1322 on dsv3)
+#ifndef MOE_HIER_CHUNK_MIB
+// DeepSeek-V3-like hierarchical combine, us on one stream: whole batch 1235,
+// 448 MiB (8 chunks) 1149, 224 MiB 1189, 112 MiB 1356
+#define MOE_HIER_CHUNK_MIB 448
 #endif
 
 #ifndef MOE_STAGE_CHUNK
@@ -51,6 +53,7 @@ namespace {
 constexpr int kGatherScanWaves = MOE_GSCAN_WAVES;  // waves per gather_scan block when E <= 64
 constexpr int kStageChunkTokens = MOE_STAGE_CHUNK;  // tokens per hop-1/hop-2 chunk (0: by bytes)
 constexpr int64_t kChunkBytes = (int64_t)MOE_STAGE_CHUNK_MIB << 20;  // staging bytes per chunk, at most
+constexpr int64_t kHierChunkBytes = (int64_t)MOE_HIER_CHUNK_MIB << 20;  // partial bytes per chunk, at most
 
 // Gather for plans whose tile-count matrix is small (nblk * E <=
 // kFusedScanInts): every block first issues its row loads, then scans the raw
@@ -266,52 +269,62 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
 // ---- hierarchical combine over the deduplication's staging rows ------------
 // Hop 1 (at the forwarder): one fp32 partial per staging row p = (token t,
 // node n), the fused multiply-add chain over t's slots on n in ascending j.
-template <int KMAX, int U>
+// Token-major: a wave-item is a segment of token t, whose k rows are loaded
+// once; each of t's staging rows gets its partial (a row all of whose slots
+// were dropped gets zeros).
+template <int KMAX>
 __global__ __launch_bounds__(kBlock) void combine_part_kernel(Dims d, const u32x4* __restrict__ y,
                                                               const float* __restrict__ wts,
-                                                              f32x4* __restrict__ part, Work w) {
-  const int staged = min(w.ctrl[kCtrlStaged], d.smax);
-  const int items = staged * d.segs;
-  const uint32_t rows = (uint32_t)(d.T * d.k);
-  Item it[U];  // it[u].t is the staging row here
-  int slot[U][KMAX];
-  float wj[U][KMAX];
-  u32x4 v[U][KMAX];
+                                                              f32x4* __restrict__ part, Work w,
+                                                              int item0, int item_end, int keep) {
+  const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
+  const Item it = wave_item<1>(d, blockIdx.x, item0, item_end, 0);
+  const int64_t at = (int64_t)it.t * d.k;
+  int slot[KMAX], p[KMAX];
+  float wj[KMAX];
+  u32x4 v[KMAX];
+  {
+    int sj[KMAX], pj[KMAX];
+    float wt[KMAX];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, items, u);
-    const int p = it[u].t;
-    const int t = it[u].live ? w.stage_src[p] : -1;
-    const bool tok = (uint32_t)t < (uint32_t)d.T;
-    const int64_t at = (int64_t)(tok ? t : 0) * d.k;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      const bool mine = tok && j < d.k && w.stage_of[at + j] == p;
-      slot[u][j] = mine ? w.slot_of[at + j] : -1;
-      if ((uint32_t)slot[u][j] >= rows) slot[u][j] = -1;
-      wj[u][j] = mine ? wts[at + j] : 0.0f;
+    for (int j = 0; j < KMAX; ++j) {  // no branch between the loads: they issue together
+      const int64_t a = slot_index(at, j, d.k);
+      sj[j] = w.slot_of[a];
+      pj[j] = w.stage_of[a];
+      wt[j] = wts[a];
     }
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (slot[u][j] >= 0 && it[u].ok) v[u][j] = load_chunk(&y[(int64_t)slot[u][j] * d.chunks + it[u].c]);
+    for (int j = 0; j < KMAX; ++j) {
+      const bool has = it.live && j < d.k;
+      slot[j] = has && (uint32_t)sj[j] < rows ? sj[j] : -1;
+      p[j] = has && (uint32_t)pj[j] < srows ? pj[j] : -1;
+      wj[j] = wt[j];
+    }
   }
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (!it[u].ok) continue;
+  for (int j = 0; j < KMAX; ++j)
+    if (slot[j] >= 0 && it.ok) v[j] = load_chunk(&y[(int64_t)slot[j] * d.chunks + it.c]);
+  if (!it.ok) return;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    bool first = p[j] >= 0;
+#pragma unroll
+    for (int jj = 0; jj < j; ++jj) first = first && p[jj] != p[j];
+    if (!first) continue;  // p[j] is done by its first slot
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (slot[u][j] < 0) continue;
+    for (int jj = j; jj < KMAX; ++jj) {
+      if (p[jj] != p[j] || slot[jj] < 0) continue;
       float f[8];
-      unpack_bf16(v[u][j], f);
+      unpack_bf16(v[jj], f);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj[u][j], f[q], acc[q]);
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj[jj], f[q], acc[q]);
     }
-    f32x4* o = part + ((int64_t)it[u].t * d.chunks + it[u].c) * 2;
-    store_chunk(o, f32x4{acc[0], acc[1], acc[2], acc[3]});
-    store_chunk(o + 1, f32x4{acc[4], acc[5], acc[6], acc[7]});
+    f32x4* o = part + ((int64_t)p[j] * d.chunks + it.c) * 2;
+    store_row(o, f32x4{acc[0], acc[1], acc[2], acc[3]}, keep);
+    store_row(o + 1, f32x4{acc[4], acc[5], acc[6], acc[7]}, keep);
   }
 }
 
@@ -320,10 +333,10 @@ __global__ __launch_bounds__(kBlock) void combine_part_kernel(Dims d, const u32x
 template <int KMAX, bool F32OUT>
 __global__ __launch_bounds__(kBlock) void combine_nodes_kernel(Dims d, const int32_t* __restrict__ idx,
                                                                const f32x4* __restrict__ part,
-                                                               Work w, void* __restrict__ out) {
-  const int items = d.T * d.segs;
+                                                               Work w, void* __restrict__ out,
+                                                               int item0, int item_end) {
   const uint32_t srows = (uint32_t)d.smax;
-  const Item it = wave_item<1>(d, items, 0);
+  const Item it = wave_item<1>(d, blockIdx.x, item0, item_end, 0);
   const int64_t at = (int64_t)it.t * d.k;
   int p[KMAX], node[KMAX];
 #pragma unroll
@@ -880,27 +893,36 @@ struct CombineFp8Launch {
   }
 };
 
+// The hierarchical combine in chunks of consecutive tokens: hop 1, then hop
+// 2, of each chunk before the next, so hop 2 reads partials hop 1 has just
+// written (at most kHierChunkBytes of partial rows a chunk, counting
+// min(k, N) rows a token; the node-limited workload uses about half).
 template <int KMAX>
 struct CombineHierLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* y, const float* wts,
                         float* part, void* out, bool f32, const Work& w, hipStream_t s) {
-    constexpr int PU = MOE_HIER_PART_U;
-    const int64_t part_items = (int64_t)d.smax * d.segs;
-    const int part_blocks = (int)((part_items + kWaves * PU - 1) / (kWaves * PU));
-    if (part_blocks > 0)
-      hipLaunchKernelGGL((combine_part_kernel<KMAX, PU>), dim3(part_blocks), dim3(kBlock), 0, s, d,
-                         reinterpret_cast<const u32x4*>(y), wts, reinterpret_cast<f32x4*>(part),
-                         w);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const f32x4* pp = reinterpret_cast<const f32x4*>(part);
-    if (f32)
-      hipLaunchKernelGGL((combine_nodes_kernel<KMAX, true>), dim3(blocks_for(d, 1)), dim3(kBlock),
-                         0, s, d, idx, pp, w, out);
-    else
-      hipLaunchKernelGGL((combine_nodes_kernel<KMAX, false>), dim3(blocks_for(d, 1)), dim3(kBlock),
-                         0, s, d, idx, pp, w, out);
-    return hipGetLastError();
+    const int64_t row_bound = (int64_t)min(d.k, d.N) * 4 * d.H;  // partial bytes per token, at most
+    const int64_t n = std::max<int64_t>(1, ((int64_t)d.T * row_bound + kHierChunkBytes - 1) / kHierChunkBytes);
+    const int chunk = (int)(((int64_t)d.T + n - 1) / n);
+    const int keep = (int64_t)chunk * row_bound <= kKeepBytes;
+    f32x4* pp = reinterpret_cast<f32x4*>(part);
+    for (int t0 = 0; t0 < d.T; t0 += chunk) {
+      const int item0 = t0 * d.segs, item_end = min(d.T, t0 + chunk) * d.segs;
+      const int blocks = (item_end - item0 + kWaves - 1) / kWaves;
+      hipLaunchKernelGGL((combine_part_kernel<KMAX>), dim3(blocks), dim3(kBlock), 0, s, d,
+                         reinterpret_cast<const u32x4*>(y), wts, pp, w, item0, item_end, keep);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (f32)
+        hipLaunchKernelGGL((combine_nodes_kernel<KMAX, true>), dim3(blocks), dim3(kBlock), 0, s, d,
+                           idx, static_cast<const f32x4*>(pp), w, out, item0, item_end);
+      else
+        hipLaunchKernelGGL((combine_nodes_kernel<KMAX, false>), dim3(blocks), dim3(kBlock), 0, s,
+                           d, idx, static_cast<const f32x4*>(pp), w, out, item0, item_end);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
 };
 
