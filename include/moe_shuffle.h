@@ -176,7 +176,8 @@ moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspa
 /* Dispatch: recv[slot_of[t, j]] = x[t] for every valid slot.  x: device
  * [T, H] bf16; recv: device [T*k, H] bf16.  staging: device
  * [staging_rows_max, H] bf16 when the plan has MOE_FLAG_NODE_DEDUP, else
- * ignored (may be NULL).  Asynchronous.
+ * ignored (may be NULL); with it, the two hops run over chunks of
+ * consecutive tokens, both hops of a chunk before the next.  Asynchronous.
  * Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
 moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint16_t* staging,
                         void* stream);
@@ -197,9 +198,10 @@ moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, v
  * topk_w[t, j] * y[slot_of[t, j]] over t's slots on n in ascending j; hop 2,
  * at the owner: out[t] = sum of t's partials in ascending node order, then
  * bf16 (nearest even) or float32.  partials: device [staging_rows_max, H]
- * float32 scratch owned by the caller (first D rows written).  Two launches;
- * asynchronous.  Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT (not a dedup
- * plan, bad pointers), HIP. */
+ * float32 scratch owned by the caller (first D rows written).  Runs over
+ * chunks of consecutive tokens, both hops of a chunk before the next (two
+ * launches a chunk); asynchronous.  Errors: PLAN_NOT_ROUTED,
+ * INVALID_ARGUMENT (not a dedup plan, bad pointers), HIP. */
 moe_status moe_combine_hier(moe_plan* plan, const uint16_t* y, const float* topk_w,
                             float* partials, void* out, int32_t out_dtype, void* stream);
 
