@@ -55,36 +55,20 @@ constexpr int kStageChunkTokens = MOE_STAGE_CHUNK;  // tokens per hop-1/hop-2 ch
 constexpr int64_t kChunkBytes = (int64_t)MOE_STAGE_CHUNK_MIB << 20;  // staging bytes per chunk, at most
 constexpr int64_t kHierChunkBytes = (int64_t)MOE_HIER_CHUNK_MIB << 20;  // partial bytes per chunk, at most
 
-// Gather for plans whose tile-count matrix is small (nblk * E <=
-// kFusedScanInts): every block first issues its row loads, then scans the raw
-// tile counts in LDS (column totals, their exclusive scan over the experts,
-// and the prefix over earlier tiles for the experts its tokens use) while
-// those loads are in flight.  The plan's separate scan launch then leaves the
-// critical path (it still runs, lazily, for anything that reads the plan
-// arrays).  Same receive rows as gather_kernel.
-template <int KMAX, int GW>
-__global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const int32_t* __restrict__ idx,
-                                                                 const u32x4* __restrict__ x,
-                                                                 u32x4* __restrict__ recv, Work w) {
-  constexpr int kGBlock = GW * kWave;
-  __shared__ int s_mat[kFusedScanInts];   // tile counts [nblk][E]
-  __shared__ int s_off[MOE_MAX_EXPERTS];  // first receive row of each expert
-  __shared__ int s_wsum[GW];
-  const int items = d.T * d.segs, lane = threadIdx.x % kWave, tid = threadIdx.x;
-  const uint32_t rows = (uint32_t)(d.T * d.k);
-  const bool keep = keep_rows(rows, 2 * d.H);
-  // wave-item g = block * GW + wave (one per wave)
-  Item it;
-  {
-    const int g = __builtin_amdgcn_readfirstlane(blockIdx.x * GW + tid / kWave);
-    it.live = g < items;
-    it.t = it.live ? g / d.segs : 0;
-    it.c = (g - it.t * d.segs) * kWave + lane;
-    it.ok = it.live && it.c < d.chunks;
-  }
-  u32x4 v;
-  if (it.ok) v = load_x_chunk(&x[(int64_t)it.t * d.chunks + it.c]);
-
+// The scan folded into the gather of a small plan (nblk * E <=
+// kFusedScanInts; single band).  The block (GB threads, all of which call
+// this) loads the raw tile counts into LDS, sums each expert's column, scans
+// the totals over the experts (one wave with lane shuffles when E <= 64) and
+// returns, in lane j < k of each wave, the receive row of slot j of token t
+// (-1 for a dropped slot): the expert's first row, plus its rows in earlier
+// tiles, plus the slot's rank in its tile.  The same rows route_scan's
+// tile bases give.
+template <int GB>
+__device__ __forceinline__ int fused_scan_slot(const Dims& d, const int32_t* __restrict__ idx,
+                                               const Work& w, bool live, int t, int* s_mat,
+                                               int* s_off, int* s_wsum) {
+  constexpr int kGBlock = GB;
+  const int tid = threadIdx.x, lane = threadIdx.x % kWave;
   const int E = d.E, n = d.nblk * E;
   for (int i = tid; i < n; i += kGBlock) s_mat[i] = w.tile_counts[i];
   __syncthreads();
@@ -126,16 +110,50 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
 
   // Lane j < k of each wave resolves slot j of the wave's token.
   int mine = -1;
-  if (it.live && lane < d.k) {
-    const int64_t at = (int64_t)it.t * d.k + lane;
+  if (live && lane < d.k) {
+    const int64_t at = (int64_t)t * d.k + lane;
     const int l = w.lr[at];
     const int e = min(max(idx[at], 0), E - 1);
     if (l >= 0) {
       int base = s_off[e];
-      for (int b = 0; b < it.t / d.tile; ++b) base += s_mat[b * E + e];
+      for (int b = 0; b < t / d.tile; ++b) base += s_mat[b * E + e];
       mine = base + l;
     }
   }
+  return mine;
+}
+
+// Gather for plans whose tile-count matrix is small (nblk * E <=
+// kFusedScanInts): every block first issues its row loads, then scans the raw
+// tile counts in LDS (column totals, their exclusive scan over the experts,
+// and the prefix over earlier tiles for the experts its tokens use) while
+// those loads are in flight.  The plan's separate scan launch then leaves the
+// critical path (it still runs, lazily, for anything that reads the plan
+// arrays).  Same receive rows as gather_kernel.
+template <int KMAX, int GW>
+__global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                                 const u32x4* __restrict__ x,
+                                                                 u32x4* __restrict__ recv, Work w) {
+  constexpr int kGBlock = GW * kWave;
+  __shared__ int s_mat[kFusedScanInts];   // tile counts [nblk][E]
+  __shared__ int s_off[MOE_MAX_EXPERTS];  // first receive row of each expert
+  __shared__ int s_wsum[GW];
+  const int items = d.T * d.segs, lane = threadIdx.x % kWave, tid = threadIdx.x;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  const bool keep = keep_rows(rows, 2 * d.H);
+  // wave-item g = block * GW + wave (one per wave)
+  Item it;
+  {
+    const int g = __builtin_amdgcn_readfirstlane(blockIdx.x * GW + tid / kWave);
+    it.live = g < items;
+    it.t = it.live ? g / d.segs : 0;
+    it.c = (g - it.t * d.segs) * kWave + lane;
+    it.ok = it.live && it.c < d.chunks;
+  }
+  u32x4 v;
+  if (it.ok) v = load_x_chunk(&x[(int64_t)it.t * d.chunks + it.c]);
+
+  const int mine = fused_scan_slot<kGBlock>(d, idx, w, it.live, it.t, s_mat, s_off, s_wsum);
   int slot[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
@@ -472,20 +490,25 @@ __device__ __forceinline__ void store_codes(uint8_t* base, int64_t row, const Di
   }
 }
 
-// The lane's 16 codes of its two chunks of token row it.t and its scale
-// block's scale 2^e (block amax by an 8-lane reduction; every lane of the
-// wave must call it).
+// The lane's 16 codes of its two chunks of a token row and its scale
+// block's scale 2^e.
 struct Fp8Piece {
   u32x2 a, b;
   float scale;
 };
 
-__device__ __forceinline__ Fp8Piece quantize_piece(const Dims& d, const Item8& it,
-                                                   const u32x4* __restrict__ x) {
+// The lane's two 16-byte chunks of token row it.t (zeros past the row).
+__device__ __forceinline__ void load_piece(const Dims& d, const Item8& it,
+                                           const u32x4* __restrict__ x, u32x4& v0, u32x4& v1) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
   const int64_t xrow = (int64_t)it.t * d.chunks;
-  const u32x4 v0 = it.ok0 ? load_x_chunk(&x[xrow + it.c0]) : zero;
-  const u32x4 v1 = it.ok1 ? load_x_chunk(&x[xrow + it.c0 + 1]) : zero;
+  v0 = it.ok0 ? load_x_chunk(&x[xrow + it.c0]) : zero;
+  v1 = it.ok1 ? load_x_chunk(&x[xrow + it.c0 + 1]) : zero;
+}
+
+// Quantizes the lane's two chunks (block amax by an 8-lane reduction, so
+// every lane of the wave must call it).
+__device__ __forceinline__ Fp8Piece quantize_loaded(u32x4 v0, u32x4 v1) {
   float f0[8], f1[8];
   unpack_bf16(v0, f0);
   unpack_bf16(v1, f1);
@@ -503,6 +526,14 @@ __device__ __forceinline__ Fp8Piece quantize_piece(const Dims& d, const Item8& i
     f1[q] *= inv;
   }
   return Fp8Piece{encode_e4m3x8(f0), encode_e4m3x8(f1), ldexpf(1.0f, e)};
+}
+
+// load_piece, then quantize_loaded.
+__device__ __forceinline__ Fp8Piece quantize_piece(const Dims& d, const Item8& it,
+                                                   const u32x4* __restrict__ x) {
+  u32x4 v0, v1;
+  load_piece(d, it, x, v0, v1);
+  return quantize_loaded(v0, v1);
 }
 
 // 16 codes of a lane from byte offset (row * H + c0 * 8), the inverse of
@@ -558,6 +589,58 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
       if ((uint32_t)slot[j] < rows) {
         store_codes(recv8, slot[j], d, it, ca, cb, keep_rows((int64_t)d.T * d.k, d.H));
         if (scale_lane) rscale[(int64_t)slot[j] * nb + blk] = scale;
+      }
+    }
+  }
+}
+
+// gather_fp8_kernel for small plans, with the scan folded in as in
+// gather_scan_kernel (GW waves per block): the row loads are issued first,
+// the scan runs while they are in flight.
+template <int KMAX, int GW>
+__global__ __launch_bounds__(GW * kWave) void gather_fp8_scan_kernel(Dims d,
+                                                                     const int32_t* __restrict__ idx,
+                                                                     const u32x4* __restrict__ x,
+                                                                     uint8_t* __restrict__ recv8,
+                                                                     float* __restrict__ rscale,
+                                                                     Work w) {
+  __shared__ int s_mat[kFusedScanInts];
+  __shared__ int s_off[MOE_MAX_EXPERTS];
+  __shared__ int s_wsum[GW];
+  const int lane = threadIdx.x % kWave;
+  const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
+  const int items = d.T * segs8;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
+  Item8 it;  // wave-item g = block * GW + wave
+  {
+    const int g = __builtin_amdgcn_readfirstlane(blockIdx.x * GW + threadIdx.x / kWave);
+    it.live = g < items;
+    it.t = it.live ? g / segs8 : 0;
+    it.c0 = (g - it.t * segs8) * kFp8ItemChunks + 2 * lane;
+    it.ok0 = it.live && it.c0 < d.chunks;
+    it.ok1 = it.live && it.c0 + 1 < d.chunks;
+  }
+  u32x4 v0, v1;
+  load_piece(d, it, x, v0, v1);
+  const int mine = fused_scan_slot<GW * kWave>(d, idx, w, it.live, it.t, s_mat, s_off, s_wsum);
+  int slot[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
+  const Fp8Piece q = quantize_loaded(v0, v1);
+  const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
+  const int blk = it.c0 / kFp8BlockChunks;
+  if (it.live && it.c0 == 2 * lane && lane < d.k) {  // first segment publishes the slots
+    w.slot_of[(int64_t)it.t * d.k + lane] = mine;
+    if ((uint32_t)mine < rows) w.row_src[mine] = it.t;
+  }
+  if (it.ok0) {
+    const bool keep = keep_rows(rows, d.H);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if ((uint32_t)slot[j] < rows) {
+        store_codes(recv8, slot[j], d, it, q.a, q.b, keep);
+        if (scale_lane) rscale[(int64_t)slot[j] * nb + blk] = q.scale;
       }
     }
   }
@@ -843,8 +926,21 @@ template <int KMAX>
 struct GatherFp8Launch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
                         float* rscale, const Work& w, hipStream_t s) {
-    hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s, d,
-                       idx, reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
+    if (d.fused_scan) {
+      const int64_t items = (int64_t)d.T * ((d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks);
+      if (d.E <= kWave)
+        hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScanWaves>),
+                           dim3((int)((items + kGatherScanWaves - 1) / kGatherScanWaves)),
+                           dim3(kGatherScanWaves * kWave), 0, s, d, idx,
+                           reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
+      else
+        hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kWaves>),
+                           dim3((int)((items + kWaves - 1) / kWaves)), dim3(kBlock), 0, s, d, idx,
+                           reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
+    } else {
+      hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s,
+                         d, idx, reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
+    }
     return hipGetLastError();
   }
 };

@@ -307,6 +307,16 @@ def test_hierarchical_combine_dsv3(dev):
     hier_check(batch, dev, False, tokens=tok)
 
 
+def test_hierarchical_combine_in_chunks(dev):
+    # 4999 tokens of up to 8 partial rows of 7168 floats: both hops run in 3
+    # chunks of consecutive tokens, the last ragged.
+    batch = gen.make_batch(gen.custom(4999, 7168, 32, 8, 8, 1, seed=21))
+    T = batch.workload.num_tokens
+    tok = np.unique(np.concatenate([[0, 1666, 1667, 3333, 3334, T - 1],
+                                    np.random.default_rng(10).integers(0, T, 256)]))
+    hier_check(batch, dev, False, tokens=tok)
+
+
 def test_hierarchical_combine_without_dispatch(dev):
     # Route, then combine rows that were placed by someone else: the plan fills
     # its per-slot tables itself.
