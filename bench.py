@@ -457,7 +457,7 @@ def main():
     else:
         sfx = "_fp8" if fp8 else ""
         # small single-hop plans scan inside the gather (gather_scan_kernel)
-        gname = "gather_fp8_kernel" if fp8 else "gather_scan_kernel|gather_kernel"
+        gname = "gather_fp8_scan_kernel|gather_fp8_kernel" if fp8 else "gather_scan_kernel|gather_kernel"
         dom = max([(gname, disp_b, disp_ms, disp_gbs),
                    (f"combine{sfx}_kernel", comb_b, comb_ms, comb_gbs)], key=lambda d: d[2])
 

@@ -16,10 +16,14 @@ constexpr int kPlanBlock = 256;    // threads per route-plan block = tokens per 
 constexpr int kPlanWaves = kPlanBlock / kWave;
 constexpr int kMaxPlanTiles = 64;  // route-plan tiles (blocks) at most
 constexpr int kScanLdsInts = 8192; // tile-count matrix the last block scans in LDS (32 KiB)
-// Tile-count matrices up to this size are scanned in the gather (measured:
-// olmoe 16 x 64 gains 2 us per step; qwen3's 32 x 128 loses 6 us, as every
-// gather block then redoes a 4096-entry scan).
-constexpr int kFusedScanInts = 2048;
+// Tile-count matrices up to this size are scanned in the gather (measured,
+// one stream: olmoe 16 x 64 gains 2 us per step; qwen3's 32 x 128, with
+// 16-wave gather blocks, 8 us; nondiv's 64 x 100 loses 14 us, as every
+// gather block then redoes a 6400-entry scan).
+#ifndef MOE_FUSED_SCAN_INTS
+#define MOE_FUSED_SCAN_INTS 4096
+#endif
+constexpr int kFusedScanInts = MOE_FUSED_SCAN_INTS;
 #ifndef MOE_FUSED_SCAN
 #define MOE_FUSED_SCAN 1  // 0: always launch the scan in the route plan
 #endif

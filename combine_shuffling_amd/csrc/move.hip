@@ -43,6 +43,9 @@
 // 224 MiB (8 chunks) 1142 / 1181, 128 MiB 1107 / 1265
 #define MOE_STAGE_CHUNK_MIB 224
 #endif
+#ifndef MOE_GSCAN_WAVES_WIDE
+#define MOE_GSCAN_WAVES_WIDE 16  // qwen3 dispatch: 4 -> 166 us, 8 -> 100, 16 -> 90
+#endif
 #ifndef MOE_GSCAN_WAVES
 #define MOE_GSCAN_WAVES 8  // olmoe dispatch: 4 -> 32.2 us, 8 -> 30.9, 16 -> 31.4
 #endif
@@ -51,6 +54,7 @@ namespace moe {
 namespace {
 
 constexpr int kGatherScanWaves = MOE_GSCAN_WAVES;  // waves per gather_scan block when E <= 64
+constexpr int kGatherScanWavesWide = MOE_GSCAN_WAVES_WIDE;  // ... when E > 64
 constexpr int kStageChunkTokens = MOE_STAGE_CHUNK;  // tokens per hop-1/hop-2 chunk (0: by bytes)
 constexpr int64_t kChunkBytes = (int64_t)MOE_STAGE_CHUNK_MIB << 20;  // staging bytes per chunk, at most
 constexpr int64_t kHierChunkBytes = (int64_t)MOE_HIER_CHUNK_MIB << 20;  // partial bytes per chunk, at most
@@ -66,7 +70,7 @@ constexpr int64_t kHierChunkBytes = (int64_t)MOE_HIER_CHUNK_MIB << 20;  // parti
 template <int GB>
 __device__ __forceinline__ int fused_scan_slot(const Dims& d, const int32_t* __restrict__ idx,
                                                const Work& w, bool live, int t, int* s_mat,
-                                               int* s_off, int* s_wsum) {
+                                               int* s_off, int* s_wsum, int* s_part) {
   constexpr int kGBlock = GB;
   const int tid = threadIdx.x, lane = threadIdx.x % kWave;
   const int E = d.E, n = d.nblk * E;
@@ -97,12 +101,31 @@ __device__ __forceinline__ int fused_scan_slot(const Dims& d, const int32_t* __r
     }
     __syncthreads();
   } else {
-    // (block_exclusive_scan covers 4 * kPlanBlock entries with its first
-    // kPlanWaves waves; any further waves carry zeros)
-    for (int e = tid; e < E; e += kGBlock) {
-      int sum = 0;
-      for (int b = 0; b < d.nblk; ++b) sum += s_mat[b * E + e];
-      s_off[e] = sum;
+    // With at least two threads per expert, kGBlock / E threads sum parts of
+    // its column into s_part (parts * E <= kGBlock entries) and the first E
+    // threads add them; else each thread sums whole columns.  Then the block
+    // scans the totals (block_exclusive_scan covers 4 * kPlanBlock entries
+    // with its first kPlanWaves waves; any further waves carry zeros).
+    const int parts = min(kGBlock / E, d.nblk);
+    if (parts >= 2) {
+      if (tid < parts * E) {
+        const int q = tid / E, e = tid - q * E;
+        int sum = 0;
+        for (int b = q * d.nblk / parts; b < (q + 1) * d.nblk / parts; ++b) sum += s_mat[b * E + e];
+        s_part[tid] = sum;
+      }
+      __syncthreads();
+      if (tid < E) {
+        int tot = 0;
+        for (int q = 0; q < parts; ++q) tot += s_part[q * E + tid];
+        s_off[tid] = tot;
+      }
+    } else {
+      for (int e = tid; e < E; e += kGBlock) {
+        int sum = 0;
+        for (int b = 0; b < d.nblk; ++b) sum += s_mat[b * E + e];
+        s_off[e] = sum;
+      }
     }
     __syncthreads();
     block_exclusive_scan(s_off, E, s_wsum);
@@ -138,6 +161,7 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
   __shared__ int s_mat[kFusedScanInts];   // tile counts [nblk][E]
   __shared__ int s_off[MOE_MAX_EXPERTS];  // first receive row of each expert
   __shared__ int s_wsum[GW];
+  __shared__ int s_part[GW * kWave];      // column parts (more than 64 experts)
   const int items = d.T * d.segs, lane = threadIdx.x % kWave, tid = threadIdx.x;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const bool keep = keep_rows(rows, 2 * d.H);
@@ -153,7 +177,7 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
   u32x4 v;
   if (it.ok) v = load_x_chunk(&x[(int64_t)it.t * d.chunks + it.c]);
 
-  const int mine = fused_scan_slot<kGBlock>(d, idx, w, it.live, it.t, s_mat, s_off, s_wsum);
+  const int mine = fused_scan_slot<kGBlock>(d, idx, w, it.live, it.t, s_mat, s_off, s_wsum, s_part);
   int slot[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
@@ -607,6 +631,7 @@ __global__ __launch_bounds__(GW * kWave) void gather_fp8_scan_kernel(Dims d,
   __shared__ int s_mat[kFusedScanInts];
   __shared__ int s_off[MOE_MAX_EXPERTS];
   __shared__ int s_wsum[GW];
+  __shared__ int s_part[GW * kWave];
   const int lane = threadIdx.x % kWave;
   const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
   const int items = d.T * segs8;
@@ -623,7 +648,7 @@ __global__ __launch_bounds__(GW * kWave) void gather_fp8_scan_kernel(Dims d,
   }
   u32x4 v0, v1;
   load_piece(d, it, x, v0, v1);
-  const int mine = fused_scan_slot<GW * kWave>(d, idx, w, it.live, it.t, s_mat, s_off, s_wsum);
+  const int mine = fused_scan_slot<GW * kWave>(d, idx, w, it.live, it.t, s_mat, s_off, s_wsum, s_part);
   int slot[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
@@ -855,9 +880,10 @@ struct GatherLaunch {
                            dim3(kGatherScanWaves * kWave), 0, s, d, idx,
                            reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), w);
       else
-        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kWaves>),
-                           dim3((int)((items + kWaves - 1) / kWaves)), dim3(kBlock), 0, s, d,
-                           idx, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), w);
+        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWavesWide>),
+                           dim3((int)((items + kGatherScanWavesWide - 1) / kGatherScanWavesWide)),
+                           dim3(kGatherScanWavesWide * kWave), 0, s, d, idx,
+                           reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), w);
     } else
       hipLaunchKernelGGL((gather_kernel<KMAX, kGatherU>), dim3(blocks_for(d, kGatherU)),
                          dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
@@ -934,8 +960,9 @@ struct GatherFp8Launch {
                            dim3(kGatherScanWaves * kWave), 0, s, d, idx,
                            reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
       else
-        hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kWaves>),
-                           dim3((int)((items + kWaves - 1) / kWaves)), dim3(kBlock), 0, s, d, idx,
+        hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScanWavesWide>),
+                           dim3((int)((items + kGatherScanWavesWide - 1) / kGatherScanWavesWide)),
+                           dim3(kGatherScanWavesWide * kWave), 0, s, d, idx,
                            reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
     } else {
       hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s,
