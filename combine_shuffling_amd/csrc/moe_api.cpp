@@ -374,8 +374,9 @@ moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, f
                         !moe::aligned(staging_scale, 4)))
     return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // small single-hop plans: the fp8 gather scans the tile counts itself
-  if (!plan->d.fused_scan && moe::ensure_scanned(plan, s) != MOE_OK) return MOE_ERR_HIP;
+  // small single-hop plans with up to 64 experts: the fp8 gather scans the
+  // tile counts itself
+  if (!moe::fp8_fused_scan(plan->d) && moe::ensure_scanned(plan, s) != MOE_OK) return MOE_ERR_HIP;
   const hipError_t e =
       plan->d.dedup ? moe::launch_stage_fp8(plan->d, plan->idx, x, staging8, staging_scale, recv8,
                                             recv_scale, plan->work, s)

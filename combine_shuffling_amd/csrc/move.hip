@@ -952,18 +952,12 @@ template <int KMAX>
 struct GatherFp8Launch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
                         float* rscale, const Work& w, hipStream_t s) {
-    if (d.fused_scan) {
+    if (fp8_fused_scan(d)) {
       const int64_t items = (int64_t)d.T * ((d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks);
-      if (d.E <= kWave)
-        hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScanWaves>),
-                           dim3((int)((items + kGatherScanWaves - 1) / kGatherScanWaves)),
-                           dim3(kGatherScanWaves * kWave), 0, s, d, idx,
-                           reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
-      else
-        hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScanWavesWide>),
-                           dim3((int)((items + kGatherScanWavesWide - 1) / kGatherScanWavesWide)),
-                           dim3(kGatherScanWavesWide * kWave), 0, s, d, idx,
-                           reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
+      hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScanWaves>),
+                         dim3((int)((items + kGatherScanWaves - 1) / kGatherScanWaves)),
+                         dim3(kGatherScanWaves * kWave), 0, s, d, idx,
+                         reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
     } else {
       hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s,
                          d, idx, reinterpret_cast<const u32x4*>(x), recv8, rscale, w);

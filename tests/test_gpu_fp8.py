@@ -71,8 +71,8 @@ def check_fp8(batch, dev, x_bits=None, tokens=None):
 @pytest.mark.parametrize("case", [
     (1, 8, 1, 1, 1), (300, 200, 8, 2, 2), (1000, 136, 24, 5, 7), (2049, 256, 64, 8, 4),
     (777, 1024, 100, 6, 7), (513, 72, 13, 13, 13),
-    (900, 64, 300, 6, 10),     # scan in the gather: 3 threads per expert column
-    (700, 64, 1024, 8, 16)],   # scan in the gather: more experts than threads
+    (900, 64, 300, 6, 10),     # 300 experts
+    (700, 64, 1024, 8, 16)],   # 1024 experts
     ids=lambda c: "T{}-H{}-E{}-k{}-R{}".format(*c))
 def test_fp8_small_shapes(case, dev):
     T, H, E, k, R = case
