@@ -13,18 +13,22 @@
 //  gather   dispatch, single hop: each source row x[t] is read once and
 //           written to its k receive rows (FUSCO article, "core innovation":
 //           no pack buffer before the send, no reorder after the receive).
-//           Also finishes slot_of / row_src from the in-tile ranks.
+//           Also finishes slot_of / row_src from the in-tile ranks.  Small
+//           plans use gather_scan, which also does the plan's scan.
 //  stage_a  deduplicated dispatch, hop 1: x[t] is read once and written once
 //           per distinct destination node, to that node's forwarder staging
 //           row (FUSCO article, "load balancing and cross-node
 //           deduplication").  Also finishes slot_of / row_src / stage_of /
 //           stage_src.
 //  stage_b  hop 2, intra-node fan-out: each staging row is read once and
-//           written to every receive row of its token on that node.
+//           written to every receive row of its token on that node.  The two
+//           hops run chunk by chunk over consecutive tokens.
 //  combine  out[t] = sum_j w[t,j] * y[slot_of[t,j]]: k row loads, one fp32
 //           fused multiply-add per element and slot in ascending j starting
 //           from 0, then round-to-nearest-even bf16 (or fp32) out (INC-MoE
-//           abstract: combine back to each token's owner).
+//           abstract: combine back to each token's owner).  The hierarchical
+//           form (combine_part, combine_nodes) and the fp8 payload follow
+//           below.
 #include "move_body.h"
 #include "plan_body.h"
 
@@ -193,11 +197,13 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
   }
 }
 
+// Hop 1 over wave-items [item0, item_end) (one chunk of tokens); keep: plain
+// stores for the staging rows.
 template <int KMAX, int U>
-__device__ __forceinline__ void stage_a_body(const Dims& d, const int32_t* __restrict__ idx,
-                                             const u32x4* __restrict__ x,
-                                             u32x4* __restrict__ staging, const Work& w, int blk,
-                                             int item0, int item_end, int keep) {
+__global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                         const u32x4* __restrict__ x,
+                                                         u32x4* __restrict__ staging, Work w,
+                                                         int item0, int item_end, int keep) {
   const int lane = threadIdx.x % kWave;
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   Item it[U];
@@ -206,7 +212,7 @@ __device__ __forceinline__ void stage_a_body(const Dims& d, const int32_t* __res
   u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, blk, item0, item_end, u);
+    it[u] = wave_item<U>(d, blockIdx.x, item0, item_end, u);
     lead[u] = 0;
     if (it[u].live) {
       token_slots_serial<KMAX>(d, w, idx, it[u].t, slot[u]);
@@ -239,13 +245,13 @@ __device__ __forceinline__ void stage_a_body(const Dims& d, const int32_t* __res
   }
 }
 
-// Hop 2, one token per wave-item: each of the token's staging rows (one per
-// destination node) is read once and written to the token's slots on that
-// node.
+// Hop 2, one token per wave-item, over wave-items [item0, item_end): each of
+// the token's staging rows (one per destination node) is read once and
+// written to the token's slots on that node.
 template <int KMAX, int U>
-__device__ __forceinline__ void stage_b_body(const Dims& d, const u32x4* __restrict__ staging,
-                                             u32x4* __restrict__ recv, const Work& w, int blk,
-                                             int item0, int item_end) {
+__global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __restrict__ staging,
+                                                         u32x4* __restrict__ recv, Work w,
+                                                         int item0, int item_end) {
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   const bool keep = keep_rows(rows, 2 * d.H);
   Item it[U];
@@ -253,7 +259,7 @@ __device__ __forceinline__ void stage_b_body(const Dims& d, const u32x4* __restr
   u32x4 v[U][KMAX];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, blk, item0, item_end, u);
+    it[u] = wave_item<U>(d, blockIdx.x, item0, item_end, u);
     const int64_t at = (int64_t)it[u].t * d.k;
     int sj[KMAX], pj[KMAX];
 #pragma unroll
@@ -291,21 +297,6 @@ __device__ __forceinline__ void stage_b_body(const Dims& d, const u32x4* __restr
       }
     }
   }
-}
-
-template <int KMAX, int U>
-__global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* __restrict__ idx,
-                                                         const u32x4* __restrict__ x,
-                                                         u32x4* __restrict__ staging, Work w,
-                                                         int item0, int item_end, int keep) {
-  stage_a_body<KMAX, U>(d, idx, x, staging, w, blockIdx.x, item0, item_end, keep);
-}
-
-template <int KMAX, int U>
-__global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __restrict__ staging,
-                                                         u32x4* __restrict__ recv, Work w,
-                                                         int item0, int item_end) {
-  stage_b_body<KMAX, U>(d, staging, recv, w, blockIdx.x, item0, item_end);
 }
 
 // ---- hierarchical combine over the deduplication's staging rows ------------
