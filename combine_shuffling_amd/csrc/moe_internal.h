@@ -15,7 +15,14 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kPlanBlock = 256;    // threads per route-plan block = tokens per pass
 constexpr int kPlanWaves = kPlanBlock / kWave;
 constexpr int kMaxPlanTiles = 64;  // route-plan tiles (blocks) at most
-constexpr int kScanLdsInts = 8192; // tile-count matrix the last block scans in LDS (32 KiB)
+// Tile-count matrix the scan holds in LDS (64 KiB of gfx950's 160 KiB per
+// workgroup).  Load-aware plans use all of it: their [tiles x (owner, node)]
+// matrix then takes 32 two-pass tiles instead of 16 four-pass ones on the
+// DeepSeek-V3-like workload (route 57.6 -> 45 us).  Other plans stay within
+// half: more tiles made the static dedup dispatch 7 us slower than the 4 us
+// they saved in the route.
+constexpr int kScanLdsInts = 16384;
+constexpr int kScanLdsIntsStatic = kScanLdsInts / 2;
 // Tile-count matrices up to this size are scanned in the gather (measured,
 // one stream: olmoe 16 x 64 gains 2 us per step; qwen3's 32 x 128, with
 // 16-wave gather blocks, 8 us; nondiv's 64 x 100 loses 14 us, as every
