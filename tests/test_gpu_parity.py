@@ -221,6 +221,42 @@ def test_bad_routing_is_flagged_and_memory_safe(dev):
     assert run.plan.status() == 0
 
 
+def test_bad_routing_in_chunked_dedup_dispatch(dev):
+    # Bad ids in both chunks of a 2-chunk deduplicated dispatch: flagged,
+    # dropped slots -1, nothing written past the buffers, and the
+    # hierarchical combine and the fp8 dispatch run over the same plan.
+    from combine_shuffling_amd import _abi
+
+    T, H, k = 2500, 7168, 8
+    batch = gen.make_batch(gen.custom(T, H, 64, k, 16, 2, seed=4))
+    idx = batch.topk_idx.copy()
+    idx[5, 3] = 64             # out of range, first chunk
+    idx[2000, 6] = -1          # negative, second chunk
+    idx[1700, 1] = idx[1700, 0]  # repeated, second chunk
+    batch.topk_idx = idx
+    run = GpuRun(batch, dev, node_dedup=True).route().dispatch()
+    assert run.plan.status() == _abi.ERR_BAD_ROUTING
+    assert run.guards_intact()
+    so = run.plan.read("slot_of").reshape(T, k)
+    assert so[5, 3] == -1 and so[2000, 6] == -1 and so[1700, 1] == -1 and so[1700, 0] >= 0
+    assert int(run.plan.read("counts").sum()) == T * k - 3
+    smax = run.plan.staging_rows_max
+    part_full = torch.full((smax + 2, H), float("nan"), dtype=torch.float32, device=dev)
+    run.plan.combine_hier(run.recv, run.w, partials=part_full[:smax])
+    torch.cuda.synchronize()
+    assert torch.isnan(part_full[smax:]).all(), "hop 1 wrote past the partials"
+    nb = run.plan.scale_blocks
+    codes_full = torch.full((run.plan.recv_rows + 2, H), 0x55, dtype=torch.uint8, device=dev)
+    stage_full = torch.full((smax + 2, H), 0x55, dtype=torch.uint8, device=dev)
+    run.plan.dispatch_fp8(run.x, codes_full[:run.plan.recv_rows],
+                          torch.empty((run.plan.recv_rows, nb), dtype=torch.float32, device=dev),
+                          stage_full[:smax], torch.empty((smax, nb), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    assert bool((codes_full[run.plan.recv_rows:] == 0x55).all())
+    assert bool((stage_full[smax:] == 0x55).all())
+    assert run.plan.status() == _abi.ERR_BAD_ROUTING
+
+
 def test_plan_reads_and_combine_without_dispatch(dev):
     # With no dispatch since the route, plan reads and combine finish the plan
     # themselves (one thread per token).
