@@ -323,7 +323,8 @@ moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint1
   }
   if (moe::ensure_scanned(plan, s) != MOE_OK) return MOE_ERR_HIP;
   plan->assigned = true;
-  return moe::from_hip(moe::launch_dedup_dispatch(plan->d, plan->idx, x, staging, recv, plan->work, s));
+  return moe::from_hip(
+      moe::launch_dedup_dispatch(plan->d, plan->idx, x, staging, recv, plan->work, s));
 }
 
 moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
