@@ -20,6 +20,11 @@ has just written, as the path does.
 Prints one JSON line.
   value       algorithmic payload bytes per step / wall time per step, over K
               steps bracketed by synchronize on both sides, no events inside.
+              Schedule (--inflight auto): after the warmup, a short trial of
+              the steps one after another on one stream and of two batches in
+              flight (step i on stream i mod 2, each stream in order) picks
+              the faster; the K timed steps run in it, and K steps of the
+              other are timed too and reported beside it.
   phases      route plan, dispatch and combine timed inside K more steps
               run one after another on one stream, with HIP events on that
               stream between the phases.  Inside a step, the non-temporal
@@ -97,10 +102,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
-    ap.add_argument("--inflight", type=int, default=2,
+    ap.add_argument("--inflight", default="auto",
                     help="batches in flight: consecutive steps go round-robin to this many HIP "
                          "streams, each stream running its steps in order (1: one stream, every "
-                         "step after the previous one)")
+                         "step after the previous one).  auto (default): a short trial of 1 and "
+                         "2 after the warmup picks the faster for the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) a few "
                          "times, to scale hardware byte counters against a known size")
@@ -322,11 +328,12 @@ def main():
                  + probe.recv_rows * H * (1 if fp8 else 2) + probe.staging_rows_max * H * 2
                  + T * H * 2)
     in_bytes = x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4
-    inflight = 1 if pipe else max(1, args.inflight)
+    auto = str(args.inflight) == "auto"
+    max_inflight = 1 if pipe else (2 if auto else max(1, int(args.inflight)))
     n_sets = args.sets or min(MAX_SETS, max(2, math.ceil((2 << 30) / set_bytes),
                                             math.ceil(4 * MALL_BYTES / in_bytes)))
     # a set always runs on the same stream, so its reuse is ordered after its last use
-    n_sets = -(-n_sets // inflight) * inflight
+    n_sets = -(-n_sets // max_inflight) * max_inflight
     sets = []
     for _ in range(n_sets):
         plan = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la,
@@ -350,7 +357,8 @@ def main():
 
     # Stream 0 is torch's current stream; the others are plain streams of the
     # default priority.
-    streams = [torch.cuda.current_stream(dev)] + [torch.cuda.Stream(dev) for _ in range(inflight - 1)]
+    streams = [torch.cuda.current_stream(dev)] + [torch.cuda.Stream(dev)
+                                                  for _ in range(max_inflight - 1)]
 
     def do_dispatch(s, st=None):
         if fp8:
@@ -375,18 +383,26 @@ def main():
         do_dispatch(s, st)
         do_combine(s, st)
 
-    def timed_steps(n_streams):
+    def timed_steps(n_streams, steps=None):
         """Wall time per step of K steps; step i on stream i % n_streams."""
+        steps = args.steps if steps is None else steps
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             step(sets[i % n_sets], streams[i % n_streams])
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / args.steps
+        return (time.perf_counter() - t0) * 1e3 / steps
 
     for i in range(args.warmup):
-        step(sets[i % n_sets], streams[i % inflight])
+        step(sets[i % n_sets], streams[i % max_inflight])
     torch.cuda.synchronize()
+    # Schedule: a trial of both, apart from the timed steps, picks the faster.
+    trial = None
+    inflight = max_inflight
+    if auto and not pipe:
+        n_trial = max(20, args.steps // 4)
+        trial = {"serial": timed_steps(1, n_trial), "two_in_flight": timed_steps(2, n_trial)}
+        inflight = 2 if trial["two_in_flight"] < trial["serial"] else 1
     D = int(sets[0]["plan"].read("num_staged")[0]) if wl.node_dedup else 0
     fwd_rows = None
     if wl.node_dedup:
@@ -397,11 +413,14 @@ def main():
     disp_b, comb_b = algorithmic_bytes(wl, D, args.payload, hier)
 
     # Timed region: K steps and nothing else, with `inflight` batches in
-    # flight; then the same K steps one after another on one stream.
+    # flight; then K steps of the other schedule, reported beside it.
     ms_per_step = timed_steps(inflight)
     value = (disp_b + comb_b) / (ms_per_step * 1e-3) / 1e9
     serial_ms = timed_steps(1) if inflight > 1 else ms_per_step
     serial_value = (disp_b + comb_b) / (serial_ms * 1e-3) / 1e9
+    two_ms = None
+    if max_inflight == 2:
+        two_ms = ms_per_step if inflight == 2 else timed_steps(2)
 
     # Phase pass: K more steps one after another on stream 0, with events
     # between the phases (route plan | dispatch | combine).
@@ -483,9 +502,17 @@ def main():
                    "payload": args.payload, "forwarder_rows": fwd_rows,
                    "combine": "hierarchical" if hier else "direct",
                    "path": f"pipeline, bands of {band} tokens" if pipe else "separate launches",
-                   "batches_in_flight": inflight},
+                   "batches_in_flight": inflight,
+                   "schedule": "chosen by trial" if trial else "fixed"},
         "serial": {"ms_per_step": round(serial_ms, 5), "value": round(serial_value, 2),
                    "pct_of_hbm_peak": round(100.0 * serial_value / HBM_PEAK_GBS, 2)},
+        "two_in_flight": (None if two_ms is None else
+                          {"ms_per_step": round(two_ms, 5),
+                           "value": round((disp_b + comb_b) / (two_ms * 1e-3) / 1e9, 2),
+                           "pct_of_hbm_peak": round(100.0 * (disp_b + comb_b) / (two_ms * 1e-3)
+                                                    / 1e9 / HBM_PEAK_GBS, 2)}),
+        "schedule_trial_ms_per_step": (None if trial is None else
+                                       {k2: round(v2, 5) for k2, v2 in trial.items()}),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "bytes_per_step": disp_b + comb_b,
         "phases": ({"pipeline": {"bytes": disp_b + comb_b, "ms_per_launch": round(pipe_ms, 5),
