@@ -36,11 +36,16 @@ Prints one JSON line.
               (about 2.5 us) that back-to-back kernels hide: the phase times
               have it subtracted, estimated as (sum of the phase intervals -
               the serial step time) / 3.  The value pass has no events.
+              Each phase also gives its median, p10 and p90 over the K steps.
   roofline    the dominant kernel: its algorithmic bytes per launch / its mean
               duration from the phase pass.
               traffic = HBM bytes per launch from the rocprofv3 FETCH_SIZE /
               WRITE_SIZE summary under profiles/, scaled by the copy
               calibration; null if the kernel sources changed since.
+  copy_ceiling a plain device-to-device copy (torch copy_) moving the step's
+              bytes, half read and half written, over source/destination
+              pairs cycled past the MALL, K times: a practical ceiling, and
+              value over it.
 Algorithmic bytes (payload rows only):
   dispatch single hop  (T + T*k) * 2H
   dispatch with dedup  (T + 2D + T*k) * 2H   (D staging rows, from the plan)
@@ -144,6 +149,28 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration": {"kernel": "torch elementwise mul (bf16)",
                                            "read_bytes": n * 2, "write_bytes": n * 2,
                                            "launches": 5}}), flush=True)
+
+
+def copy_ceiling(torch, dev, half_bytes, steps):
+    """Wall time of a plain device-to-device copy of half_bytes (torch copy_),
+    over pairs of buffers cycled so the sources total at least 4x the MALL."""
+    n = half_bytes // 2
+    pairs = max(2, math.ceil(4 * MALL_BYTES / half_bytes))
+    src = [torch.empty(n, dtype=torch.int16, device=dev).fill_(i) for i in range(pairs)]
+    dst = [torch.empty_like(a) for a in src]
+    for i in range(2 * pairs):
+        dst[i % pairs].copy_(src[i % pairs])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        dst[i % pairs].copy_(src[i % pairs])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "torch copy_ (device to device)", "bytes": 2 * half_bytes,
+            "buffer_pairs": pairs, "ms": round(ms, 5),
+            "GB/s": round(2 * half_bytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def _pmc_means(path, counter):
@@ -442,11 +469,11 @@ def main():
                 do_combine(s)
             ev[3].record()
         torch.cuda.synchronize()
-        t = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
-                      for e in evs])
-        return t.mean(axis=0)
+        return np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]),
+                          e[2].elapsed_time(e[3])] for e in evs])
 
-    route_ms, disp_ms, comb_ms = (float(v) for v in phase_pass())
+    phase_t = phase_pass()
+    route_ms, disp_ms, comb_ms = (float(v) for v in phase_t.mean(axis=0))
     # An event makes the GPU finish the kernel before it and only then launch
     # the next one, so each interval also holds one kernel-launch latency
     # that back-to-back kernels hide.  The same steps without events (the
@@ -457,6 +484,13 @@ def main():
     route_ms -= event_gap_ms
     disp_ms -= event_gap_ms
     comb_ms -= event_gap_ms
+    phase_t = phase_t - event_gap_ms
+
+    def spread(col):
+        """Median, p10 and p90 over the K steps of one phase (event gap removed)."""
+        q = np.percentile(phase_t[:, col], [50, 10, 90])
+        return {"ms_median": round(float(q[0]), 5), "ms_p10": round(float(q[1]), 5),
+                "ms_p90": round(float(q[2]), 5)}
     if pipe:
         # one launch per step does everything
         pipe_ms = route_ms
@@ -479,6 +513,12 @@ def main():
         gname = "gather_fp8_scan_kernel|gather_fp8_kernel" if fp8 else "gather_scan_kernel|gather_kernel"
         dom = max([(gname, disp_b, disp_ms, disp_gbs),
                    (f"combine{sfx}_kernel", comb_b, comb_ms, comb_gbs)], key=lambda d: d[2])
+
+    # Practical ceiling: a plain device-to-device copy moving the step's bytes
+    # (half read, half written), its sources and destinations cycled past the
+    # MALL like the step's buffers.
+    copy = copy_ceiling(torch, dev, (disp_b + comb_b) // 2, args.steps)
+    copy["value_over_copy"] = round(value / copy["GB/s"], 4)
 
     # which committed traffic summary covers this run
     variant = "_pipeline" if pipe else "_fp8" if fp8 else "_hier" if hier else ""
@@ -517,11 +557,14 @@ def main():
         "bytes_per_step": disp_b + comb_b,
         "phases": ({"pipeline": {"bytes": disp_b + comb_b, "ms_per_launch": round(pipe_ms, 5),
                                  "GB/s": round(disp_gbs, 1), "launches": 1}} if pipe else
-                   {"route": {"ms_per_step": round(route_ms, 5)},
+                   {"route": {"ms_per_step": round(route_ms, 5), **spread(0)},
                     "dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),
-                                 "GB/s": round(disp_gbs, 1), "launches": 2 if wl.node_dedup else 1},
+                                 "GB/s": round(disp_gbs, 1), "launches": 2 if wl.node_dedup else 1,
+                                 **spread(1)},
                     "combine": {"bytes": comb_b, "ms_per_launch": round(comb_ms, 5),
-                                "GB/s": round(comb_gbs, 1), "launches": 2 if hier else 1}}),
+                                "GB/s": round(comb_gbs, 1), "launches": 2 if hier else 1,
+                                **spread(2)}}),
+        "copy_ceiling": copy,
         "roofline": {"bound": "hbm", "kernel": traffic_kernel or dom[0], "achieved": round(dom[3], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
