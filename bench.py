@@ -19,12 +19,16 @@ has just written, as the path does.
 
 Prints one JSON line.
   value       algorithmic payload bytes per step / wall time per step, over K
-              steps bracketed by synchronize on both sides, no events inside.
-              Schedule (--inflight auto): after the warmup, a short trial of
-              the steps one after another on one stream and of two batches in
-              flight (step i on stream i mod 2, each stream in order) picks
-              the faster; the K timed steps run in it, and K steps of the
-              other are timed too and reported beside it.
+              steps bracketed by synchronize on both sides, no timing events
+              inside.  Schedule (--inflight auto): after the warmup, a short
+              trial of three schedules picks the fastest: serial (the steps
+              one after another on one stream), two_in_flight (step i on
+              stream i mod 2, each stream in order) and staggered (as
+              two_in_flight, with each step's dispatch waiting on an event
+              after the previous step's dispatch, so a dispatch always runs
+              beside the other batch's combine).  The K timed steps run in the
+              chosen one; K steps of each other schedule are timed too and
+              reported beside it.
   phases      route plan, dispatch and combine timed inside K more steps
               run one after another on one stream, with HIP events on that
               stream between the phases.  Inside a step, the non-temporal
@@ -77,6 +81,7 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20   # MI355X last-level cache (AMD Infinity Cache)
 MAX_SETS = 256
 METRIC = "dispatch+combine effective GB/s and % of HBM peak, 1 MI355X"
+SCHEDULES = ("serial", "two_in_flight", "staggered")
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("combine_shuffling_amd/csrc/move.hip", "combine_shuffling_amd/csrc/move_body.h",
                   "combine_shuffling_amd/csrc/pipeline.hip", "combine_shuffling_amd/csrc/plan_body.h",
@@ -107,11 +112,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
-    ap.add_argument("--inflight", default="auto",
-                    help="batches in flight: consecutive steps go round-robin to this many HIP "
-                         "streams, each stream running its steps in order (1: one stream, every "
-                         "step after the previous one).  auto (default): a short trial of 1 and "
-                         "2 after the warmup picks the faster for the timed steps")
+    ap.add_argument("--inflight", default="auto", choices=("auto", "1", "2", "staggered"),
+                    help="schedule of the steps.  1: one stream, every step after the previous "
+                         "one.  2: two batches in flight, step i on HIP stream i mod 2, each "
+                         "stream running its steps in order.  staggered: as 2, but each step's "
+                         "dispatch waits for the previous step's dispatch, so a dispatch always "
+                         "overlaps the other batch's combine.  auto (default): a short trial of "
+                         "the three after the warmup picks the fastest for the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) a few "
                          "times, to scale hardware byte counters against a known size")
@@ -356,7 +363,7 @@ def main():
                  + T * H * 2)
     in_bytes = x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4
     auto = str(args.inflight) == "auto"
-    max_inflight = 1 if pipe else (2 if auto else max(1, int(args.inflight)))
+    max_inflight = 1 if pipe or args.inflight == "1" else 2
     n_sets = args.sets or min(MAX_SETS, max(2, math.ceil((2 << 30) / set_bytes),
                                             math.ceil(4 * MALL_BYTES / in_bytes)))
     # a set always runs on the same stream, so its reuse is ordered after its last use
@@ -410,26 +417,46 @@ def main():
         do_dispatch(s, st)
         do_combine(s, st)
 
-    def timed_steps(n_streams, steps=None):
-        """Wall time per step of K steps; step i on stream i % n_streams."""
+    def staggered_step(i, done):
+        """Step i on stream i % 2, its dispatch after step i - 1's dispatch
+        (event done[i - 1]), so that it overlaps step i - 1's combine."""
+        s, st = sets[i % n_sets], streams[i % 2]
+        s["plan"].route(s["idx"], stream=st)
+        if i > 0:
+            st.wait_event(done[(i - 1) % 2])
+        do_dispatch(s, st)
+        done[i % 2].record(st)
+        do_combine(s, st)
+
+    def timed_steps(schedule, steps=None):
+        """Wall time per step of K steps in one schedule: "serial" (one
+        stream), "two_in_flight" (step i on stream i % 2) or "staggered"."""
         steps = args.steps if steps is None else steps
+        done = [torch.cuda.Event(), torch.cuda.Event()]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            step(sets[i % n_sets], streams[i % n_streams])
+            if schedule == "staggered":
+                staggered_step(i, done)
+            else:
+                step(sets[i % n_sets], streams[i % (2 if schedule == "two_in_flight" else 1)])
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
     for i in range(args.warmup):
         step(sets[i % n_sets], streams[i % max_inflight])
     torch.cuda.synchronize()
-    # Schedule: a trial of both, apart from the timed steps, picks the faster.
+    # Schedule: a trial of each, apart from the timed steps, picks the fastest.
     trial = None
-    inflight = max_inflight
-    if auto and not pipe:
+    if max_inflight == 1:
+        schedule = "serial"
+    elif auto:
         n_trial = max(20, args.steps // 4)
-        trial = {"serial": timed_steps(1, n_trial), "two_in_flight": timed_steps(2, n_trial)}
-        inflight = 2 if trial["two_in_flight"] < trial["serial"] else 1
+        trial = {name: timed_steps(name, n_trial) for name in SCHEDULES}
+        schedule = min(trial, key=trial.get)
+    else:
+        schedule = "staggered" if args.inflight == "staggered" else "two_in_flight"
+    inflight = 1 if schedule == "serial" else 2
     D = int(sets[0]["plan"].read("num_staged")[0]) if wl.node_dedup else 0
     fwd_rows = None
     if wl.node_dedup:
@@ -441,13 +468,21 @@ def main():
 
     # Timed region: K steps and nothing else, with `inflight` batches in
     # flight; then K steps of the other schedule, reported beside it.
-    ms_per_step = timed_steps(inflight)
+    ms_per_step = timed_steps(schedule)
     value = (disp_b + comb_b) / (ms_per_step * 1e-3) / 1e9
-    serial_ms = timed_steps(1) if inflight > 1 else ms_per_step
+    per_schedule = {schedule: ms_per_step}
+    for name in (SCHEDULES if max_inflight == 2 else ("serial",)):
+        if name not in per_schedule:
+            per_schedule[name] = timed_steps(name)
+    serial_ms = per_schedule["serial"]
     serial_value = (disp_b + comb_b) / (serial_ms * 1e-3) / 1e9
-    two_ms = None
-    if max_inflight == 2:
-        two_ms = ms_per_step if inflight == 2 else timed_steps(2)
+
+    def schedule_entry(name):
+        if name not in per_schedule:
+            return None
+        v = (disp_b + comb_b) / (per_schedule[name] * 1e-3) / 1e9
+        return {"ms_per_step": round(per_schedule[name], 5), "value": round(v, 2),
+                "pct_of_hbm_peak": round(100.0 * v / HBM_PEAK_GBS, 2)}
 
     # Phase pass: K more steps one after another on stream 0, with events
     # between the phases (route plan | dispatch | combine).
@@ -543,14 +578,12 @@ def main():
                    "combine": "hierarchical" if hier else "direct",
                    "path": f"pipeline, bands of {band} tokens" if pipe else "separate launches",
                    "batches_in_flight": inflight,
-                   "schedule": "chosen by trial" if trial else "fixed"},
+                   "schedule": schedule,
+                   "schedule_choice": "trial" if trial else "fixed"},
         "serial": {"ms_per_step": round(serial_ms, 5), "value": round(serial_value, 2),
                    "pct_of_hbm_peak": round(100.0 * serial_value / HBM_PEAK_GBS, 2)},
-        "two_in_flight": (None if two_ms is None else
-                          {"ms_per_step": round(two_ms, 5),
-                           "value": round((disp_b + comb_b) / (two_ms * 1e-3) / 1e9, 2),
-                           "pct_of_hbm_peak": round(100.0 * (disp_b + comb_b) / (two_ms * 1e-3)
-                                                    / 1e9 / HBM_PEAK_GBS, 2)}),
+        "two_in_flight": schedule_entry("two_in_flight"),
+        "staggered": schedule_entry("staggered"),
         "schedule_trial_ms_per_step": (None if trial is None else
                                        {k2: round(v2, 5) for k2, v2 in trial.items()}),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
