@@ -1,4 +1,5 @@
-"""Two batches in flight: independent plans on two HIP streams.
+"""Two batches in flight: independent plans on two HIP streams, free-running
+or staggered (each dispatch after the previous batch's dispatch).
 
 A caller may keep a second batch's route plan, dispatch and combine running
 on another stream while the first batch's are still running (the library
@@ -68,6 +69,48 @@ def test_two_batches_in_flight(case, dev):
         assert r["plan"].status() == 0
         assert np.array_equal(r["plan"].read("slot_of").reshape(T, k), p["slot_of"])
         assert np.array_equal(r["plan"].read("expert_offsets"), p["expert_offsets"])
+        recv = bits(r["recv"])
+        assert np.array_equal(recv, oracle.dispatch(b.x, p)), "receive rows differ"
+        if wl.node_dedup:
+            D = p["num_staged"]
+            assert np.array_equal(bits(r["st"])[:D], oracle.dedup_stage_a(b.x, p))
+        check_combine(r["out"].cpu().numpy(), recv, b.topk_w, p["slot_of"], True, wl.name)
+
+
+@pytest.mark.parametrize("case", CASES[1:3], ids=lambda c: "T{}-H{}-E{}-k{}-R{}-G{}".format(*c))
+def test_staggered_batches(case, dev):
+    """Four batches on two streams, each batch's dispatch ordered after the
+    previous batch's dispatch by an event (so it runs beside that batch's
+    combine): every batch still matches the oracle."""
+    T, H, E, k, R, G = case
+    streams = [torch.cuda.Stream(dev) for _ in range(2)]
+    done = [torch.cuda.Event() for _ in range(2)]
+    runs = []
+    for seed in (21, 22, 23, 24):
+        b = gen.make_batch(gen.custom(T, H, E, k, R, G, seed=seed))
+        wl = b.workload
+        say(f"[staggered] {wl.describe()}")
+        plan = cs.Plan(T, H, E, k, R, G, wl.node_dedup)
+        runs.append(dict(
+            b=b, plan=plan, x=to_dev(b.x, dev), idx=to_dev(b.topk_idx, dev), w=to_dev(b.topk_w, dev),
+            recv=torch.full((plan.recv_rows, H), -1, dtype=torch.int16, device=dev),
+            st=(torch.full((plan.staging_rows_max, H), -1, dtype=torch.int16, device=dev)
+                if wl.node_dedup else None),
+            out=torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+    for i, r in enumerate(runs):
+        st = streams[i % 2]
+        r["plan"].route(r["idx"], stream=st)
+        if i > 0:
+            st.wait_event(done[(i - 1) % 2])
+        r["plan"].dispatch(r["x"], r["recv"], r["st"], stream=st)
+        done[i % 2].record(st)
+        r["plan"].combine(r["recv"], r["w"], r["out"], torch.float32, stream=st)
+    torch.cuda.synchronize()
+    for r in runs:
+        b, wl = r["b"], r["b"].workload
+        p = oracle.route_plan(b.topk_idx, E, R, G)
+        assert r["plan"].status() == 0
         recv = bits(r["recv"])
         assert np.array_equal(recv, oracle.dispatch(b.x, p)), "receive rows differ"
         if wl.node_dedup:
