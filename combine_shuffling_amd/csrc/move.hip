@@ -50,6 +50,17 @@
 #ifndef MOE_GSCAN_WAVES_WIDE
 #define MOE_GSCAN_WAVES_WIDE 16  // qwen3 dispatch: 4 -> 166 us, 8 -> 100, 16 -> 90
 #endif
+#ifndef MOE_GSCAN_U
+// wave-items (consecutive segments) per wave of gather_scan, up to 64 experts;
+// olmoe, two batches in flight: 1 -> 50.3 us a step, 2 -> 48.2, 3 -> 48.4, 4 -> 51.1
+#define MOE_GSCAN_U 2
+#endif
+#ifndef MOE_GSCAN8_U
+#define MOE_GSCAN8_U 1  // fp8 olmoe, two batches in flight: 1 -> 32.5 us, 2 -> 33.0, 4 -> 33.4
+#endif
+#ifndef MOE_GSCAN_U_WIDE
+#define MOE_GSCAN_U_WIDE 1  // qwen3, staggered: 1 -> 204.9 us, 2 -> 208.3, 4 -> 212.3
+#endif
 #ifndef MOE_GSCAN_WAVES
 #define MOE_GSCAN_WAVES 8  // olmoe dispatch: 4 -> 32.2 us, 8 -> 30.9, 16 -> 31.4
 #endif
@@ -59,22 +70,23 @@ namespace {
 
 constexpr int kGatherScanWaves = MOE_GSCAN_WAVES;  // waves per gather_scan block when E <= 64
 constexpr int kGatherScanWavesWide = MOE_GSCAN_WAVES_WIDE;  // ... when E > 64
+constexpr int kGatherScanU = MOE_GSCAN_U;           // wave-items per wave, E <= 64
+constexpr int kGatherScanUWide = MOE_GSCAN_U_WIDE;  // ... E > 64
+constexpr int kGatherScan8U = MOE_GSCAN8_U;         // ... fp8 payload (E <= 64)
 constexpr int kStageChunkTokens = MOE_STAGE_CHUNK;  // tokens per hop-1/hop-2 chunk (0: by bytes)
 constexpr int64_t kChunkBytes = (int64_t)MOE_STAGE_CHUNK_MIB << 20;  // staging bytes per chunk, at most
 constexpr int64_t kHierChunkBytes = (int64_t)MOE_HIER_CHUNK_MIB << 20;  // partial bytes per chunk, at most
 
 // The scan folded into the gather of a small plan (nblk * E <=
 // kFusedScanInts; single band).  The block (GB threads, all of which call
-// this) loads the raw tile counts into LDS, sums each expert's column, scans
-// the totals over the experts (one wave with lane shuffles when E <= 64) and
-// returns, in lane j < k of each wave, the receive row of slot j of token t
-// (-1 for a dropped slot): the expert's first row, plus its rows in earlier
-// tiles, plus the slot's rank in its tile.  The same rows route_scan's
-// tile bases give.
+// this) loads the raw tile counts into LDS, sums each expert's column and
+// scans the totals over the experts (one wave with lane shuffles when E <=
+// 64) into s_off.  fused_slot then gives each token's receive rows: the
+// expert's first row, plus its rows in earlier tiles, plus the slot's rank in
+// its tile (the same rows route_scan's tile bases give).
 template <int GB>
-__device__ __forceinline__ int fused_scan_slot(const Dims& d, const int32_t* __restrict__ idx,
-                                               const Work& w, bool live, int t, int* s_mat,
-                                               int* s_off, int* s_wsum, int* s_part) {
+__device__ __forceinline__ void fused_scan_block(const Dims& d, const Work& w, int* s_mat,
+                                                 int* s_off, int* s_wsum, int* s_part) {
   constexpr int kGBlock = GB;
   const int tid = threadIdx.x, lane = threadIdx.x % kWave;
   const int E = d.E, n = d.nblk * E;
@@ -134,8 +146,14 @@ __device__ __forceinline__ int fused_scan_slot(const Dims& d, const int32_t* __r
     __syncthreads();
     block_exclusive_scan(s_off, E, s_wsum);
   }
+}
 
-  // Lane j < k of each wave resolves slot j of the wave's token.
+// After fused_scan_block: lane j < k of the wave returns the receive row of
+// slot j of token t (-1 for a dropped slot).
+__device__ __forceinline__ int fused_slot(const Dims& d, const int32_t* __restrict__ idx,
+                                          const Work& w, bool live, int t, const int* s_mat,
+                                          const int* s_off) {
+  const int lane = threadIdx.x % kWave, E = d.E;
   int mine = -1;
   if (live && lane < d.k) {
     const int64_t at = (int64_t)t * d.k + lane;
@@ -156,8 +174,9 @@ __device__ __forceinline__ int fused_scan_slot(const Dims& d, const int32_t* __r
 // and the prefix over earlier tiles for the experts its tokens use) while
 // those loads are in flight.  The plan's separate scan launch then leaves the
 // critical path (it still runs, lazily, for anything that reads the plan
-// arrays).  Same receive rows as gather_kernel.
-template <int KMAX, int GW>
+// arrays).  Each wave takes U consecutive segments, so a block's scan serves
+// GW * U of them.  Same receive rows as gather_kernel.
+template <int KMAX, int GW, int U>
 __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const int32_t* __restrict__ idx,
                                                                  const u32x4* __restrict__ x,
                                                                  u32x4* __restrict__ recv, Work w) {
@@ -169,31 +188,39 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
   const int items = d.T * d.segs, lane = threadIdx.x % kWave, tid = threadIdx.x;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const bool keep = keep_rows(rows, 2 * d.H);
-  // wave-item g = block * GW + wave (one per wave)
-  Item it;
-  {
-    const int g = __builtin_amdgcn_readfirstlane(blockIdx.x * GW + tid / kWave);
-    it.live = g < items;
-    it.t = it.live ? g / d.segs : 0;
-    it.c = (g - it.t * d.segs) * kWave + lane;
-    it.ok = it.live && it.c < d.chunks;
-  }
-  u32x4 v;
-  if (it.ok) v = load_x_chunk(&x[(int64_t)it.t * d.chunks + it.c]);
-
-  const int mine = fused_scan_slot<kGBlock>(d, idx, w, it.live, it.t, s_mat, s_off, s_wsum, s_part);
-  int slot[KMAX];
+  // wave-items g = (block * GW + wave) * U + u: U consecutive segments
+  Item it[U];
+  u32x4 v[U];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
-
-  if (it.live && it.c == lane && lane < d.k) {  // the first segment publishes the slots
-    w.slot_of[(int64_t)it.t * d.k + lane] = mine;
-    if ((uint32_t)mine < rows) w.row_src[mine] = it.t;
+  for (int u = 0; u < U; ++u) {
+    const int g = __builtin_amdgcn_readfirstlane((blockIdx.x * GW + tid / kWave) * U + u);
+    it[u].live = g < items;
+    it[u].t = it[u].live ? g / d.segs : 0;
+    it[u].c = (g - it[u].t * d.segs) * kWave + lane;
+    it[u].ok = it[u].live && it[u].c < d.chunks;
+    if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
   }
-  if (it.ok) {
+
+  fused_scan_block<kGBlock>(d, w, s_mat, s_off, s_wsum, s_part);
+  int mine = -1;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if ((uint32_t)slot[j] < rows) store_row(&recv[(int64_t)slot[j] * d.chunks + it.c], v, keep);
+  for (int u = 0; u < U; ++u) {
+    if (u == 0 || it[u].t != it[u - 1].t)  // wave-uniform: a new token
+      mine = fused_slot(d, idx, w, it[u].live, it[u].t, s_mat, s_off);
+    int slot[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
+
+    if (it[u].live && it[u].c == lane && lane < d.k) {  // the first segment publishes the slots
+      w.slot_of[(int64_t)it[u].t * d.k + lane] = mine;
+      if ((uint32_t)mine < rows) w.row_src[mine] = it[u].t;
+    }
+    if (it[u].ok) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if ((uint32_t)slot[j] < rows)
+          store_row(&recv[(int64_t)slot[j] * d.chunks + it[u].c], v[u], keep);
+    }
   }
 }
 
@@ -612,7 +639,7 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
 // gather_fp8_kernel for small plans, with the scan folded in as in
 // gather_scan_kernel (GW waves per block): the row loads are issued first,
 // the scan runs while they are in flight.
-template <int KMAX, int GW>
+template <int KMAX, int GW, int U>
 __global__ __launch_bounds__(GW * kWave) void gather_fp8_scan_kernel(Dims d,
                                                                      const int32_t* __restrict__ idx,
                                                                      const u32x4* __restrict__ x,
@@ -628,35 +655,42 @@ __global__ __launch_bounds__(GW * kWave) void gather_fp8_scan_kernel(Dims d,
   const int items = d.T * segs8;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  Item8 it;  // wave-item g = block * GW + wave
-  {
-    const int g = __builtin_amdgcn_readfirstlane(blockIdx.x * GW + threadIdx.x / kWave);
-    it.live = g < items;
-    it.t = it.live ? g / segs8 : 0;
-    it.c0 = (g - it.t * segs8) * kFp8ItemChunks + 2 * lane;
-    it.ok0 = it.live && it.c0 < d.chunks;
-    it.ok1 = it.live && it.c0 + 1 < d.chunks;
-  }
-  u32x4 v0, v1;
-  load_piece(d, it, x, v0, v1);
-  const int mine = fused_scan_slot<GW * kWave>(d, idx, w, it.live, it.t, s_mat, s_off, s_wsum, s_part);
-  int slot[KMAX];
+  const bool keep = keep_rows(rows, d.H);
+  Item8 it[U];  // wave-items g = (block * GW + wave) * U + u
+  u32x4 v0[U], v1[U];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
-  const Fp8Piece q = quantize_loaded(v0, v1);
-  const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
-  const int blk = it.c0 / kFp8BlockChunks;
-  if (it.live && it.c0 == 2 * lane && lane < d.k) {  // first segment publishes the slots
-    w.slot_of[(int64_t)it.t * d.k + lane] = mine;
-    if ((uint32_t)mine < rows) w.row_src[mine] = it.t;
+  for (int u = 0; u < U; ++u) {
+    const int g = __builtin_amdgcn_readfirstlane((blockIdx.x * GW + threadIdx.x / kWave) * U + u);
+    it[u].live = g < items;
+    it[u].t = it[u].live ? g / segs8 : 0;
+    it[u].c0 = (g - it[u].t * segs8) * kFp8ItemChunks + 2 * lane;
+    it[u].ok0 = it[u].live && it[u].c0 < d.chunks;
+    it[u].ok1 = it[u].live && it[u].c0 + 1 < d.chunks;
+    load_piece(d, it[u], x, v0[u], v1[u]);
   }
-  if (it.ok0) {
-    const bool keep = keep_rows(rows, d.H);
+  fused_scan_block<GW * kWave>(d, w, s_mat, s_off, s_wsum, s_part);
+  int mine = -1;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if ((uint32_t)slot[j] < rows) {
-        store_codes(recv8, slot[j], d, it, q.a, q.b, keep);
-        if (scale_lane) rscale[(int64_t)slot[j] * nb + blk] = q.scale;
+  for (int u = 0; u < U; ++u) {
+    if (u == 0 || it[u].t != it[u - 1].t)  // wave-uniform: a new token
+      mine = fused_slot(d, idx, w, it[u].live, it[u].t, s_mat, s_off);
+    int slot[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
+    const Fp8Piece q = quantize_loaded(v0[u], v1[u]);
+    const bool scale_lane = it[u].ok0 && (lane % kFp8BlockLanes) == 0;
+    const int blk = it[u].c0 / kFp8BlockChunks;
+    if (it[u].live && it[u].c0 == 2 * lane && lane < d.k) {  // first segment publishes the slots
+      w.slot_of[(int64_t)it[u].t * d.k + lane] = mine;
+      if ((uint32_t)mine < rows) w.row_src[mine] = it[u].t;
+    }
+    if (it[u].ok0) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if ((uint32_t)slot[j] < rows) {
+          store_codes(recv8, slot[j], d, it[u], q.a, q.b, keep);
+          if (scale_lane) rscale[(int64_t)slot[j] * nb + blk] = q.scale;
+        }
       }
     }
   }
@@ -865,16 +899,19 @@ struct GatherLaunch {
     if (d.fused_scan) {
       // larger blocks where the experts fit one wave: fewer blocks redo the scan
       const int64_t items = (int64_t)d.T * d.segs;
-      if (d.E <= kWave)
-        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWaves>),
-                           dim3((int)((items + kGatherScanWaves - 1) / kGatherScanWaves)),
+      if (d.E <= kWave) {
+        constexpr int per_block = kGatherScanWaves * kGatherScanU;
+        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWaves, kGatherScanU>),
+                           dim3((int)((items + per_block - 1) / per_block)),
                            dim3(kGatherScanWaves * kWave), 0, s, d, idx,
                            reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), w);
-      else
-        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWavesWide>),
-                           dim3((int)((items + kGatherScanWavesWide - 1) / kGatherScanWavesWide)),
+      } else {
+        constexpr int per_block = kGatherScanWavesWide * kGatherScanUWide;
+        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWavesWide, kGatherScanUWide>),
+                           dim3((int)((items + per_block - 1) / per_block)),
                            dim3(kGatherScanWavesWide * kWave), 0, s, d, idx,
                            reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), w);
+      }
     } else
       hipLaunchKernelGGL((gather_kernel<KMAX, kGatherU>), dim3(blocks_for(d, kGatherU)),
                          dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
@@ -945,8 +982,9 @@ struct GatherFp8Launch {
                         float* rscale, const Work& w, hipStream_t s) {
     if (fp8_fused_scan(d)) {
       const int64_t items = (int64_t)d.T * ((d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks);
-      hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScanWaves>),
-                         dim3((int)((items + kGatherScanWaves - 1) / kGatherScanWaves)),
+      constexpr int per_block = kGatherScanWaves * kGatherScan8U;
+      hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScanWaves, kGatherScan8U>),
+                         dim3((int)((items + per_block - 1) / per_block)),
                          dim3(kGatherScanWaves * kWave), 0, s, d, idx,
                          reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
     } else {
