@@ -41,6 +41,12 @@
 #ifndef MOE_STAGE_CHUNK
 #define MOE_STAGE_CHUNK 0
 #endif
+#ifndef MOE_STAGE_A_U
+// wave-items per wave of stage_a.  DeepSeek-V3-like dispatch, one stream:
+// 1 -> 679 us, 2 -> 694, 2 consecutive segments sharing their lookups -> 689,
+// 4 consecutive -> 714
+#define MOE_STAGE_A_U 1
+#endif
 #ifndef MOE_STAGE_CHUNK_MIB
 // DeepSeek-V3-like dispatch, us with two batches in flight / one stream:
 // no chunks 1217 / 1217, 512 MiB 1228 / 1187, 256 MiB 1178 / 1180,
@@ -73,6 +79,7 @@ constexpr int kGatherScanWavesWide = MOE_GSCAN_WAVES_WIDE;  // ... when E > 64
 constexpr int kGatherScanU = MOE_GSCAN_U;           // wave-items per wave, E <= 64
 constexpr int kGatherScanUWide = MOE_GSCAN_U_WIDE;  // ... E > 64
 constexpr int kGatherScan8U = MOE_GSCAN8_U;         // ... fp8 payload (E <= 64)
+constexpr int kStageAU = MOE_STAGE_A_U;  // wave-items per wave of stage_a
 constexpr int kStageChunkTokens = MOE_STAGE_CHUNK;  // tokens per hop-1/hop-2 chunk (0: by bytes)
 constexpr int64_t kChunkBytes = (int64_t)MOE_STAGE_CHUNK_MIB << 20;  // staging bytes per chunk, at most
 constexpr int64_t kHierChunkBytes = (int64_t)MOE_HIER_CHUNK_MIB << 20;  // partial bytes per chunk, at most
@@ -241,16 +248,24 @@ __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* 
   for (int u = 0; u < U; ++u) {
     it[u] = wave_item<U>(d, blockIdx.x, item0, item_end, u);
     lead[u] = 0;
+    // x first, so its latency overlaps the plan lookups (DeepSeek-V3-like
+    // dispatch 715 -> 695 us); non-temporal here (826 -> 794 us with x read
+    // from HBM), while the single-hop gather keeps plain loads
+    if (it[u].ok) v[u] = load_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
     if (it[u].live) {
-      token_slots_serial<KMAX>(d, w, idx, it[u].t, slot[u]);
+      // only a row's first segment publishes the slots: the others skip
+      // their lookups (DeepSeek-V3-like dispatch 756 -> 715 us)
+      if (__builtin_amdgcn_readfirstlane(it[u].c - lane) == 0) {
+        token_slots_serial<KMAX>(d, w, idx, it[u].t, slot[u]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) slot[u][j] = -1;
+      }
       token_stages<KMAX>(d, w, it[u].t, p[u], lead[u]);
     } else {
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) slot[u][j] = p[u][j] = -1;
     }
-    // non-temporal here (measured: DeepSeek-V3-like dispatch 826 -> 794 us
-    // with x read from HBM); the single-hop gather keeps plain loads
-    if (it[u].ok) v[u] = load_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -570,14 +585,6 @@ __device__ __forceinline__ Fp8Piece quantize_loaded(u32x4 v0, u32x4 v1) {
   return Fp8Piece{encode_e4m3x8(f0), encode_e4m3x8(f1), ldexpf(1.0f, e)};
 }
 
-// load_piece, then quantize_loaded.
-__device__ __forceinline__ Fp8Piece quantize_piece(const Dims& d, const Item8& it,
-                                                   const u32x4* __restrict__ x) {
-  u32x4 v0, v1;
-  load_piece(d, it, x, v0, v1);
-  return quantize_loaded(v0, v1);
-}
-
 // 16 codes of a lane from byte offset (row * H + c0 * 8), the inverse of
 // store_codes.
 __device__ __forceinline__ void load_codes(const uint8_t* base, int64_t row, const Dims& d,
@@ -607,6 +614,8 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
   const Item8 it = wave_item8<1>(d, segs8, 0, items, 0);
+  u32x4 v0, v1;  // x first, so its latency overlaps the slot lookups
+  load_piece(d, it, x, v0, v1);
   int slot[KMAX];
   if (it.live) {
     token_slots<KMAX>(d, w, idx, it.t, slot);
@@ -614,7 +623,7 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) slot[j] = -1;
   }
-  const Fp8Piece q = quantize_piece(d, it, x);
+  const Fp8Piece q = quantize_loaded(v0, v1);
   const u32x2 ca = q.a, cb = q.b;
   const float scale = q.scale;
   const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
@@ -711,16 +720,24 @@ __global__ __launch_bounds__(kBlock) void stage_a_fp8_kernel(Dims d, const int32
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
   const Item8 it = wave_item8<1>(d, segs8, item0, item_end, 0);
+  u32x4 v0, v1;  // x first, so its latency overlaps the plan lookups
+  load_piece(d, it, x, v0, v1);
   int slot[KMAX], p[KMAX];
   uint32_t lead = 0;
   if (it.live) {
-    token_slots_serial<KMAX>(d, w, idx, it.t, slot);
+    // only a row's first segment publishes the slots: the others skip them
+    if (__builtin_amdgcn_readfirstlane(it.c0 - 2 * lane) == 0) {
+      token_slots_serial<KMAX>(d, w, idx, it.t, slot);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) slot[j] = -1;
+    }
     token_stages<KMAX>(d, w, it.t, p, lead);
   } else {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) slot[j] = p[j] = -1;
   }
-  const Fp8Piece q = quantize_piece(d, it, x);
+  const Fp8Piece q = quantize_loaded(v0, v1);
   const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
   const int blk = it.c0 / kFp8BlockChunks;
   if (it.live && it.c0 == 2 * lane && lane < d.k) {  // first segment publishes the plan
@@ -941,17 +958,18 @@ struct DedupLaunch {
                         uint16_t* recv, const Work& w, hipStream_t s) {
     const int64_t row_bound = (int64_t)min(d.k, d.N) * 2 * d.H;  // staging bytes per token, at most
     const int chunk = stage_chunk_tokens(d, row_bound);
-    const int per_block = kWaves * kStageU;
+    const int per_block_a = kWaves * kStageAU, per_block_b = kWaves * kStageU;
     const int keep = (int64_t)chunk * row_bound <= kKeepBytes;
     for (int t0 = 0; t0 < d.T; t0 += chunk) {
       const int item0 = t0 * d.segs, item_end = min(d.T, t0 + chunk) * d.segs;
-      const int blocks = (item_end - item0 + per_block - 1) / per_block;
-      hipLaunchKernelGGL((stage_a_kernel<KMAX, kStageU>), dim3(blocks), dim3(kBlock), 0, s, d,
+      const int blocks_a = (item_end - item0 + per_block_a - 1) / per_block_a;
+      const int blocks_b = (item_end - item0 + per_block_b - 1) / per_block_b;
+      hipLaunchKernelGGL((stage_a_kernel<KMAX, kStageAU>), dim3(blocks_a), dim3(kBlock), 0, s, d,
                          idx, reinterpret_cast<const u32x4*>(x),
                          reinterpret_cast<u32x4*>(staging), w, item0, item_end, keep);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((stage_b_kernel<KMAX, kStageU>), dim3(blocks), dim3(kBlock), 0, s, d,
+      hipLaunchKernelGGL((stage_b_kernel<KMAX, kStageU>), dim3(blocks_b), dim3(kBlock), 0, s, d,
                          reinterpret_cast<const u32x4*>(staging), reinterpret_cast<u32x4*>(recv), w,
                          item0, item_end);
       e = hipGetLastError();

@@ -42,7 +42,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = MOE_MOVE_WAVES;   // waves per block
 constexpr int kBlock = kWaves * kWave;
 constexpr int kGatherU = MOE_GATHER_U;    // wave-items per wave: gather
-constexpr int kStageU = MOE_STAGE_U;      // wave-items per wave: stage_a, stage_b
+constexpr int kStageU = MOE_STAGE_U;      // wave-items per wave: stage_b (stage_a in move.hip)
 constexpr int kCombineU = MOE_COMBINE_U;  // wave-items per wave: combine
 constexpr int kCombine8U = MOE_COMBINE8_U; // wave-items per wave: combine of an fp8 payload
 
@@ -162,6 +162,7 @@ __device__ __forceinline__ void gather_chunk(const Dims& d, const int32_t* idx, 
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) slot[u][j] = -1;
     }
+    // after the slot loads (loading x first: nondiv gather 152.6 -> 158.8 us)
     if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
   }
 #pragma unroll
