@@ -210,12 +210,11 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
     d.band = c.band_tokens;
     d.tpb = d.band / d.tile;
     d.nbands = (int32_t)((T + d.band - 1) / d.band);
-    if ((int64_t)d.tpb * d.E > moe::kScanLdsIntsStatic || d.nbands > 192) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)d.tpb * d.E > moe::kBandScanLdsInts || d.nbands > 192) return MOE_ERR_UNSUPPORTED;
   } else {
     // At most kMaxPlanTiles tiles, and few enough that the scan kernel holds
     // the [tiles x experts] (and [tiles x staging keys]) count matrix in LDS.
-    const int64_t lds_ints = load_aware ? moe::kScanLdsInts : moe::kScanLdsIntsStatic;
-    const int64_t max_tiles = std::min<int64_t>(moe::kMaxPlanTiles, lds_ints / widest);
+    const int64_t max_tiles = std::min<int64_t>(moe::kMaxPlanTiles, moe::kScanLdsInts / widest);
     const int64_t per_tile_cap = (int64_t)moe::kPlanBlock * max_tiles;
     d.passes = (int32_t)std::max<int64_t>(1, (T + per_tile_cap - 1) / per_tile_cap);
     d.tile = moe::kPlanBlock * d.passes;

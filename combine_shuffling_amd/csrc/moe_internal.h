@@ -16,13 +16,15 @@ constexpr int kPlanBlock = 256;    // threads per route-plan block = tokens per 
 constexpr int kPlanWaves = kPlanBlock / kWave;
 constexpr int kMaxPlanTiles = 64;  // route-plan tiles (blocks) at most
 // Tile-count matrix the scan holds in LDS (64 KiB of gfx950's 160 KiB per
-// workgroup).  Load-aware plans use all of it: their [tiles x (owner, node)]
-// matrix then takes 32 two-pass tiles instead of 16 four-pass ones on the
-// DeepSeek-V3-like workload (route 57.6 -> 45 us).  Other plans stay within
-// half: more tiles made the static dedup dispatch 7 us slower than the 4 us
-// they saved in the route.
+// workgroup).  More, smaller tiles shorten the count kernel: on the
+// DeepSeek-V3-like workload the [tiles x (owner, node)] matrix of load-aware
+// forwarders takes 32 two-pass tiles instead of 16 four-pass ones (route 57.6
+// -> 45 us), and the static plan's [tiles x experts] matrix 64 one-pass tiles
+// instead of 32 two-pass ones (route 27.4 -> 23.1 us).
 constexpr int kScanLdsInts = 16384;
-constexpr int kScanLdsIntsStatic = kScanLdsInts / 2;
+// A band's matrix in the banded pipeline, whose dynamic LDS stays under the
+// default 64 KiB limit.
+constexpr int kBandScanLdsInts = kScanLdsInts / 2;
 // Tile-count matrices up to this size are scanned in the gather (measured,
 // one stream: olmoe 16 x 64 gains 2 us per step; qwen3's 32 x 128, with
 // 16-wave gather blocks, 8 us; nondiv's 64 x 100 loses 14 us, as every

@@ -61,6 +61,9 @@
 // olmoe, two batches in flight: 1 -> 50.3 us a step, 2 -> 48.2, 3 -> 48.4, 4 -> 51.1
 #define MOE_GSCAN_U 2
 #endif
+#ifndef MOE_GSCAN8_WAVES
+#define MOE_GSCAN8_WAVES MOE_GSCAN_WAVES
+#endif
 #ifndef MOE_GSCAN8_U
 #define MOE_GSCAN8_U 1  // fp8 olmoe, two batches in flight: 1 -> 32.5 us, 2 -> 33.0, 4 -> 33.4
 #endif
@@ -79,6 +82,7 @@ constexpr int kGatherScanWavesWide = MOE_GSCAN_WAVES_WIDE;  // ... when E > 64
 constexpr int kGatherScanU = MOE_GSCAN_U;           // wave-items per wave, E <= 64
 constexpr int kGatherScanUWide = MOE_GSCAN_U_WIDE;  // ... E > 64
 constexpr int kGatherScan8U = MOE_GSCAN8_U;         // ... fp8 payload (E <= 64)
+constexpr int kGatherScan8Waves = MOE_GSCAN8_WAVES;  // waves per gather_fp8_scan block
 constexpr int kStageAU = MOE_STAGE_A_U;  // wave-items per wave of stage_a
 constexpr int kStageChunkTokens = MOE_STAGE_CHUNK;  // tokens per hop-1/hop-2 chunk (0: by bytes)
 constexpr int64_t kChunkBytes = (int64_t)MOE_STAGE_CHUNK_MIB << 20;  // staging bytes per chunk, at most
@@ -1000,10 +1004,10 @@ struct GatherFp8Launch {
                         float* rscale, const Work& w, hipStream_t s) {
     if (fp8_fused_scan(d)) {
       const int64_t items = (int64_t)d.T * ((d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks);
-      constexpr int per_block = kGatherScanWaves * kGatherScan8U;
-      hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScanWaves, kGatherScan8U>),
+      constexpr int per_block = kGatherScan8Waves * kGatherScan8U;
+      hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScan8Waves, kGatherScan8U>),
                          dim3((int)((items + per_block - 1) / per_block)),
-                         dim3(kGatherScanWaves * kWave), 0, s, d, idx,
+                         dim3(kGatherScan8Waves * kWave), 0, s, d, idx,
                          reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
     } else {
       hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s,
