@@ -355,7 +355,7 @@ moe_status moe_combine_hier(moe_plan* plan, const uint16_t* y, const float* topk
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe_status st = moe::ensure_assigned(plan, s);
   if (st != MOE_OK) return st;
-  return moe::from_hip(moe::launch_combine_hier(plan->d, plan->idx, y, topk_w, partials, out,
+  return moe::from_hip(moe::launch_combine_hier(plan->d, y, topk_w, partials, out,
                                                 out_dtype == MOE_OUT_F32, plan->work, s));
 }
 

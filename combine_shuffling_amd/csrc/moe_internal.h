@@ -135,7 +135,7 @@ hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* wts, vo
                           bool out_f32, const Work& w, hipStream_t s);
 // Two-hop combine of a node-deduplicated plan: fp32 partial per staging row,
 // then the sum over the token's nodes.  part: [smax, H] float32.
-hipError_t launch_combine_hier(const Dims& d, const int32_t* idx, const uint16_t* y,
+hipError_t launch_combine_hier(const Dims& d, const uint16_t* y,
                                const float* wts, float* part, void* out, bool out_f32,
                                const Work& w, hipStream_t s);
 // Banded pipeline: route, dispatch and combine (identity expert) of every
