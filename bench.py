@@ -21,12 +21,14 @@ Prints one JSON line.
   value       algorithmic payload bytes per step / wall time per step, over K
               steps bracketed by synchronize on both sides, no timing events
               inside.  Schedule (--inflight auto): after the warmup, a short
-              trial of three schedules picks the fastest: serial (the steps
+              trial of four schedules picks the fastest: serial (the steps
               one after another on one stream), two_in_flight (step i on
-              stream i mod 2, each stream in order) and staggered (as
+              stream i mod 2, each stream in order), staggered (as
               two_in_flight, with each step's dispatch waiting on an event
               after the previous step's dispatch, so a dispatch always runs
-              beside the other batch's combine).  The K timed steps run in the
+              beside the other batch's combine) and plan_ahead (dispatch and
+              combine on one stream, each step's route plan on a second
+              stream while the previous step moves its rows).  The K timed steps run in the
               chosen one; K steps of each other schedule are timed too and
               reported beside it.
   phases      route plan, dispatch and combine timed inside K more steps
@@ -81,7 +83,7 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20   # MI355X last-level cache (AMD Infinity Cache)
 MAX_SETS = 256
 METRIC = "dispatch+combine effective GB/s and % of HBM peak, 1 MI355X"
-SCHEDULES = ("serial", "two_in_flight", "staggered")
+SCHEDULES = ("serial", "two_in_flight", "staggered", "plan_ahead")
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("combine_shuffling_amd/csrc/move.hip", "combine_shuffling_amd/csrc/move_body.h",
                   "combine_shuffling_amd/csrc/pipeline.hip", "combine_shuffling_amd/csrc/plan_body.h",
@@ -112,13 +114,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
-    ap.add_argument("--inflight", default="auto", choices=("auto", "1", "2", "staggered"),
+    ap.add_argument("--inflight", default="auto", choices=("auto", "1", "2", "staggered", "plan_ahead"),
                     help="schedule of the steps.  1: one stream, every step after the previous "
                          "one.  2: two batches in flight, step i on HIP stream i mod 2, each "
                          "stream running its steps in order.  staggered: as 2, but each step's "
                          "dispatch waits for the previous step's dispatch, so a dispatch always "
-                         "overlaps the other batch's combine.  auto (default): a short trial of "
-                         "the three after the warmup picks the fastest for the timed steps")
+                         "overlaps the other batch's combine.  plan_ahead: dispatch and combine "
+                         "on one stream, each step's route plan on a second stream during the "
+                         "previous step's movement.  auto (default): a short trial of the four "
+                         "after the warmup picks the fastest for the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) a few "
                          "times, to scale hardware byte counters against a known size")
@@ -428,14 +432,38 @@ def main():
         done[i % 2].record(st)
         do_combine(s, st)
 
+    def plan_ahead_steps(steps):
+        """Step i's dispatch and combine on stream 0; its route plan on
+        stream 1, during step i - 1's dispatch and combine (the event moving
+        orders it after step i - 2, the last user of its buffer set)."""
+        main, side = streams[0], streams[1]
+        routed = [torch.cuda.Event(), torch.cuda.Event()]
+        moving = torch.cuda.Event()
+        sets[0]["plan"].route(sets[0]["idx"], stream=side)
+        routed[0].record(side)
+        for i in range(steps):
+            s = sets[i % n_sets]
+            main.wait_event(routed[i % 2])
+            moving.record(main)
+            do_dispatch(s, main)
+            do_combine(s, main)
+            if i + 1 < steps:
+                s1 = sets[(i + 1) % n_sets]
+                side.wait_event(moving)
+                s1["plan"].route(s1["idx"], stream=side)
+                routed[(i + 1) % 2].record(side)
+
     def timed_steps(schedule, steps=None):
         """Wall time per step of K steps in one schedule: "serial" (one
-        stream), "two_in_flight" (step i on stream i % 2) or "staggered"."""
+        stream), "two_in_flight" (step i on stream i % 2), "staggered" or
+        "plan_ahead"."""
         steps = args.steps if steps is None else steps
         done = [torch.cuda.Event(), torch.cuda.Event()]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
+        if schedule == "plan_ahead":
+            plan_ahead_steps(steps)
+        for i in range(steps if schedule != "plan_ahead" else 0):
             if schedule == "staggered":
                 staggered_step(i, done)
             else:
@@ -455,7 +483,7 @@ def main():
         trial = {name: timed_steps(name, n_trial) for name in SCHEDULES}
         schedule = min(trial, key=trial.get)
     else:
-        schedule = "staggered" if args.inflight == "staggered" else "two_in_flight"
+        schedule = {"2": "two_in_flight"}.get(args.inflight, args.inflight)
     inflight = 1 if schedule == "serial" else 2
     D = int(sets[0]["plan"].read("num_staged")[0]) if wl.node_dedup else 0
     fwd_rows = None
@@ -584,6 +612,7 @@ def main():
                    "pct_of_hbm_peak": round(100.0 * serial_value / HBM_PEAK_GBS, 2)},
         "two_in_flight": schedule_entry("two_in_flight"),
         "staggered": schedule_entry("staggered"),
+        "plan_ahead": schedule_entry("plan_ahead"),
         "schedule_trial_ms_per_step": (None if trial is None else
                                        {k2: round(v2, 5) for k2, v2 in trial.items()}),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),

@@ -1,5 +1,6 @@
-"""Two batches in flight: independent plans on two HIP streams, free-running
-or staggered (each dispatch after the previous batch's dispatch).
+"""Two batches in flight: independent plans on two HIP streams, free-running,
+staggered (each dispatch after the previous batch's dispatch) or planned
+ahead (each route plan on a side stream while the previous batch moves).
 
 A caller may keep a second batch's route plan, dispatch and combine running
 on another stream while the first batch's are still running (the library
@@ -106,6 +107,52 @@ def test_staggered_batches(case, dev):
         r["plan"].dispatch(r["x"], r["recv"], r["st"], stream=st)
         done[i % 2].record(st)
         r["plan"].combine(r["recv"], r["w"], r["out"], torch.float32, stream=st)
+    torch.cuda.synchronize()
+    for r in runs:
+        b, wl = r["b"], r["b"].workload
+        p = oracle.route_plan(b.topk_idx, E, R, G)
+        assert r["plan"].status() == 0
+        recv = bits(r["recv"])
+        assert np.array_equal(recv, oracle.dispatch(b.x, p)), "receive rows differ"
+        if wl.node_dedup:
+            D = p["num_staged"]
+            assert np.array_equal(bits(r["st"])[:D], oracle.dedup_stage_a(b.x, p))
+        check_combine(r["out"].cpu().numpy(), recv, b.topk_w, p["slot_of"], True, wl.name)
+
+
+@pytest.mark.parametrize("case", CASES[1:3], ids=lambda c: "T{}-H{}-E{}-k{}-R{}-G{}".format(*c))
+def test_plan_ahead_batches(case, dev):
+    """Four batches: dispatch and combine on one stream, each batch's route
+    plan on a second stream while the previous batch moves (ordered by
+    events both ways): every batch still matches the oracle."""
+    T, H, E, k, R, G = case
+    main, side = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    routed = [torch.cuda.Event() for _ in range(2)]
+    moving = torch.cuda.Event()
+    runs = []
+    for seed in (31, 32, 33, 34):
+        b = gen.make_batch(gen.custom(T, H, E, k, R, G, seed=seed))
+        wl = b.workload
+        say(f"[plan ahead] {wl.describe()}")
+        plan = cs.Plan(T, H, E, k, R, G, wl.node_dedup)
+        runs.append(dict(
+            b=b, plan=plan, x=to_dev(b.x, dev), idx=to_dev(b.topk_idx, dev), w=to_dev(b.topk_w, dev),
+            recv=torch.full((plan.recv_rows, H), -1, dtype=torch.int16, device=dev),
+            st=(torch.full((plan.staging_rows_max, H), -1, dtype=torch.int16, device=dev)
+                if wl.node_dedup else None),
+            out=torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+    runs[0]["plan"].route(runs[0]["idx"], stream=side)
+    routed[0].record(side)
+    for i, r in enumerate(runs):
+        main.wait_event(routed[i % 2])
+        moving.record(main)
+        r["plan"].dispatch(r["x"], r["recv"], r["st"], stream=main)
+        r["plan"].combine(r["recv"], r["w"], r["out"], torch.float32, stream=main)
+        if i + 1 < len(runs):
+            side.wait_event(moving)
+            runs[i + 1]["plan"].route(runs[i + 1]["idx"], stream=side)
+            routed[(i + 1) % 2].record(side)
     torch.cuda.synchronize()
     for r in runs:
         b, wl = r["b"], r["b"].workload
