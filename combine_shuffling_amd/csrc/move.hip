@@ -48,9 +48,10 @@
 #define MOE_STAGE_A_U 1
 #endif
 #ifndef MOE_STAGE_CHUNK_MIB
-// DeepSeek-V3-like dispatch, us with two batches in flight / one stream:
-// no chunks 1217 / 1217, 512 MiB 1228 / 1187, 256 MiB 1178 / 1180,
-// 224 MiB (8 chunks) 1142 / 1181, 128 MiB 1107 / 1265
+// DeepSeek-V3-like dispatch, us with two batches in flight / one stream
+// (before stage A skipped its unused lookups): no chunks 1217 / 1217,
+// 512 MiB 1228 / 1187, 256 MiB 1178 / 1180, 224 MiB (8 chunks) 1142 / 1181,
+// 128 MiB 1107 / 1265
 #define MOE_STAGE_CHUNK_MIB 224
 #endif
 #ifndef MOE_GSCAN_WAVES_WIDE
