@@ -48,6 +48,7 @@ Prints one JSON line.
               traffic = HBM bytes per launch from the rocprofv3 FETCH_SIZE /
               WRITE_SIZE summary under profiles/, scaled by the copy
               calibration; null if the kernel sources changed since.
+              traffic_over_algorithmic: above 1 means bytes moved twice.
   copy_ceiling a plain device-to-device copy (torch copy_) moving the step's
               bytes, half read and half written, over source/destination
               pairs cycled past the MALL, K times: a practical ceiling, and
@@ -630,6 +631,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": traffic_kernel or dom[0], "achieved": round(dom[3], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "traffic_over_algorithmic": (None if traffic is None or not dom[1] else
+                                                  round(traffic / dom[1], 4)),
                      "bytes_per_launch": dom[1], "ms_per_launch": round(float(dom[2]), 5),
                      "event_gap_ms": round(event_gap_ms, 5)},
         "cpu_baseline": None,
