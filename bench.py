@@ -66,6 +66,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import hashlib
 import json
 import math
@@ -112,6 +113,9 @@ def parse():
                          "tokens in one persistent launch (banded plan)")
     ap.add_argument("--band-tokens", type=int, default=2048,
                     help="tokens per band with --pipeline (a multiple of 256)")
+    ap.add_argument("--single-hop", action="store_true",
+                    help="plan a workload with virtual nodes (dsv3) as one node: the same routing "
+                         "moved by the single-hop gather, the lower bound on its bytes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
@@ -344,6 +348,9 @@ def main():
     wl = gen.get(args.workload)
     fp8 = args.payload == "fp8"
     batch = gen.make_batch(wl)
+    if args.single_hop and wl.node_dedup:
+        # the same routing, planned as one node: dispatch is the single-hop gather
+        wl = dataclasses.replace(wl, name=wl.name + "-single-hop", ranks_per_node=wl.num_ranks)
     T, H, k = wl.num_tokens, wl.hidden, wl.top_k
 
     x0 = torch.from_numpy(batch.x.view(np.int16)).to(dev)
@@ -585,7 +592,8 @@ def main():
     copy["value_over_copy"] = round(value / copy["GB/s"], 4)
 
     # which committed traffic summary covers this run
-    variant = "_pipeline" if pipe else "_fp8" if fp8 else "_hier" if hier else ""
+    variant = ("_pipeline" if pipe else "_fp8" if fp8 else "_hier" if hier else
+               "_single_hop" if wl.name.endswith("-single-hop") else "")
     traffic_kernel, traffic = recorded_traffic(args.workload + variant, dom[0])
     result = {
         "metric": METRIC,
