@@ -181,7 +181,9 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   const bool banded = c.band_tokens > 0 && c.band_tokens < T;
   if (banded && dedup) return MOE_ERR_UNSUPPORTED;
   const int64_t staging_max = dedup ? T * std::min<int64_t>(c.top_k, nodes) : 0;
-  const int64_t lim = INT32_MAX;
+  // Row and wave-item numbers are 32-bit; the last block of a launch numbers
+  // a few wave-items past the end before it finds them dead, so keep 4096 clear.
+  const int64_t lim = (int64_t)INT32_MAX - 4096;
   if (T * c.top_k >= lim || T * chunks >= lim || staging_max * chunks >= lim)
     return MOE_ERR_UNSUPPORTED;
 

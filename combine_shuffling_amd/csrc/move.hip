@@ -191,22 +191,23 @@ __device__ __forceinline__ int fused_slot(const Dims& d, const int32_t* __restri
 template <int KMAX, int GW, int U>
 __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const int32_t* __restrict__ idx,
                                                                  const u32x4* __restrict__ x,
-                                                                 u32x4* __restrict__ recv, Work w) {
+                                                                 u32x4* __restrict__ recv, Work w,
+                                                                 int base, int limit) {
   constexpr int kGBlock = GW * kWave;
   __shared__ int s_mat[kFusedScanInts];   // tile counts [nblk][E]
   __shared__ int s_off[MOE_MAX_EXPERTS];  // first receive row of each expert
   __shared__ int s_wsum[GW];
   __shared__ int s_part[GW * kWave];      // column parts (more than 64 experts)
-  const int items = d.T * d.segs, lane = threadIdx.x % kWave, tid = threadIdx.x;
+  const int lane = threadIdx.x % kWave, tid = threadIdx.x;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const bool keep = keep_rows(rows, 2 * d.H);
-  // wave-items g = (block * GW + wave) * U + u: U consecutive segments
+  // wave-items g = base + (block * GW + wave) * U + u: U consecutive segments
   Item it[U];
   u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int g = __builtin_amdgcn_readfirstlane((blockIdx.x * GW + tid / kWave) * U + u);
-    it[u].live = g < items;
+    const int g = __builtin_amdgcn_readfirstlane(base + (blockIdx.x * GW + tid / kWave) * U + u);
+    it[u].live = g < limit;
     it[u].t = it[u].live ? g / d.segs : 0;
     it[u].c = (g - it[u].t * d.segs) * kWave + lane;
     it[u].ok = it[u].live && it[u].c < d.chunks;
@@ -614,13 +615,13 @@ template <int KMAX>
 __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
                                                             const u32x4* __restrict__ x,
                                                             uint8_t* __restrict__ recv8,
-                                                            float* __restrict__ rscale, Work w) {
+                                                            float* __restrict__ rscale, Work w,
+                                                            int base, int limit) {
   const int lane = threadIdx.x % kWave;
   const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
-  const int items = d.T * segs8;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  const Item8 it = wave_item8<1>(d, segs8, 0, items, 0);
+  const Item8 it = wave_item8<1>(d, segs8, base, limit, 0);
   u32x4 v0, v1;  // x first, so its latency overlaps the slot lookups
   load_piece(d, it, x, v0, v1);
   int slot[KMAX];
@@ -661,23 +662,22 @@ __global__ __launch_bounds__(GW * kWave) void gather_fp8_scan_kernel(Dims d,
                                                                      const u32x4* __restrict__ x,
                                                                      uint8_t* __restrict__ recv8,
                                                                      float* __restrict__ rscale,
-                                                                     Work w) {
+                                                                     Work w, int base, int limit) {
   __shared__ int s_mat[kFusedScanInts];
   __shared__ int s_off[MOE_MAX_EXPERTS];
   __shared__ int s_wsum[GW];
   __shared__ int s_part[GW * kWave];
   const int lane = threadIdx.x % kWave;
   const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
-  const int items = d.T * segs8;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
   const bool keep = keep_rows(rows, d.H);
-  Item8 it[U];  // wave-items g = (block * GW + wave) * U + u
+  Item8 it[U];  // wave-items g = base + (block * GW + wave) * U + u
   u32x4 v0[U], v1[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int g = __builtin_amdgcn_readfirstlane((blockIdx.x * GW + threadIdx.x / kWave) * U + u);
-    it[u].live = g < items;
+    const int g = __builtin_amdgcn_readfirstlane(base + (blockIdx.x * GW + threadIdx.x / kWave) * U + u);
+    it[u].live = g < limit;
     it[u].t = it[u].live ? g / segs8 : 0;
     it[u].c0 = (g - it[u].t * segs8) * kFp8ItemChunks + 2 * lane;
     it[u].ok0 = it[u].live && it[u].c0 < d.chunks;
@@ -832,8 +832,8 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_kernel(Dims d, const u32x2
                                                              const float* __restrict__ yscale,
                                                              const float* __restrict__ wts,
                                                              const int32_t* __restrict__ slot_of,
-                                                             void* __restrict__ out) {
-  const int items = d.T * d.segs;
+                                                             void* __restrict__ out, int base,
+                                                             int limit) {
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
   Item it[U];
@@ -842,7 +842,7 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_kernel(Dims d, const u32x2
   u32x2 v[U][KMAX];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, items, u);
+    it[u] = wave_item<U>(d, blockIdx.x, base, limit, u);
     const int64_t at = (int64_t)it[u].t * d.k;
     const int blk = it[u].c / kFp8BlockChunks;
     int sj[KMAX];
@@ -897,15 +897,17 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_kernel(Dims d, const u32x2
   }
 }
 
-inline int blocks_for8(const Dims& d, int per_wave) {
-  const int64_t segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
-  const int64_t items = (int64_t)d.T * segs8, per_block = (int64_t)kWaves * per_wave;
-  return (int)((items + per_block - 1) / per_block);
-}
-
-inline int blocks_for(const Dims& d, int per_wave) {
-  const int64_t items = (int64_t)d.T * d.segs, per_block = (int64_t)kWaves * per_wave;
-  return (int)((items + per_block - 1) / per_block);
+// Launches f(grid, base, limit) over wave-items [0, items), at most
+// kMaxLaunchItems a launch, per_block wave-items a block.
+template <typename F>
+hipError_t launch_ranges(int64_t items, int per_block, F f) {
+  for (int64_t base = 0; base < items; base += kMaxLaunchItems) {
+    const int64_t limit = std::min<int64_t>(items, base + kMaxLaunchItems);
+    f(dim3((unsigned)((limit - base + per_block - 1) / per_block)), (int)base, (int)limit);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <template <int> class Launch, typename... A>
@@ -920,27 +922,25 @@ template <int KMAX>
 struct GatherLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* recv,
                         const Work& w, hipStream_t s) {
+    const int64_t items = (int64_t)d.T * d.segs;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    u32x4* rv = reinterpret_cast<u32x4*>(recv);
     if (d.fused_scan) {
       // larger blocks where the experts fit one wave: fewer blocks redo the scan
-      const int64_t items = (int64_t)d.T * d.segs;
-      if (d.E <= kWave) {
-        constexpr int per_block = kGatherScanWaves * kGatherScanU;
-        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWaves, kGatherScanU>),
-                           dim3((int)((items + per_block - 1) / per_block)),
-                           dim3(kGatherScanWaves * kWave), 0, s, d, idx,
-                           reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), w);
-      } else {
-        constexpr int per_block = kGatherScanWavesWide * kGatherScanUWide;
-        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWavesWide, kGatherScanUWide>),
-                           dim3((int)((items + per_block - 1) / per_block)),
-                           dim3(kGatherScanWavesWide * kWave), 0, s, d, idx,
-                           reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), w);
-      }
-    } else
-      hipLaunchKernelGGL((gather_kernel<KMAX, kGatherU>), dim3(blocks_for(d, kGatherU)),
-                         dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
-                         reinterpret_cast<u32x4*>(recv), w);
-    return hipGetLastError();
+      if (d.E <= kWave)
+        return launch_ranges(items, kGatherScanWaves * kGatherScanU, [&](dim3 g, int b, int l) {
+          hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWaves, kGatherScanU>), g,
+                             dim3(kGatherScanWaves * kWave), 0, s, d, idx, xv, rv, w, b, l);
+        });
+      return launch_ranges(items, kGatherScanWavesWide * kGatherScanUWide, [&](dim3 g, int b, int l) {
+        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWavesWide, kGatherScanUWide>), g,
+                           dim3(kGatherScanWavesWide * kWave), 0, s, d, idx, xv, rv, w, b, l);
+      });
+    }
+    return launch_ranges(items, kWaves * kGatherU, [&](dim3 g, int b, int l) {
+      hipLaunchKernelGGL((gather_kernel<KMAX, kGatherU>), g, dim3(kBlock), 0, s, d, idx, xv, rv, w,
+                         b, l);
+    });
   }
 };
 
@@ -990,14 +990,15 @@ template <int KMAX>
 struct CombineLaunch {
   static hipError_t run(const Dims& d, const uint16_t* y, const float* wts, void* out, bool f32,
                         const Work& w, hipStream_t s) {
-    const dim3 grid(blocks_for(d, kCombineU));
-    if (f32)
-      hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, true>), grid, dim3(kBlock), 0, s, d,
-                         reinterpret_cast<const u32x4*>(y), wts, w.slot_of, out);
-    else
-      hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, false>), grid, dim3(kBlock), 0, s, d,
-                         reinterpret_cast<const u32x4*>(y), wts, w.slot_of, out);
-    return hipGetLastError();
+    const u32x4* yv = reinterpret_cast<const u32x4*>(y);
+    return launch_ranges((int64_t)d.T * d.segs, kWaves * kCombineU, [&](dim3 g, int b, int l) {
+      if (f32)
+        hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, true>), g, dim3(kBlock), 0, s, d, yv,
+                           wts, w.slot_of, out, b, l);
+      else
+        hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, false>), g, dim3(kBlock), 0, s, d, yv,
+                           wts, w.slot_of, out, b, l);
+    });
   }
 };
 
@@ -1005,18 +1006,18 @@ template <int KMAX>
 struct GatherFp8Launch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* recv8,
                         float* rscale, const Work& w, hipStream_t s) {
-    if (fp8_fused_scan(d)) {
-      const int64_t items = (int64_t)d.T * ((d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks);
-      constexpr int per_block = kGatherScan8Waves * kGatherScan8U;
-      hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScan8Waves, kGatherScan8U>),
-                         dim3((int)((items + per_block - 1) / per_block)),
-                         dim3(kGatherScan8Waves * kWave), 0, s, d, idx,
-                         reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
-    } else {
-      hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), dim3(blocks_for8(d, 1)), dim3(kBlock), 0, s,
-                         d, idx, reinterpret_cast<const u32x4*>(x), recv8, rscale, w);
-    }
-    return hipGetLastError();
+    const int64_t items = (int64_t)d.T * ((d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks);
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    if (fp8_fused_scan(d))
+      return launch_ranges(items, kGatherScan8Waves * kGatherScan8U, [&](dim3 g, int b, int l) {
+        hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScan8Waves, kGatherScan8U>), g,
+                           dim3(kGatherScan8Waves * kWave), 0, s, d, idx, xv, recv8, rscale, w, b,
+                           l);
+      });
+    return launch_ranges(items, kWaves, [&](dim3 g, int b, int l) {
+      hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), g, dim3(kBlock), 0, s, d, idx, xv, recv8,
+                         rscale, w, b, l);
+    });
   }
 };
 
@@ -1052,15 +1053,15 @@ template <int KMAX>
 struct CombineFp8Launch {
   static hipError_t run(const Dims& d, const uint8_t* y8, const float* yscale, const float* wts,
                         void* out, bool f32, const Work& w, hipStream_t s) {
-    const dim3 grid(blocks_for(d, kCombine8U));
     const u32x2* y = reinterpret_cast<const u32x2*>(y8);
-    if (f32)
-      hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, true>), grid, dim3(kBlock), 0, s, d,
-                         y, yscale, wts, w.slot_of, out);
-    else
-      hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, false>), grid, dim3(kBlock), 0, s,
-                         d, y, yscale, wts, w.slot_of, out);
-    return hipGetLastError();
+    return launch_ranges((int64_t)d.T * d.segs, kWaves * kCombine8U, [&](dim3 g, int b, int l) {
+      if (f32)
+        hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, true>), g, dim3(kBlock), 0, s, d, y,
+                           yscale, wts, w.slot_of, out, b, l);
+      else
+        hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, false>), g, dim3(kBlock), 0, s, d,
+                           y, yscale, wts, w.slot_of, out, b, l);
+    });
   }
 };
 

@@ -45,6 +45,10 @@ constexpr int kGatherU = MOE_GATHER_U;    // wave-items per wave: gather
 constexpr int kStageU = MOE_STAGE_U;      // wave-items per wave: stage_b (stage_a in move.hip)
 constexpr int kCombineU = MOE_COMBINE_U;  // wave-items per wave: combine
 constexpr int kCombine8U = MOE_COMBINE8_U; // wave-items per wave: combine of an fp8 payload
+// Wave-items per launch at most: a grid is sized in work-items, a 32-bit count,
+// so a batch of more wave-items is moved in several launches (2^24 items of
+// at most 64 threads each).
+constexpr int64_t kMaxLaunchItems = (int64_t)1 << 24;
 
 // Rows are touched once per call: stream them past the caches (measured
 // faster on gfx950 for both the row reads and the row writes).
@@ -128,10 +132,6 @@ __device__ __forceinline__ Item wave_item(const Dims& d, int blk, int base, int 
   return it;
 }
 
-template <int U>
-__device__ __forceinline__ Item wave_item(const Dims& d, int items, int u) {
-  return wave_item<U>(d, blockIdx.x, 0, items, u);
-}
 
 // Lane j (< k) writes the token's entry j of a per-slot plan array.
 template <int KMAX>
@@ -182,11 +182,13 @@ __device__ __forceinline__ void gather_chunk(const Dims& d, const int32_t* idx, 
   }
 }
 
+// Wave-items [base, limit) of the batch (one launch of at most kMaxLaunchItems).
 template <int KMAX, int U>
 __global__ __launch_bounds__(kBlock) void gather_kernel(Dims d, const int32_t* __restrict__ idx,
                                                         const u32x4* __restrict__ x,
-                                                        u32x4* __restrict__ recv, Work w) {
-  gather_chunk<KMAX, U>(d, idx, x, recv, w, blockIdx.x, 0, d.T * d.segs);
+                                                        u32x4* __restrict__ recv, Work w, int base,
+                                                        int limit) {
+  gather_chunk<KMAX, U>(d, idx, x, recv, w, blockIdx.x, base, limit);
 }
 
 __device__ __forceinline__ void unpack_bf16(u32x4 v, float (&f)[8]) {
@@ -269,12 +271,13 @@ __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, con
   }
 }
 
+// Wave-items [base, limit) of the batch (one launch of at most kMaxLaunchItems).
 template <int KMAX, int U, bool F32OUT>
 __global__ __launch_bounds__(kBlock) void combine_kernel(Dims d, const u32x4* __restrict__ y,
                                                          const float* __restrict__ wts,
                                                          const int32_t* __restrict__ slot_of,
-                                                         void* __restrict__ out) {
-  combine_chunk<KMAX, U, F32OUT>(d, y, wts, slot_of, out, blockIdx.x, 0, d.T * d.segs);
+                                                         void* __restrict__ out, int base, int limit) {
+  combine_chunk<KMAX, U, F32OUT>(d, y, wts, slot_of, out, blockIdx.x, base, limit);
 }
 
 }  // namespace

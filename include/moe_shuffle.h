@@ -91,7 +91,10 @@ typedef enum moe_status {
 } moe_status;
 
 /* Limits: E <= 1024, 1 <= k <= 16, k <= E, R <= E, R % G == 0, H % 8 == 0,
- * T*k < 2^31, T*H < 2^31 * 8 (row indices are 32-bit, byte offsets 64-bit). */
+ * T*k, T*H/8 and (with node dedup) T*min(k,N)*H/8 each below 2^31 - 4096
+ * (row indices are 32-bit, byte offsets 64-bit); beyond, MOE_ERR_UNSUPPORTED.
+ * Batches of more than 2^24 wave-items (1 KiB row segments) are moved in
+ * several launches, since a grid counts its work-items in 32 bits. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 

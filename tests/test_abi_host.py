@@ -57,6 +57,8 @@ def make(T=128, H=256, E=8, k=2, R=2, G=None, flags=0, band=0):
     (dict(E=1024, R=1024, G=1, flags=_abi.FLAG_NODE_DEDUP | _abi.FLAG_LOAD_AWARE_FORWARDERS),
      _abi.ERR_UNSUPPORTED),                            # R*N past the key space
     (dict(T=1 << 28, k=8), _abi.ERR_UNSUPPORTED),     # T*k past 32-bit row indices
+    (dict(T=(2 ** 31 - 4096) // 8, k=8), _abi.ERR_UNSUPPORTED),  # inside the 4096 margin
+    (dict(T=(2 ** 31 - 4097) // 8 - 1, H=8, k=8, E=16), _abi.OK),  # just below it
     (dict(T=4096, band=512), _abi.OK),
     (dict(T=4096, band=100), _abi.ERR_INVALID_ARGUMENT),   # not a multiple of 256
     (dict(T=4096, band=-256), _abi.ERR_INVALID_ARGUMENT),

@@ -1,0 +1,86 @@
+"""The largest batch the 32-bit row indices allow (GPU, about 90 GB of HBM).
+
+T*k = 2,147,479,536 receive rows, just under the library's limit of
+2**31 - 4097 (32-bit row indices, with a margin for the last block of a
+launch): every row index, every slot and every 64-bit byte offset of the
+single-hop path is exercised at the top of its range, and the batch takes
+several launches of at most 2**24 wave-items each.  The oracle cannot run at this size, so the expected
+results come from closed forms of a round-robin routing (the oracle's own
+round-robin pin, tests/test_oracle_shuffle.py, checks the same closed form):
+idx[t, j] = (t*k + j) mod E with E dividing T*k gives every expert T*k/E rows,
+and the flat slot f = t*k + j lands on row (f mod E) * T*k/E + f div E.
+Each 16-byte token row carries its token id in four bf16 integers (7 bits
+each, exact), so every receive row names the token it came from; weights
+1/k (k a power of two) make the combine return x bit for bit.
+"""
+
+import pytest
+import torch
+
+import combine_shuffling_amd as cs
+
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+E, K, R, H = 16, 8, 2, 8
+LIMIT = 2 ** 31 - 1 - 4096                 # the library's bound on T*k
+T = ((LIMIT - 1) // K) // 2 * 2            # even, so E divides T*K
+ROWS = T * K
+PER_EXPERT = ROWS // E
+STEP = 1 << 26                              # rows checked per pass
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    free, _ = torch.cuda.mem_get_info()
+    if free < 120 * (1 << 30):
+        pytest.skip("needs about 100 GiB of free device memory")
+    return torch.device("cuda:0")
+
+
+def token_rows(t: torch.Tensor) -> torch.Tensor:
+    """[n, 8] bf16 rows: t in four 7-bit pieces, then 1.0 four times."""
+    pieces = torch.stack([(t >> (7 * i)) & 127 for i in range(4)], dim=1).to(torch.float32)
+    ones = torch.ones((t.numel(), 4), dtype=torch.float32, device=t.device)
+    return torch.cat([pieces, ones], dim=1).to(torch.bfloat16)
+
+
+def row_token(rows: torch.Tensor) -> torch.Tensor:
+    """Inverse of token_rows (int64 token ids)."""
+    p = rows[:, :4].to(torch.float32).to(torch.int64)
+    return p[:, 0] | (p[:, 1] << 7) | (p[:, 2] << 14) | (p[:, 3] << 21)
+
+
+def test_maximum_size_round_robin(dev):
+    assert ROWS < LIMIT and ROWS % E == 0
+    say(f"[max size] T={T} k={K} E={E} R={R} H={H}: {ROWS} receive rows")
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    for a in range(0, T, STEP):
+        b = min(T, a + STEP)
+        x[a:b] = token_rows(torch.arange(a, b, device=dev))
+    idx = ((torch.arange(T, device=dev, dtype=torch.int64)[:, None] * K
+            + torch.arange(K, device=dev)[None, :]) % E).to(torch.int32)
+    w = torch.full((T, K), 1.0 / K, dtype=torch.float32, device=dev)
+
+    plan = cs.route_plan(idx, E, R, H)
+    recv, _ = cs.dispatch(plan, x)
+    out = cs.combine(plan, recv, w)
+    torch.cuda.synchronize()
+    assert plan.status() == 0
+    counts = plan.read("counts")
+    assert counts.tolist() == [PER_EXPERT] * E
+
+    # receive row r holds the token whose flat slot lands there
+    for a in range(0, ROWS, STEP):
+        b = min(ROWS, a + STEP)
+        r = torch.arange(a, b, device=dev, dtype=torch.int64)
+        e = r // PER_EXPERT
+        f = (r - e * PER_EXPERT) * E + e
+        assert torch.equal(row_token(recv[a:b]), f // K), f"receive rows [{a}, {b})"
+    # identity expert and weights 1/k: the combine returns x exactly
+    for a in range(0, T, STEP):
+        b = min(T, a + STEP)
+        assert torch.equal(out[a:b].view(torch.int16), x[a:b].view(torch.int16)), f"out [{a}, {b})"
