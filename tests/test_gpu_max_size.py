@@ -1,4 +1,4 @@
-"""The largest batch the 32-bit row indices allow (GPU, about 90 GB of HBM).
+"""The largest batch the 32-bit row indices allow (GPU, 90 to 130 GB of HBM).
 
 T*k = 2,147,479,536 receive rows, just under the library's limit of
 2**31 - 4097 (32-bit row indices, with a margin for the last block of a
@@ -81,6 +81,51 @@ def test_maximum_size_round_robin(dev):
         f = (r - e * PER_EXPERT) * E + e
         assert torch.equal(row_token(recv[a:b]), f // K), f"receive rows [{a}, {b})"
     # identity expert and weights 1/k: the combine returns x exactly
+    for a in range(0, T, STEP):
+        b = min(T, a + STEP)
+        assert torch.equal(out[a:b].view(torch.int16), x[a:b].view(torch.int16)), f"out [{a}, {b})"
+
+
+def test_maximum_size_node_dedup(dev):
+    """The same batch over two one-rank nodes with node deduplication.
+
+    Experts 0-7 sit on node 0 and 8-15 on node 1, so the round-robin routing
+    sends even tokens to node 0 only and odd tokens to node 1 only: one
+    staging row per token (D = T), forwarder 0 holding the even tokens in
+    order and forwarder 1 the odd ones, and the same receive rows as the
+    single hop."""
+    free, _ = torch.cuda.mem_get_info()
+    if free < 140 * (1 << 30):
+        pytest.skip("needs about 130 GiB of free device memory")
+    say(f"[max size, dedup] T={T} k={K} E={E} R={R} G=1: {ROWS} receive rows, {T} staging rows")
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    for a in range(0, T, STEP):
+        b = min(T, a + STEP)
+        x[a:b] = token_rows(torch.arange(a, b, device=dev))
+    idx = ((torch.arange(T, device=dev, dtype=torch.int64)[:, None] * K
+            + torch.arange(K, device=dev)[None, :]) % E).to(torch.int32)
+    w = torch.full((T, K), 1.0 / K, dtype=torch.float32, device=dev)
+
+    plan = cs.route_plan(idx, E, R, H, ranks_per_node=1, node_dedup=True)
+    recv, staging = cs.dispatch(plan, x)
+    out = cs.combine(plan, recv, w)
+    torch.cuda.synchronize()
+    assert plan.status() == 0
+    assert int(plan.read("num_staged")[0]) == T
+    assert plan.read("stage_offsets").tolist() == [0, T // 2, T]
+
+    half = T // 2
+    for a in range(0, T, STEP):
+        b = min(T, a + STEP)
+        q = torch.arange(a, b, device=dev, dtype=torch.int64)
+        want = torch.where(q < half, 2 * q, 2 * (q - half) + 1)
+        assert torch.equal(row_token(staging[a:b]), want), f"staging rows [{a}, {b})"
+    for a in range(0, ROWS, STEP):
+        b = min(ROWS, a + STEP)
+        r = torch.arange(a, b, device=dev, dtype=torch.int64)
+        e = r // PER_EXPERT
+        f = (r - e * PER_EXPERT) * E + e
+        assert torch.equal(row_token(recv[a:b]), f // K), f"receive rows [{a}, {b})"
     for a in range(0, T, STEP):
         b = min(T, a + STEP)
         assert torch.equal(out[a:b].view(torch.int16), x[a:b].view(torch.int16)), f"out [{a}, {b})"
