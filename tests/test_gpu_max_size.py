@@ -129,3 +129,50 @@ def test_maximum_size_node_dedup(dev):
     for a in range(0, T, STEP):
         b = min(T, a + STEP)
         assert torch.equal(out[a:b].view(torch.int16), x[a:b].view(torch.int16)), f"out [{a}, {b})"
+
+
+def test_maximum_size_fp8(dev):
+    """The same batch with the fp8 payload.  A row now holds its token id in
+    seven base-16 digits plus a 15, so every 8-element block has amax 15,
+    scale 2^-4 and exact E4M3 codes (a digit times 16 needs at most four
+    significant bits): the codes name each row's token, and the combine
+    still returns x bit for bit."""
+    free, _ = torch.cuda.mem_get_info()
+    if free < 110 * (1 << 30):
+        pytest.skip("needs about 100 GiB of free device memory")
+    say(f"[max size, fp8] T={T} k={K} E={E} R={R}: {ROWS} receive rows")
+
+    def rows16(t):
+        d = torch.stack([(t >> (4 * i)) & 15 for i in range(7)] + [torch.full_like(t, 15)], dim=1)
+        return d.to(torch.float32).to(torch.bfloat16)
+
+    table = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn) \
+        .to(torch.float32).to(dev)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    for a in range(0, T, STEP):
+        b = min(T, a + STEP)
+        x[a:b] = rows16(torch.arange(a, b, device=dev))
+    idx = ((torch.arange(T, device=dev, dtype=torch.int64)[:, None] * K
+            + torch.arange(K, device=dev)[None, :]) % E).to(torch.int32)
+    w = torch.full((T, K), 1.0 / K, dtype=torch.float32, device=dev)
+
+    plan = cs.route_plan(idx, E, R, H)
+    codes, scales = cs.dispatch_fp8(plan, x)
+    out = cs.combine_fp8(plan, codes, scales, w)
+    torch.cuda.synchronize()
+    assert plan.status() == 0
+    assert scales.shape == (ROWS, 1)
+
+    for a in range(0, ROWS, STEP):
+        b = min(ROWS, a + STEP)
+        assert torch.all(scales[a:b] == 1.0 / 16), f"scales [{a}, {b})"
+        digits = (table[codes[a:b].long()] * (1.0 / 16)).to(torch.int64)
+        got = sum(digits[:, i] << (4 * i) for i in range(7))
+        r = torch.arange(a, b, device=dev, dtype=torch.int64)
+        e = r // PER_EXPERT
+        f = (r - e * PER_EXPERT) * E + e
+        assert torch.equal(got, f // K), f"receive rows [{a}, {b})"
+        assert torch.all(digits[:, 7] == 15)
+    for a in range(0, T, STEP):
+        b = min(T, a + STEP)
+        assert torch.equal(out[a:b].view(torch.int16), x[a:b].view(torch.int16)), f"out [{a}, {b})"
