@@ -1,0 +1,108 @@
+"""The benchmark's host-side arithmetic (CPU): algorithmic bytes, the
+one-GPU guard, the rocprofv3 summaries and the traffic lookup."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from workloads import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("name,disp,comb", [
+    ("tiny", 196_608, 196_608),
+    ("olmoe", 150_994_944, 150_994_944),
+    ("qwen3", 603_979_776, 603_979_776),
+    ("nondiv", 939_524_096, 939_524_096),
+])
+def test_single_hop_bytes(name, disp, comb):
+    # (T + T*k) * 2H each way: the per-workload figures of the measurement plan
+    assert bench.algorithmic_bytes(gen.get(name), 0) == (disp, comb)
+
+
+def test_dedup_and_variant_bytes():
+    wl = gen.get("dsv3")
+    T, k, row = wl.num_tokens, wl.top_k, 2 * wl.hidden
+    D = 65_085
+    assert bench.algorithmic_bytes(wl, D) == ((T + 2 * D + T * k) * row, (T * k + T) * row)
+    # the D = 4T upper bound of the measurement plan
+    assert sum(bench.algorithmic_bytes(wl, 4 * T)) == 6_106_906_624
+    # hierarchical: the fp32 partials are written once and read once
+    assert bench.algorithmic_bytes(wl, D, hier=True)[1] == (T * k + T) * row + 4 * D * row
+    # fp8: one byte an element plus a float32 scale per 128 elements on the k rows
+    row8 = wl.hidden + 4 * ((wl.hidden + 127) // 128)
+    assert bench.algorithmic_bytes(gen.get("olmoe"), 0, "fp8") == \
+        (4096 * 4096 + 4096 * 8 * (2048 + 64), 4096 * 8 * (2048 + 64) + 4096 * 4096)
+    assert bench.algorithmic_bytes(wl, D, "fp8")[0] == T * row + (2 * D + T * k) * row8
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _write_csv(path, rows, fields):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_pmc_summary_scales_by_the_copy_kernel(tmp_path):
+    fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    kern = "void moe::(anonymous namespace)::combine_kernel<8, 1, false>(moe::Dims)"
+    copy = "void at::native::vectorized_elementwise_kernel<8>(int)"
+    # FETCH_SIZE reads half of what moved (as measured on gfx950), WRITE_SIZE all of it
+    _write_csv(tmp_path / "f.csv", [dict(Kernel_Name=kern, Counter_Name="FETCH_SIZE",
+                                         Counter_Value=v) for v in (100.0, 102.0)], fields)
+    _write_csv(tmp_path / "w.csv", [dict(Kernel_Name=kern, Counter_Name="WRITE_SIZE",
+                                         Counter_Value=v) for v in (50.0, 50.0)], fields)
+    _write_csv(tmp_path / "cf.csv", [dict(Kernel_Name=copy, Counter_Name="FETCH_SIZE",
+                                          Counter_Value=512.0)] * 5, fields)
+    _write_csv(tmp_path / "cw.csv", [dict(Kernel_Name=copy, Counter_Name="WRITE_SIZE",
+                                          Counter_Value=1024.0)] * 5, fields)
+    out = tmp_path / "s.txt"
+    bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                        str(tmp_path / "cw.csv"), str(out), 1, "cmd")
+    text = "".join(ln for ln in open(out) if not ln.startswith("#"))
+    s = json.loads(text)
+    assert s["fetch_factor"] == 2.0 and s["write_factor"] == 1.0
+    k = s["kernels"]["combine_kernel<8, 1, false>"]
+    assert k["dispatches"] == 2
+    assert k["traffic_bytes"] == int((101.0 * 2 + 50.0) * 1024)
+    assert s["source_hash"] == bench.kernel_source_hash() and s["command"] == "cmd"
+
+
+def test_trace_summary(tmp_path):
+    fields = ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"]
+    _write_csv(tmp_path / "t.csv", [dict(Name="void moe::gather_kernel<8, 1>()", Calls=110,
+                                         AverageNs=26550.0, MinNs=25000.0, MaxNs=30000.0)], fields)
+    out = tmp_path / "t.txt"
+    bench.summarize_trace(str(tmp_path / "t.csv"), str(out), "cmd")
+    lines = open(out).read().splitlines()
+    assert lines[1] == "# command: cmd"
+    assert lines[3].split()[-4:] == ["110", "26.55", "25.00", "30.00"]
+
+
+def test_traffic_lookup_needs_current_sources(tmp_path, monkeypatch):
+    summary = {"source_hash": bench.kernel_source_hash(),
+               "kernels": {"gather_kernel<8, 1>": {"traffic_bytes": 123},
+                           "combine_kernel<8, 1, false>": {"traffic_bytes": 456}}}
+    (tmp_path / "hbm_traffic_w.txt").write_text("# header\n" + json.dumps(summary))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.recorded_traffic("w", "gather_scan_kernel|gather_kernel") == ("gather_kernel<8, 1>", 123)
+    assert bench.recorded_traffic("w", "combine_kernel") == ("combine_kernel<8, 1, false>", 456)
+    assert bench.recorded_traffic("w", "stage_a_kernel") == (None, None)
+    assert bench.recorded_traffic("missing", "gather_kernel") == (None, None)
+    summary["source_hash"] = "0" * 16             # the kernels changed since
+    (tmp_path / "hbm_traffic_w.txt").write_text(json.dumps(summary))
+    assert bench.recorded_traffic("w", "gather_kernel") == (None, None)
+
