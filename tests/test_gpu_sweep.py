@@ -40,7 +40,7 @@ def draw(seed):
     return T, H, E, k, R, G, routing
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_shape(seed, dev):
     T, H, E, k, R, G, routing = draw(seed)
     wl = gen.custom(T, H, E, k, R, G, routing=routing, seed=seed)
@@ -67,7 +67,7 @@ def test_random_shape(seed, dev):
     check_combine(bits(out), recv, batch.topk_w, p["slot_of"], False, wl.name)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_banded_pipeline(seed, dev):
     rng = np.random.default_rng(2000 + seed)
     E = int(rng.choice([8, 64, 100, 256]))
