@@ -79,6 +79,22 @@ def test_fp8_small_shapes(case, dev):
     check_fp8(gen.make_batch(gen.custom(T, H, E, k, R, seed=T + H)), dev)
 
 
+@pytest.mark.parametrize("seed", range(32))
+def test_fp8_random_shapes(seed, dev):
+    # H a multiple of 8 up to 632: one to five scale blocks a row, rows of
+    # whole and of half 16-byte code chunks; up to 1000 experts (the folded
+    # scan up to 64, the separate one above)
+    rng = np.random.default_rng(3000 + seed)
+    E = int(rng.choice([3, 8, 17, 64, 100, 256, 1000]))
+    R = int(rng.integers(1, min(E, 64) + 1))
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(1, 3000))
+    H = int(8 * rng.integers(1, 80))
+    routing = str(rng.choice(["uniform", "zipf"]))
+    kw = dict(zipf_s=1.2) if routing == "zipf" else {}
+    check_fp8(gen.make_batch(gen.custom(T, H, E, k, R, routing=routing, seed=seed, **kw)), dev)
+
+
 @pytest.mark.parametrize("name", ["tiny", "olmoe", "qwen3", "nondiv"])
 def test_fp8_workloads_full_size(name, dev):
     batch = gen.make_batch(gen.get(name))
