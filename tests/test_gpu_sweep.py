@@ -3,8 +3,9 @@
 Each case draws T, H, E, k, R, G and the routing from a fixed seed (sizes the
 oracle handles in well under a second), then checks the whole path: plan
 arrays and receive rows bit for bit, combine within the tolerance of
-tests/gpu_util.py; with node deduplication also the staging rows, with
-load-aware forwarders the forwarder table, with bands the banded plan.
+tests/gpu_util.py; with node deduplication also the staging rows and the
+hierarchical combine, with load-aware forwarders the forwarder table, with
+bands the banded plan.
 """
 
 import numpy as np
@@ -16,6 +17,7 @@ import oracle
 from workloads import gen
 
 from gpu_util import GpuRun, bits, check_combine, say, to_dev
+from test_gpu_parity import hier_check
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +67,8 @@ def test_random_shape(seed, dev):
         assert np.array_equal(plan.read("forwarders").reshape(R, N), p["forwarders"])
     out = run.combine(out_dtype=torch.bfloat16)
     check_combine(bits(out), recv, batch.topk_w, p["slot_of"], False, wl.name)
+    if dedup:  # the hierarchical combine: partials and output
+        hier_check(batch, dev, load_aware)
 
 
 @pytest.mark.parametrize("seed", range(32))
