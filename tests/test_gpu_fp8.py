@@ -178,6 +178,19 @@ def test_fp8_dedup_small(case, load_aware, dev):
                                               seed=T + H)), dev, load_aware)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_fp8_dedup_random_shapes(seed, dev):
+    rng = np.random.default_rng(4000 + seed)
+    E = int(rng.choice([8, 17, 64, 100, 256]))
+    R = int(rng.integers(2, min(E, 64) + 1))
+    G = int(rng.choice([g for g in range(1, R) if R % g == 0]))   # at least two nodes
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(1, 3000))
+    H = int(8 * rng.integers(1, 80))
+    load_aware = seed % 2 == 1 and R * (R // G) <= 1024
+    check_fp8_dedup(gen.make_batch(gen.custom(T, H, E, k, R, G, seed=seed)), dev, load_aware)
+
+
 def test_fp8_dedup_dsv3(dev):
     batch = gen.make_batch(gen.get("dsv3"))
     T = batch.workload.num_tokens
