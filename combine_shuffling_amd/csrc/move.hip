@@ -828,7 +828,7 @@ __global__ __launch_bounds__(kBlock) void stage_b_fp8_kernel(Dims d, const uint8
 // Combine of an fp8 payload: codes decoded and scaled (exact), then the same
 // fp32 fused multiply-add chain as the bf16 combine.
 template <int KMAX, int U, bool F32OUT>
-__global__ __launch_bounds__(kBlock) void combine_fp8_kernel(Dims d, const u32x2* __restrict__ y8,
+__global__ __launch_bounds__(kCombine8Waves * kWave) void combine_fp8_kernel(Dims d, const u32x2* __restrict__ y8,
                                                              const float* __restrict__ yscale,
                                                              const float* __restrict__ wts,
                                                              const int32_t* __restrict__ slot_of,
@@ -842,7 +842,7 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_kernel(Dims d, const u32x2
   u32x2 v[U][KMAX];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, blockIdx.x, base, limit, u);
+    it[u] = wave_item<U, kCombine8Waves>(d, blockIdx.x, base, limit, u);
     const int64_t at = (int64_t)it[u].t * d.k;
     const int blk = it[u].c / kFp8BlockChunks;
     int sj[KMAX];
@@ -991,13 +991,14 @@ struct CombineLaunch {
   static hipError_t run(const Dims& d, const uint16_t* y, const float* wts, void* out, bool f32,
                         const Work& w, hipStream_t s) {
     const u32x4* yv = reinterpret_cast<const u32x4*>(y);
-    return launch_ranges((int64_t)d.T * d.segs, kWaves * kCombineU, [&](dim3 g, int b, int l) {
+    const dim3 block(kCombineWaves * kWave);
+    return launch_ranges((int64_t)d.T * d.segs, kCombineWaves * kCombineU, [&](dim3 g, int b, int l) {
       if (f32)
-        hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, true>), g, dim3(kBlock), 0, s, d, yv,
-                           wts, w.slot_of, out, b, l);
+        hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, true>), g, block, 0, s, d, yv, wts,
+                           w.slot_of, out, b, l);
       else
-        hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, false>), g, dim3(kBlock), 0, s, d, yv,
-                           wts, w.slot_of, out, b, l);
+        hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, false>), g, block, 0, s, d, yv, wts,
+                           w.slot_of, out, b, l);
     });
   }
 };
@@ -1054,13 +1055,14 @@ struct CombineFp8Launch {
   static hipError_t run(const Dims& d, const uint8_t* y8, const float* yscale, const float* wts,
                         void* out, bool f32, const Work& w, hipStream_t s) {
     const u32x2* y = reinterpret_cast<const u32x2*>(y8);
-    return launch_ranges((int64_t)d.T * d.segs, kWaves * kCombine8U, [&](dim3 g, int b, int l) {
+    const dim3 block(kCombine8Waves * kWave);
+    return launch_ranges((int64_t)d.T * d.segs, kCombine8Waves * kCombine8U, [&](dim3 g, int b, int l) {
       if (f32)
-        hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, true>), g, dim3(kBlock), 0, s, d, y,
+        hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, true>), g, block, 0, s, d, y,
                            yscale, wts, w.slot_of, out, b, l);
       else
-        hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, false>), g, dim3(kBlock), 0, s, d,
-                           y, yscale, wts, w.slot_of, out, b, l);
+        hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, false>), g, block, 0, s, d, y,
+                           yscale, wts, w.slot_of, out, b, l);
     });
   }
 };

@@ -26,6 +26,16 @@
 #ifndef MOE_NT_LOAD_X
 #define MOE_NT_LOAD_X 0
 #endif
+#ifndef MOE_COMBINE_WAVES
+// waves per block of the bf16 combine; best step, against 4-wave blocks:
+// qwen3 205.2 -> 203.9 us, nondiv 339.1 -> 335.6, dsv3 1083.3 -> 1078.2,
+// olmoe unchanged (2-wave blocks: olmoe 48.9 against 48.3, dsv3 1075)
+#define MOE_COMBINE_WAVES 1
+#endif
+#ifndef MOE_COMBINE8_WAVES
+// ... of the fp8 combine: 2-wave blocks made qwen3 fp8 118.1 us against 114.7
+#define MOE_COMBINE8_WAVES 4
+#endif
 #ifndef MOE_MOVE_WAVES
 #define MOE_MOVE_WAVES 4
 #endif
@@ -45,6 +55,8 @@ constexpr int kGatherU = MOE_GATHER_U;    // wave-items per wave: gather
 constexpr int kStageU = MOE_STAGE_U;      // wave-items per wave: stage_b (stage_a in move.hip)
 constexpr int kCombineU = MOE_COMBINE_U;  // wave-items per wave: combine
 constexpr int kCombine8U = MOE_COMBINE8_U; // wave-items per wave: combine of an fp8 payload
+constexpr int kCombineWaves = MOE_COMBINE_WAVES;    // waves per block of the bf16 combine
+constexpr int kCombine8Waves = MOE_COMBINE8_WAVES;  // ... of the fp8 combine
 // Wave-items per launch at most: a grid is sized in work-items, a 32-bit count,
 // so a batch of more wave-items is moved in several launches (2^24 items of
 // at most 64 threads each).
@@ -116,13 +128,14 @@ struct Item {
   bool live, ok;
 };
 
-// Wave-items are numbered g = base + (blk * U + u) * kWaves + wave; those
-// at or past `limit` do not exist.  A kernel takes blk = its block index and
-// base 0; the banded pipeline takes blk from its ticket and the band's range.
-template <int U>
+// Wave-items are numbered g = base + (blk * U + u) * W + wave (W waves a
+// block); those at or past `limit` do not exist.  A kernel takes blk = its
+// block index and its launch's range; the banded pipeline takes blk from its
+// ticket and the band's range.
+template <int U, int W = kWaves>
 __device__ __forceinline__ Item wave_item(const Dims& d, int blk, int base, int limit, int u) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int g = __builtin_amdgcn_readfirstlane(base + (blk * U + u) * kWaves + wave);
+  const int g = __builtin_amdgcn_readfirstlane(base + (blk * U + u) * W + wave);
   Item it;
   it.live = g < limit;
   it.t = it.live ? g / d.segs : 0;
@@ -206,8 +219,8 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Weighted combine for the wave-items of block-chunk blk.
-template <int KMAX, int U, bool F32OUT, bool COH = false>
+// Weighted combine for the wave-items of block-chunk blk (W waves a block).
+template <int KMAX, int U, bool F32OUT, bool COH = false, int W = kWaves>
 __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, const float* wts,
                                               const int32_t* slot_of, void* out, int blk, int base,
                                               int limit) {
@@ -218,7 +231,7 @@ __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, con
   u32x4 v[U][KMAX];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, blk, base, limit, u);
+    it[u] = wave_item<U, W>(d, blk, base, limit, u);
     const int64_t at = (int64_t)it[u].t * d.k;
     int sj[KMAX];
     float wt[KMAX];
@@ -273,11 +286,11 @@ __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, con
 
 // Wave-items [base, limit) of the batch (one launch of at most kMaxLaunchItems).
 template <int KMAX, int U, bool F32OUT>
-__global__ __launch_bounds__(kBlock) void combine_kernel(Dims d, const u32x4* __restrict__ y,
-                                                         const float* __restrict__ wts,
-                                                         const int32_t* __restrict__ slot_of,
-                                                         void* __restrict__ out, int base, int limit) {
-  combine_chunk<KMAX, U, F32OUT>(d, y, wts, slot_of, out, blockIdx.x, base, limit);
+__global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(
+    Dims d, const u32x4* __restrict__ y, const float* __restrict__ wts,
+    const int32_t* __restrict__ slot_of, void* __restrict__ out, int base, int limit) {
+  combine_chunk<KMAX, U, F32OUT, false, kCombineWaves>(d, y, wts, slot_of, out, blockIdx.x, base,
+                                                       limit);
 }
 
 }  // namespace
