@@ -94,7 +94,7 @@ def check_combine_values(out, ref, yv, w, slot_of, out_f32, what, roundings=None
     return info
 
 
-class GpuRun:
+class DeviceRun:
     """One route plan + dispatch (+ combine) on the GPU through the C ABI."""
 
     def __init__(self, batch, dev, node_dedup=None, load_aware=False):

@@ -12,7 +12,7 @@ import torch
 import oracle
 from workloads import gen
 
-from gpu_util import GpuRun, bits, check_combine, check_combine_values, say, to_dev
+from gpu_util import DeviceRun, bits, check_combine, check_combine_values, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def check_plan(run: GpuRun, p: dict):
+def check_plan(run: DeviceRun, p: dict):
     wl = run.wl
     T, k = wl.num_tokens, wl.top_k
     r = run.plan
@@ -48,7 +48,7 @@ def full_check(batch, dev, dedup=None, combine_tokens=None, traffic=False, load_
     say(f"[parity] {wl.describe()} dedup={dedup} load_aware={load_aware}")
     p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node,
                           forwarders="load_aware" if load_aware else "static")
-    run = GpuRun(batch, dev, node_dedup=dedup, load_aware=load_aware).route().dispatch()
+    run = DeviceRun(batch, dev, node_dedup=dedup, load_aware=load_aware).route().dispatch()
     torch.cuda.synchronize()
     check_plan(run, p)
     assert run.guards_intact()
@@ -132,7 +132,7 @@ def test_dedup_workload_single_hop_too(dev):
     # The DeepSeek-V3-like routing through the single-hop path gives the same rows.
     batch = gen.make_batch(gen.get("dsv3"))
     p = oracle.route_plan(batch.topk_idx, 256, 64, 8)
-    run = GpuRun(batch, dev, node_dedup=False).route().dispatch()
+    run = DeviceRun(batch, dev, node_dedup=False).route().dispatch()
     torch.cuda.synchronize()
     assert np.array_equal(bits(run.recv), oracle.dispatch(batch.x, p))
 
@@ -146,7 +146,7 @@ def test_combine_one_hot_is_bit_exact_gather(dev):
     w = np.zeros((T, k), dtype=np.float32)
     w[np.arange(T), pick] = 1.0
     p = oracle.route_plan(batch.topk_idx, 64, 4)
-    run = GpuRun(batch, dev).route().dispatch()
+    run = DeviceRun(batch, dev).route().dispatch()
     y = np.random.default_rng(6).integers(0, 0x7F00, (T * k, 256), dtype=np.uint16)
     out = run.combine(y=to_dev(y, dev), w=to_dev(w, dev))
     assert np.array_equal(bits(out), y[p["slot_of"][np.arange(T), pick]])
@@ -157,7 +157,7 @@ def test_identity_roundtrip_power_of_two_exact(k, dev):
     batch = gen.make_batch(gen.custom(2000, 128, 32, k, 4, 2, seed=k))
     T = batch.topk_idx.shape[0]
     w = np.full((T, k), 1.0 / k, dtype=np.float32)
-    run = GpuRun(batch, dev).route().dispatch()
+    run = DeviceRun(batch, dev).route().dispatch()
     out = run.combine(w=to_dev(w, dev))
     assert np.array_equal(bits(out), batch.x)
 
@@ -165,7 +165,7 @@ def test_identity_roundtrip_power_of_two_exact(k, dev):
 @pytest.mark.parametrize("name", ["tiny", "olmoe", "nondiv"])
 def test_roundtrip_renormalised_within_one_ulp(name, dev):
     batch = gen.make_batch(gen.get(name))
-    run = GpuRun(batch, dev).route().dispatch()
+    run = DeviceRun(batch, dev).route().dispatch()
     out = bits(run.combine())
     assert int(oracle.bf16_ulp_distance(out, batch.x).max()) <= 1
 
@@ -174,7 +174,7 @@ def test_roundtrip_renormalised_within_one_ulp(name, dev):
 
 def test_deterministic_and_reusable(dev):
     batch = gen.make_batch(gen.custom(5000, 512, 100, 6, 7, 7, seed=9))
-    run = GpuRun(batch, dev).route().dispatch()
+    run = DeviceRun(batch, dev).route().dispatch()
     a = bits(run.recv).copy()
     o1 = bits(run.combine())
     run.recv.fill_(-1)
@@ -208,7 +208,7 @@ def test_bad_routing_is_flagged_and_memory_safe(dev):
     idx[700, 3] = idx[700, 0]  # repeated in a row
     batch.topk_idx = idx
     for dedup in (False, True):
-        run = GpuRun(batch, dev, node_dedup=dedup).route().dispatch()
+        run = DeviceRun(batch, dev, node_dedup=dedup).route().dispatch()
         assert run.plan.status() == _abi.ERR_BAD_ROUTING
         assert run.guards_intact()
         so = run.plan.read("slot_of").reshape(1500, 4)
@@ -217,7 +217,7 @@ def test_bad_routing_is_flagged_and_memory_safe(dev):
         run.combine()
     # a clean routing afterwards clears the status
     good = gen.make_batch(gen.custom(1500, 64, 16, 4, 4, 2, seed=2))
-    run = GpuRun(good, dev).route()
+    run = DeviceRun(good, dev).route()
     assert run.plan.status() == 0
 
 
@@ -234,7 +234,7 @@ def test_bad_routing_in_chunked_dedup_dispatch(dev):
     idx[2000, 6] = -1          # negative, second chunk
     idx[1700, 1] = idx[1700, 0]  # repeated, second chunk
     batch.topk_idx = idx
-    run = GpuRun(batch, dev, node_dedup=True).route().dispatch()
+    run = DeviceRun(batch, dev, node_dedup=True).route().dispatch()
     assert run.plan.status() == _abi.ERR_BAD_ROUTING
     assert run.guards_intact()
     so = run.plan.read("slot_of").reshape(T, k)
@@ -264,7 +264,7 @@ def test_plan_reads_and_combine_without_dispatch(dev):
     p = oracle.route_plan(batch.topk_idx, 40, 8, 2)
     y = oracle.dispatch(batch.x, p)
     for dedup in (False, True):
-        run = GpuRun(batch, dev, node_dedup=dedup).route()
+        run = DeviceRun(batch, dev, node_dedup=dedup).route()
         check_plan(run, p)
         out = run.combine(y=to_dev(y, dev), out_dtype=torch.float32)
         check_combine(out.cpu().numpy(), y, batch.topk_w, p["slot_of"], True, "no-dispatch")
@@ -296,7 +296,7 @@ def hier_check(batch, dev, load_aware, tokens=None):
     say(f"[hier] {wl.describe()} load_aware={load_aware}")
     p = oracle.route_plan(batch.topk_idx, wl.num_experts, wl.num_ranks, wl.ranks_per_node,
                           forwarders="load_aware" if load_aware else "static")
-    run = GpuRun(batch, dev, node_dedup=True, load_aware=load_aware).route().dispatch()
+    run = DeviceRun(batch, dev, node_dedup=True, load_aware=load_aware).route().dispatch()
     y = bits(run.recv)
     tok = np.arange(wl.num_tokens) if tokens is None else np.asarray(tokens)
     # The plan restricted to the checked tokens and their staging rows, renumbered.

@@ -16,7 +16,7 @@ import combine_shuffling_amd as cs
 import oracle
 from workloads import gen
 
-from gpu_util import GpuRun, bits, check_combine, say, to_dev
+from gpu_util import DeviceRun, bits, check_combine, say, to_dev
 from test_gpu_parity import hier_check
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,7 @@ def test_random_shape(seed, dev):
     load_aware = dedup and seed % 2 == 1 and R * N <= 1024
     say(f"[sweep {seed}] {wl.describe()} dedup={dedup} load_aware={load_aware}")
     p = oracle.route_plan(batch.topk_idx, E, R, G, forwarders="load_aware" if load_aware else "static")
-    run = GpuRun(batch, dev, node_dedup=dedup, load_aware=load_aware).route().dispatch()
+    run = DeviceRun(batch, dev, node_dedup=dedup, load_aware=load_aware).route().dispatch()
     torch.cuda.synchronize()
     plan = run.plan
     assert plan.status() == 0
