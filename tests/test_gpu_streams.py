@@ -7,7 +7,9 @@ on another stream while the first batch's are still running (the library
 holds no state shared between plans).  Launches of the two batches are
 interleaved, repeated, and each batch must still match the oracle to the
 usual bars: plan arrays and receive rows bit-exact, combine within the
-tolerance of tests/gpu_util.py.
+tolerance of tests/gpu_util.py.  The last test runs each workload at full size
+in the schedule the benchmark picks for it, with the benchmark's cycling of
+buffer sets.
 """
 
 import numpy as np
@@ -164,3 +166,79 @@ def test_plan_ahead_batches(case, dev):
             D = p["num_staged"]
             assert np.array_equal(bits(r["st"])[:D], oracle.dedup_stage_a(b.x, p))
         check_combine(r["out"].cpu().numpy(), recv, b.topk_w, p["slot_of"], True, wl.name)
+
+
+def _run_schedule(sets, schedule, steps, dev):
+    """The benchmark's schedules over buffer sets cycled in order: step i
+    uses set i % len(sets); "two_in_flight" and "staggered" run it on stream
+    i % 2 (an even number of sets keeps each set on one stream), "plan_ahead"
+    moves every step on one stream and routes the next on the other."""
+    streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+    if schedule == "plan_ahead":
+        main, side = streams
+        routed = [torch.cuda.Event(), torch.cuda.Event()]
+        moving = torch.cuda.Event()
+        sets[0]["plan"].route(sets[0]["idx"], stream=side)
+        routed[0].record(side)
+        for i in range(steps):
+            s = sets[i % len(sets)]
+            main.wait_event(routed[i % 2])
+            moving.record(main)
+            s["plan"].dispatch(s["x"], s["recv"], s["st"], stream=main)
+            s["plan"].combine(s["recv"], s["w"], s["out"], stream=main)
+            if i + 1 < steps:
+                s1 = sets[(i + 1) % len(sets)]
+                side.wait_event(moving)
+                s1["plan"].route(s1["idx"], stream=side)
+                routed[(i + 1) % 2].record(side)
+        return
+    for i in range(steps):
+        s, st = sets[i % len(sets)], streams[i % 2]
+        s["plan"].route(s["idx"], stream=st)
+        if schedule == "staggered" and i > 0:
+            st.wait_event(done[(i - 1) % 2])
+        s["plan"].dispatch(s["x"], s["recv"], s["st"], stream=st)
+        done[i % 2].record(st)
+        s["plan"].combine(s["recv"], s["w"], s["out"], stream=st)
+
+
+@pytest.mark.parametrize("name,schedule", [("olmoe", "two_in_flight"), ("qwen3", "staggered"),
+                                           ("nondiv", "staggered"), ("dsv3", "plan_ahead")])
+def test_full_size_in_benchmark_schedule(name, schedule, dev):
+    """Each workload at full size in the schedule the benchmark's trial picks
+    for it: four buffer sets holding four different batches (seeds 0-3 of the
+    workload's recipe, so that rows taken from the wrong set would show),
+    cycled over eight steps, bf16 output.  Every set's receive (and staging)
+    rows are compared bit for bit, its combine on sampled tokens."""
+    wl = gen.get(name)
+    T, H, E, k, R, G = (wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
+                        wl.ranks_per_node)
+    sets = []
+    for seed in range(4):
+        b = gen.make_batch(wl, seed=seed)
+        plan = cs.Plan(T, H, E, k, R, G, wl.node_dedup)
+        sets.append(dict(
+            b=b, plan=plan, x=to_dev(b.x, dev), idx=to_dev(b.topk_idx, dev), w=to_dev(b.topk_w, dev),
+            recv=torch.full((plan.recv_rows, H), -1, dtype=torch.int16, device=dev),
+            st=(torch.full((plan.staging_rows_max, H), -1, dtype=torch.int16, device=dev)
+                if wl.node_dedup else None),
+            out=torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+    say(f"[full size, {schedule}] {wl.describe()}: 4 sets, 8 steps")
+    _run_schedule(sets, schedule, 8, dev)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    tok = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, min(T, 768))]))
+    for seed, s in enumerate(sets):
+        b = s["b"]
+        p = oracle.route_plan(b.topk_idx, E, R, G)
+        assert s["plan"].status() == 0
+        recv = bits(s["recv"])
+        assert np.array_equal(recv, oracle.dispatch(b.x, p)), f"receive rows of set {seed}"
+        if wl.node_dedup:
+            D = p["num_staged"]
+            assert np.array_equal(bits(s["st"])[:D], oracle.dedup_stage_a(b.x, p)), \
+                f"staging rows of set {seed}"
+        check_combine(bits(s["out"])[tok], recv, b.topk_w[tok], p["slot_of"][tok], False,
+                      f"{wl.name} set {seed}")
