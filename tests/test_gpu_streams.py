@@ -18,9 +18,10 @@ import torch
 
 import combine_shuffling_amd as cs
 import oracle
+from oracle import fp8
 from workloads import gen
 
-from gpu_util import bits, check_combine, say, to_dev
+from gpu_util import bits, check_combine, check_combine_values, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -168,6 +169,20 @@ def test_plan_ahead_batches(case, dev):
         check_combine(r["out"].cpu().numpy(), recv, b.topk_w, p["slot_of"], True, wl.name)
 
 
+def _dispatch(s, st):
+    if "scale" in s:   # fp8 payload
+        s["plan"].dispatch_fp8(s["x"], s["recv"], s["scale"], s["st"], s["sscale"], stream=st)
+    else:
+        s["plan"].dispatch(s["x"], s["recv"], s["st"], stream=st)
+
+
+def _combine(s, st):
+    if "scale" in s:
+        s["plan"].combine_fp8(s["recv"], s["scale"], s["w"], s["out"], stream=st)
+    else:
+        s["plan"].combine(s["recv"], s["w"], s["out"], stream=st)
+
+
 def _run_schedule(sets, schedule, steps, dev):
     """The benchmark's schedules over buffer sets cycled in order: step i
     uses set i % len(sets); "two_in_flight" and "staggered" run it on stream
@@ -185,8 +200,8 @@ def _run_schedule(sets, schedule, steps, dev):
             s = sets[i % len(sets)]
             main.wait_event(routed[i % 2])
             moving.record(main)
-            s["plan"].dispatch(s["x"], s["recv"], s["st"], stream=main)
-            s["plan"].combine(s["recv"], s["w"], s["out"], stream=main)
+            _dispatch(s, main)
+            _combine(s, main)
             if i + 1 < steps:
                 s1 = sets[(i + 1) % len(sets)]
                 side.wait_event(moving)
@@ -198,9 +213,9 @@ def _run_schedule(sets, schedule, steps, dev):
         s["plan"].route(s["idx"], stream=st)
         if schedule == "staggered" and i > 0:
             st.wait_event(done[(i - 1) % 2])
-        s["plan"].dispatch(s["x"], s["recv"], s["st"], stream=st)
+        _dispatch(s, st)
         done[i % 2].record(st)
-        s["plan"].combine(s["recv"], s["w"], s["out"], stream=st)
+        _combine(s, st)
 
 
 @pytest.mark.parametrize("name,schedule", [("olmoe", "two_in_flight"), ("qwen3", "staggered"),
@@ -242,3 +257,54 @@ def test_full_size_in_benchmark_schedule(name, schedule, dev):
                 f"staging rows of set {seed}"
         check_combine(bits(s["out"])[tok], recv, b.topk_w[tok], p["slot_of"][tok], False,
                       f"{wl.name} set {seed}")
+
+
+@pytest.mark.parametrize("name,schedule", [("qwen3", "staggered"), ("dsv3", "plan_ahead")])
+def test_full_size_fp8_in_benchmark_schedule(name, schedule, dev):
+    """The same with the fp8 payload (with node deduplication on the
+    DeepSeek-V3-like workload): every set's codes and block scales bit for
+    bit, staging ones too, its combine on sampled tokens against the
+    oracle's float64 sum of the decoded rows."""
+    wl = gen.get(name)
+    T, H, E, k, R, G = (wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
+                        wl.ranks_per_node)
+    sets = []
+    for seed in range(4):
+        b = gen.make_batch(wl, seed=seed)
+        plan = cs.Plan(T, H, E, k, R, G, wl.node_dedup)
+        rows, smax, nb = plan.recv_rows, plan.staging_rows_max, plan.scale_blocks
+        sets.append(dict(
+            b=b, plan=plan, x=to_dev(b.x, dev), idx=to_dev(b.topk_idx, dev), w=to_dev(b.topk_w, dev),
+            recv=torch.full((rows, H), 0x55, dtype=torch.uint8, device=dev),
+            scale=torch.full((rows, nb), -1.0, dtype=torch.float32, device=dev),
+            st=(torch.full((smax, H), 0x55, dtype=torch.uint8, device=dev) if wl.node_dedup else None),
+            sscale=(torch.full((smax, nb), -1.0, dtype=torch.float32, device=dev)
+                    if wl.node_dedup else None),
+            out=torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+    say(f"[full size fp8, {schedule}] {wl.describe()}: 4 sets, 8 steps")
+    _run_schedule(sets, schedule, 8, dev)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    tok = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, min(T, 768))]))
+    for seed, s in enumerate(sets):
+        b = s["b"]
+        p = oracle.route_plan(b.topk_idx, E, R, G)
+        assert s["plan"].status() == 0
+        if wl.node_dedup:
+            sc, se, rc, re = fp8.dedup_dispatch_fp8(b.x, p)
+            D = p["num_staged"]
+            assert np.array_equal(s["st"][:D].cpu().numpy(), sc), f"staging codes of set {seed}"
+            assert np.array_equal(s["sscale"][:D].cpu().numpy().astype(np.float64), np.ldexp(1.0, se))
+        else:
+            rc, re = fp8.dispatch_fp8(b.x, p)
+        assert np.array_equal(s["recv"].cpu().numpy(), rc), f"receive codes of set {seed}"
+        assert np.array_equal(s["scale"].cpu().numpy().astype(np.float64), np.ldexp(1.0, re)), \
+            f"receive scales of set {seed}"
+        # the receive rows of the sampled tokens, renumbered
+        so = p["slot_of"][tok]
+        used = np.unique(so)
+        sub = np.searchsorted(used, so)
+        ref = fp8.combine_fp8(rc[used], re[used], b.topk_w[tok], {"slot_of": sub})
+        check_combine_values(bits(s["out"])[tok], ref, fp8.dequantize_rows(rc[used], re[used]),
+                             b.topk_w[tok], sub, False, f"{wl.name} fp8 set {seed}")
