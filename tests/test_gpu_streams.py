@@ -7,9 +7,9 @@ on another stream while the first batch's are still running (the library
 holds no state shared between plans).  Launches of the two batches are
 interleaved, repeated, and each batch must still match the oracle to the
 usual bars: plan arrays and receive rows bit-exact, combine within the
-tolerance of tests/gpu_util.py.  The last test runs each workload at full size
+tolerance of tests/gpu_util.py.  The last tests run each workload at full size
 in the schedule the benchmark picks for it, with the benchmark's cycling of
-buffer sets.
+buffer sets (bf16 and fp8 payloads, direct and hierarchical combine).
 """
 
 import numpy as np
@@ -177,7 +177,9 @@ def _dispatch(s, st):
 
 
 def _combine(s, st):
-    if "scale" in s:
+    if "part" in s:    # hierarchical combine through fp32 partials
+        s["plan"].combine_hier(s["recv"], s["w"], s["part"], s["out"], stream=st)
+    elif "scale" in s:
         s["plan"].combine_fp8(s["recv"], s["scale"], s["w"], s["out"], stream=st)
     else:
         s["plan"].combine(s["recv"], s["w"], s["out"], stream=st)
@@ -308,3 +310,46 @@ def test_full_size_fp8_in_benchmark_schedule(name, schedule, dev):
         ref = fp8.combine_fp8(rc[used], re[used], b.topk_w[tok], {"slot_of": sub})
         check_combine_values(bits(s["out"])[tok], ref, fp8.dequantize_rows(rc[used], re[used]),
                              b.topk_w[tok], sub, False, f"{wl.name} fp8 set {seed}")
+
+
+def test_full_size_hierarchical_combine_in_benchmark_schedule(dev):
+    """The DeepSeek-V3-like workload with the hierarchical combine (an fp32
+    partial per staging row, then the sum over nodes), staggered, four sets
+    over eight steps: receive and staging rows bit for bit, the output on
+    sampled tokens within the bound of k + N float32 roundings."""
+    wl = gen.get("dsv3")
+    T, H, E, k, R, G = (wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
+                        wl.ranks_per_node)
+    N = R // G
+    sets = []
+    for seed in range(4):
+        b = gen.make_batch(wl, seed=seed)
+        plan = cs.Plan(T, H, E, k, R, G, True)
+        sets.append(dict(
+            b=b, plan=plan, x=to_dev(b.x, dev), idx=to_dev(b.topk_idx, dev), w=to_dev(b.topk_w, dev),
+            recv=torch.full((plan.recv_rows, H), -1, dtype=torch.int16, device=dev),
+            st=torch.full((plan.staging_rows_max, H), -1, dtype=torch.int16, device=dev),
+            part=torch.full((plan.staging_rows_max, H), float("nan"), dtype=torch.float32, device=dev),
+            out=torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+    say(f"[full size hierarchical combine, staggered] {wl.describe()}: 4 sets, 8 steps")
+    _run_schedule(sets, "staggered", 8, dev)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    tok = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 768)]))
+    for seed, s in enumerate(sets):
+        b = s["b"]
+        p = oracle.route_plan(b.topk_idx, E, R, G)
+        assert s["plan"].status() == 0
+        recv = bits(s["recv"])
+        assert np.array_equal(recv, oracle.dispatch(b.x, p)), f"receive rows of set {seed}"
+        D = p["num_staged"]
+        assert np.array_equal(bits(s["st"])[:D], oracle.dedup_stage_a(b.x, p)), \
+            f"staging rows of set {seed}"
+        so = p["slot_of"][tok]
+        used = np.unique(so)
+        sub = np.searchsorted(used, so)
+        ref = oracle.combine(recv[used], b.topk_w[tok], {"slot_of": sub})
+        yv = oracle.bf16_to_f32(recv[used]).astype(np.float64)
+        check_combine_values(bits(s["out"])[tok], ref, yv, b.topk_w[tok], sub, False,
+                             f"{wl.name} hierarchical set {seed}", roundings=k + N)
