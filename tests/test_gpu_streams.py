@@ -220,21 +220,23 @@ def _run_schedule(sets, schedule, steps, dev):
         _combine(s, st)
 
 
-@pytest.mark.parametrize("name,schedule", [("olmoe", "two_in_flight"), ("qwen3", "staggered"),
-                                           ("nondiv", "staggered"), ("dsv3", "plan_ahead")])
-def test_full_size_in_benchmark_schedule(name, schedule, dev):
+@pytest.mark.parametrize("name,schedule,load_aware", [
+    ("olmoe", "two_in_flight", False), ("qwen3", "staggered", False),
+    ("nondiv", "staggered", False), ("dsv3", "plan_ahead", False), ("dsv3", "plan_ahead", True)])
+def test_full_size_in_benchmark_schedule(name, schedule, load_aware, dev):
     """Each workload at full size in the schedule the benchmark's trial picks
     for it: four buffer sets holding four different batches (seeds 0-3 of the
     workload's recipe, so that rows taken from the wrong set would show),
     cycled over eight steps, bf16 output.  Every set's receive (and staging)
-    rows are compared bit for bit, its combine on sampled tokens."""
+    rows are compared bit for bit, its combine on sampled tokens; on the
+    DeepSeek-V3-like workload also with load-aware forwarders."""
     wl = gen.get(name)
     T, H, E, k, R, G = (wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
                         wl.ranks_per_node)
     sets = []
     for seed in range(4):
         b = gen.make_batch(wl, seed=seed)
-        plan = cs.Plan(T, H, E, k, R, G, wl.node_dedup)
+        plan = cs.Plan(T, H, E, k, R, G, wl.node_dedup, load_aware)
         sets.append(dict(
             b=b, plan=plan, x=to_dev(b.x, dev), idx=to_dev(b.topk_idx, dev), w=to_dev(b.topk_w, dev),
             recv=torch.full((plan.recv_rows, H), -1, dtype=torch.int16, device=dev),
@@ -242,15 +244,17 @@ def test_full_size_in_benchmark_schedule(name, schedule, dev):
                 if wl.node_dedup else None),
             out=torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev)))
     torch.cuda.synchronize()
-    say(f"[full size, {schedule}] {wl.describe()}: 4 sets, 8 steps")
+    say(f"[full size, {schedule}] {wl.describe()} load_aware={load_aware}: 4 sets, 8 steps")
     _run_schedule(sets, schedule, 8, dev)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     tok = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, min(T, 768))]))
     for seed, s in enumerate(sets):
         b = s["b"]
-        p = oracle.route_plan(b.topk_idx, E, R, G)
+        p = oracle.route_plan(b.topk_idx, E, R, G, forwarders="load_aware" if load_aware else "static")
         assert s["plan"].status() == 0
+        if load_aware:
+            assert np.array_equal(s["plan"].read("forwarders").reshape(R, -1), p["forwarders"])
         recv = bits(s["recv"])
         assert np.array_equal(recv, oracle.dispatch(b.x, p)), f"receive rows of set {seed}"
         if wl.node_dedup:
