@@ -447,12 +447,7 @@ moe_status moe_plan_read(moe_plan* plan, int32_t item, void* host_dst, size_t by
     if (st != MOE_OK) return st;
   }
   if (traffic) {
-    const size_t mat = (size_t)d.R * d.R * sizeof(int32_t);
-    hipError_t e = hipMemsetAsync(w.send_rows, 0, mat, s);
-    if (e == hipSuccess) e = hipMemsetAsync(w.send_copies, 0, mat, s);
-    if (e == hipSuccess) e = hipMemsetAsync(w.node_copies, 0, (size_t)d.R * d.N * sizeof(int32_t), s);
-    if (e == hipSuccess && d.T > 0) e = moe::launch_traffic(d, plan->idx, w, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_traffic(d, plan->idx, w, s) != hipSuccess) return MOE_ERR_HIP;
   }
   if (item == MOE_ITEM_STATUS) {
     // One status per band: report the first that is not MOE_OK.

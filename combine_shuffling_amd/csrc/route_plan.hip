@@ -88,6 +88,18 @@ __global__ __launch_bounds__(kPlanBlock) void route_assign_kernel(Dims d,
   }
 }
 
+// Clears the three traffic matrices before traffic_kernel adds into them (a
+// fill kernel rather than memset nodes, so that the sequence holds kernels
+// only).
+__global__ __launch_bounds__(kPlanBlock) void traffic_clear_kernel(Dims d, Work w) {
+  const int i = blockIdx.x * kPlanBlock + threadIdx.x;
+  if (i < d.R * d.R) {
+    w.send_rows[i] = 0;
+    w.send_copies[i] = 0;
+  }
+  if (i < d.R * d.N) w.node_copies[i] = 0;
+}
+
 // Modelled link traffic for plan reads (not on the shuffle's path): rows,
 // distinct tokens per destination rank, and distinct tokens per destination
 // node, for every owner rank.  Counters must be zero on entry.
@@ -171,7 +183,12 @@ hipError_t launch_route_assign(const Dims& d, const int32_t* idx, const Work& w,
   return by_topk<AssignLaunch>(d.k, d, idx, w, s);
 }
 
+// Clears the counters, then counts (no counting launch for an empty batch).
 hipError_t launch_traffic(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
+  const int blocks = (d.R * d.R + kPlanBlock - 1) / kPlanBlock;
+  hipLaunchKernelGGL(traffic_clear_kernel, dim3(blocks), dim3(kPlanBlock), 0, s, d, w);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return by_topk<TrafficLaunch>(d.k, d, idx, w, s);
 }
 
