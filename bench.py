@@ -2,57 +2,52 @@
 
 One step = one pass of the whole path over one batch: moe_route_plan (histogram,
 scan, segment descriptors), moe_dispatch (single hop, or the two hops of node
-deduplication for the DeepSeek-V3-like workload) and moe_combine (bf16 out),
-with the identity expert between dispatch and combine.
+deduplication on the DeepSeek-V3-like workload) and moe_combine (bf16 out),
+with the identity expert between dispatch and combine.  Inputs are resident in
+HBM before any timing starts.
 
-Inputs are resident in HBM before timing starts, and no step finds them in
-a cache.  Consecutive steps cycle through independent copies of every buffer
-(inputs, plan workspace, receive and staging rows, outputs).  The rows are
-streamed with non-temporal accesses, which leave the 256 MB last-level cache
-(MALL) to what is read with plain loads, the token rows x above all; so the
-copies of the inputs total at least four times the MALL (and the copies of
-everything at least 2 GiB), and each step reads its x from HBM.  With fewer
-copies the MALL keeps x between steps: on the non-divisible workload, x
-cycled over 2 copies (268 MB) gives a 164 us dispatch, over 4 copies 183 us,
-and one copy reused 151 us.  Within a step combine reads the rows dispatch
-has just written, as the path does.
+Default workload: the DeepSeek-V3-like multi-node shuffle (T=16384, H=7168,
+E=256, k=8, R=64 in 8 virtual nodes, node deduplication), the largest
+configuration; the OLMoE-like, Qwen3-like and non-divisible workloads are
+measured the same way in the same run (`per_config`).
 
-Prints one JSON line.
-  value       algorithmic payload bytes per step / wall time per step, over K
-              steps bracketed by synchronize on both sides, no timing events
-              inside.  Schedule (--inflight auto): after the warmup, a short
-              trial of four schedules picks the fastest: serial (the steps
-              one after another on one stream), two_in_flight (step i on
-              stream i mod 2, each stream in order), staggered (as
-              two_in_flight, with each step's dispatch waiting on an event
-              after the previous step's dispatch, so a dispatch always runs
-              beside the other batch's combine) and plan_ahead (dispatch and
-              combine on one stream, each step's route plan on a second
-              stream while the previous step moves its rows).  The K timed steps run in the
-              chosen one; K steps of each other schedule are timed too and
-              reported beside it.
-  phases      route plan, dispatch and combine timed inside K more steps
-              run one after another on one stream, with HIP events on that
-              stream between the phases.  Inside a step, the non-temporal
-              writes a kernel leaves behind drain while the next kernel runs,
-              so each phase is timed in the order the step runs it (timed
-              alone, back to back, the same kernels measured the other way
-              round: qwen3 gather 117 us alone vs 93 us in a step, combine
-              104 vs 116 us).  An event exposes one kernel-launch latency
-              (about 2.5 us) that back-to-back kernels hide: the phase times
-              have it subtracted, estimated as (sum of the phase intervals -
-              the serial step time) / 3.  The value pass has no events.
-              Each phase also gives its median, p10 and p90 over the K steps.
-  roofline    the dominant kernel: its algorithmic bytes per launch / its mean
-              duration from the phase pass.
-              traffic = HBM bytes per launch from the rocprofv3 FETCH_SIZE /
-              WRITE_SIZE summary under profiles/, scaled by the copy
-              calibration; null if the kernel sources changed since.
-              traffic_over_algorithmic: above 1 means bytes moved twice.
-  copy_ceiling a plain device-to-device copy (torch copy_) moving the step's
-              bytes, half read and half written, over source/destination
-              pairs cycled past the MALL, K times: a practical ceiling, and
-              value over it.
+Timing protocol (`value`):
+  * W warmup steps, then EXACTLY K timed steps, bracketed by synchronize.
+  * Before each timed phase the last-level cache (256 MB MALL) is flushed:
+    a 1 GiB scratch buffer is written, then a second 1 GiB buffer is read, so
+    the phase finds neither its inputs nor dirty flush lines in the cache.
+    The flush is not timed.
+  * HIP events on the step's stream bracket phase 1 (route plan + dispatch)
+    and phase 2 (combine).
+  * value = algorithmic bytes per step / (median phase-1 time + median
+    phase-2 time); ms_per_step is that sum.  Mean, p10 and p90 are given for
+    each phase.
+  * An event interval also holds one kernel-launch latency (a few us) that
+    back-to-back kernels hide; it is not subtracted.
+
+Other figures in the same line:
+  kernels      every kernel's time, from a second pass of K flushed steps in
+               which the library times each launch with HIP events bound to
+               the kernel itself (moe_plan_timing): launches per step, mean
+               duration, algorithmic bytes, GB/s and fraction of 8 TB/s.
+  roofline     the kernel with the most time per step (of those that move the
+               payload): its algorithmic bytes per launch / its mean launch
+               duration.  traffic = its HBM bytes per launch from the
+               rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/,
+               scaled by the copy calibration; null once the kernel sources
+               have changed since the counters were taken.
+  schedules    back-to-back steps without flushes, over buffer sets cycled so
+               that the sets' inputs total at least 4x the MALL: serial (one
+               stream), two_in_flight (step i on stream i mod 2), staggered
+               (as two_in_flight, each dispatch after the previous step's
+               dispatch) and plan_ahead (each route plan on a second stream
+               during the previous step's movement).
+  copy_ceiling a plain device-to-device copy (torch copy_) of the step's
+               bytes, half read and half written, over buffer pairs cycled
+               past the MALL.
+  cpu_baseline the oracle (numpy, as it stands) on this host's cores, on the
+               headline workload: whole passes until --cpu-seconds is spent.
+
 Algorithmic bytes (payload rows only):
   dispatch single hop  (T + T*k) * 2H
   dispatch with dedup  (T + 2D + T*k) * 2H   (D staging rows, from the plan)
@@ -83,6 +78,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20   # MI355X last-level cache (AMD Infinity Cache)
+FLUSH_BYTES = 1 << 30
 MAX_SETS = 256
 METRIC = "dispatch+combine effective GB/s and % of HBM peak, 1 MI355X"
 SCHEDULES = ("serial", "two_in_flight", "staggered", "plan_ahead")
@@ -91,15 +87,22 @@ KERNEL_SOURCES = ("combine_shuffling_amd/csrc/move.hip", "combine_shuffling_amd/
                   "combine_shuffling_amd/csrc/pipeline.hip", "combine_shuffling_amd/csrc/plan_body.h",
                   "combine_shuffling_amd/csrc/moe_device.h",
                   "combine_shuffling_amd/csrc/moe_internal.h")
+# Kernels that carry no payload rows (plan metadata, counters).
+PLAN_KERNELS = ("route_count_kernel", "route_scan_kernel", "route_assign_kernel",
+                "traffic_clear_kernel", "traffic_kernel", "counters_clear_kernel")
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="olmoe",
-                    help="tiny | olmoe | qwen3 | dsv3 | nondiv (default: olmoe, the OLMoE-like prefill)")
+    ap.add_argument("--workload", default="dsv3",
+                    help="tiny | olmoe | qwen3 | dsv3 | nondiv (default: dsv3, the DeepSeek-V3-like "
+                         "multi-node shuffle with node deduplication)")
+    ap.add_argument("--configs", default="olmoe,qwen3,nondiv",
+                    help="further workloads measured the same way in this run, comma separated, "
+                         "or 'none'")
     ap.add_argument("--payload", choices=("bf16", "fp8"), default="bf16",
                     help="row payload: bf16, or fp8 (OCP E4M3 codes + one float32 scale per "
                          "128-element block; with node dedup, the staging rows are fp8 too)")
@@ -116,18 +119,12 @@ def parse():
     ap.add_argument("--single-hop", action="store_true",
                     help="plan a workload with virtual nodes (dsv3) as one node: the same routing "
                          "moved by the single-hop gather, the lower bound on its bytes")
+    ap.add_argument("--no-schedules", action="store_true",
+                    help="leave out the back-to-back schedule passes (for profiler runs, so every "
+                         "traced launch runs in the flushed protocol)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0: auto)")
-    ap.add_argument("--inflight", default="auto", choices=("auto", "1", "2", "staggered", "plan_ahead"),
-                    help="schedule of the steps.  1: one stream, every step after the previous "
-                         "one.  2: two batches in flight, step i on HIP stream i mod 2, each "
-                         "stream running its steps in order.  staggered: as 2, but each step's "
-                         "dispatch waits for the previous step's dispatch, so a dispatch always "
-                         "overlaps the other batch's combine.  plan_ahead: dispatch and combine "
-                         "on one stream, each step's route plan on a second stream during the "
-                         "previous step's movement.  auto (default): a short trial of the four "
-                         "after the warmup picks the fastest for the timed steps")
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled by the schedules (0: auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) a few "
                          "times, to scale hardware byte counters against a known size")
@@ -140,7 +137,7 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="size the copy calibration ran with (--copy-calibration MIB)")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def kernel_source_hash():
@@ -248,9 +245,9 @@ def summarize_trace(stats_csv, out, command):
     print(out)
 
 
-def recorded_traffic(workload, kernels):
-    """(kernel, traffic per launch) of the first of `kernels` (names separated by
-    '|') in the committed summary, if the summary is still current."""
+def recorded_traffic(workload, kernel):
+    """(kernel, traffic per launch) of `kernel` in the committed summary for
+    the workload, if the summary is still current."""
     path = os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None, None
@@ -258,14 +255,14 @@ def recorded_traffic(workload, kernels):
     s = json.loads(text)
     if s.get("source_hash") != kernel_source_hash():
         return None, None
-    for kernel in kernels.split("|"):
-        for name, v in s["kernels"].items():
-            if name.split("<")[0] == kernel:
-                return name, v["traffic_bytes"]
+    for name, v in s["kernels"].items():
+        if name.split("<")[0] == kernel:
+            return name, v["traffic_bytes"]
     return None, None
 
 
 def algorithmic_bytes(wl, D, payload="bf16", hier=False):
+    """(dispatch, combine) payload bytes of one step."""
     row = 2 * wl.hidden
     T, k = wl.num_tokens, wl.top_k
     if hier:
@@ -282,8 +279,28 @@ def algorithmic_bytes(wl, D, payload="bf16", hier=False):
     return disp, comb
 
 
-def cpu_baseline(batch, seconds, payload="bf16", band=0):
-    """The oracle (numpy, as it stands) timed on this host on the same batch."""
+def kernel_bytes(wl, D, payload="bf16"):
+    """Algorithmic payload bytes per step moved by each kernel (by symbol)."""
+    row = 2 * wl.hidden
+    row8 = wl.hidden + 4 * ((wl.hidden + 127) // 128)
+    T, k = wl.num_tokens, wl.top_k
+    single = (T + T * k) * row
+    return {
+        "gather_kernel": single, "gather_scan_kernel": single,
+        "stage_a_kernel": (T + D) * row, "stage_b_kernel": (D + T * k) * row,
+        "combine_kernel": (T * k + T) * row,
+        "combine_part_kernel": T * k * row + D * 2 * row,
+        "combine_nodes_kernel": D * 2 * row + T * row,
+        "gather_fp8_kernel": T * row + T * k * row8, "gather_fp8_scan_kernel": T * row + T * k * row8,
+        "stage_a_fp8_kernel": T * row + D * row8, "stage_b_fp8_kernel": D * row8 + T * k * row8,
+        "combine_fp8_kernel": T * k * row8 + T * row,
+        "pipeline_kernel": 2 * (T + T * k) * row,
+    }
+
+
+def cpu_baseline(batch, seconds, payload="bf16", band=0, hier=False):
+    """The oracle (numpy, as it stands) timed on this host on the same batch:
+    whole passes until `seconds` have been spent (at least one)."""
     import oracle
     from oracle import fp8 as ofp8
 
@@ -306,19 +323,310 @@ def cpu_baseline(batch, seconds, payload="bf16", band=0):
                 recv = oracle.dedup_stage_b(oracle.dedup_stage_a(batch.x, p), p)
             else:
                 recv = oracle.dispatch(batch.x, p)
-            oracle.combine(recv, batch.topk_w, p)
+            if hier:
+                oracle.combine_hierarchical(recv, batch.topk_w, p)
+            else:
+                oracle.combine(recv, batch.topk_w, p)
         D = p.get("num_staged", 0)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    disp, comb = algorithmic_bytes(wl, D, payload)
+    disp, comb = algorithmic_bytes(wl, D, payload, hier)
     return {"value": round((disp + comb) * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{reps} full passes of the {wl.name} batch ({payload} payload: "
-                      f"{'banded ' if band else ''}route plan, dispatch, combine in float64) "
-                      f"in {el:.1f} s on 1 thread; "
-                      f"os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"}
+            "sample": f"{reps} full pass(es) of the {wl.name} batch ({payload} payload: "
+                      f"{'banded ' if band else ''}route plan, dispatch, "
+                      f"{'hierarchical ' if hier else ''}combine in float64) in {el:.1f} s on "
+                      f"1 thread (numpy element-wise); os.cpu_count()={os.cpu_count()}, "
+                      f"affinity={len(os.sched_getaffinity(0))}"}
+
+
+def stats(ms):
+    """Median, mean, p10 and p90 of a list of milliseconds."""
+    a = np.asarray(ms, dtype=np.float64)
+    q = np.percentile(a, [50, 10, 90])
+    return {"ms_median": round(float(q[0]), 5), "ms_mean": round(float(a.mean()), 5),
+            "ms_p10": round(float(q[1]), 5), "ms_p90": round(float(q[2]), 5)}
+
+
+class Flush:
+    """Evicts the last-level cache: writes a 1 GiB scratch buffer, then reads
+    another 1 GiB buffer (clean lines of unrelated data in the cache)."""
+
+    def __init__(self, torch, dev):
+        n = FLUSH_BYTES // 4
+        self.w = torch.empty(n, dtype=torch.int32, device=dev)
+        self.r = torch.ones(n, dtype=torch.int32, device=dev)
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.w.fill_(self.i)
+        return self.r.sum()
+
+
+def run_workload(torch, cs, gen, name, args, dev, flush, primary):
+    """Everything measured on one workload; returns (result dict, batch)."""
+    wl = gen.get(name)
+    fp8 = args.payload == "fp8"
+    batch = gen.make_batch(wl)
+    if args.single_hop and wl.node_dedup:
+        # the same routing, planned as one node: dispatch is the single-hop gather
+        wl = dataclasses.replace(wl, name=wl.name + "-single-hop", ranks_per_node=wl.num_ranks)
+    T, H, k = wl.num_tokens, wl.hidden, wl.top_k
+    la = args.load_aware_forwarders and wl.node_dedup
+    hier = args.hier_combine and wl.node_dedup
+    pipe = args.pipeline and not wl.node_dedup and not fp8
+    band = args.band_tokens if pipe else 0
+
+    x0 = torch.from_numpy(batch.x.view(np.int16)).to(dev)
+    idx0 = torch.from_numpy(batch.topk_idx).to(dev)
+    w0 = torch.from_numpy(batch.topk_w).to(dev)
+
+    def new_set(x, idx, w):
+        plan = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la,
+                       band)
+        s = dict(plan=plan, x=x, idx=idx, w=w,
+                 recv=torch.empty((plan.recv_rows, H), dtype=torch.int16, device=dev),
+                 staging=(torch.empty((plan.staging_rows_max, H), dtype=torch.int16, device=dev)
+                          if wl.node_dedup else None),
+                 out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+        if hier:
+            s["part"] = torch.empty((plan.staging_rows_max, H), dtype=torch.float32, device=dev)
+        if fp8:
+            s["recv"] = torch.empty((plan.recv_rows, H), dtype=torch.uint8, device=dev)
+            s["scale"] = torch.empty((plan.recv_rows, plan.scale_blocks), dtype=torch.float32,
+                                     device=dev)
+            if wl.node_dedup:
+                s["staging"] = torch.empty((plan.staging_rows_max, H), dtype=torch.uint8, device=dev)
+                s["sscale"] = torch.empty((plan.staging_rows_max, plan.scale_blocks),
+                                          dtype=torch.float32, device=dev)
+        return s
+
+    def do_route(s, st=None):
+        s["plan"].route(s["idx"], stream=st)
+
+    def do_dispatch(s, st=None):
+        if fp8:
+            s["plan"].dispatch_fp8(s["x"], s["recv"], s["scale"], s["staging"], s.get("sscale"),
+                                   stream=st)
+        else:
+            s["plan"].dispatch(s["x"], s["recv"], s["staging"], stream=st)
+
+    def do_combine(s, st=None):
+        if hier:
+            s["plan"].combine_hier(s["recv"], s["w"], s["part"], s["out"], stream=st)
+        elif fp8:
+            s["plan"].combine_fp8(s["recv"], s["scale"], s["w"], s["out"], stream=st)
+        else:
+            s["plan"].combine(s["recv"], s["w"], s["out"], stream=st)
+
+    def phase1(s, st=None):
+        if pipe:
+            s["plan"].pipeline(s["idx"], s["x"], s["w"], s["recv"], s["out"], stream=st)
+        else:
+            do_route(s, st)
+            do_dispatch(s, st)
+
+    def step(s, st=None):
+        phase1(s, st)
+        if not pipe:
+            do_combine(s, st)
+
+    main = torch.cuda.current_stream(dev)
+    s0 = new_set(x0, idx0, w0)
+
+    def protocol_steps(n, flush_mid=True, timing=False):
+        """n flushed steps on stream 0: flush, phase 1, flush, phase 2."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for i in range(n):
+            ev = evs[i]
+            flush()
+            ev[0].record()
+            phase1(s0)
+            ev[1].record()
+            if not pipe:
+                if flush_mid:
+                    flush()
+                ev[2].record()
+                do_combine(s0)
+                ev[3].record()
+        torch.cuda.synchronize()
+        p1 = [e[0].elapsed_time(e[1]) for e in evs]
+        p2 = [] if pipe else [e[2].elapsed_time(e[3]) for e in evs]
+        return p1, p2
+
+    # Warmup, in the protocol's own flushed form.
+    protocol_steps(max(1, args.warmup))
+    D = int(s0["plan"].read("num_staged")[0]) if wl.node_dedup else 0
+    fwd_rows = None
+    if wl.node_dedup:
+        per = np.diff(s0["plan"].read("stage_offsets"))
+        fwd_rows = {"rule": "load_aware" if la else "static", "max": int(per.max()),
+                    "mean": round(float(per.mean()), 1),
+                    "max_over_mean": round(float(per.max() / max(per.mean(), 1e-9)), 4)}
+    disp_b, comb_b = algorithmic_bytes(wl, D, args.payload, hier)
+    step_b = disp_b + comb_b
+
+    # The timed region: exactly K flushed steps, bracketed by synchronize.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    p1, p2 = protocol_steps(args.steps)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    s1, s2 = stats(p1), (stats(p2) if p2 else None)
+    ms_step = s1["ms_median"] + (s2["ms_median"] if s2 else 0.0)
+    value = step_b / (ms_step * 1e-3) / 1e9
+    if pipe:
+        phases = {"pipeline": {"bytes": step_b, **s1, "GB/s": round(step_b / (s1["ms_median"] * 1e-3) / 1e9, 1)}}
+    else:
+        phases = {"route_dispatch": {"bytes": disp_b, **s1,
+                                     "GB/s": round(disp_b / (s1["ms_median"] * 1e-3) / 1e9, 1)},
+                  "combine": {"bytes": comb_b, **s2,
+                              "GB/s": round(comb_b / (s2["ms_median"] * 1e-3) / 1e9, 1)}}
+    res = {"value": round(value, 2), "ms_per_step": round(ms_step, 5),
+           "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+           "bytes_per_step": step_b,
+           "config": {"workload": wl.name, "T": T, "H": H, "E": wl.num_experts, "k": k,
+                      "R": wl.num_ranks, "G": wl.ranks_per_node, "node_dedup": wl.node_dedup,
+                      "staging_rows": D, "seed": wl.seed, "payload": args.payload,
+                      "forwarder_rows": fwd_rows,
+                      "combine": "hierarchical" if hier else "direct",
+                      "path": f"pipeline, bands of {band} tokens" if pipe else "separate launches"},
+           "protocol": {"flush": "1 GiB written, then another 1 GiB read, before each phase "
+                                 "(not timed)",
+                        "phases": phases, "wall_ms_per_step_incl_flush": round(wall_ms, 5)}}
+    if not pipe and wl.name.startswith("olmoe"):
+        # The receive rows (128 MiB) fit the MALL: the combine without the
+        # flush between the phases, for comparison.
+        _, p2r = protocol_steps(args.steps, flush_mid=False)
+        r = stats(p2r)
+        res["protocol"]["combine_mall_resident"] = {
+            **r, "GB/s": round(comb_b / (r["ms_median"] * 1e-3) / 1e9, 1),
+            "note": "no flush between dispatch and combine: the receive rows stay in the MALL"}
+
+    # Kernel pass: K more flushed steps with every launch timed by the library
+    # (the event pairs are read back, and so reused, after each step).
+    s0["plan"].timing(256)
+    launches = []
+    for _ in range(args.steps):
+        protocol_steps(1)
+        launches += s0["plan"].timing_read()
+    s0["plan"].timing(0)
+    kb = kernel_bytes(wl, D, args.payload)
+    agg = {}
+    for kname, ms in launches:
+        a = agg.setdefault(kname, [0, 0.0])
+        a[0] += 1
+        a[1] += ms
+    kernels = {}
+    for kname, (n, tot) in agg.items():
+        e = {"launches_per_step": round(n / args.steps, 3), "avg_us": round(1e3 * tot / n, 3),
+             "us_per_step": round(1e3 * tot / args.steps, 3)}
+        if kname in kb:
+            gbs = kb[kname] / (tot / args.steps * 1e-3) / 1e9
+            e.update({"bytes_per_step": kb[kname], "GB/s": round(gbs, 1),
+                      "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        kernels[kname] = e
+    res["kernels"] = kernels
+    moving = [kn for kn in kernels if kn in kb]
+    dom = max(moving, key=lambda kn: kernels[kn]["us_per_step"])
+    dk = kernels[dom]
+    per_launch_b = kb[dom] / dk["launches_per_step"]
+    variant = ("_pipeline" if pipe else "_fp8" if fp8 else "_hier" if hier else
+               "_single_hop" if wl.name.endswith("-single-hop") else "")
+    traffic_kernel, traffic = recorded_traffic(name + variant, dom)
+    res["roofline"] = {"bound": "hbm", "kernel": traffic_kernel or dom, "achieved": dk["GB/s"],
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["frac"],
+                       "traffic": traffic,
+                       "traffic_over_algorithmic": (None if traffic is None else
+                                                    round(traffic / per_launch_b, 4)),
+                       "bytes_per_launch": int(round(per_launch_b)), "us_per_launch": dk["avg_us"],
+                       "launches_per_step": dk["launches_per_step"],
+                       "timing": "HIP events bound to each launch (moe_plan_timing), flushed steps"}
+
+    if not args.no_schedules:
+        res["schedules"] = schedules(torch, wl, args, dev, x0, idx0, w0, new_set, do_route,
+                                     do_dispatch, do_combine, step, pipe, step_b)
+        res["copy_ceiling"] = copy_ceiling(torch, dev, step_b // 2, args.steps)
+        res["copy_ceiling"]["value_over_copy"] = round(value / res["copy_ceiling"]["GB/s"], 4)
+    del s0
+    torch.cuda.empty_cache()
+    return res, batch, hier, band
+
+
+def schedules(torch, wl, args, dev, x0, idx0, w0, new_set, do_route, do_dispatch, do_combine,
+              step, pipe, step_b):
+    """Back-to-back steps (no flush) in four schedules over cycled buffer sets."""
+    set_b = (x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4)
+    probe = new_set(x0, idx0, w0)
+    full_b = set_b + sum(t.numel() * t.element_size() for key, t in probe.items()
+                         if key in ("recv", "staging", "out", "part", "scale", "sscale")
+                         and t is not None) + probe["plan"].workspace_bytes
+    del probe
+    max_inflight = 1 if pipe else 2
+    n_sets = args.sets or min(MAX_SETS, max(2, math.ceil((2 << 30) / full_b),
+                                            math.ceil(4 * MALL_BYTES / set_b)))
+    n_sets = -(-n_sets // max_inflight) * max_inflight
+    sets = [new_set(x0.clone(), idx0.clone(), w0.clone()) for _ in range(n_sets)]
+    streams = [torch.cuda.current_stream(dev)] + [torch.cuda.Stream(dev)
+                                                  for _ in range(max_inflight - 1)]
+
+    def staggered_step(i, done):
+        s, st = sets[i % n_sets], streams[i % 2]
+        do_route(s, st)
+        if i > 0:
+            st.wait_event(done[(i - 1) % 2])
+        do_dispatch(s, st)
+        done[i % 2].record(st)
+        do_combine(s, st)
+
+    def plan_ahead_steps(steps):
+        main, side = streams[0], streams[1]
+        routed = [torch.cuda.Event(), torch.cuda.Event()]
+        moving = torch.cuda.Event()
+        do_route(sets[0], side)
+        routed[0].record(side)
+        for i in range(steps):
+            s = sets[i % n_sets]
+            main.wait_event(routed[i % 2])
+            moving.record(main)
+            do_dispatch(s, main)
+            do_combine(s, main)
+            if i + 1 < steps:
+                s1 = sets[(i + 1) % n_sets]
+                side.wait_event(moving)
+                do_route(s1, side)
+                routed[(i + 1) % 2].record(side)
+
+    def timed(schedule, steps):
+        done = [torch.cuda.Event(), torch.cuda.Event()]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if schedule == "plan_ahead":
+            plan_ahead_steps(steps)
+        else:
+            for i in range(steps):
+                if schedule == "staggered":
+                    staggered_step(i, done)
+                else:
+                    step(sets[i % n_sets], streams[i % (2 if schedule == "two_in_flight" else 1)])
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    for i in range(max(args.warmup, n_sets)):
+        step(sets[i % n_sets], streams[i % max_inflight])
+    names = SCHEDULES if max_inflight == 2 else ("serial",)
+    out = {"buffer_sets": n_sets}
+    for nm in names:
+        ms = timed(nm, args.steps)
+        v = step_b / (ms * 1e-3) / 1e9
+        out[nm] = {"ms_per_step": round(ms, 5), "value": round(v, 2),
+                   "pct_of_hbm_peak": round(100.0 * v / HBM_PEAK_GBS, 2)}
+    out["best"] = min(names, key=lambda nm: out[nm]["ms_per_step"])
+    del sets
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -337,6 +645,9 @@ def main():
               f"partitions of a single MI355X's HBM; --gpus {args.gpus} is not supported.",
               file=sys.stderr)
         sys.exit(2)
+    if args.hier_combine and args.payload == "fp8":
+        print("the hierarchical combine takes the bf16 payload", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -345,308 +656,45 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    wl = gen.get(args.workload)
-    fp8 = args.payload == "fp8"
-    batch = gen.make_batch(wl)
-    if args.single_hop and wl.node_dedup:
-        # the same routing, planned as one node: dispatch is the single-hop gather
-        wl = dataclasses.replace(wl, name=wl.name + "-single-hop", ranks_per_node=wl.num_ranks)
-    T, H, k = wl.num_tokens, wl.hidden, wl.top_k
+    flush = Flush(torch, dev)
+    head, batch, hier, band = run_workload(torch, cs, gen, args.workload, args, dev, flush, True)
+    print(f"# {args.workload}: {head['value']} GB/s ({head['pct_of_hbm_peak']}%)", file=sys.stderr,
+          flush=True)
+    per_config = {}
+    extra = [] if args.configs in ("", "none") else args.configs.split(",")
+    for nm in extra:
+        if nm == args.workload:
+            continue
+        r, _, _, _ = run_workload(torch, cs, gen, nm, args, dev, flush, False)
+        per_config[nm] = r
+        print(f"# {nm}: {r['value']} GB/s ({r['pct_of_hbm_peak']}%)", file=sys.stderr, flush=True)
 
-    x0 = torch.from_numpy(batch.x.view(np.int16)).to(dev)
-    idx0 = torch.from_numpy(batch.topk_idx).to(dev)
-    w0 = torch.from_numpy(batch.topk_w).to(dev)
-
-    la = args.load_aware_forwarders and wl.node_dedup
-    hier = args.hier_combine and wl.node_dedup
-    if hier and fp8:
-        print("the hierarchical combine takes the bf16 payload", file=sys.stderr)
-        sys.exit(2)
-    pipe = args.pipeline
-    if pipe and (wl.node_dedup or fp8):
-        print("the banded pipeline runs single-hop workloads with the bf16 payload",
-              file=sys.stderr)
-        sys.exit(2)
-    band = args.band_tokens if pipe else 0
-    probe = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la,
-                    band)
-    set_bytes = (x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4 + probe.workspace_bytes
-                 + probe.recv_rows * H * (1 if fp8 else 2) + probe.staging_rows_max * H * 2
-                 + T * H * 2)
-    in_bytes = x0.numel() * 2 + idx0.numel() * 4 + w0.numel() * 4
-    auto = str(args.inflight) == "auto"
-    max_inflight = 1 if pipe or args.inflight == "1" else 2
-    n_sets = args.sets or min(MAX_SETS, max(2, math.ceil((2 << 30) / set_bytes),
-                                            math.ceil(4 * MALL_BYTES / in_bytes)))
-    # a set always runs on the same stream, so its reuse is ordered after its last use
-    n_sets = -(-n_sets // max_inflight) * max_inflight
-    sets = []
-    for _ in range(n_sets):
-        plan = cs.Plan(T, H, wl.num_experts, k, wl.num_ranks, wl.ranks_per_node, wl.node_dedup, la,
-                       band)
-        s = dict(plan=plan, x=x0.clone(), idx=idx0.clone(), w=w0.clone(),
-                 recv=torch.empty((plan.recv_rows, H), dtype=torch.int16, device=dev),
-                 staging=(torch.empty((plan.staging_rows_max, H), dtype=torch.int16, device=dev)
-                          if wl.node_dedup else None),
-                 out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
-        if hier:
-            s["part"] = torch.empty((plan.staging_rows_max, H), dtype=torch.float32, device=dev)
-        if fp8:
-            s["recv"] = torch.empty((plan.recv_rows, H), dtype=torch.uint8, device=dev)
-            s["scale"] = torch.empty((plan.recv_rows, plan.scale_blocks), dtype=torch.float32,
-                                     device=dev)
-            if wl.node_dedup:
-                s["staging"] = torch.empty((plan.staging_rows_max, H), dtype=torch.uint8, device=dev)
-                s["sscale"] = torch.empty((plan.staging_rows_max, plan.scale_blocks),
-                                          dtype=torch.float32, device=dev)
-        sets.append(s)
-
-    # Stream 0 is torch's current stream; the others are plain streams of the
-    # default priority.
-    streams = [torch.cuda.current_stream(dev)] + [torch.cuda.Stream(dev)
-                                                  for _ in range(max_inflight - 1)]
-
-    def do_dispatch(s, st=None):
-        if fp8:
-            s["plan"].dispatch_fp8(s["x"], s["recv"], s["scale"], s["staging"], s.get("sscale"),
-                                   stream=st)
-        else:
-            s["plan"].dispatch(s["x"], s["recv"], s["staging"], stream=st)
-
-    def do_combine(s, st=None):
-        if hier:
-            s["plan"].combine_hier(s["recv"], s["w"], s["part"], s["out"], stream=st)
-        elif fp8:
-            s["plan"].combine_fp8(s["recv"], s["scale"], s["w"], s["out"], stream=st)
-        else:
-            s["plan"].combine(s["recv"], s["w"], s["out"], stream=st)
-
-    def step(s, st=None):
-        if pipe:
-            s["plan"].pipeline(s["idx"], s["x"], s["w"], s["recv"], s["out"], stream=st)
-            return
-        s["plan"].route(s["idx"], stream=st)
-        do_dispatch(s, st)
-        do_combine(s, st)
-
-    def staggered_step(i, done):
-        """Step i on stream i % 2, its dispatch after step i - 1's dispatch
-        (event done[i - 1]), so that it overlaps step i - 1's combine."""
-        s, st = sets[i % n_sets], streams[i % 2]
-        s["plan"].route(s["idx"], stream=st)
-        if i > 0:
-            st.wait_event(done[(i - 1) % 2])
-        do_dispatch(s, st)
-        done[i % 2].record(st)
-        do_combine(s, st)
-
-    def plan_ahead_steps(steps):
-        """Step i's dispatch and combine on stream 0; its route plan on
-        stream 1, during step i - 1's dispatch and combine (the event moving
-        orders it after step i - 2, the last user of its buffer set)."""
-        main, side = streams[0], streams[1]
-        routed = [torch.cuda.Event(), torch.cuda.Event()]
-        moving = torch.cuda.Event()
-        sets[0]["plan"].route(sets[0]["idx"], stream=side)
-        routed[0].record(side)
-        for i in range(steps):
-            s = sets[i % n_sets]
-            main.wait_event(routed[i % 2])
-            moving.record(main)
-            do_dispatch(s, main)
-            do_combine(s, main)
-            if i + 1 < steps:
-                s1 = sets[(i + 1) % n_sets]
-                side.wait_event(moving)
-                s1["plan"].route(s1["idx"], stream=side)
-                routed[(i + 1) % 2].record(side)
-
-    def timed_steps(schedule, steps=None):
-        """Wall time per step of K steps in one schedule: "serial" (one
-        stream), "two_in_flight" (step i on stream i % 2), "staggered" or
-        "plan_ahead"."""
-        steps = args.steps if steps is None else steps
-        done = [torch.cuda.Event(), torch.cuda.Event()]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        if schedule == "plan_ahead":
-            plan_ahead_steps(steps)
-        for i in range(steps if schedule != "plan_ahead" else 0):
-            if schedule == "staggered":
-                staggered_step(i, done)
-            else:
-                step(sets[i % n_sets], streams[i % (2 if schedule == "two_in_flight" else 1)])
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / steps
-
-    for i in range(args.warmup):
-        step(sets[i % n_sets], streams[i % max_inflight])
-    torch.cuda.synchronize()
-    # Schedule: a trial of each, apart from the timed steps, picks the fastest.
-    trial = None
-    if max_inflight == 1:
-        schedule = "serial"
-    elif auto:
-        n_trial = max(20, args.steps // 4)
-        trial = {name: timed_steps(name, n_trial) for name in SCHEDULES}
-        schedule = min(trial, key=trial.get)
-    else:
-        schedule = {"2": "two_in_flight"}.get(args.inflight, args.inflight)
-    inflight = 1 if schedule == "serial" else 2
-    D = int(sets[0]["plan"].read("num_staged")[0]) if wl.node_dedup else 0
-    fwd_rows = None
-    if wl.node_dedup:
-        per = np.diff(sets[0]["plan"].read("stage_offsets"))
-        fwd_rows = {"rule": "load_aware" if la else "static", "max": int(per.max()),
-                    "mean": round(float(per.mean()), 1),
-                    "max_over_mean": round(float(per.max() / max(per.mean(), 1e-9)), 4)}
-    disp_b, comb_b = algorithmic_bytes(wl, D, args.payload, hier)
-
-    # Timed region: K steps and nothing else, with `inflight` batches in
-    # flight; then K steps of the other schedule, reported beside it.
-    ms_per_step = timed_steps(schedule)
-    value = (disp_b + comb_b) / (ms_per_step * 1e-3) / 1e9
-    per_schedule = {schedule: ms_per_step}
-    for name in (SCHEDULES if max_inflight == 2 else ("serial",)):
-        if name not in per_schedule:
-            per_schedule[name] = timed_steps(name)
-    serial_ms = per_schedule["serial"]
-    serial_value = (disp_b + comb_b) / (serial_ms * 1e-3) / 1e9
-
-    def schedule_entry(name):
-        if name not in per_schedule:
-            return None
-        v = (disp_b + comb_b) / (per_schedule[name] * 1e-3) / 1e9
-        return {"ms_per_step": round(per_schedule[name], 5), "value": round(v, 2),
-                "pct_of_hbm_peak": round(100.0 * v / HBM_PEAK_GBS, 2)}
-
-    # Phase pass: K more steps one after another on stream 0, with events
-    # between the phases (route plan | dispatch | combine).
-    def phase_pass():
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            s, ev = sets[i % n_sets], evs[i]
-            ev[0].record()
-            if pipe:
-                step(s)
-                ev[1].record()
-                ev[2].record()
-            else:
-                s["plan"].route(s["idx"])
-                ev[1].record()
-                do_dispatch(s)
-                ev[2].record()
-                do_combine(s)
-            ev[3].record()
-        torch.cuda.synchronize()
-        return np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]),
-                          e[2].elapsed_time(e[3])] for e in evs])
-
-    phase_t = phase_pass()
-    route_ms, disp_ms, comb_ms = (float(v) for v in phase_t.mean(axis=0))
-    # An event makes the GPU finish the kernel before it and only then launch
-    # the next one, so each interval also holds one kernel-launch latency
-    # that back-to-back kernels hide.  The same steps without events (the
-    # serial timing above) give it: (sum of intervals - step) / intervals.
-    intervals = 1 if pipe else 3
-    event_gap_ms = max(0.0, ((route_ms + disp_ms + comb_ms) if not pipe else route_ms) - serial_ms)
-    event_gap_ms /= intervals
-    route_ms -= event_gap_ms
-    disp_ms -= event_gap_ms
-    comb_ms -= event_gap_ms
-    phase_t = phase_t - event_gap_ms
-
-    def spread(col):
-        """Median, p10 and p90 over the K steps of one phase (event gap removed)."""
-        q = np.percentile(phase_t[:, col], [50, 10, 90])
-        return {"ms_median": round(float(q[0]), 5), "ms_p10": round(float(q[1]), 5),
-                "ms_p90": round(float(q[2]), 5)}
-    if pipe:
-        # one launch per step does everything
-        pipe_ms = route_ms
-        disp_ms = comb_ms = pipe_ms
-        disp_gbs = comb_gbs = (disp_b + comb_b) / (pipe_ms * 1e-3) / 1e9
-    else:
-        disp_gbs = disp_b / (disp_ms * 1e-3) / 1e9
-        comb_gbs = comb_b / (comb_ms * 1e-3) / 1e9
-    if pipe:
-        dom = ("pipeline_kernel", disp_b + comb_b, pipe_ms, disp_gbs)
-    elif hier:
-        # both phases are two launches here; report the combine phase
-        dom = ("combine_part_kernel+combine_nodes_kernel", comb_b, comb_ms, comb_gbs)
-    elif wl.node_dedup:
-        # dispatch is two launches here; the dominant single launch timed is combine
-        dom = ("combine_fp8_kernel" if fp8 else "combine_kernel", comb_b, comb_ms, comb_gbs)
-    else:
-        sfx = "_fp8" if fp8 else ""
-        # small single-hop plans scan inside the gather (gather_scan_kernel)
-        gname = "gather_fp8_scan_kernel|gather_fp8_kernel" if fp8 else "gather_scan_kernel|gather_kernel"
-        dom = max([(gname, disp_b, disp_ms, disp_gbs),
-                   (f"combine{sfx}_kernel", comb_b, comb_ms, comb_gbs)], key=lambda d: d[2])
-
-    # Practical ceiling: a plain device-to-device copy moving the step's bytes
-    # (half read, half written), its sources and destinations cycled past the
-    # MALL like the step's buffers.
-    copy = copy_ceiling(torch, dev, (disp_b + comb_b) // 2, args.steps)
-    copy["value_over_copy"] = round(value / copy["GB/s"], 4)
-
-    # which committed traffic summary covers this run
-    variant = ("_pipeline" if pipe else "_fp8" if fp8 else "_hier" if hier else
-               "_single_hop" if wl.name.endswith("-single-hop") else "")
-    traffic_kernel, traffic = recorded_traffic(args.workload + variant, dom[0])
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": args.payload,
         "data": "synthetic",
-        "config": {"workload": wl.name, "T": T, "H": H, "E": wl.num_experts, "k": k,
-                   "R": wl.num_ranks, "G": wl.ranks_per_node, "node_dedup": wl.node_dedup,
-                   "staging_rows": D, "seed": wl.seed, "buffer_sets": n_sets,
-                   "payload": args.payload, "forwarder_rows": fwd_rows,
-                   "combine": "hierarchical" if hier else "direct",
-                   "path": f"pipeline, bands of {band} tokens" if pipe else "separate launches",
-                   "batches_in_flight": inflight,
-                   "schedule": schedule,
-                   "schedule_choice": "trial" if trial else "fixed"},
-        "serial": {"ms_per_step": round(serial_ms, 5), "value": round(serial_value, 2),
-                   "pct_of_hbm_peak": round(100.0 * serial_value / HBM_PEAK_GBS, 2)},
-        "two_in_flight": schedule_entry("two_in_flight"),
-        "staggered": schedule_entry("staggered"),
-        "plan_ahead": schedule_entry("plan_ahead"),
-        "schedule_trial_ms_per_step": (None if trial is None else
-                                       {k2: round(v2, 5) for k2, v2 in trial.items()}),
-        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "bytes_per_step": disp_b + comb_b,
-        "phases": ({"pipeline": {"bytes": disp_b + comb_b, "ms_per_launch": round(pipe_ms, 5),
-                                 "GB/s": round(disp_gbs, 1), "launches": 1}} if pipe else
-                   {"route": {"ms_per_step": round(route_ms, 5), **spread(0)},
-                    "dispatch": {"bytes": disp_b, "ms_per_launch": round(disp_ms, 5),
-                                 "GB/s": round(disp_gbs, 1), "launches": 2 if wl.node_dedup else 1,
-                                 **spread(1)},
-                    "combine": {"bytes": comb_b, "ms_per_launch": round(comb_ms, 5),
-                                "GB/s": round(comb_gbs, 1), "launches": 2 if hier else 1,
-                                **spread(2)}}),
-        "copy_ceiling": copy,
-        "roofline": {"bound": "hbm", "kernel": traffic_kernel or dom[0], "achieved": round(dom[3], 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "traffic_over_algorithmic": (None if traffic is None or not dom[1] else
-                                                  round(traffic / dom[1], 4)),
-                     "bytes_per_launch": dom[1], "ms_per_launch": round(float(dom[2]), 5),
-                     "event_gap_ms": round(event_gap_ms, 5)},
+        "config": head["config"],
+        "pct_of_hbm_peak": head["pct_of_hbm_peak"],
+        "bytes_per_step": head["bytes_per_step"],
+        "protocol": head["protocol"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "schedules": head.get("schedules"),
+        "copy_ceiling": head.get("copy_ceiling"),
+        "per_config": per_config,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, args.payload, band)
+        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, args.payload, band, hier)
     print(json.dumps(result), flush=True)
 
 

@@ -256,6 +256,23 @@ class Plan:
                    "moe_combine_fp8")
         return out
 
+    # -- moe_plan_timing / moe_plan_timing_read
+    def timing(self, capacity: int) -> None:
+        """Time each kernel this plan's calls launch (up to `capacity` launches;
+        0 stops).  Needs the plan's device to be current."""
+        _abi.check(self._lib.moe_plan_timing(self._h, int(capacity)), "moe_plan_timing")
+        self._timing_cap = int(capacity)
+
+    def timing_read(self) -> list[tuple[str, float]]:
+        """(kernel name, milliseconds) of each timed launch since the last read, in order."""
+        cap = getattr(self, "_timing_cap", 0)
+        ids = (ctypes.c_int32 * max(cap, 1))()
+        ms = (ctypes.c_float * max(cap, 1))()
+        n = ctypes.c_int32()
+        _abi.check(self._lib.moe_plan_timing_read(self._h, ids, ms, cap, ctypes.byref(n)),
+                   "moe_plan_timing_read")
+        return [(_abi.kernel_name(ids[i]), float(ms[i])) for i in range(min(n.value, cap))]
+
     # -- moe_plan_read
     def read(self, item: str, stream=None) -> np.ndarray:
         nb = self.bands

@@ -53,7 +53,10 @@ EXPORTS = (
     "moe_plan_recv_rows", "moe_plan_staging_rows_max", "moe_route_plan", "moe_dispatch",
     "moe_combine", "moe_plan_read", "moe_status_str", "moe_plan_scale_blocks",
     "moe_dispatch_fp8", "moe_combine_fp8", "moe_combine_hier", "moe_plan_bands", "moe_pipeline",
+    "moe_kernel_name", "moe_plan_timing", "moe_plan_timing_read",
 )
+
+KERNEL_COUNT = 19
 
 
 class MoeError(RuntimeError):
@@ -107,10 +110,21 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_bands.restype = i64
     L.moe_pipeline.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]
     L.moe_pipeline.restype = i32
+    L.moe_kernel_name.argtypes = [i32]
+    L.moe_kernel_name.restype = ctypes.c_char_p
+    L.moe_plan_timing.argtypes = [vp, i32]
+    L.moe_plan_timing.restype = i32
+    L.moe_plan_timing_read.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float), i32,
+                                       ctypes.POINTER(i32)]
+    L.moe_plan_timing_read.restype = i32
     L.moe_status_str.argtypes = [i32]
     L.moe_status_str.restype = ctypes.c_char_p
     _lib = L
     return L
+
+
+def kernel_name(kernel: int) -> str:
+    return lib().moe_kernel_name(kernel).decode()
 
 
 def status_str(status: int) -> str:

@@ -12,6 +12,15 @@
 
 #include "moe_internal.h"
 
+namespace moe {
+// Event pairs of moe_plan_timing and the kernel of each recorded launch.
+struct LaunchTimer {
+  std::vector<hipEvent_t> start, stop;
+  std::vector<int32_t> ids;
+  int used = 0;
+};
+}  // namespace moe
+
 struct moe_plan {
   moe_config cfg;
   moe::Dims d;
@@ -24,7 +33,7 @@ struct moe_plan {
   bool routed;     // route_count has been launched for the bound routing
   bool scanned;    // route_scan has been launched for it (tile bases, offsets, status)
   bool assigned;   // slot_of / row_src (and stage_of / stage_src) are final
-  void* clean_ws;  // workspace whose pipeline counters are known to be zero
+  moe::LaunchTimer* timer;  // per-launch timing, or null
 };
 
 namespace moe {
@@ -36,7 +45,37 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The timer of the plan whose call is running on this thread.
+thread_local LaunchTimer* tl_timer = nullptr;
+
+// Makes `plan`'s timer the active one for the lifetime of the scope (each
+// API call that launches kernels opens one).
+struct TimerScope {
+  LaunchTimer* prev;
+  explicit TimerScope(const moe_plan* plan) : prev(tl_timer) { tl_timer = plan->timer; }
+  ~TimerScope() { tl_timer = prev; }
+};
+
+void destroy_events(LaunchTimer* t) {
+  for (hipEvent_t e : t->start) hipEventDestroy(e);
+  for (hipEvent_t e : t->stop) hipEventDestroy(e);
+  t->start.clear();
+  t->stop.clear();
+  t->ids.clear();
+  t->used = 0;
+}
+
 }  // namespace
+
+bool timer_take(int id, hipEvent_t* start, hipEvent_t* stop) {
+  LaunchTimer* t = tl_timer;
+  if (t == nullptr || t->used >= (int)t->start.size()) return false;
+  *start = t->start[t->used];
+  *stop = t->stop[t->used];
+  t->ids[t->used] = id;
+  ++t->used;
+  return true;
+}
 
 Layout make_layout(const Dims& d) {
   Layout l{};
@@ -102,15 +141,6 @@ Work bind_work(const Layout& l, void* base) {
   w.send_copies = p(l.send_copies);
   w.node_copies = p(l.node_copies);
   return w;
-}
-
-// The first pipeline launch of a plan on a workspace zeroes its counters;
-// every pipeline launch leaves them at zero.
-moe_status ensure_counters_clear(moe_plan* plan, hipStream_t s) {
-  if (plan->clean_ws == plan->ws) return MOE_OK;
-  if (launch_counters_clear(plan->d, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
-  plan->clean_ws = plan->ws;
-  return MOE_OK;
 }
 
 // Launches the plan's scan if the route left it to the gather (small plans).
@@ -226,7 +256,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
     d.nbands = 1;
   }
   // Small single-hop plans: the gather scans the tile counts itself.
-  d.fused_scan = (MOE_FUSED_SCAN && !dedup && d.nbands == 1 &&
+  d.fused_scan = (!dedup && d.nbands == 1 &&
                   (int64_t)d.nblk * d.E <= moe::kFusedScanInts) ? 1 : 0;
   d.chunks = (int32_t)chunks;
   d.segs = (int32_t)((chunks + moe::kWave - 1) / moe::kWave);
@@ -243,12 +273,80 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan** out) {
   p->routed = false;
   p->scanned = false;
   p->assigned = false;
-  p->clean_ws = nullptr;
+  p->timer = nullptr;
   *out = p;
   return MOE_OK;
 }
 
-void moe_plan_destroy(moe_plan* plan) { delete plan; }
+void moe_plan_destroy(moe_plan* plan) {
+  if (plan && plan->timer) {
+    moe::destroy_events(plan->timer);
+    delete plan->timer;
+  }
+  delete plan;
+}
+
+const char* moe_kernel_name(int32_t kernel) {
+  static const char* const names[MOE_KERNEL_COUNT] = {
+      "route_count_kernel",   "route_scan_kernel",      "route_assign_kernel",
+      "traffic_clear_kernel", "traffic_kernel",         "gather_kernel",
+      "gather_scan_kernel",   "stage_a_kernel",         "stage_b_kernel",
+      "combine_kernel",       "combine_part_kernel",    "combine_nodes_kernel",
+      "gather_fp8_kernel",    "gather_fp8_scan_kernel", "stage_a_fp8_kernel",
+      "stage_b_fp8_kernel",   "combine_fp8_kernel",     "pipeline_kernel",
+      "counters_clear_kernel"};
+  return kernel >= 0 && kernel < MOE_KERNEL_COUNT ? names[kernel] : "?";
+}
+
+moe_status moe_plan_timing(moe_plan* plan, int32_t capacity) {
+  if (!plan || capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->timer) {
+    moe::destroy_events(plan->timer);
+    if (capacity == 0) {
+      delete plan->timer;
+      plan->timer = nullptr;
+      return MOE_OK;
+    }
+  } else {
+    if (capacity == 0) return MOE_OK;
+    plan->timer = new (std::nothrow) moe::LaunchTimer();
+    if (!plan->timer) return MOE_ERR_UNSUPPORTED;
+  }
+  moe::LaunchTimer* t = plan->timer;
+  for (int32_t i = 0; i < capacity; ++i) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess) return MOE_ERR_HIP;
+    if (hipEventCreate(&b) != hipSuccess) {
+      hipEventDestroy(a);
+      return MOE_ERR_HIP;
+    }
+    t->start.push_back(a);
+    t->stop.push_back(b);
+  }
+  t->ids.assign(capacity, -1);
+  t->used = 0;
+  return MOE_OK;
+}
+
+moe_status moe_plan_timing_read(moe_plan* plan, int32_t* kernel_ids, float* ms, int32_t cap,
+                                int32_t* count) {
+  if (!plan || !plan->timer || !count || cap < 0 || (cap > 0 && (!kernel_ids || !ms)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe::LaunchTimer* t = plan->timer;
+  const int n = t->used;
+  for (int i = 0; i < n; ++i) {
+    if (hipEventSynchronize(t->stop[i]) != hipSuccess) return MOE_ERR_HIP;
+    if (i < cap) {
+      float e = 0.0f;
+      if (hipEventElapsedTime(&e, t->start[i], t->stop[i]) != hipSuccess) return MOE_ERR_HIP;
+      kernel_ids[i] = t->ids[i];
+      ms[i] = e;
+    }
+  }
+  *count = n;
+  t->used = 0;
+  return MOE_OK;
+}
 
 size_t moe_plan_workspace_bytes(const moe_plan* plan) { return plan ? plan->layout.total : 0; }
 
@@ -264,6 +362,7 @@ int64_t moe_plan_bands(const moe_plan* plan) { return plan ? plan->d.nbands : 0;
 
 moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspace, void* stream) {
   if (!plan || !workspace || !moe::aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  const moe::TimerScope timing(plan);
   if (plan->d.T > 0 && (!topk_idx || !moe::aligned(topk_idx, 4))) return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   plan->routed = false;
@@ -284,6 +383,7 @@ moe_status moe_pipeline(moe_plan* plan, const int32_t* topk_idx, void* workspace
                         const uint16_t* x, uint16_t* recv, const float* topk_w, void* out,
                         int32_t out_dtype, void* stream) {
   if (!plan || !workspace || !moe::aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  const moe::TimerScope timing(plan);
   if (plan->d.dedup || plan->d.H % 64) return MOE_ERR_UNSUPPORTED;
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARGUMENT;
   if (plan->d.T > 0 &&
@@ -298,7 +398,9 @@ moe_status moe_pipeline(moe_plan* plan, const int32_t* topk_idx, void* workspace
   plan->idx = topk_idx;
   plan->ws = workspace;
   plan->work = moe::bind_work(plan->layout, workspace);
-  if (moe::ensure_counters_clear(plan, s) != MOE_OK) return MOE_ERR_HIP;
+  // Every launch zeroes the counters first (one small kernel): a caller's
+  // workspace may hold anything, a reused allocation included.
+  if (moe::launch_counters_clear(plan->d, plan->work, s) != hipSuccess) return MOE_ERR_HIP;
   if (moe::launch_pipeline(plan->d, topk_idx, x, recv, topk_w, out, out_dtype == MOE_OUT_F32,
                            plan->work, s) != hipSuccess)
     return MOE_ERR_HIP;
@@ -311,6 +413,7 @@ moe_status moe_pipeline(moe_plan* plan, const int32_t* topk_idx, void* workspace
 moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint16_t* staging,
                         void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  const moe::TimerScope timing(plan);
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   if (plan->d.T == 0) return MOE_OK;
   if (!x || !recv || !moe::aligned(x, 16) || !moe::aligned(recv, 16)) return MOE_ERR_INVALID_ARGUMENT;
@@ -331,6 +434,7 @@ moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint1
 moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, void* out,
                        int32_t out_dtype, void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  const moe::TimerScope timing(plan);
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARGUMENT;
   if (plan->d.T == 0) return MOE_OK;
@@ -347,6 +451,7 @@ moe_status moe_combine(moe_plan* plan, const uint16_t* y, const float* topk_w, v
 moe_status moe_combine_hier(moe_plan* plan, const uint16_t* y, const float* topk_w,
                             float* partials, void* out, int32_t out_dtype, void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  const moe::TimerScope timing(plan);
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   if (!plan->d.dedup) return MOE_ERR_INVALID_ARGUMENT;
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARGUMENT;
@@ -368,6 +473,7 @@ int64_t moe_plan_scale_blocks(const moe_plan* plan) {
 moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, float* recv_scale,
                             uint8_t* staging8, float* staging_scale, void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  const moe::TimerScope timing(plan);
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   if (plan->d.T == 0) return MOE_OK;
   if (!x || !recv8 || !recv_scale || !moe::aligned(x, 16) || !moe::aligned(recv8, 16) ||
@@ -392,6 +498,7 @@ moe_status moe_dispatch_fp8(moe_plan* plan, const uint16_t* x, uint8_t* recv8, f
 moe_status moe_combine_fp8(moe_plan* plan, const uint8_t* y8, const float* y_scale,
                            const float* topk_w, void* out, int32_t out_dtype, void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  const moe::TimerScope timing(plan);
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARGUMENT;
   if (plan->d.T == 0) return MOE_OK;
@@ -408,6 +515,7 @@ moe_status moe_combine_fp8(moe_plan* plan, const uint8_t* y8, const float* y_sca
 moe_status moe_plan_read(moe_plan* plan, int32_t item, void* host_dst, size_t bytes,
                          void* stream) {
   if (!plan || !host_dst) return MOE_ERR_INVALID_ARGUMENT;
+  const moe::TimerScope timing(plan);
   if (!plan->routed) return MOE_ERR_PLAN_NOT_ROUTED;
   const moe::Dims& d = plan->d;
   const moe::Work w = plan->work;

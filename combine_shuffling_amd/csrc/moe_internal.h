@@ -2,6 +2,7 @@
 // kernels (route_plan.hip, move.hip).  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -29,13 +30,7 @@ constexpr int kBandScanLdsInts = kScanLdsInts / 2;
 // one stream: olmoe 16 x 64 gains 2 us per step; qwen3's 32 x 128, with
 // 16-wave gather blocks, 8 us; nondiv's 64 x 100 loses 14 us, as every
 // gather block then redoes a 6400-entry scan).
-#ifndef MOE_FUSED_SCAN_INTS
-#define MOE_FUSED_SCAN_INTS 4096
-#endif
-constexpr int kFusedScanInts = MOE_FUSED_SCAN_INTS;
-#ifndef MOE_FUSED_SCAN
-#define MOE_FUSED_SCAN 1  // 0: always launch the scan in the route plan
-#endif
+constexpr int kFusedScanInts = 4096;
 
 // ctrl words at the start of the workspace.
 constexpr int kCtrlStaged = 1;     // D, staging rows used
@@ -52,6 +47,24 @@ constexpr int kPipeExit = 1;       // blocks that have left the ticket loop
 constexpr int kPipeStall = 2;      // set when a bounded wait gave up
 constexpr int kPipeHead = 4;       // head slots
 constexpr int kPipeMaxSteps = 256; // schedule steps (bands + stage lags) at most
+
+// Per-launch kernel timing (moe_plan_timing): while a call on a plan whose
+// timing is on runs on this thread, timer_take hands out the next event pair
+// for a launch of kernel `id` (moe_kernel); false: launch untimed.
+bool timer_take(int id, hipEvent_t* start, hipEvent_t* stop);
+
+// Launches `kernel` on stream s; with a pair from timer_take, the pair is
+// bound to the kernel's own start and end (hipExtLaunchKernel).
+template <typename... P, typename... A>
+hipError_t launch(int id, void (*kernel)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                  A... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  if (timer_take(id, &start, &stop))
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, start, stop, 0u, static_cast<P>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<P>(args)...);
+  return hipGetLastError();
+}
 
 // Sizes and the hoisted constants of the two ceil/floor splits.  Passed by
 // value to every kernel.

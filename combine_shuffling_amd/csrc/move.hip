@@ -32,62 +32,37 @@
 #include "move_body.h"
 #include "plan_body.h"
 
-#ifndef MOE_HIER_CHUNK_MIB
-// DeepSeek-V3-like hierarchical combine, us on one stream: whole batch 1235,
-// 448 MiB (8 chunks) 1149, 224 MiB 1189, 112 MiB 1356
-#define MOE_HIER_CHUNK_MIB 448
-#endif
-
-#ifndef MOE_STAGE_CHUNK
-#define MOE_STAGE_CHUNK 0
-#endif
-#ifndef MOE_STAGE_A_U
-// wave-items per wave of stage_a.  DeepSeek-V3-like dispatch, one stream:
-// 1 -> 679 us, 2 -> 694, 2 consecutive segments sharing their lookups -> 689,
-// 4 consecutive -> 714
-#define MOE_STAGE_A_U 1
-#endif
-#ifndef MOE_STAGE_CHUNK_MIB
-// DeepSeek-V3-like dispatch, us with two batches in flight / one stream
-// (before stage A skipped its unused lookups): no chunks 1217 / 1217,
-// 512 MiB 1228 / 1187, 256 MiB 1178 / 1180, 224 MiB (8 chunks) 1142 / 1181,
-// 128 MiB 1107 / 1265
-#define MOE_STAGE_CHUNK_MIB 224
-#endif
-#ifndef MOE_GSCAN_WAVES_WIDE
-#define MOE_GSCAN_WAVES_WIDE 16  // qwen3 dispatch: 4 -> 166 us, 8 -> 100, 16 -> 90
-#endif
-#ifndef MOE_GSCAN_U
-// wave-items (consecutive segments) per wave of gather_scan, up to 64 experts;
-// olmoe, two batches in flight: 1 -> 50.3 us a step, 2 -> 48.2, 3 -> 48.4, 4 -> 51.1
-#define MOE_GSCAN_U 2
-#endif
-#ifndef MOE_GSCAN8_WAVES
-#define MOE_GSCAN8_WAVES MOE_GSCAN_WAVES
-#endif
-#ifndef MOE_GSCAN8_U
-#define MOE_GSCAN8_U 1  // fp8 olmoe, two batches in flight: 1 -> 32.5 us, 2 -> 33.0, 4 -> 33.4
-#endif
-#ifndef MOE_GSCAN_U_WIDE
-#define MOE_GSCAN_U_WIDE 1  // qwen3, staggered: 1 -> 204.9 us, 2 -> 208.3, 4 -> 212.3
-#endif
-#ifndef MOE_GSCAN_WAVES
-#define MOE_GSCAN_WAVES 8  // olmoe dispatch: 4 -> 32.2 us, 8 -> 30.9, 16 -> 31.4
-#endif
-
 namespace moe {
 namespace {
 
-constexpr int kGatherScanWaves = MOE_GSCAN_WAVES;  // waves per gather_scan block when E <= 64
-constexpr int kGatherScanWavesWide = MOE_GSCAN_WAVES_WIDE;  // ... when E > 64
-constexpr int kGatherScanU = MOE_GSCAN_U;           // wave-items per wave, E <= 64
-constexpr int kGatherScanUWide = MOE_GSCAN_U_WIDE;  // ... E > 64
-constexpr int kGatherScan8U = MOE_GSCAN8_U;         // ... fp8 payload (E <= 64)
-constexpr int kGatherScan8Waves = MOE_GSCAN8_WAVES;  // waves per gather_fp8_scan block
-constexpr int kStageAU = MOE_STAGE_A_U;  // wave-items per wave of stage_a
-constexpr int kStageChunkTokens = MOE_STAGE_CHUNK;  // tokens per hop-1/hop-2 chunk (0: by bytes)
-constexpr int64_t kChunkBytes = (int64_t)MOE_STAGE_CHUNK_MIB << 20;  // staging bytes per chunk, at most
-constexpr int64_t kHierChunkBytes = (int64_t)MOE_HIER_CHUNK_MIB << 20;  // partial bytes per chunk, at most
+// Waves per gather_scan block when E <= 64 (olmoe dispatch: 4 -> 32.2 us,
+// 8 -> 30.9, 16 -> 31.4), and when E > 64 (qwen3 dispatch: 4 -> 166 us,
+// 8 -> 100, 16 -> 90).
+constexpr int kGatherScanWaves = 8;
+constexpr int kGatherScanWavesWide = 16;
+// Wave-items (consecutive segments) per wave of gather_scan, E <= 64 (olmoe,
+// two batches in flight: 1 -> 50.3 us a step, 2 -> 48.2, 3 -> 48.4, 4 ->
+// 51.1), and E > 64 (qwen3, staggered: 1 -> 204.9 us, 2 -> 208.3, 4 -> 212.3).
+constexpr int kGatherScanU = 2;
+constexpr int kGatherScanUWide = 1;
+// ... of the fp8 gather_scan (fp8 olmoe, two batches in flight: 1 -> 32.5 us,
+// 2 -> 33.0, 4 -> 33.4), and its waves per block.
+constexpr int kGatherScan8U = 1;
+constexpr int kGatherScan8Waves = kGatherScanWaves;
+// Wave-items per wave of stage_a.  DeepSeek-V3-like dispatch, one stream:
+// 1 -> 679 us, 2 -> 694, 2 consecutive segments sharing their lookups -> 689,
+// 4 consecutive -> 714.
+constexpr int kStageAU = 1;
+// Staging bytes per chunk of the deduplicated dispatch, at most.
+// DeepSeek-V3-like dispatch, us with two batches in flight / one stream
+// (before stage A skipped its unused lookups): no chunks 1217 / 1217,
+// 512 MiB 1228 / 1187, 256 MiB 1178 / 1180, 224 MiB (8 chunks) 1142 / 1181,
+// 128 MiB 1107 / 1265.
+constexpr int64_t kChunkBytes = (int64_t)224 << 20;
+// Partial bytes per chunk of the hierarchical combine, at most.
+// DeepSeek-V3-like, us on one stream: whole batch 1235, 448 MiB (8 chunks)
+// 1149, 224 MiB 1189, 112 MiB 1356.
+constexpr int64_t kHierChunkBytes = (int64_t)448 << 20;
 
 // The scan folded into the gather of a small plan (nblk * E <=
 // kFusedScanInts; single band).  The block (GB threads, all of which call
@@ -483,10 +458,14 @@ __global__ __launch_bounds__(kBlock) void combine_nodes_kernel(Dims d, const f32
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kFp8BlockChunks = 16;  // 16-byte bf16 chunks per scale block
 
-__device__ __forceinline__ int fp8_block_exp(float amax) {
-  if (!(amax > 0.0f) || amax > 3.0e38f) return 0;
+// Block exponent of a block whose largest magnitude has the float bits
+// `abits` (sign cleared): 0 for an all-zero block and for a block holding an
+// infinity or a NaN (whose codes are then unspecified), else the smallest e
+// with amax <= 448 * 2^e.
+__device__ __forceinline__ int fp8_block_exp(uint32_t abits) {
+  if (abits == 0u || abits >= 0x7f800000u) return 0;
   int p;
-  const float m = frexpf(amax, &p);  // amax = m * 2^p, m in [0.5, 1)
+  const float m = frexpf(__uint_as_float(abits), &p);  // amax = m * 2^p, m in [0.5, 1)
   const int e = p - 9 + (m > 0.875f ? 1 : 0);
   return min(max(e, -126), 127);
 }
@@ -577,13 +556,18 @@ __device__ __forceinline__ Fp8Piece quantize_loaded(u32x4 v0, u32x4 v1) {
   float f0[8], f1[8];
   unpack_bf16(v0, f0);
   unpack_bf16(v1, f1);
-  float amax = 0.0f;
+  // The largest magnitude as float bits with the sign cleared: for
+  // non-negative floats the integer order is the numeric order, and an
+  // infinity or NaN compares above every finite value (a float max would
+  // skip a NaN).
+  uint32_t abits = 0u;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fmaxf(fabsf(f0[q]), fabsf(f1[q])));
+  for (int q = 0; q < 8; ++q)
+    abits = max(abits, max(__float_as_uint(f0[q]) & 0x7fffffffu, __float_as_uint(f1[q]) & 0x7fffffffu));
 #pragma unroll
   for (int o = kFp8BlockLanes / 2; o > 0; o >>= 1)
-    amax = fmaxf(amax, __shfl_xor(amax, o, kFp8BlockLanes));
-  const int e = fp8_block_exp(amax);
+    abits = max(abits, (uint32_t)__shfl_xor((int)abits, o, kFp8BlockLanes));
+  const int e = fp8_block_exp(abits);
   const float inv = ldexpf(1.0f, -e);
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -897,14 +881,14 @@ __global__ __launch_bounds__(kCombine8Waves * kWave) void combine_fp8_kernel(Dim
   }
 }
 
-// Launches f(grid, base, limit) over wave-items [0, items), at most
-// kMaxLaunchItems a launch, per_block wave-items a block.
+// Launches f(grid, base, limit) -> hipError_t over wave-items [0, items), at
+// most kMaxLaunchItems a launch, per_block wave-items a block.
 template <typename F>
 hipError_t launch_ranges(int64_t items, int per_block, F f) {
   for (int64_t base = 0; base < items; base += kMaxLaunchItems) {
     const int64_t limit = std::min<int64_t>(items, base + kMaxLaunchItems);
-    f(dim3((unsigned)((limit - base + per_block - 1) / per_block)), (int)base, (int)limit);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e =
+        f(dim3((unsigned)((limit - base + per_block - 1) / per_block)), (int)base, (int)limit);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -929,17 +913,18 @@ struct GatherLaunch {
       // larger blocks where the experts fit one wave: fewer blocks redo the scan
       if (d.E <= kWave)
         return launch_ranges(items, kGatherScanWaves * kGatherScanU, [&](dim3 g, int b, int l) {
-          hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWaves, kGatherScanU>), g,
-                             dim3(kGatherScanWaves * kWave), 0, s, d, idx, xv, rv, w, b, l);
+          return launch(MOE_KERNEL_GATHER_SCAN, gather_scan_kernel<KMAX, kGatherScanWaves, kGatherScanU>,
+                        g, dim3(kGatherScanWaves * kWave), 0, s, d, idx, xv, rv, w, b, l);
         });
       return launch_ranges(items, kGatherScanWavesWide * kGatherScanUWide, [&](dim3 g, int b, int l) {
-        hipLaunchKernelGGL((gather_scan_kernel<KMAX, kGatherScanWavesWide, kGatherScanUWide>), g,
-                           dim3(kGatherScanWavesWide * kWave), 0, s, d, idx, xv, rv, w, b, l);
+        return launch(MOE_KERNEL_GATHER_SCAN,
+                      gather_scan_kernel<KMAX, kGatherScanWavesWide, kGatherScanUWide>, g,
+                      dim3(kGatherScanWavesWide * kWave), 0, s, d, idx, xv, rv, w, b, l);
       });
     }
     return launch_ranges(items, kWaves * kGatherU, [&](dim3 g, int b, int l) {
-      hipLaunchKernelGGL((gather_kernel<KMAX, kGatherU>), g, dim3(kBlock), 0, s, d, idx, xv, rv, w,
-                         b, l);
+      return launch(MOE_KERNEL_GATHER, gather_kernel<KMAX, kGatherU>, g, dim3(kBlock), 0, s, d, idx,
+                    xv, rv, w, b, l);
     });
   }
 };
@@ -947,7 +932,6 @@ struct GatherLaunch {
 // Tokens per chunk of the deduplicated dispatch: even chunks, each with at
 // most kChunkBytes of staging rows (row_bound bytes a token, at most).
 inline int stage_chunk_tokens(const Dims& d, int64_t row_bound) {
-  if (kStageChunkTokens > 0) return kStageChunkTokens;
   const int64_t n = std::max<int64_t>(1, ((int64_t)d.T * row_bound + kChunkBytes - 1) / kChunkBytes);
   return (int)(((int64_t)d.T + n - 1) / n);
 }
@@ -971,15 +955,13 @@ struct DedupLaunch {
       const int item0 = t0 * d.segs, item_end = min(d.T, t0 + chunk) * d.segs;
       const int blocks_a = (item_end - item0 + per_block_a - 1) / per_block_a;
       const int blocks_b = (item_end - item0 + per_block_b - 1) / per_block_b;
-      hipLaunchKernelGGL((stage_a_kernel<KMAX, kStageAU>), dim3(blocks_a), dim3(kBlock), 0, s, d,
-                         idx, reinterpret_cast<const u32x4*>(x),
-                         reinterpret_cast<u32x4*>(staging), w, item0, item_end, keep);
-      hipError_t e = hipGetLastError();
+      hipError_t e = launch(MOE_KERNEL_STAGE_A, stage_a_kernel<KMAX, kStageAU>, dim3(blocks_a),
+                            dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
+                            reinterpret_cast<u32x4*>(staging), w, item0, item_end, keep);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((stage_b_kernel<KMAX, kStageU>), dim3(blocks_b), dim3(kBlock), 0, s, d,
-                         reinterpret_cast<const u32x4*>(staging), reinterpret_cast<u32x4*>(recv), w,
-                         item0, item_end);
-      e = hipGetLastError();
+      e = launch(MOE_KERNEL_STAGE_B, stage_b_kernel<KMAX, kStageU>, dim3(blocks_b), dim3(kBlock), 0,
+                 s, d, reinterpret_cast<const u32x4*>(staging), reinterpret_cast<u32x4*>(recv), w,
+                 item0, item_end);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -994,11 +976,10 @@ struct CombineLaunch {
     const dim3 block(kCombineWaves * kWave);
     return launch_ranges((int64_t)d.T * d.segs, kCombineWaves * kCombineU, [&](dim3 g, int b, int l) {
       if (f32)
-        hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, true>), g, block, 0, s, d, yv, wts,
-                           w.slot_of, out, b, l);
-      else
-        hipLaunchKernelGGL((combine_kernel<KMAX, kCombineU, false>), g, block, 0, s, d, yv, wts,
-                           w.slot_of, out, b, l);
+        return launch(MOE_KERNEL_COMBINE, combine_kernel<KMAX, kCombineU, true>, g, block, 0, s, d,
+                      yv, wts, w.slot_of, out, b, l);
+      return launch(MOE_KERNEL_COMBINE, combine_kernel<KMAX, kCombineU, false>, g, block, 0, s, d,
+                    yv, wts, w.slot_of, out, b, l);
     });
   }
 };
@@ -1011,13 +992,13 @@ struct GatherFp8Launch {
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
     if (fp8_fused_scan(d))
       return launch_ranges(items, kGatherScan8Waves * kGatherScan8U, [&](dim3 g, int b, int l) {
-        hipLaunchKernelGGL((gather_fp8_scan_kernel<KMAX, kGatherScan8Waves, kGatherScan8U>), g,
-                           dim3(kGatherScan8Waves * kWave), 0, s, d, idx, xv, recv8, rscale, w, b,
-                           l);
+        return launch(MOE_KERNEL_GATHER_FP8_SCAN,
+                      gather_fp8_scan_kernel<KMAX, kGatherScan8Waves, kGatherScan8U>, g,
+                      dim3(kGatherScan8Waves * kWave), 0, s, d, idx, xv, recv8, rscale, w, b, l);
       });
     return launch_ranges(items, kWaves, [&](dim3 g, int b, int l) {
-      hipLaunchKernelGGL((gather_fp8_kernel<KMAX>), g, dim3(kBlock), 0, s, d, idx, xv, recv8,
-                         rscale, w, b, l);
+      return launch(MOE_KERNEL_GATHER_FP8, gather_fp8_kernel<KMAX>, g, dim3(kBlock), 0, s, d, idx,
+                    xv, recv8, rscale, w, b, l);
     });
   }
 };
@@ -1036,14 +1017,13 @@ struct DedupFp8Launch {
     for (int t0 = 0; t0 < d.T; t0 += chunk) {
       const int item0 = t0 * segs8, item_end = min(d.T, t0 + chunk) * segs8;
       const int blocks = (item_end - item0 + kWaves - 1) / kWaves;
-      hipLaunchKernelGGL((stage_a_fp8_kernel<KMAX>), dim3(blocks), dim3(kBlock), 0, s, d, idx,
-                         reinterpret_cast<const u32x4*>(x), stage8, sscale, w, item0, item_end,
-                         keep);
-      hipError_t e = hipGetLastError();
+      hipError_t e = launch(MOE_KERNEL_STAGE_A_FP8, stage_a_fp8_kernel<KMAX>, dim3(blocks),
+                            dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x), stage8,
+                            sscale, w, item0, item_end, keep);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((stage_b_fp8_kernel<KMAX>), dim3(blocks), dim3(kBlock), 0, s, d, stage8,
-                         static_cast<const float*>(sscale), recv8, rscale, w, item0, item_end);
-      e = hipGetLastError();
+      e = launch(MOE_KERNEL_STAGE_B_FP8, stage_b_fp8_kernel<KMAX>, dim3(blocks), dim3(kBlock), 0, s,
+                 d, static_cast<const uint8_t*>(stage8), static_cast<const float*>(sscale), recv8,
+                 rscale, w, item0, item_end);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1058,11 +1038,10 @@ struct CombineFp8Launch {
     const dim3 block(kCombine8Waves * kWave);
     return launch_ranges((int64_t)d.T * d.segs, kCombine8Waves * kCombine8U, [&](dim3 g, int b, int l) {
       if (f32)
-        hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, true>), g, block, 0, s, d, y,
-                           yscale, wts, w.slot_of, out, b, l);
-      else
-        hipLaunchKernelGGL((combine_fp8_kernel<KMAX, kCombine8U, false>), g, block, 0, s, d, y,
-                           yscale, wts, w.slot_of, out, b, l);
+        return launch(MOE_KERNEL_COMBINE_FP8, combine_fp8_kernel<KMAX, kCombine8U, true>, g, block, 0,
+                      s, d, y, yscale, wts, w.slot_of, out, b, l);
+      return launch(MOE_KERNEL_COMBINE_FP8, combine_fp8_kernel<KMAX, kCombine8U, false>, g, block, 0,
+                    s, d, y, yscale, wts, w.slot_of, out, b, l);
     });
   }
 };
@@ -1083,17 +1062,14 @@ struct CombineHierLaunch {
     for (int t0 = 0; t0 < d.T; t0 += chunk) {
       const int item0 = t0 * d.segs, item_end = min(d.T, t0 + chunk) * d.segs;
       const int blocks = (item_end - item0 + kWaves - 1) / kWaves;
-      hipLaunchKernelGGL((combine_part_kernel<KMAX>), dim3(blocks), dim3(kBlock), 0, s, d,
-                         reinterpret_cast<const u32x4*>(y), wts, pp, w, item0, item_end, keep);
-      hipError_t e = hipGetLastError();
+      hipError_t e = launch(MOE_KERNEL_COMBINE_PART, combine_part_kernel<KMAX>, dim3(blocks),
+                            dim3(kBlock), 0, s, d, reinterpret_cast<const u32x4*>(y), wts, pp, w,
+                            item0, item_end, keep);
       if (e != hipSuccess) return e;
-      if (f32)
-        hipLaunchKernelGGL((combine_nodes_kernel<KMAX, true>), dim3(blocks), dim3(kBlock), 0, s, d,
-                           static_cast<const f32x4*>(pp), w, out, item0, item_end);
-      else
-        hipLaunchKernelGGL((combine_nodes_kernel<KMAX, false>), dim3(blocks), dim3(kBlock), 0, s,
-                           d, static_cast<const f32x4*>(pp), w, out, item0, item_end);
-      e = hipGetLastError();
+      e = f32 ? launch(MOE_KERNEL_COMBINE_NODES, combine_nodes_kernel<KMAX, true>, dim3(blocks),
+                       dim3(kBlock), 0, s, d, static_cast<const f32x4*>(pp), w, out, item0, item_end)
+              : launch(MOE_KERNEL_COMBINE_NODES, combine_nodes_kernel<KMAX, false>, dim3(blocks),
+                       dim3(kBlock), 0, s, d, static_cast<const f32x4*>(pp), w, out, item0, item_end);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -6,57 +6,28 @@
 
 #include "moe_device.h"
 
-#ifndef MOE_GATHER_U
-#define MOE_GATHER_U 1
-#endif
-#ifndef MOE_STAGE_U
-#define MOE_STAGE_U 2
-#endif
-#ifndef MOE_COMBINE_U
-// one wave-item per wave: more waves resident (measured in whole steps with
-// x read from HBM, one stream: olmoe 59.2 -> 56.8 us, dsv3 1180 -> 1176 against 2)
-#define MOE_COMBINE_U 1
-#endif
-#ifndef MOE_NT_LOAD
-#define MOE_NT_LOAD 1
-#endif
-#ifndef MOE_COMBINE8_U
-#define MOE_COMBINE8_U 1  // fp8 payload, one stream: qwen3 step 132.4 -> 122.4 us against 2
-#endif
-#ifndef MOE_NT_LOAD_X
-#define MOE_NT_LOAD_X 0
-#endif
-#ifndef MOE_COMBINE_WAVES
-// waves per block of the bf16 combine; best step, against 4-wave blocks:
-// qwen3 205.2 -> 203.9 us, nondiv 339.1 -> 335.6, dsv3 1083.3 -> 1078.2,
-// olmoe unchanged (2-wave blocks: olmoe 48.9 against 48.3, dsv3 1075)
-#define MOE_COMBINE_WAVES 1
-#endif
-#ifndef MOE_COMBINE8_WAVES
-// ... of the fp8 combine: 2-wave blocks made qwen3 fp8 118.1 us against 114.7
-#define MOE_COMBINE8_WAVES 4
-#endif
-#ifndef MOE_MOVE_WAVES
-#define MOE_MOVE_WAVES 4
-#endif
-#ifndef MOE_NT_STORE
-#define MOE_NT_STORE 1
-#endif
-
 namespace moe {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = MOE_MOVE_WAVES;   // waves per block
+constexpr int kWaves = 4;           // waves per block of the movement kernels
 constexpr int kBlock = kWaves * kWave;
-constexpr int kGatherU = MOE_GATHER_U;    // wave-items per wave: gather
-constexpr int kStageU = MOE_STAGE_U;      // wave-items per wave: stage_b (stage_a in move.hip)
-constexpr int kCombineU = MOE_COMBINE_U;  // wave-items per wave: combine
-constexpr int kCombine8U = MOE_COMBINE8_U; // wave-items per wave: combine of an fp8 payload
-constexpr int kCombineWaves = MOE_COMBINE_WAVES;    // waves per block of the bf16 combine
-constexpr int kCombine8Waves = MOE_COMBINE8_WAVES;  // ... of the fp8 combine
+constexpr int kGatherU = 1;         // wave-items per wave: gather
+constexpr int kStageU = 2;          // wave-items per wave: stage_b
+// Wave-items per wave of the combine: one, so that more waves are resident
+// (whole steps with x read from HBM, one stream: olmoe 59.2 -> 56.8 us,
+// dsv3 1180 -> 1176 against two).
+constexpr int kCombineU = 1;
+// ... of the fp8 combine (one stream: qwen3 step 132.4 -> 122.4 us against two).
+constexpr int kCombine8U = 1;
+// Waves per block of the bf16 combine; best step, against 4-wave blocks:
+// qwen3 205.2 -> 203.9 us, nondiv 339.1 -> 335.6, dsv3 1083.3 -> 1078.2,
+// olmoe unchanged (2-wave blocks: olmoe 48.9 against 48.3, dsv3 1075).
+constexpr int kCombineWaves = 1;
+// ... of the fp8 combine: 2-wave blocks made qwen3 fp8 118.1 us against 114.7.
+constexpr int kCombine8Waves = 4;
 // Wave-items per launch at most: a grid is sized in work-items, a 32-bit count,
 // so a batch of more wave-items is moved in several launches (2^24 items of
 // at most 64 threads each).
@@ -66,11 +37,7 @@ constexpr int64_t kMaxLaunchItems = (int64_t)1 << 24;
 // faster on gfx950 for both the row reads and the row writes).
 template <typename V>
 __device__ __forceinline__ void store_chunk(V* p, V v) {
-#if MOE_NT_STORE
   __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
 }
 
 // Rows that the next kernel of the step reads back (receive rows for the
@@ -94,11 +61,7 @@ __device__ __forceinline__ void store_row(V* p, V v, bool keep) {
 }
 
 __device__ __forceinline__ u32x4 load_chunk(const u32x4* p) {
-#if MOE_NT_LOAD
   return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
 }
 
 // Row store that another block reads in the same launch (the banded
@@ -113,13 +76,7 @@ __device__ __forceinline__ void store_row_chunk(u32x4* p, u32x4 v, bool keep) {
 }
 
 // Token rows of x (dispatch source): plain loads measured faster here.
-__device__ __forceinline__ u32x4 load_x_chunk(const u32x4* p) {
-#if MOE_NT_LOAD_X
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
+__device__ __forceinline__ u32x4 load_x_chunk(const u32x4* p) { return *p; }
 
 // Wave-item u of this wave: token t, chunk c of the lane, and whether the
 // item exists / the lane's chunk is inside the row.

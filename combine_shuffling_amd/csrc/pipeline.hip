@@ -47,29 +47,19 @@
 #include "move_body.h"
 #include "plan_body.h"
 
-#ifndef MOE_PIPE_GATHER_U
-#define MOE_PIPE_GATHER_U 4
-#endif
-#ifndef MOE_PIPE_COMBINE_U
-#define MOE_PIPE_COMBINE_U 4
-#endif
-#ifndef MOE_PIPE_LAG_SCAN
-#define MOE_PIPE_LAG_SCAN 1
-#endif
-#ifndef MOE_PIPE_LAG_GATHER
-#define MOE_PIPE_LAG_GATHER 1
-#endif
-#ifndef MOE_PIPE_SLEEP
-#define MOE_PIPE_SLEEP 1
-#endif
-
 namespace moe {
 namespace {
 
 static_assert(kBlock == kPlanBlock, "pipeline roles share one block shape");
 
-constexpr int kPipeGatherU = MOE_PIPE_GATHER_U;
-constexpr int kPipeCombineU = MOE_PIPE_COMBINE_U;
+// Wave-items per wave of a gather / combine ticket (1, 2, 4 and 8 measured:
+// 4 for both was best).
+constexpr int kPipeGatherU = 4;
+constexpr int kPipeCombineU = 4;
+// Schedule lags, in steps, of the scan after the count and of the gather
+// after the scan (the combine's lag is sized from the resident grid).
+constexpr int kLagScan = 1;
+constexpr int kLagGather = 1;
 constexpr int kSpinLimit = 1 << 17;  // polls before a wait gives up
 
 enum Role { kCount = 0, kScan = 1, kGather = 2, kCombine = 3, kRoles = 4 };
@@ -111,7 +101,7 @@ __device__ __forceinline__ Ticket decode(const Sched& S, int nbands, int tk) {
 __device__ __forceinline__ bool wait_for(int32_t* p, int need, int32_t* stall) {
   for (int spin = 0; spin < kSpinLimit; ++spin) {
     if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) return true;
-    __builtin_amdgcn_s_sleep(MOE_PIPE_SLEEP);
+    __builtin_amdgcn_s_sleep(1);
   }
   __hip_atomic_store(stall, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return false;
@@ -254,10 +244,9 @@ struct PipelineLaunch {
     // Combine lag: about a grid's worth of tickets between gather(b) and combine(b).
     const int per_step = S.full[kCount] + 1 + S.full[kGather] + S.full[kCombine];
     const int lc = std::min(32, std::max(1, ceil_div(resident, per_step)));
-    const int lag_plan = MOE_PIPE_LAG_SCAN > 0 ? MOE_PIPE_LAG_SCAN : lc;
     S.lag[kCount] = 0;
-    S.lag[kScan] = lag_plan;
-    S.lag[kGather] = S.lag[kScan] + (MOE_PIPE_LAG_GATHER > 0 ? MOE_PIPE_LAG_GATHER : lc);
+    S.lag[kScan] = kLagScan;
+    S.lag[kGather] = S.lag[kScan] + kLagGather;
     S.lag[kCombine] = S.lag[kGather] + lc;
     S.nsteps = d.nbands + S.lag[kCombine];
     if (S.nsteps > kPipeMaxSteps) return hipErrorInvalidValue;
@@ -272,10 +261,9 @@ struct PipelineLaunch {
     S.step_start[S.nsteps] = at;
     S.total = at;
     const int grid = std::min(S.total, resident);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), lds, s, d, idx,
-                       reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), wts,
-                       out, w, S, count_run);
-    return hipGetLastError();
+    return launch(MOE_KERNEL_PIPELINE, kernel, dim3(grid), dim3(kBlock), (uint32_t)lds, s, d, idx,
+                  reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), wts, out, w, S,
+                  count_run);
   }
 };
 
@@ -297,9 +285,8 @@ hipError_t launch_pipeline(const Dims& d, const int32_t* idx, const uint16_t* x,
 }
 
 hipError_t launch_counters_clear(const Dims& d, const Work& w, hipStream_t s) {
-  hipLaunchKernelGGL(counters_clear_kernel, dim3(1), dim3(kBlock), 0, s, w.pipe,
-                     (kPipeHead + 3 * d.nbands) * kPipeSlot);
-  return hipGetLastError();
+  return launch(MOE_KERNEL_COUNTERS_CLEAR, counters_clear_kernel, dim3(1), dim3(kBlock), 0, s,
+                w.pipe, (kPipeHead + 3 * d.nbands) * kPipeSlot);
 }
 
 }  // namespace moe

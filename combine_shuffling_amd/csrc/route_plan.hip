@@ -34,6 +34,7 @@
 namespace moe {
 namespace {
 
+
 template <int KMAX>
 __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
                                                                  const int32_t* __restrict__ idx,
@@ -143,8 +144,8 @@ hipError_t by_topk(int k, A... a) {
 template <int KMAX>
 struct CountLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
-    hipLaunchKernelGGL(route_count_kernel<KMAX>, dim3(d.nblk), dim3(kPlanBlock), 0, s, d, idx, w);
-    return hipGetLastError();
+    return launch(MOE_KERNEL_ROUTE_COUNT, route_count_kernel<KMAX>, dim3(d.nblk), dim3(kPlanBlock),
+                  0, s, d, idx, w);
   }
 };
 
@@ -153,8 +154,8 @@ struct AssignLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
     const int blocks = (d.T + kPlanBlock - 1) / kPlanBlock;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(route_assign_kernel<KMAX>, dim3(blocks), dim3(kPlanBlock), 0, s, d, idx, w);
-    return hipGetLastError();
+    return launch(MOE_KERNEL_ROUTE_ASSIGN, route_assign_kernel<KMAX>, dim3(blocks),
+                  dim3(kPlanBlock), 0, s, d, idx, w);
   }
 };
 
@@ -163,8 +164,8 @@ struct TrafficLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
     const int blocks = (d.T + kPlanBlock - 1) / kPlanBlock;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(traffic_kernel<KMAX>, dim3(blocks), dim3(kPlanBlock), 0, s, d, idx, w);
-    return hipGetLastError();
+    return launch(MOE_KERNEL_TRAFFIC, traffic_kernel<KMAX>, dim3(blocks), dim3(kPlanBlock), 0, s, d,
+                  idx, w);
   }
 };
 
@@ -175,8 +176,8 @@ hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, 
 }
 
 hipError_t launch_route_scan(const Dims& d, const Work& w, hipStream_t s) {
-  hipLaunchKernelGGL(route_scan_kernel, dim3(d.nbands), dim3(kPlanBlock), 0, s, d, w);
-  return hipGetLastError();
+  return launch(MOE_KERNEL_ROUTE_SCAN, route_scan_kernel, dim3(d.nbands), dim3(kPlanBlock), 0, s, d,
+                w);
 }
 
 hipError_t launch_route_assign(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
@@ -186,8 +187,8 @@ hipError_t launch_route_assign(const Dims& d, const int32_t* idx, const Work& w,
 // Clears the counters, then counts (no counting launch for an empty batch).
 hipError_t launch_traffic(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
   const int blocks = (d.R * d.R + kPlanBlock - 1) / kPlanBlock;
-  hipLaunchKernelGGL(traffic_clear_kernel, dim3(blocks), dim3(kPlanBlock), 0, s, d, w);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = launch(MOE_KERNEL_TRAFFIC_CLEAR, traffic_clear_kernel, dim3(blocks),
+                              dim3(kPlanBlock), 0, s, d, w);
   if (e != hipSuccess) return e;
   return by_topk<TrafficLaunch>(d.k, d, idx, w, s);
 }

@@ -170,7 +170,7 @@ int64_t moe_plan_bands(const moe_plan* plan);             /* nb (1 without bands
  * exclusive scan and the segment descriptors (and, with dedup, the per-
  * forwarder staging descriptors).  topk_idx: device [T, k] int32.
  * workspace: device, moe_plan_workspace_bytes(plan) bytes, contents need
- * no initialisation (but see moe_pipeline).  Asynchronous.  The slot arrays (slot_of, row_src and
+ * no initialisation.  Asynchronous.  The slot arrays (slot_of, row_src and
  * the staging ones) are finished by the next moe_dispatch, or by the next
  * moe_combine / moe_plan_read if no dispatch comes first.
  * Errors: INVALID_ARGUMENT, HIP. */
@@ -254,16 +254,66 @@ moe_status moe_combine_fp8(moe_plan* plan, const uint8_t* y8, const float* y_sca
  * the plan as by moe_route_plan, and the plan is routed afterwards.  Needs
  * H % 64 == 0 (rows of whole 128-byte lines) and recv 128-byte aligned, so
  * that no cache line holds bytes of two bands.  The workspace also holds the
- * pipeline's counters: the first moe_pipeline of a plan on a workspace zeroes
- * them (one small extra launch) and every launch leaves them at zero, so a
- * workspace used with moe_pipeline must not be written by anyone else, nor
- * shared with another plan, while the plan uses it.  Every wait inside the
+ * pipeline's counters, which every moe_pipeline zeroes before its launch (one
+ * small extra kernel on the stream), so the workspace's contents need no
+ * initialisation here either.  Every wait inside the
  * launch is bounded; a wait that gives up makes moe_plan_read(STATUS) report
  * MOE_ERR_PIPELINE_STALL (the outputs are then unspecified).
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (MOE_FLAG_NODE_DEDUP, H % 64 != 0), HIP. */
 moe_status moe_pipeline(moe_plan* plan, const int32_t* topk_idx, void* workspace,
                         const uint16_t* x, uint16_t* recv, const float* topk_w, void* out,
                         int32_t out_dtype, void* stream);
+
+/* ---- per-launch kernel timing ---------------------------------------------
+ * For measuring the library's kernels where they run, in the caller's own
+ * sequence of calls.  The kernels, as moe_plan_timing_read names them (each
+ * id's name is the kernel's symbol, as profilers list it): */
+typedef enum moe_kernel {
+  MOE_KERNEL_ROUTE_COUNT = 0,     /* histogram, in-tile ranks (moe_route_plan)               */
+  MOE_KERNEL_ROUTE_SCAN = 1,      /* exclusive scan -> segment descriptors                   */
+  MOE_KERNEL_ROUTE_ASSIGN = 2,    /* slot arrays for a combine / read without a dispatch      */
+  MOE_KERNEL_TRAFFIC_CLEAR = 3,   /* zeroes the link-traffic matrices (moe_plan_read)        */
+  MOE_KERNEL_TRAFFIC = 4,         /* link-traffic matrices (moe_plan_read)                   */
+  MOE_KERNEL_GATHER = 5,          /* single-hop dispatch                                     */
+  MOE_KERNEL_GATHER_SCAN = 6,     /* single-hop dispatch with the scan folded in (small plans) */
+  MOE_KERNEL_STAGE_A = 7,         /* deduplicated dispatch, hop 1 (one launch per chunk)      */
+  MOE_KERNEL_STAGE_B = 8,         /* deduplicated dispatch, hop 2 (one launch per chunk)      */
+  MOE_KERNEL_COMBINE = 9,         /* moe_combine                                             */
+  MOE_KERNEL_COMBINE_PART = 10,   /* moe_combine_hier, hop 1                                 */
+  MOE_KERNEL_COMBINE_NODES = 11,  /* moe_combine_hier, hop 2                                 */
+  MOE_KERNEL_GATHER_FP8 = 12,     /* moe_dispatch_fp8, single hop                            */
+  MOE_KERNEL_GATHER_FP8_SCAN = 13,/* ... with the scan folded in                             */
+  MOE_KERNEL_STAGE_A_FP8 = 14,    /* moe_dispatch_fp8 with dedup, hop 1                      */
+  MOE_KERNEL_STAGE_B_FP8 = 15,    /* moe_dispatch_fp8 with dedup, hop 2                      */
+  MOE_KERNEL_COMBINE_FP8 = 16,    /* moe_combine_fp8                                         */
+  MOE_KERNEL_PIPELINE = 17,       /* moe_pipeline                                            */
+  MOE_KERNEL_COUNTERS_CLEAR = 18, /* moe_pipeline: zeroes the pipeline's counters            */
+  MOE_KERNEL_COUNT = 19
+} moe_kernel;
+
+/* Symbol name of a moe_kernel id (static text; "?" outside the enum). */
+const char* moe_kernel_name(int32_t kernel);
+
+/* Starts (capacity > 0) or stops (capacity = 0) per-launch timing of the
+ * kernels that calls on this plan launch.  capacity > 0 creates `capacity`
+ * pairs of HIP events on the current device (the plan's earlier pairs are
+ * destroyed) and clears the record; from then on each kernel launched by a
+ * call on this plan, up to `capacity` launches, is launched with
+ * hipExtLaunchKernel and a pair bound to the kernel's own start and end, so a
+ * pair's elapsed time is that kernel's execution on the GPU, with no launch
+ * gap in it.  Launches beyond `capacity` run untimed.  capacity = 0 destroys
+ * the events.  The plan owns the events.  Host call; no kernel is launched.
+ * Errors: INVALID_ARGUMENT (null plan, capacity < 0), HIP. */
+moe_status moe_plan_timing(moe_plan* plan, int32_t capacity);
+
+/* Waits for the timed launches recorded since moe_plan_timing or the last
+ * read (each pair's end event), writes the moe_kernel id and the elapsed
+ * milliseconds of the first min(*count, cap) of them, in launch order, to the
+ * caller's host arrays kernel_ids [cap] and ms [cap], sets *count to the
+ * number recorded, and clears the record (the event pairs are reused).
+ * Errors: INVALID_ARGUMENT (null arguments, timing not started), HIP. */
+moe_status moe_plan_timing_read(moe_plan* plan, int32_t* kernel_ids, float* ms, int32_t cap,
+                                int32_t* count);
 
 /* Copies one plan item to host memory (synchronises the stream).  bytes must
  * be at least the item's size (see moe_item).  The traffic matrices

@@ -9,8 +9,9 @@ The pages fix no format or scale convention; the reading taken here:
     finite value 448 (S.1111.110), subnormals m * 2^-9;
   * scaling: every row is cut into blocks of 128 elements (the last block may
     be shorter); each block has one power-of-two scale 2^e, the smallest
-    with amax(|block|) <= 448 * 2^e (e = 0 for an all-zero block; e kept in
-    [-126, 127]).  Dividing by a power of two is exact, so the only rounding
+    with amax(|block|) <= 448 * 2^e (e = 0 for an all-zero block, and for a
+    block holding an infinity or a NaN, whose codes are then unspecified;
+    e kept in [-126, 127]).  Dividing by a power of two is exact, so the only rounding
     is the code choice;
   * code choice: round to the nearest representable E4M3 value, ties to the
     even code (last mantissa bit 0), saturating at +-448; NaN stays NaN;
@@ -71,13 +72,20 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
 
 
 def block_exponent(amax: np.ndarray) -> np.ndarray:
-    """Smallest e with amax <= 448 * 2^e, by comparing against the powers of two."""
+    """Smallest e with amax <= 448 * 2^e, by comparing against the powers of two.
+
+    e = 0 for an all-zero block, and for a block whose largest magnitude is
+    not finite (an infinity or a NaN in the block); such a block's codes are
+    left unspecified (reading: the pages give no rule for non-finite inputs).
+    """
     a = np.asarray(amax, dtype=np.float64)
-    e = np.ceil(np.log2(np.where(a > 0, a, 1.0) / MAX_FINITE)).astype(np.int64)
+    ok = np.isfinite(a) & (a > 0)
+    s = np.where(ok, a, 1.0)
+    e = np.ceil(np.log2(s / MAX_FINITE)).astype(np.int64)
     # settle the borderline cases exactly: 448*2^(e-1) < amax <= 448*2^e
-    e = np.where(a > MAX_FINITE * np.ldexp(1.0, e), e + 1, e)
-    e = np.where(a <= MAX_FINITE * np.ldexp(1.0, e - 1), e - 1, e)
-    e = np.where(a > 0, e, 0)
+    e = np.where(s > MAX_FINITE * np.ldexp(1.0, e), e + 1, e)
+    e = np.where(s <= MAX_FINITE * np.ldexp(1.0, e - 1), e - 1, e)
+    e = np.where(ok, e, 0)
     return np.clip(e, -126, 127)
 
 

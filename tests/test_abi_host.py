@@ -166,3 +166,30 @@ def test_fp8_entry_points_on_host():
     assert L.moe_dispatch_fp8(h, vp(16), vp(16), vp(16), None, None, None) == _abi.ERR_PLAN_NOT_ROUTED
     assert L.moe_combine_fp8(h, vp(16), vp(16), vp(16), vp(16), 0, None) == _abi.ERR_PLAN_NOT_ROUTED
     L.moe_plan_destroy(h)
+
+
+def test_kernel_names_are_the_kernels_symbols():
+    # Every moe_kernel id names a __global__ function of the sources, as a
+    # profiler lists it; ids outside the enum give "?".
+    csrc = os.path.join(os.path.dirname(HEADER), "..", "combine_shuffling_amd", "csrc")
+    text = "".join(open(os.path.join(csrc, f)).read() for f in os.listdir(csrc)
+                   if f.endswith((".hip", ".h")))
+    kernels = set(re.findall(r"void\s+(\w+_kernel)\s*\(", text))
+    names = [_abi.kernel_name(i) for i in range(_abi.KERNEL_COUNT)]
+    assert len(set(names)) == _abi.KERNEL_COUNT
+    assert set(names) <= kernels, set(names) - kernels
+    assert _abi.kernel_name(_abi.KERNEL_COUNT) == "?" and _abi.kernel_name(-1) == "?"
+
+
+def test_timing_host_errors():
+    L = _abi.lib()
+    st, h = make()
+    assert st == _abi.OK
+    n = ctypes.c_int32()
+    ids = (ctypes.c_int32 * 1)()
+    ms = (ctypes.c_float * 1)()
+    assert L.moe_plan_timing(None, 4) == _abi.ERR_INVALID_ARGUMENT
+    assert L.moe_plan_timing(h, -1) == _abi.ERR_INVALID_ARGUMENT
+    assert L.moe_plan_timing(h, 0) == _abi.OK                     # off: no HIP call
+    assert L.moe_plan_timing_read(h, ids, ms, 1, ctypes.byref(n)) == _abi.ERR_INVALID_ARGUMENT
+    L.moe_plan_destroy(h)

@@ -42,6 +42,34 @@ def test_dedup_and_variant_bytes():
     assert bench.algorithmic_bytes(wl, D, "fp8")[0] == T * row + (2 * D + T * k) * row8
 
 
+@pytest.mark.parametrize("payload", ["bf16", "fp8"])
+def test_kernel_bytes_add_up_to_the_phases(payload):
+    # The per-kernel bytes of the roofline split each phase's algorithmic bytes
+    # between its kernels: the two hops make up the deduplicated dispatch.
+    wl, D = gen.get("dsv3"), 65_085
+    kb = bench.kernel_bytes(wl, D, payload)
+    sfx = "_fp8" if payload == "fp8" else ""
+    disp, comb = bench.algorithmic_bytes(wl, D, payload)
+    assert kb[f"stage_a{sfx}_kernel"] + kb[f"stage_b{sfx}_kernel"] == disp
+    assert kb[f"combine{sfx}_kernel"] == comb
+    one = gen.get("nondiv")
+    kb1 = bench.kernel_bytes(one, 0, payload)
+    d1, c1 = bench.algorithmic_bytes(one, 0, payload)
+    assert kb1[f"gather{sfx}_kernel"] == kb1[f"gather{sfx}_scan_kernel"] == d1
+    assert kb1[f"combine{sfx}_kernel"] == c1
+    hd, hc = bench.algorithmic_bytes(wl, D, hier=True)
+    assert kb["combine_part_kernel"] + kb["combine_nodes_kernel"] == hc
+    assert kb1["pipeline_kernel"] == sum(bench.algorithmic_bytes(one, 0))
+
+
+def test_default_is_the_largest_workload():
+    # The headline is the DeepSeek-V3-like shuffle (the largest configuration);
+    # the other large workloads are measured in the same run.
+    a = bench.parse([])
+    assert a.workload == "dsv3" and a.payload == "bf16"
+    assert set(a.configs.split(",")) == {"olmoe", "qwen3", "nondiv"}
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
@@ -98,7 +126,8 @@ def test_traffic_lookup_needs_current_sources(tmp_path, monkeypatch):
                            "combine_kernel<8, 1, false>": {"traffic_bytes": 456}}}
     (tmp_path / "hbm_traffic_w.txt").write_text("# header\n" + json.dumps(summary))
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    assert bench.recorded_traffic("w", "gather_scan_kernel|gather_kernel") == ("gather_kernel<8, 1>", 123)
+    assert bench.recorded_traffic("w", "gather_kernel") == ("gather_kernel<8, 1>", 123)
+    assert bench.recorded_traffic("w", "gather_scan_kernel") == (None, None)
     assert bench.recorded_traffic("w", "combine_kernel") == ("combine_kernel<8, 1, false>", 456)
     assert bench.recorded_traffic("w", "stage_a_kernel") == (None, None)
     assert bench.recorded_traffic("missing", "gather_kernel") == (None, None)

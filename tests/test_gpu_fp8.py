@@ -113,6 +113,33 @@ def test_fp8_zero_rows_and_tiny_values(dev):
     check_fp8(batch, dev, x_bits=x)
 
 
+def test_fp8_large_and_non_finite_blocks(dev):
+    # Blocks whose largest magnitude is near the top of the bf16 range (e =
+    # 120), and blocks holding +-inf or a NaN (e = 0, codes unspecified): the
+    # scales match the oracle everywhere, the codes in every finite block.
+    batch = gen.make_batch(gen.custom(300, 256, 16, 4, 4, seed=11))
+    x = batch.x.copy()
+    big = oracle.f32_to_bf16_rne(np.array([3.2e38, -3.2e38, 3.3895313892515355e38], np.float32))
+    x[0:20, 3] = big[0]
+    x[20:40, 130] = big[1]
+    x[40:60, 200] = big[2]
+    x[60:80, 9] = np.uint16(0x7F80)       # +inf in block 0
+    x[80:100, 250] = np.uint16(0xFF80)    # -inf in block 1
+    x[100:120, 64] = np.uint16(0x7FC0)    # NaN in block 0
+    say("[fp8] large and non-finite blocks T300-H256-E16-k4-R4")
+    p = oracle.route_plan(batch.topk_idx, 16, 4)
+    plan, codes, scales = run_fp8(batch, dev, x)
+    want_c, want_e = fp8.dispatch_fp8(x, p)
+    got_s = scales.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got_s, np.ldexp(1.0, want_e)), "block scales differ"
+    src = p["row_src"]
+    finite = np.isfinite(oracle.bf16_to_f32(x).astype(np.float64)).reshape(300, 2, 128).all(axis=2)
+    keep = np.repeat(finite[src], 128, axis=1)
+    got_c = codes.cpu().numpy()
+    assert np.array_equal(got_c[keep], want_c[keep]), "codes of finite blocks differ"
+    assert (want_e[np.isin(src, np.arange(0, 60))] == 120).any()
+
+
 def test_fp8_one_hot_combine_is_exact_decode(dev):
     batch = gen.make_batch(gen.custom(1000, 512, 32, 4, 4, seed=8))
     T, k = batch.topk_idx.shape

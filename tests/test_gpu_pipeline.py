@@ -140,6 +140,26 @@ def test_pipeline_repeated_calls_reuse_counters(dev):
                       True, wl.name)
 
 
+def test_pipeline_on_a_workspace_holding_stale_counters(dev):
+    # A caller's workspace may hold anything (a reused allocation, another
+    # plan's routing): every launch zeroes its counters first, so stale
+    # values cannot let a ticket pass its wait early.
+    batch = gen.make_batch(gen.custom(2048, 64, 64, 8, 4, 4, seed=9))
+    wl = batch.workload
+    p = oracle.route_plan_banded(batch.topk_idx, 64, 4, 256)
+    plan = _plan(wl, 256)
+    ws = torch.full((plan.workspace_bytes,), 0x7F, dtype=torch.uint8, device=dev)
+    idx, x, w = to_dev(batch.topk_idx, dev), to_dev(batch.x, dev), to_dev(batch.topk_w, dev)
+    for fill in (0x7F, 0x01):
+        ws.fill_(fill)          # every counter large, then every counter small
+        recv, out = plan.pipeline(idx, x, w, out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert plan.status() == 0
+        assert np.array_equal(bits(recv), oracle.dispatch(batch.x, p))
+        check_combine(out.cpu().numpy(), oracle.dispatch(batch.x, p), batch.topk_w, p["slot_of"],
+                      True, wl.name)
+
+
 def test_pipeline_bad_routing_flagged(dev):
     batch = gen.make_batch(gen.custom(1024, 64, 16, 4, 4, 4, seed=5))
     idx = batch.topk_idx.copy()

@@ -56,6 +56,36 @@ def test_block_exponent_is_smallest():
     assert fp8.block_exponent(np.array([448.0, 449.0, 224.0, 1.0])).tolist() == [0, 1, -1, -8]
 
 
+def test_block_exponent_every_bf16_magnitude():
+    # Every positive finite bf16 magnitude (bit patterns 0x0001..0x7F7F), the
+    # top of the range included: 2^e is the smallest power of two with
+    # amax <= 448 * 2^e, unless the clamp to [-126, 127] applies (tiny blocks).
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    amax = oracle.bf16_to_f32(bits).astype(np.float64)
+    e = fp8.block_exponent(amax)
+    assert np.all(amax <= 448.0 * np.ldexp(1.0, e))
+    small = e > -126
+    assert np.all(amax[small] > 448.0 * np.ldexp(1.0, e[small] - 1))
+    # 448 * 2^119 = 2.98e38 < 3.2e38 <= 448 * 2^120; 0x7F7F (3.39e38) likewise
+    assert fp8.block_exponent(np.array([3.2e38, 3.3895313892515355e38])).tolist() == [120, 120]
+
+
+def test_block_exponent_non_finite_blocks():
+    # Reading: a block whose largest magnitude is an infinity or a NaN keeps
+    # the scale 1 (e = 0); its codes are unspecified.
+    assert fp8.block_exponent(np.array([np.inf, np.nan, 0.0])).tolist() == [0, 0, 0]
+    row = np.zeros((3, 256), dtype=np.float32)
+    row[0, :128] = 1.0
+    row[0, 5] = np.inf          # block 0 of row 0: inf -> e = 0
+    row[0, 128:] = 3.0
+    row[1, 130] = np.nan        # block 1 of row 1: NaN -> e = 0
+    row[1, :128] = -2.0
+    row[2, 7] = -3.2e38         # a large finite magnitude -> e = 120
+    bits = oracle.f32_to_bf16_rne(row)
+    _, exps = fp8.quantize_rows(bits)
+    assert exps.tolist() == [[0, -7], [-7, 0], [120, 0]]
+
+
 def test_quantize_error_bound_and_block_layout():
     wl = gen.custom(300, 200, 8, 2, 2)        # H=200: blocks of 128 and 72
     b = gen.make_batch(wl)
