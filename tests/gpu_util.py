@@ -94,6 +94,32 @@ def check_combine_values(out, ref, yv, w, slot_of, out_f32, what, roundings=None
     return info
 
 
+def check_combine_chunks(out, w, slot_of, out_f32, what, ref_and_values, chunk=2048,
+                         roundings=None) -> None:
+    """The bars of check_combine_values on every token, chunk by chunk so that
+    host memory stays bounded at full size.  ref_and_values(used, w_chunk,
+    sub) returns the oracle's float64 combine of the chunk's tokens over the
+    receive rows `used` (renumbered: slot_of[chunk] == used[sub]) and those
+    rows' exact float64 values."""
+    T = slot_of.shape[0]
+    for s in range(0, T, chunk):
+        e = min(T, s + chunk)
+        so = slot_of[s:e]
+        used = np.unique(so)
+        sub = np.searchsorted(used, so)
+        ref, yv = ref_and_values(used, w[s:e], sub)
+        check_combine_values(out[s:e], ref, yv, w[s:e], sub, out_f32,
+                             f"{what} (tokens {s}..{e - 1})", roundings)
+
+
+def check_combine_all(out, y, w, slot_of, out_f32, what) -> None:
+    """check_combine on every token (bf16 receive rows y), chunk by chunk."""
+    check_combine_chunks(
+        out, w, slot_of, out_f32, what,
+        lambda used, wc, sub: (oracle.combine(y[used], wc, {"slot_of": sub}),
+                               oracle.bf16_to_f32(y[used]).astype(np.float64)))
+
+
 class DeviceRun:
     """One route plan + dispatch (+ combine) on the GPU through the C ABI."""
 

@@ -13,7 +13,7 @@ import oracle
 from oracle import fp8
 from workloads import gen
 
-from gpu_util import check_combine_values, say, to_dev
+from gpu_util import check_combine_chunks, check_combine_values, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,7 @@ def run_fp8(batch, dev, x_bits=None):
     return plan, codes_full[:rows], scale_full[:rows]
 
 
-def check_fp8(batch, dev, x_bits=None, tokens=None):
+def check_fp8(batch, dev, x_bits=None):
     wl = batch.workload
     say(f"[fp8] {wl.describe()}")
     x = batch.x if x_bits is None else x_bits
@@ -54,18 +54,16 @@ def check_fp8(batch, dev, x_bits=None, tokens=None):
     assert bad.size == 0, f"codes differ at {bad[:3].tolist()}: {got_c[tuple(bad[0])]:#x} vs {want_c[tuple(bad[0])]:#x}"
     assert np.array_equal(got_s, np.ldexp(1.0, want_e)), "block scales differ"
     assert np.array_equal(plan.read("slot_of").reshape(p["slot_of"].shape), p["slot_of"])
-    tok = np.arange(wl.num_tokens) if tokens is None else tokens
-    so = p["slot_of"][tok]
-    ref = fp8.combine_fp8(want_c, want_e, batch.topk_w[tok], {"slot_of": so})
-    yv = fp8.dequantize_rows(want_c, want_e)
     w = to_dev(batch.topk_w, dev)
     for out_dtype in (torch.float32, torch.bfloat16):
         out = plan.combine_fp8(codes, scales, w, out_dtype=out_dtype)
         torch.cuda.synchronize()
         o = out.cpu().numpy() if out_dtype == torch.float32 else \
             out.cpu().view(torch.int16).numpy().view(np.uint16)
-        check_combine_values(o[tok], ref, yv, batch.topk_w[tok], so, out_dtype == torch.float32,
-                             wl.name + " fp8")
+        check_combine_chunks(
+            o, batch.topk_w, p["slot_of"], out_dtype == torch.float32, wl.name + " fp8",
+            lambda used, wc, sub: (fp8.combine_fp8(want_c[used], want_e[used], wc, {"slot_of": sub}),
+                                   fp8.dequantize_rows(want_c[used], want_e[used])))
 
 
 @pytest.mark.parametrize("case", [
@@ -97,11 +95,7 @@ def test_fp8_random_shapes(seed, dev):
 
 @pytest.mark.parametrize("name", ["tiny", "olmoe", "qwen3", "nondiv"])
 def test_fp8_workloads_full_size(name, dev):
-    batch = gen.make_batch(gen.get(name))
-    T = batch.workload.num_tokens
-    rng = np.random.default_rng(7)
-    tok = None if T <= 4096 else np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 512)]))
-    check_fp8(batch, dev, tokens=tok)
+    check_fp8(gen.make_batch(gen.get(name)), dev)
 
 
 def test_fp8_zero_rows_and_tiny_values(dev):
@@ -154,7 +148,7 @@ def test_fp8_one_hot_combine_is_exact_decode(dev):
     assert np.array_equal(out.astype(np.float64), fp8.dequantize_rows(c[rows], e[rows]))
 
 
-def check_fp8_dedup(batch, dev, load_aware=False, tokens=None):
+def check_fp8_dedup(batch, dev, load_aware=False):
     import combine_shuffling_amd as cs
 
     wl = batch.workload
@@ -184,14 +178,13 @@ def check_fp8_dedup(batch, dev, load_aware=False, tokens=None):
     assert np.array_equal(scale_full[:rows].cpu().numpy().astype(np.float64), np.ldexp(1.0, re))
     assert np.array_equal(plan.read("stage_of").reshape(T, k), p["stage_of"])
     assert np.array_equal(plan.read("stage_src")[:D], p["stage_src"])
-    tok = np.arange(T) if tokens is None else tokens
-    so = p["slot_of"][tok]
-    ref = fp8.combine_fp8(rc, re, batch.topk_w[tok], {"slot_of": so})
     out = plan.combine_fp8(codes_full[:rows], scale_full[:rows], to_dev(batch.topk_w, dev),
                            out_dtype=torch.float32)
     torch.cuda.synchronize()
-    check_combine_values(out.cpu().numpy()[tok], ref, fp8.dequantize_rows(rc, re),
-                         batch.topk_w[tok], so, True, wl.name + " fp8 dedup")
+    check_combine_chunks(
+        out.cpu().numpy(), batch.topk_w, p["slot_of"], True, wl.name + " fp8 dedup",
+        lambda used, wc, sub: (fp8.combine_fp8(rc[used], re[used], wc, {"slot_of": sub}),
+                               fp8.dequantize_rows(rc[used], re[used])))
 
 
 @pytest.mark.parametrize("load_aware", [False, True])
@@ -219,19 +212,13 @@ def test_fp8_dedup_random_shapes(seed, dev):
 
 
 def test_fp8_dedup_dsv3(dev):
-    batch = gen.make_batch(gen.get("dsv3"))
-    T = batch.workload.num_tokens
-    tok = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(11).integers(0, T, 384)]))
-    check_fp8_dedup(batch, dev, tokens=tok)
+    check_fp8_dedup(gen.make_batch(gen.get("dsv3")), dev)
 
 
 def test_fp8_dedup_in_chunks(dev):
     # 8999 tokens of 8 staging rows of 7168 codes + 56 scales at most: the
     # fp8 dispatch runs hop 1 and hop 2 in 3 chunks, the last ragged.
-    batch = gen.make_batch(gen.custom(8999, 7168, 32, 8, 8, 1, seed=9))
-    T = batch.workload.num_tokens
-    tok = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(12).integers(0, T, 256)]))
-    check_fp8_dedup(batch, dev, tokens=tok)
+    check_fp8_dedup(gen.make_batch(gen.custom(8999, 7168, 32, 8, 8, 1, seed=9)), dev)
 
 
 def test_fp8_combines_without_dispatch(dev):

@@ -12,7 +12,7 @@ import torch
 import oracle
 from workloads import gen
 
-from gpu_util import DeviceRun, bits, check_combine, check_combine_values, say, to_dev
+from gpu_util import check_combine_all, DeviceRun, bits, check_combine, check_combine_values, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -62,12 +62,16 @@ def full_check(batch, dev, dedup=None, combine_tokens=None, traffic=False, load_
         assert np.array_equal(run.plan.read("send_rows").reshape(R, R), p["send_rows"])
         assert np.array_equal(run.plan.read("send_copies").reshape(R, R), p["send_copies"])
         assert np.array_equal(run.plan.read("node_copies").reshape(R, N), p["node_copies"])
-    tok = np.arange(wl.num_tokens) if combine_tokens is None else combine_tokens
     for out_dtype in (torch.bfloat16, torch.float32):
         out = run.combine(out_dtype=out_dtype)
         o = out.cpu().numpy() if out_dtype == torch.float32 else bits(out)
-        check_combine(o[tok], recv, batch.topk_w[tok], p["slot_of"][tok],
-                      out_dtype == torch.float32, wl.name)
+        if combine_tokens is None:
+            check_combine_all(o, recv, batch.topk_w, p["slot_of"], out_dtype == torch.float32,
+                              wl.name)
+        else:
+            tok = combine_tokens
+            check_combine(o[tok], recv, batch.topk_w[tok], p["slot_of"][tok],
+                          out_dtype == torch.float32, wl.name)
     return run, p
 
 
@@ -106,11 +110,8 @@ def test_small_shapes(case, dev):
 
 @pytest.mark.parametrize("name", gen.WORKLOAD_ORDER)
 def test_workload_full_size(name, dev):
-    batch = gen.make_batch(gen.get(name))
-    T = batch.workload.num_tokens
-    rng = np.random.default_rng(123)
-    sample = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, min(T, 768))]))
-    full_check(batch, dev, combine_tokens=None if T <= 4096 else sample, traffic=True)
+    # every token's combine is compared (in chunks of tokens)
+    full_check(gen.make_batch(gen.get(name)), dev, traffic=True)
 
 
 @pytest.mark.parametrize("case", [
@@ -122,10 +123,7 @@ def test_dedup_dispatch_in_chunks(case, dev):
     # Hop 1 and hop 2 run chunk by chunk over consecutive tokens; the rows
     # must be those of the whole-batch oracle.
     T, H, E, k, R, G = case
-    batch = gen.make_batch(gen.custom(T, H, E, k, R, G, seed=T))
-    rng = np.random.default_rng(7)
-    sample = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 512)]))
-    full_check(batch, dev, combine_tokens=sample)
+    full_check(gen.make_batch(gen.custom(T, H, E, k, R, G, seed=T)), dev)
 
 
 def test_dedup_workload_single_hop_too(dev):
@@ -285,10 +283,7 @@ def test_load_aware_forwarders(case, dev):
 
 
 def test_load_aware_forwarders_dsv3(dev):
-    batch = gen.make_batch(gen.get("dsv3"))
-    T = batch.workload.num_tokens
-    sample = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(5).integers(0, T, 256)]))
-    full_check(batch, dev, combine_tokens=sample, load_aware=True)
+    full_check(gen.make_batch(gen.get("dsv3")), dev, load_aware=True)
 
 
 def hier_check(batch, dev, load_aware, tokens=None):

@@ -21,7 +21,8 @@ import oracle
 from oracle import fp8
 from workloads import gen
 
-from gpu_util import bits, check_combine, check_combine_values, say, to_dev
+from gpu_util import (bits, check_combine, check_combine_all, check_combine_chunks,
+                      check_combine_values, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -228,7 +229,7 @@ def test_full_size_in_benchmark_schedule(name, schedule, load_aware, dev):
     for it: four buffer sets holding four different batches (seeds 0-3 of the
     workload's recipe, so that rows taken from the wrong set would show),
     cycled over eight steps, bf16 output.  Every set's receive (and staging)
-    rows are compared bit for bit, its combine on sampled tokens; on the
+    rows are compared bit for bit, its combine on every token; on the
     DeepSeek-V3-like workload also with load-aware forwarders."""
     wl = gen.get(name)
     T, H, E, k, R, G = (wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
@@ -247,8 +248,6 @@ def test_full_size_in_benchmark_schedule(name, schedule, load_aware, dev):
     say(f"[full size, {schedule}] {wl.describe()} load_aware={load_aware}: 4 sets, 8 steps")
     _run_schedule(sets, schedule, 8, dev)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(5)
-    tok = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, min(T, 768))]))
     for seed, s in enumerate(sets):
         b = s["b"]
         p = oracle.route_plan(b.topk_idx, E, R, G, forwarders="load_aware" if load_aware else "static")
@@ -261,15 +260,15 @@ def test_full_size_in_benchmark_schedule(name, schedule, load_aware, dev):
             D = p["num_staged"]
             assert np.array_equal(bits(s["st"])[:D], oracle.dedup_stage_a(b.x, p)), \
                 f"staging rows of set {seed}"
-        check_combine(bits(s["out"])[tok], recv, b.topk_w[tok], p["slot_of"][tok], False,
-                      f"{wl.name} set {seed}")
+        check_combine_all(bits(s["out"]), recv, b.topk_w, p["slot_of"], False,
+                          f"{wl.name} set {seed}")
 
 
 @pytest.mark.parametrize("name,schedule", [("qwen3", "staggered"), ("dsv3", "plan_ahead")])
 def test_full_size_fp8_in_benchmark_schedule(name, schedule, dev):
     """The same with the fp8 payload (with node deduplication on the
     DeepSeek-V3-like workload): every set's codes and block scales bit for
-    bit, staging ones too, its combine on sampled tokens against the
+    bit, staging ones too, its combine on every token against the
     oracle's float64 sum of the decoded rows."""
     wl = gen.get(name)
     T, H, E, k, R, G = (wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
@@ -291,8 +290,6 @@ def test_full_size_fp8_in_benchmark_schedule(name, schedule, dev):
     say(f"[full size fp8, {schedule}] {wl.describe()}: 4 sets, 8 steps")
     _run_schedule(sets, schedule, 8, dev)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(6)
-    tok = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, min(T, 768))]))
     for seed, s in enumerate(sets):
         b = s["b"]
         p = oracle.route_plan(b.topk_idx, E, R, G)
@@ -307,13 +304,10 @@ def test_full_size_fp8_in_benchmark_schedule(name, schedule, dev):
         assert np.array_equal(s["recv"].cpu().numpy(), rc), f"receive codes of set {seed}"
         assert np.array_equal(s["scale"].cpu().numpy().astype(np.float64), np.ldexp(1.0, re)), \
             f"receive scales of set {seed}"
-        # the receive rows of the sampled tokens, renumbered
-        so = p["slot_of"][tok]
-        used = np.unique(so)
-        sub = np.searchsorted(used, so)
-        ref = fp8.combine_fp8(rc[used], re[used], b.topk_w[tok], {"slot_of": sub})
-        check_combine_values(bits(s["out"])[tok], ref, fp8.dequantize_rows(rc[used], re[used]),
-                             b.topk_w[tok], sub, False, f"{wl.name} fp8 set {seed}")
+        check_combine_chunks(
+            bits(s["out"]), b.topk_w, p["slot_of"], False, f"{wl.name} fp8 set {seed}",
+            lambda used, wc, sub: (fp8.combine_fp8(rc[used], re[used], wc, {"slot_of": sub}),
+                                   fp8.dequantize_rows(rc[used], re[used])))
 
 
 def test_full_size_hierarchical_combine_in_benchmark_schedule(dev):
