@@ -110,6 +110,19 @@ class Plan:
                                             _stream_handle(dev, stream)), "moe_route_plan")
         return self
 
+    # -- moe_route_plan_static
+    def route_static(self, topk_idx: torch.Tensor, stream=None):
+        """moe_route_plan_static: the route plan on the library's per-device
+        static workspace; allocates nothing.  Plans routed this way on one GPU
+        share that workspace: the last one routed is the one that holds it."""
+        dev = topk_idx.device
+        _need(topk_idx, (self.T, self.k), (torch.int32,), "topk_idx", dev)
+        self.workspace, self.topk_idx, self.device = None, topk_idx, dev
+        _abi.check(self._lib.moe_route_plan_static(self._h, _ptr(topk_idx),
+                                                   _stream_handle(dev, stream)),
+                   "moe_route_plan_static")
+        return self
+
     # -- moe_pipeline
     def pipeline(self, topk_idx: torch.Tensor, x: torch.Tensor, topk_w: torch.Tensor,
                  recv: torch.Tensor | None = None, out: torch.Tensor | None = None,

@@ -20,6 +20,8 @@ ERR_PLAN_NOT_ROUTED = 4
 ERR_HIP = 5
 ERR_UNSUPPORTED = 6
 ERR_PIPELINE_STALL = 7
+ERR_STATIC_WORKSPACE = 8
+STATIC_WORKSPACE_BYTES = 32 << 20
 
 FLAG_NODE_DEDUP = 1
 FLAG_LOAD_AWARE_FORWARDERS = 2
@@ -53,7 +55,7 @@ EXPORTS = (
     "moe_plan_recv_rows", "moe_plan_staging_rows_max", "moe_route_plan", "moe_dispatch",
     "moe_combine", "moe_plan_read", "moe_status_str", "moe_plan_scale_blocks",
     "moe_dispatch_fp8", "moe_combine_fp8", "moe_combine_hier", "moe_plan_bands", "moe_pipeline",
-    "moe_kernel_name", "moe_plan_timing", "moe_plan_timing_read",
+    "moe_kernel_name", "moe_plan_timing", "moe_plan_timing_read", "moe_route_plan_static",
 )
 
 KERNEL_COUNT = 19
@@ -110,6 +112,8 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_bands.restype = i64
     L.moe_pipeline.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]
     L.moe_pipeline.restype = i32
+    L.moe_route_plan_static.argtypes = [vp, vp, vp]
+    L.moe_route_plan_static.restype = i32
     L.moe_kernel_name.argtypes = [i32]
     L.moe_kernel_name.restype = ctypes.c_char_p
     L.moe_plan_timing.argtypes = [vp, i32]

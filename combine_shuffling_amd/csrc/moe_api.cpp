@@ -175,6 +175,8 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_HIP: return "HIP runtime error";
     case MOE_ERR_UNSUPPORTED: return "sizes beyond the library's limits";
     case MOE_ERR_PIPELINE_STALL: return "a banded-pipeline wait gave up; outputs are unspecified";
+    case MOE_ERR_STATIC_WORKSPACE:
+      return "the plan's workspace exceeds the static per-device workspace (MOE_STATIC_WORKSPACE_BYTES)";
   }
   return "unknown status";
 }
@@ -377,6 +379,15 @@ moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspa
   // the plan arrays before it).
   if (!plan->d.fused_scan && moe::ensure_scanned(plan, s) != MOE_OK) return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+moe_status moe_route_plan_static(moe_plan* plan, const int32_t* topk_idx, void* stream) {
+  if (!plan) return MOE_ERR_INVALID_ARGUMENT;
+  if (plan->layout.total > (size_t)MOE_STATIC_WORKSPACE_BYTES) return MOE_ERR_STATIC_WORKSPACE;
+  if (plan->d.T > 0 && (!topk_idx || !moe::aligned(topk_idx, 4))) return MOE_ERR_INVALID_ARGUMENT;
+  void* ws = nullptr;
+  if (moe::static_workspace(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return moe_route_plan(plan, topk_idx, ws, stream);
 }
 
 moe_status moe_pipeline(moe_plan* plan, const int32_t* topk_idx, void* workspace,

@@ -130,6 +130,10 @@ struct Layout {
 Layout make_layout(const Dims& d);
 Work bind_work(const Layout& l, void* base);
 
+// The per-device static workspace of moe_route_plan_static (route_plan.hip):
+// its device address on the current device, looked up once per device.
+hipError_t static_workspace(void** out);
+
 // Route plan (route_plan.hip).
 // route_count, and route_scan (one block per band).
 hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s);

@@ -29,11 +29,19 @@
 // finish slot_of / row_src (and stage_of / stage_src) on the fly; the
 // per-token route_assign kernel does the same when a consumer needs the plan
 // without a dispatch.
+#include <mutex>
+
 #include "plan_body.h"
 
 namespace moe {
 namespace {
 
+// Workspace of moe_route_plan_static: one copy on every GPU the library runs
+// on, held until the process ends.  In host code `scratch` only stands in for
+// the symbol; its device address comes from hipGetSymbolAddress.
+__device__ __align__(256) unsigned char scratch[MOE_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
 
 template <int KMAX>
 __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
@@ -170,6 +178,24 @@ struct TrafficLaunch {
 };
 
 }  // namespace
+
+hipError_t static_workspace(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {
   return by_topk<CountLaunch>(d.k, d, idx, w, s);

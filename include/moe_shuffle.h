@@ -87,7 +87,9 @@ typedef enum moe_status {
   MOE_ERR_PLAN_NOT_ROUTED = 4,  /* dispatch/combine/read before moe_route_plan          */
   MOE_ERR_HIP = 5,              /* a HIP runtime call or kernel launch failed           */
   MOE_ERR_UNSUPPORTED = 6,      /* sizes beyond the library's limits (below)            */
-  MOE_ERR_PIPELINE_STALL = 7    /* a banded-pipeline wait gave up (moe_pipeline)         */
+  MOE_ERR_PIPELINE_STALL = 7,   /* a banded-pipeline wait gave up (moe_pipeline)         */
+  MOE_ERR_STATIC_WORKSPACE = 8  /* moe_route_plan_static: the plan's workspace is larger
+                                   than MOE_STATIC_WORKSPACE_BYTES                        */
 } moe_status;
 
 /* Limits: E <= 1024, 1 <= k <= 16, k <= E, R <= E, R % G == 0, H % 8 == 0,
@@ -175,6 +177,25 @@ int64_t moe_plan_bands(const moe_plan* plan);             /* nb (1 without bands
  * moe_combine / moe_plan_read if no dispatch comes first.
  * Errors: INVALID_ARGUMENT, HIP. */
 moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspace, void* stream);
+
+/* Route plan without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The same route plan as moe_route_plan, with the
+ * workspace taken from a buffer the library holds on each GPU instead of a
+ * caller buffer: a static device array of MOE_STATIC_WORKSPACE_BYTES, present
+ * on every GPU the library runs on until the process ends.  Nothing is
+ * allocated.  The plan stays bound to that buffer (as to a caller workspace)
+ * until its next route, and the moe_dispatch / moe_combine / moe_plan_read
+ * calls that follow use it.  Every plan routed this way on one GPU shares
+ * that GPU's buffer, which keeps the last route's contents: a later
+ * moe_route_plan_static on the same GPU replaces the descriptors of the plan
+ * routed before it, so calls of two such plans that overlap in time race
+ * (route each plan again, on the same stream, before using it).  The buffer
+ * needs no initialisation.  Not for moe_pipeline.
+ * Errors: INVALID_ARGUMENT, STATIC_WORKSPACE (moe_plan_workspace_bytes(plan) >
+ * MOE_STATIC_WORKSPACE_BYTES; checked before any HIP call), HIP. */
+#define MOE_STATIC_WORKSPACE_BYTES (32u << 20)
+moe_status moe_route_plan_static(moe_plan* plan, const int32_t* topk_idx, void* stream);
 
 /* Dispatch: recv[slot_of[t, j]] = x[t] for every valid slot.  x: device
  * [T, H] bf16; recv: device [T*k, H] bf16.  staging: device
