@@ -276,15 +276,18 @@ class Plan:
         _abi.check(self._lib.moe_plan_timing(self._h, int(capacity)), "moe_plan_timing")
         self._timing_cap = int(capacity)
 
-    def timing_read(self) -> list[tuple[str, float]]:
-        """(kernel name, milliseconds) of each timed launch since the last read, in order."""
+    def timing_read(self) -> list[tuple[str, float, float]]:
+        """(kernel name, start in ms after the first launch's start, duration in ms) of
+        each timed launch since the last read, in launch order."""
         cap = getattr(self, "_timing_cap", 0)
         ids = (ctypes.c_int32 * max(cap, 1))()
+        start = (ctypes.c_float * max(cap, 1))()
         ms = (ctypes.c_float * max(cap, 1))()
         n = ctypes.c_int32()
-        _abi.check(self._lib.moe_plan_timing_read(self._h, ids, ms, cap, ctypes.byref(n)),
+        _abi.check(self._lib.moe_plan_timing_read(self._h, ids, start, ms, cap, ctypes.byref(n)),
                    "moe_plan_timing_read")
-        return [(_abi.kernel_name(ids[i]), float(ms[i])) for i in range(min(n.value, cap))]
+        return [(_abi.kernel_name(ids[i]), float(start[i]), float(ms[i]))
+                for i in range(min(n.value, cap))]
 
     # -- moe_plan_read
     def read(self, item: str, stream=None) -> np.ndarray:

@@ -118,8 +118,8 @@ def lib() -> ctypes.CDLL:
     L.moe_kernel_name.restype = ctypes.c_char_p
     L.moe_plan_timing.argtypes = [vp, i32]
     L.moe_plan_timing.restype = i32
-    L.moe_plan_timing_read.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float), i32,
-                                       ctypes.POINTER(i32)]
+    L.moe_plan_timing_read.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float),
+                                       ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
     L.moe_plan_timing_read.restype = i32
     L.moe_status_str.argtypes = [i32]
     L.moe_status_str.restype = ctypes.c_char_p

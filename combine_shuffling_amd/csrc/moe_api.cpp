@@ -57,8 +57,8 @@ struct TimerScope {
 };
 
 void destroy_events(LaunchTimer* t) {
-  for (hipEvent_t e : t->start) hipEventDestroy(e);
-  for (hipEvent_t e : t->stop) hipEventDestroy(e);
+  for (hipEvent_t e : t->start) (void)hipEventDestroy(e);
+  for (hipEvent_t e : t->stop) (void)hipEventDestroy(e);
   t->start.clear();
   t->stop.clear();
   t->ids.clear();
@@ -319,7 +319,7 @@ moe_status moe_plan_timing(moe_plan* plan, int32_t capacity) {
     hipEvent_t a = nullptr, b = nullptr;
     if (hipEventCreate(&a) != hipSuccess) return MOE_ERR_HIP;
     if (hipEventCreate(&b) != hipSuccess) {
-      hipEventDestroy(a);
+      (void)hipEventDestroy(a);
       return MOE_ERR_HIP;
     }
     t->start.push_back(a);
@@ -330,18 +330,22 @@ moe_status moe_plan_timing(moe_plan* plan, int32_t capacity) {
   return MOE_OK;
 }
 
-moe_status moe_plan_timing_read(moe_plan* plan, int32_t* kernel_ids, float* ms, int32_t cap,
-                                int32_t* count) {
-  if (!plan || !plan->timer || !count || cap < 0 || (cap > 0 && (!kernel_ids || !ms)))
+moe_status moe_plan_timing_read(moe_plan* plan, int32_t* kernel_ids, float* start_ms, float* ms,
+                                int32_t cap, int32_t* count) {
+  if (!plan || !plan->timer || !count || cap < 0 ||
+      (cap > 0 && (!kernel_ids || !start_ms || !ms)))
     return MOE_ERR_INVALID_ARGUMENT;
   moe::LaunchTimer* t = plan->timer;
   const int n = t->used;
   for (int i = 0; i < n; ++i) {
     if (hipEventSynchronize(t->stop[i]) != hipSuccess) return MOE_ERR_HIP;
     if (i < cap) {
-      float e = 0.0f;
+      float e = 0.0f, st = 0.0f;
       if (hipEventElapsedTime(&e, t->start[i], t->stop[i]) != hipSuccess) return MOE_ERR_HIP;
+      if (i > 0 && hipEventElapsedTime(&st, t->start[0], t->start[i]) != hipSuccess)
+        return MOE_ERR_HIP;
       kernel_ids[i] = t->ids[i];
+      start_ms[i] = st;
       ms[i] = e;
     }
   }

@@ -328,13 +328,16 @@ const char* moe_kernel_name(int32_t kernel);
 moe_status moe_plan_timing(moe_plan* plan, int32_t capacity);
 
 /* Waits for the timed launches recorded since moe_plan_timing or the last
- * read (each pair's end event), writes the moe_kernel id and the elapsed
- * milliseconds of the first min(*count, cap) of them, in launch order, to the
- * caller's host arrays kernel_ids [cap] and ms [cap], sets *count to the
- * number recorded, and clears the record (the event pairs are reused).
- * Errors: INVALID_ARGUMENT (null arguments, timing not started), HIP. */
-moe_status moe_plan_timing_read(moe_plan* plan, int32_t* kernel_ids, float* ms, int32_t cap,
-                                int32_t* count);
+ * read (each pair's end event) and writes, for the first min(*count, cap) of
+ * them in launch order, to the caller's host arrays of cap entries:
+ * kernel_ids (moe_kernel), start_ms (milliseconds from the first recorded
+ * launch's start to this launch's start; launches on other streams may start
+ * earlier, giving a negative offset) and ms (the launch's own duration).
+ * Sets *count to the number recorded and clears the record (the event pairs
+ * are reused).  Errors: INVALID_ARGUMENT (null arguments, timing not
+ * started), HIP. */
+moe_status moe_plan_timing_read(moe_plan* plan, int32_t* kernel_ids, float* start_ms, float* ms,
+                                int32_t cap, int32_t* count);
 
 /* Copies one plan item to host memory (synchronises the stream).  bytes must
  * be at least the item's size (see moe_item).  The traffic matrices

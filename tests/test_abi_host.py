@@ -188,8 +188,9 @@ def test_timing_host_errors():
     n = ctypes.c_int32()
     ids = (ctypes.c_int32 * 1)()
     ms = (ctypes.c_float * 1)()
+    st = (ctypes.c_float * 1)()
     assert L.moe_plan_timing(None, 4) == _abi.ERR_INVALID_ARGUMENT
     assert L.moe_plan_timing(h, -1) == _abi.ERR_INVALID_ARGUMENT
     assert L.moe_plan_timing(h, 0) == _abi.OK                     # off: no HIP call
-    assert L.moe_plan_timing_read(h, ids, ms, 1, ctypes.byref(n)) == _abi.ERR_INVALID_ARGUMENT
+    assert L.moe_plan_timing_read(h, ids, st, ms, 1, ctypes.byref(n)) == _abi.ERR_INVALID_ARGUMENT
     L.moe_plan_destroy(h)
