@@ -17,19 +17,21 @@ Timing protocol (`value`):
     a 1 GiB scratch buffer is written, then a second 1 GiB buffer is read, so
     the phase finds neither its inputs nor dirty flush lines in the cache.
     The flush is not timed.
-  * HIP events on the step's stream bracket phase 1 (route plan + dispatch)
-    and phase 2 (combine).
+  * Phase 1 is route plan + dispatch, phase 2 the combine, each between two
+    hipEventRecord markers on the step's stream.  A marker interval also
+    holds the launch latency of the phase's first kernel (a few us), which
+    back-to-back kernels hide; it is not subtracted.
   * value = algorithmic bytes per step / (median phase-1 time + median
     phase-2 time); ms_per_step is that sum.  Mean, p10 and p90 are given for
     each phase.
-  * An event interval also holds one kernel-launch latency (a few us) that
-    back-to-back kernels hide; it is not subtracted.
 
 Other figures in the same line:
-  kernels      every kernel's time, from a second pass of K flushed steps in
-               which the library times each launch with HIP events bound to
-               the kernel itself (moe_plan_timing): launches per step, mean
+  kernels      every kernel's launches in K more flushed steps, each launch
+               timed by the library with HIP events bound to the kernel's own
+               start and end (moe_plan_timing): launches per step, mean
                duration, algorithmic bytes, GB/s and fraction of 8 TB/s.
+               (Bound events add a few us of gap after each launch, so that
+               pass gives kernel durations, not phase times.)
   roofline     the kernel with the most time per step (of those that move the
                payload): its algorithmic bytes per launch / its mean launch
                duration.  traffic = its HBM bytes per launch from the
@@ -437,25 +439,42 @@ def run_workload(torch, cs, gen, name, args, dev, flush, primary):
     main = torch.cuda.current_stream(dev)
     s0 = new_set(x0, idx0, w0)
 
-    def protocol_steps(n, flush_mid=True, timing=False):
-        """n flushed steps on stream 0: flush, phase 1, flush, phase 2."""
+    def protocol_steps(n, flush_mid=True, timed=False):
+        """n flushed steps on stream 0: flush, phase 1, flush, phase 2.
+
+        Marker events bracket each phase.  timed: the library also times every
+        launch (events bound to each kernel's own start and end), read back
+        after each phase.  Returns the per-step marker times of both phases,
+        each phase's span from its first kernel's start to its last kernel's
+        end (timed only), and the timed launches."""
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        kern = [[], []]
+        launches = []
+
+        def span(ls):
+            launches.extend(ls)
+            return max(st + ms for _, st, ms in ls) - min(st for _, st, _ in ls)
+
         for i in range(n):
             ev = evs[i]
             flush()
             ev[0].record()
             phase1(s0)
             ev[1].record()
+            if timed:
+                kern[0].append(span(s0["plan"].timing_read()))
             if not pipe:
                 if flush_mid:
                     flush()
                 ev[2].record()
                 do_combine(s0)
                 ev[3].record()
+                if timed:
+                    kern[1].append(span(s0["plan"].timing_read()))
         torch.cuda.synchronize()
         p1 = [e[0].elapsed_time(e[1]) for e in evs]
         p2 = [] if pipe else [e[2].elapsed_time(e[3]) for e in evs]
-        return p1, p2
+        return p1, p2, kern[0], kern[1], launches
 
     # Warmup, in the protocol's own flushed form.
     protocol_steps(max(1, args.warmup))
@@ -469,21 +488,31 @@ def run_workload(torch, cs, gen, name, args, dev, flush, primary):
     disp_b, comb_b = algorithmic_bytes(wl, D, args.payload, hier)
     step_b = disp_b + comb_b
 
-    # The timed region: exactly K flushed steps, bracketed by synchronize.
+    # The timed region: exactly K flushed steps, bracketed by synchronize,
+    # each phase between two hipEventRecord markers on the step's stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    p1, p2 = protocol_steps(args.steps)
+    p1, p2, _, _, _ = protocol_steps(args.steps)
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    s1, s2 = stats(p1), (stats(p2) if p2 else None)
-    ms_step = s1["ms_median"] + (s2["ms_median"] if s2 else 0.0)
-    value = step_b / (ms_step * 1e-3) / 1e9
+
+    # Kernel pass: K more flushed steps with every launch timed by the
+    # library.  Binding events to a launch adds a gap of a few microseconds
+    # after it, so this pass gives kernel durations, not phase times.
+    s0["plan"].timing(256)
+    launches = protocol_steps(args.steps, timed=True)[4]
+    s0["plan"].timing(0)
+
+    def phase_stats(marker, nbytes):
+        st = stats(marker)
+        return {"bytes": nbytes, **st, "GB/s": round(nbytes / (st["ms_median"] * 1e-3) / 1e9, 1)}
+
     if pipe:
-        phases = {"pipeline": {"bytes": step_b, **s1, "GB/s": round(step_b / (s1["ms_median"] * 1e-3) / 1e9, 1)}}
+        phases = {"pipeline": phase_stats(p1, step_b)}
+        ms_step = phases["pipeline"]["ms_median"]
     else:
-        phases = {"route_dispatch": {"bytes": disp_b, **s1,
-                                     "GB/s": round(disp_b / (s1["ms_median"] * 1e-3) / 1e9, 1)},
-                  "combine": {"bytes": comb_b, **s2,
-                              "GB/s": round(comb_b / (s2["ms_median"] * 1e-3) / 1e9, 1)}}
+        phases = {"route_dispatch": phase_stats(p1, disp_b), "combine": phase_stats(p2, comb_b)}
+        ms_step = phases["route_dispatch"]["ms_median"] + phases["combine"]["ms_median"]
+    value = step_b / (ms_step * 1e-3) / 1e9
     res = {"value": round(value, 2), "ms_per_step": round(ms_step, 5),
            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
            "bytes_per_step": step_b,
@@ -495,27 +524,24 @@ def run_workload(torch, cs, gen, name, args, dev, flush, primary):
                       "path": f"pipeline, bands of {band} tokens" if pipe else "separate launches"},
            "protocol": {"flush": "1 GiB written, then another 1 GiB read, before each phase "
                                  "(not timed)",
-                        "phases": phases, "wall_ms_per_step_incl_flush": round(wall_ms, 5)}}
+                        "phase_time": "hipEventRecord markers around each phase on the step's "
+                                      "stream; an interval also holds the launch latency of the "
+                                      "phase's first kernel (not subtracted)",
+                        "phases": phases,
+                        "wall_ms_per_step_incl_flush": round(wall_ms, 5)}}
     if not pipe and wl.name.startswith("olmoe"):
         # The receive rows (128 MiB) fit the MALL: the combine without the
         # flush between the phases, for comparison.
-        _, p2r = protocol_steps(args.steps, flush_mid=False)
+        _, p2r, _, _, _ = protocol_steps(args.steps, flush_mid=False)
         r = stats(p2r)
         res["protocol"]["combine_mall_resident"] = {
             **r, "GB/s": round(comb_b / (r["ms_median"] * 1e-3) / 1e9, 1),
             "note": "no flush between dispatch and combine: the receive rows stay in the MALL"}
 
-    # Kernel pass: K more flushed steps with every launch timed by the library
-    # (the event pairs are read back, and so reused, after each step).
-    s0["plan"].timing(256)
-    launches = []
-    for _ in range(args.steps):
-        protocol_steps(1)
-        launches += s0["plan"].timing_read()
-    s0["plan"].timing(0)
+    # Every kernel's launches in the timed steps.
     kb = kernel_bytes(wl, D, args.payload)
     agg = {}
-    for kname, ms in launches:
+    for kname, _, ms in launches:
         a = agg.setdefault(kname, [0, 0.0])
         a[0] += 1
         a[1] += ms
@@ -529,6 +555,10 @@ def run_workload(torch, cs, gen, name, args, dev, flush, primary):
                       "frac": round(gbs / HBM_PEAK_GBS, 4)})
         kernels[kname] = e
     res["kernels"] = kernels
+    ksum = sum(e["us_per_step"] for e in kernels.values()) * 1e-3
+    res["kernel_time_per_step"] = {
+        "ms": round(ksum, 5), "value": round(step_b / (ksum * 1e-3) / 1e9, 2),
+        "note": "sum of every kernel's mean duration per step (no launch gaps)"}
     moving = [kn for kn in kernels if kn in kb]
     dom = max(moving, key=lambda kn: kernels[kn]["us_per_step"])
     dk = kernels[dom]
@@ -543,7 +573,8 @@ def run_workload(torch, cs, gen, name, args, dev, flush, primary):
                                                     round(traffic / per_launch_b, 4)),
                        "bytes_per_launch": int(round(per_launch_b)), "us_per_launch": dk["avg_us"],
                        "launches_per_step": dk["launches_per_step"],
-                       "timing": "HIP events bound to each launch (moe_plan_timing), flushed steps"}
+                       "timing": "HIP events bound to each launch (moe_plan_timing) in the "
+                                 "timed steps"}
 
     if not args.no_schedules:
         res["schedules"] = schedules(torch, wl, args, dev, x0, idx0, w0, new_set, do_route,
@@ -688,6 +719,7 @@ def main():
         "protocol": head["protocol"],
         "roofline": head["roofline"],
         "kernels": head["kernels"],
+        "kernel_time_per_step": head["kernel_time_per_step"],
         "schedules": head.get("schedules"),
         "copy_ceiling": head.get("copy_ceiling"),
         "per_config": per_config,

@@ -16,16 +16,18 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kPlanBlock = 256;    // threads per route-plan block = tokens per pass
 constexpr int kPlanWaves = kPlanBlock / kWave;
 constexpr int kMaxPlanTiles = 64;  // route-plan tiles (blocks) at most
-// Tile-count matrix the scan holds in LDS (64 KiB of gfx950's 160 KiB per
-// workgroup).  More, smaller tiles shorten the count kernel: on the
-// DeepSeek-V3-like workload the [tiles x (owner, node)] matrix of load-aware
-// forwarders takes 32 two-pass tiles instead of 16 four-pass ones (route 57.6
-// -> 45 us), and the static plan's [tiles x experts] matrix 64 one-pass tiles
-// instead of 32 two-pass ones (route 27.4 -> 23.1 us).
-constexpr int kScanLdsInts = 16384;
+// Tile-count matrix the route-plan scan holds in LDS (128 KiB of gfx950's
+// 160 KiB per workgroup).  More, smaller tiles shorten the count kernel: the
+// [tiles x experts] matrix of the DeepSeek-V3-like workload takes 64
+// one-pass tiles instead of 32 two-pass ones (route 27.4 -> 23.1 us), and
+// its [tiles x (owner, node)] matrix of load-aware forwarders 64 one-pass
+// tiles instead of 32 two-pass ones.
+constexpr int kScanLdsInts = 32768;
+// Threads of the route-plan scan block.
+constexpr int kScanBlock = 1024;
 // A band's matrix in the banded pipeline, whose dynamic LDS stays under the
 // default 64 KiB limit.
-constexpr int kBandScanLdsInts = kScanLdsInts / 2;
+constexpr int kBandScanLdsInts = 8192;
 // Tile-count matrices up to this size are scanned in the gather (measured,
 // one stream: olmoe 16 x 64 gains 2 us per step; qwen3's 32 x 128, with
 // 16-wave gather blocks, 8 us; nondiv's 64 x 100 loses 14 us, as every

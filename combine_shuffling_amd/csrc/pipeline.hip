@@ -131,7 +131,8 @@ __global__ __launch_bounds__(kBlock) void pipeline_kernel(Dims d, const int32_t*
   const CountLds cl{reinterpret_cast<unsigned long long*>(s_dyn),
                     s_ints + lds_count_run - kPlanWaves * d.E, s_ints + lds_count_run, nullptr,
                     nullptr, &s_bad};
-  const ScanLds sl{s_ints, s_ints + d.tpb * d.E, s_ints + d.tpb * d.E + d.E};
+  const ScanLds sl{s_ints, s_ints + d.tpb * d.E, s_ints + d.tpb * d.E + d.E,
+                   s_ints + d.tpb * d.E + d.E + kPlanWaves};
 
   // The next ticket is claimed while the current one runs (thread 0 keeps
   // the claim in a register), which hides the atomic's round trip.  A block
@@ -222,10 +223,10 @@ struct PipelineLaunch {
                         const float* wts, void* out, bool out_f32, const Work& w, hipStream_t s) {
     // Dynamic LDS: count needs kPlanWaves * E ballots (64-bit), a
     // kPlanWaves * E prefix table and E running counts; scan needs the band's
-    // tpb * E count matrix, E totals and kPlanWaves sums.
+    // tpb * E count matrix, E totals, kPlanWaves sums and kPlanBlock column parts.
     const int count_run = kPlanWaves * d.E * 3;  // in ints: ballots, then the prefix table
     const size_t count_bytes = sizeof(int) * ((size_t)count_run + d.E);
-    const size_t scan_bytes = sizeof(int) * ((size_t)d.tpb * d.E + d.E + kPlanWaves);
+    const size_t scan_bytes = sizeof(int) * ((size_t)d.tpb * d.E + d.E + kPlanWaves + kPlanBlock);
     const size_t lds = (std::max(count_bytes, scan_bytes) + 15) / 16 * 16;
     auto kernel = out_f32 ? pipeline_kernel<KMAX, true> : pipeline_kernel<KMAX, false>;
 

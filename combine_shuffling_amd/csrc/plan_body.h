@@ -8,8 +8,9 @@
 namespace moe {
 namespace {
 
-// In-place exclusive scan of a[0..n) (n <= 4 * kPlanBlock) by the whole
-// block; returns the total.  s_wsum: kPlanWaves ints of LDS.
+// In-place exclusive scan of a[0..n) (n <= 4 * NT) by the whole block of NT
+// threads; returns the total.  s_wsum: NT / 64 ints of LDS.
+template <int NT = kPlanBlock>
 __device__ int block_exclusive_scan(int* a, int n, int* s_wsum) {
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   int v[4];
@@ -30,7 +31,7 @@ __device__ int block_exclusive_scan(int* a, int n, int* s_wsum) {
   __syncthreads();
   int run = 0, total = 0;
 #pragma unroll
-  for (int w2 = 0; w2 < kPlanWaves; ++w2) {
+  for (int w2 = 0; w2 < NT / kWave; ++w2) {
     run += (w2 < wv) ? s_wsum[w2] : 0;
     total += s_wsum[w2];
   }
@@ -45,34 +46,89 @@ __device__ int block_exclusive_scan(int* a, int n, int* s_wsum) {
   return total;
 }
 
-// Scan of a [nblk, W] tile-major count matrix: column totals (to `totals` if
-// given), exclusive offsets of the columns (to off[0..W]), and the first row
-// of every (tile, column) (to base), all counted on from row0.  Leaves the
-// offsets from 0 in s_tot; returns the grand total.  Needs W * nblk <=
-// kScanLdsInts.
-template <bool COH = false>
-__device__ int scan_tiles(const int32_t* src, int32_t* base, int32_t* totals, int32_t* off, int W,
-                          int nblk, int row0, int* s_mat, int* s_tot, int* s_wsum) {
-  const int tid = threadIdx.x, n = W * nblk;
-#pragma unroll 8
-  for (int i = tid; i < n; i += kPlanBlock) s_mat[i] = ld_plan<COH>(&src[i]);
-  __syncthreads();
-  for (int c = tid; c < W; c += kPlanBlock) {
-    int s = 0;
-    for (int b = 0; b < nblk; ++b) s += s_mat[b * W + c];
-    s_tot[c] = s;
-    if (totals) totals[c] = s;
+// Column sums of a [nblk, W] tile-major matrix in LDS by a block of NT
+// threads.  With W <= NT each column is cut into P = min(NT / W, nblk) parts
+// of consecutive tiles, one part a thread (thread q * W + c takes part q of
+// column c): the part sums go to s_part, are turned into exclusive prefixes
+// over the column's parts in place, and the column totals go to tot[c].
+// Returns P (0 when W > NT: then each thread sums whole columns and s_part is
+// unused).  Ends with the block synchronised.
+template <int NT>
+__device__ int column_parts(const int* s_mat, int W, int nblk, int* s_part, int* tot) {
+  const int tid = threadIdx.x;
+  if (W > NT) {
+    for (int c = tid; c < W; c += NT) {
+      int sum = 0;
+      for (int b = 0; b < nblk; ++b) sum += s_mat[b * W + c];
+      tot[c] = sum;
+    }
+    __syncthreads();
+    return 0;
+  }
+  const int P = max(1, min(NT / W, nblk));
+  if (tid < P * W) {
+    const int q = tid / W, c = tid - q * W;
+    int sum = 0;
+    for (int b = q * nblk / P; b < (q + 1) * nblk / P; ++b) sum += s_mat[b * W + c];
+    s_part[tid] = sum;
   }
   __syncthreads();
-  const int total = block_exclusive_scan(s_tot, W, s_wsum);
-  for (int c = tid; c < W; c += kPlanBlock) {
-    int run = row0 + s_tot[c];
-    off[c] = run;
-    for (int b = 0; b < nblk; ++b) {
+  if (tid < W) {
+    int run = 0;
+    for (int q = 0; q < P; ++q) {
+      const int v = s_part[q * W + tid];
+      s_part[q * W + tid] = run;
+      run += v;
+    }
+    tot[tid] = run;
+  }
+  __syncthreads();
+  return P;
+}
+
+// First row of every (tile, column) of a [nblk, W] matrix in LDS: column c
+// starts at first(c), and each tile adds its count.  P and s_part as left by
+// column_parts (P = 0: one thread per column).
+template <bool COH, int NT, typename F>
+__device__ void column_bases(const int* s_mat, int W, int nblk, int P, const int* s_part,
+                             int32_t* base, F first) {
+  const int tid = threadIdx.x;
+  if (P == 0) {
+    for (int c = tid; c < W; c += NT) {
+      int run = first(c);
+      for (int b = 0; b < nblk; ++b) {
+        st_plan<COH>(&base[b * W + c], run);
+        run += s_mat[b * W + c];
+      }
+    }
+  } else if (tid < P * W) {
+    const int q = tid / W, c = tid - q * W;
+    int run = first(c) + s_part[tid];
+    for (int b = q * nblk / P; b < (q + 1) * nblk / P; ++b) {
       st_plan<COH>(&base[b * W + c], run);
       run += s_mat[b * W + c];
     }
   }
+}
+
+// Scan of a [nblk, W] tile-major count matrix by a block of NT threads:
+// column totals (to `totals` if given), exclusive offsets of the columns (to
+// off[0..W]), and the first row of every (tile, column) (to base), all
+// counted on from row0.  Leaves the offsets from 0 in s_tot; returns the
+// grand total.  Needs W * nblk <= the LDS matrix; s_part holds NT ints.
+template <bool COH = false, int NT = kPlanBlock>
+__device__ int scan_tiles(const int32_t* src, int32_t* base, int32_t* totals, int32_t* off, int W,
+                          int nblk, int row0, int* s_mat, int* s_tot, int* s_wsum, int* s_part) {
+  const int tid = threadIdx.x, n = W * nblk;
+#pragma unroll 16
+  for (int i = tid; i < n; i += NT) s_mat[i] = ld_plan<COH>(&src[i]);
+  __syncthreads();
+  const int P = column_parts<NT>(s_mat, W, nblk, s_part, s_tot);
+  if (totals)
+    for (int c = tid; c < W; c += NT) totals[c] = s_tot[c];
+  const int total = block_exclusive_scan<NT>(s_tot, W, s_wsum);
+  column_bases<COH, NT>(s_mat, W, nblk, P, s_part, base, [&](int c) { return row0 + s_tot[c]; });
+  for (int c = tid; c < W; c += NT) off[c] = row0 + s_tot[c];
   if (tid == 0) off[W] = row0 + total;
   __syncthreads();
   return total;
@@ -223,74 +279,83 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
 
 // Load-aware forwarders (FUSCO article, "load balancing and cross-node
 // deduplication": forwarding follows the load and is spread evenly over a
-// node's GPUs).  Keys are (owner s, node n) pairs; the load of a pair is its
-// staging rows.  In each node the owners are ranked by load (more first, ties
-// to the lower owner) and dealt to the node's G ranks in snake order.  Staging
-// rows stay ordered by (forwarder, token); owners hold ascending token ranges,
-// so inside a forwarder that is (owner, token).  Writes the forwarder table,
-// stage_off and the (tile, pair) bases; returns D.  Needs R*N <= 1024 and
-// nblk * R * N <= kScanLdsInts.
-template <bool COH = false>
-__device__ int scan_load_aware(const Dims& d, const Work& w, int* s_mat, int* s_tot, int* s_wsum) {
-  __shared__ int s_load[MOE_MAX_EXPERTS];  // per pair
-  __shared__ int s_fwd[MOE_MAX_EXPERTS];   // per pair
+// node's GPUs).  Keys are (owner s, node n) pairs, c = s * N + n; the load of
+// a pair is its staging rows.  In each node the owners are ranked by load
+// (more first, ties to the lower owner) and dealt to the node's G ranks in
+// snake order, so the forwarder with local index g gets the R / G owners of
+// ranks lap * G + g (even laps) and lap * G + G - 1 - g (odd laps).  Staging
+// rows stay ordered by (forwarder, token); owners hold ascending token
+// ranges, so inside a forwarder that is (owner, token).  Each pair's first
+// row is its forwarder's first row plus the loads of the forwarder's owners
+// with a lower id: R / G terms, read through a per-node owner-by-rank table.
+// Writes the forwarder table, stage_off and the (tile, pair) bases; returns
+// D.  Needs R * N <= 1024.
+template <bool COH = false, int NT = kPlanBlock>
+__device__ int scan_load_aware(const Dims& d, const Work& w, int* s_mat, int* s_tot, int* s_wsum,
+                               int* s_part) {
+  __shared__ int s_load[MOE_MAX_EXPERTS];   // per pair
+  __shared__ int s_rank[MOE_MAX_EXPERTS];   // per pair: its owner's rank in the node
+  __shared__ int s_order[MOE_MAX_EXPERTS];  // per node n: owner of rank r at n * R + r
+  __shared__ int s_first[MOE_MAX_EXPERTS];  // per pair: first staging row
   const int tid = threadIdx.x, R = d.R, N = d.N, G = d.G, K = d.fkeys, nblk = d.nblk;
-#pragma unroll 8
-  for (int i = tid; i < K * nblk; i += kPlanBlock) s_mat[i] = ld_plan<COH>(&w.tile_fcounts[i]);
+  const int laps = R / G;
+#pragma unroll 16
+  for (int i = tid; i < K * nblk; i += NT) s_mat[i] = ld_plan<COH>(&w.tile_fcounts[i]);
   __syncthreads();
-  for (int c = tid; c < K; c += kPlanBlock) {
-    int l = 0;
-    for (int b = 0; b < nblk; ++b) l += s_mat[b * K + c];
-    s_load[c] = l;
-  }
-  __syncthreads();
-  for (int c = tid; c < K; c += kPlanBlock) {
-    const int s = c / N, n = c % N, l = s_load[c];
+  const int P = column_parts<NT>(s_mat, K, nblk, s_part, s_load);
+  for (int c = tid; c < K; c += NT) {
+    const int s = c / N, n = c - (c / N) * N, l = s_load[c];
     int rank = 0;
     for (int s2 = 0; s2 < R; ++s2) {
       const int l2 = s_load[s2 * N + n];
       rank += (l2 > l || (l2 == l && s2 < s)) ? 1 : 0;
     }
-    const int lap = rank / G, pos = rank % G;
-    const int f = n * G + ((lap & 1) ? G - 1 - pos : pos);
-    s_fwd[c] = f;
-    w.fwd[c] = f;
+    s_rank[c] = rank;
+    s_order[n * R + rank] = s;
   }
   __syncthreads();
-  for (int f = tid; f < R; f += kPlanBlock) {  // rows each forwarder stages
-    const int n = f / G;
+  // owner of the forwarder with local index g in node n, lap `lap`
+  auto owner = [&](int n, int g, int lap) { return s_order[n * R + lap * G + ((lap & 1) ? G - 1 - g : g)]; };
+  for (int f = tid; f < R; f += NT) {
+    const int n = f / G, g = f - n * G;
     int tot = 0;
-    for (int s = 0; s < R; ++s) tot += s_fwd[s * N + n] == f ? s_load[s * N + n] : 0;
+    for (int lap = 0; lap < laps; ++lap) tot += s_load[owner(n, g, lap) * N + n];
     s_tot[f] = tot;
   }
   __syncthreads();
-  const int staged = block_exclusive_scan(s_tot, R, s_wsum);
-  for (int f = tid; f <= R; f += kPlanBlock) w.stage_off[f] = f < R ? s_tot[f] : staged;
-  for (int c = tid; c < K; c += kPlanBlock) {
-    const int s = c / N, n = c % N, f = s_fwd[c];
-    int run = s_tot[f];
-    for (int s2 = 0; s2 < s; ++s2) run += s_fwd[s2 * N + n] == f ? s_load[s2 * N + n] : 0;
-    for (int b = 0; b < nblk; ++b) {
-      w.tile_fbase[b * K + c] = run;
-      run += s_mat[b * K + c];
+  const int staged = block_exclusive_scan<NT>(s_tot, R, s_wsum);
+  for (int f = tid; f <= R; f += NT) w.stage_off[f] = f < R ? s_tot[f] : staged;
+  for (int c = tid; c < K; c += NT) {
+    const int s = c / N, n = c - (c / N) * N, rank = s_rank[c];
+    const int lap = rank / G, pos = rank - lap * G;
+    const int g = (lap & 1) ? G - 1 - pos : pos;
+    int first = s_tot[n * G + g];
+    for (int l2 = 0; l2 < laps; ++l2) {
+      const int o = owner(n, g, l2);
+      first += o < s ? s_load[o * N + n] : 0;
     }
+    s_first[c] = first;
+    w.fwd[c] = n * G + g;
   }
+  __syncthreads();
+  column_bases<COH, NT>(s_mat, K, nblk, P, s_part, w.tile_fbase, [&](int c) { return s_first[c]; });
   __syncthreads();
   return staged;
 }
 
 // LDS of one band scan.
 struct ScanLds {
-  int* mat;   // [kScanLdsInts] count matrix of the band's tiles
+  int* mat;   // count matrix of the band's tiles
   int* tot;   // [MOE_MAX_EXPERTS]
-  int* wsum;  // [kPlanWaves]
+  int* wsum;  // [NT / 64]
+  int* part;  // [NT] column parts
 };
 
 // One band by the whole block: scans its [tiles x experts] count matrix (and,
 // with dedup, which runs with one band only, the [tiles x staging keys] one)
 // into base rows, the band's expert and rank offsets and its status.  The
 // band's receive rows start at band * d.band * k.
-template <bool DEDUP = true, bool COH = false>
+template <bool DEDUP = true, bool COH = false, int NT = kPlanBlock>
 __device__ __forceinline__ void scan_band(const Dims& d, const Work& w, int band,
                                           const ScanLds& L) {
   int* s_mat = L.mat;
@@ -299,28 +364,30 @@ __device__ __forceinline__ void scan_band(const Dims& d, const Work& w, int band
   const int tid = threadIdx.x, E = d.E, R = d.R;
   const int t0 = band * d.tpb, nt = min(d.tpb, d.nblk - t0);
   const int row0 = band * d.band * d.k;
-  const int rows = scan_tiles<COH>(w.tile_counts + (int64_t)t0 * E, w.tile_base + (int64_t)t0 * E,
+  const int rows = scan_tiles<COH, NT>(w.tile_counts + (int64_t)t0 * E, w.tile_base + (int64_t)t0 * E,
                               w.counts + (int64_t)band * E, w.expert_off + (int64_t)band * (E + 1),
-                              E, nt, row0, s_mat, s_tot, s_wsum);
+                              E, nt, row0, s_mat, s_tot, s_wsum, L.part);
   int32_t* roff = w.rank_off + (int64_t)band * (R + 1);
-  for (int r = tid; r <= R; r += kPlanBlock) {
+  for (int r = tid; r <= R; r += NT) {
     const int first = r * d.ebase + min(r, d.erem);  // first expert of rank r
     roff[r] = row0 + (first < E ? s_tot[first] : rows);
   }
   int staged = 0;
-  if (DEDUP && d.dedup) {
-    __syncthreads();
-    if (d.load_aware) {
-      staged = scan_load_aware<COH>(d, w, s_mat, s_tot, s_wsum);
-    } else {
-      staged = scan_tiles<COH>(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, R, d.nblk, 0,
-                               s_mat, s_tot, s_wsum);
-      for (int c = tid; c < R * d.N; c += kPlanBlock)
-        w.fwd[c] = (c % d.N) * d.G + (c / d.N) % d.G;
+  if constexpr (DEDUP) {
+    if (d.dedup) {
+      __syncthreads();
+      if (d.load_aware) {
+        staged = scan_load_aware<COH, NT>(d, w, s_mat, s_tot, s_wsum, L.part);
+      } else {
+        staged = scan_tiles<COH, NT>(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, R, d.nblk,
+                                     0, s_mat, s_tot, s_wsum, L.part);
+        for (int c = tid; c < R * d.N; c += NT)
+          w.fwd[c] = (c % d.N) * d.G + (c / d.N) % d.G;
+      }
     }
   }
   int bad = 0;
-  for (int b = tid; b < nt; b += kPlanBlock) bad |= ld_plan<COH>(&w.tile_flags[t0 + b]);
+  for (int b = tid; b < nt; b += NT) bad |= ld_plan<COH>(&w.tile_flags[t0 + b]);
   bad = __syncthreads_or(bad);
   if (tid == 0) {
     w.band_status[band] = bad ? MOE_ERR_BAD_ROUTING : MOE_OK;
