@@ -281,13 +281,19 @@ def algorithmic_bytes(wl, D, payload="bf16", hier=False):
     return disp, comb
 
 
-def kernel_bytes(wl, D, payload="bf16"):
-    """Algorithmic payload bytes per step moved by each kernel (by symbol)."""
+def kernel_bytes(wl, D, payload="bf16", chunks=None, hier_chunks=None):
+    """Algorithmic payload bytes per step moved by each kernel (by symbol).
+
+    chunks: (tokens, staging rows) of each chunk of the deduplicated dispatch,
+    which launches hop 1 of chunk 0, then hop 2 of chunk c with hop 1 of
+    chunk c + 1 (stage_ab), then hop 2 of the last chunk; hier_chunks: the
+    same for the hierarchical combine (combine_part, combine_pn,
+    combine_nodes)."""
     row = 2 * wl.hidden
     row8 = wl.hidden + 4 * ((wl.hidden + 127) // 128)
     T, k = wl.num_tokens, wl.top_k
     single = (T + T * k) * row
-    return {
+    out = {
         "gather_kernel": single, "gather_scan_kernel": single,
         "stage_a_kernel": (T + D) * row, "stage_b_kernel": (D + T * k) * row,
         "combine_kernel": (T * k + T) * row,
@@ -298,6 +304,27 @@ def kernel_bytes(wl, D, payload="bf16"):
         "combine_fp8_kernel": T * k * row8 + T * row,
         "pipeline_kernel": 2 * (T + T * k) * row,
     }
+
+    def split(first_b, last_b, fused, hop1, hop2):
+        out[first_b] = hop1[0]
+        out[last_b] = hop2[-1]
+        out[fused] = sum(hop2[:-1]) + sum(hop1[1:])
+
+    if chunks is not None:
+        tc, dc = chunks
+        if payload == "fp8":
+            split("stage_a_fp8_kernel", "stage_b_fp8_kernel", "stage_ab_fp8_kernel",
+                  [t * row + d * row8 for t, d in zip(tc, dc)],
+                  [d * row8 + t * k * row8 for t, d in zip(tc, dc)])
+        else:
+            split("stage_a_kernel", "stage_b_kernel", "stage_ab_kernel",
+                  [(t + d) * row for t, d in zip(tc, dc)], [(d + t * k) * row for t, d in zip(tc, dc)])
+    if hier_chunks is not None:
+        tc, dc = hier_chunks
+        split("combine_part_kernel", "combine_nodes_kernel", "combine_pn_kernel",
+              [t * k * row + d * 2 * row for t, d in zip(tc, dc)],
+              [d * 2 * row + t * row for t, d in zip(tc, dc)])
+    return out
 
 
 def cpu_baseline(batch, seconds, payload="bf16", band=0, hier=False):
@@ -539,7 +566,20 @@ def run_workload(torch, cs, gen, name, args, dev, flush, primary):
             "note": "no flush between dispatch and combine: the receive rows stay in the MALL"}
 
     # Every kernel's launches in the timed steps.
-    kb = kernel_bytes(wl, D, args.payload)
+    chunks = hier_chunks = None
+    if wl.node_dedup:
+        src = s0["plan"].read("stage_src")[:D]
+
+        def per_chunk(n):
+            """(tokens, staging rows) of each chunk of n tokens."""
+            nch = -(-T // n)
+            return ([min(T, (c + 1) * n) - c * n for c in range(nch)],
+                    np.bincount(src // n, minlength=nch).tolist())
+
+        chunks = per_chunk(s0["plan"].chunk_tokens["dispatch_fp8" if fp8 else "dispatch"])
+        if hier:
+            hier_chunks = per_chunk(s0["plan"].chunk_tokens["combine_hier"])
+    kb = kernel_bytes(wl, D, args.payload, chunks, hier_chunks)
     agg = {}
     for kname, _, ms in launches:
         a = agg.setdefault(kname, [0, 0.0])

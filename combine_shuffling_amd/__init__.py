@@ -85,6 +85,9 @@ class Plan:
         self.staging_rows_max = int(self._lib.moe_plan_staging_rows_max(h))
         self.scale_blocks = int(self._lib.moe_plan_scale_blocks(h))
         self.bands = int(self._lib.moe_plan_bands(h))
+        # tokens per chunk of the chunked calls of a node-deduplicated plan
+        self.chunk_tokens = {call: int(self._lib.moe_plan_chunk_tokens(h, i))
+                             for i, call in enumerate(("dispatch", "dispatch_fp8", "combine_hier"))}
         self.workspace = None
         self.topk_idx = None
         self.device = None

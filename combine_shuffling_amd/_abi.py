@@ -56,9 +56,10 @@ EXPORTS = (
     "moe_combine", "moe_plan_read", "moe_status_str", "moe_plan_scale_blocks",
     "moe_dispatch_fp8", "moe_combine_fp8", "moe_combine_hier", "moe_plan_bands", "moe_pipeline",
     "moe_kernel_name", "moe_plan_timing", "moe_plan_timing_read", "moe_route_plan_static",
+    "moe_plan_chunk_tokens",
 )
 
-KERNEL_COUNT = 19
+KERNEL_COUNT = 22
 
 
 class MoeError(RuntimeError):
@@ -108,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.moe_combine_fp8.restype = i32
     L.moe_combine_hier.argtypes = [vp, vp, vp, vp, vp, i32, vp]
     L.moe_combine_hier.restype = i32
+    L.moe_plan_chunk_tokens.argtypes = [vp, i32]
+    L.moe_plan_chunk_tokens.restype = i64
     L.moe_plan_bands.argtypes = [vp]
     L.moe_plan_bands.restype = i64
     L.moe_pipeline.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]

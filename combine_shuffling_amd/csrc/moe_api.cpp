@@ -296,7 +296,8 @@ const char* moe_kernel_name(int32_t kernel) {
       "combine_kernel",       "combine_part_kernel",    "combine_nodes_kernel",
       "gather_fp8_kernel",    "gather_fp8_scan_kernel", "stage_a_fp8_kernel",
       "stage_b_fp8_kernel",   "combine_fp8_kernel",     "pipeline_kernel",
-      "counters_clear_kernel"};
+      "counters_clear_kernel", "stage_ab_kernel",       "stage_ab_fp8_kernel",
+      "combine_pn_kernel"};
   return kernel >= 0 && kernel < MOE_KERNEL_COUNT ? names[kernel] : "?";
 }
 
@@ -365,6 +366,12 @@ int64_t moe_plan_staging_rows_max(const moe_plan* plan) {
 }
 
 int64_t moe_plan_bands(const moe_plan* plan) { return plan ? plan->d.nbands : 0; }
+
+int64_t moe_plan_chunk_tokens(const moe_plan* plan, int32_t call) {
+  if (!plan) return 0;
+  if (!plan->d.dedup || call < 0 || call > 2) return plan->d.T;
+  return moe::chunk_tokens(plan->d, call);
+}
 
 moe_status moe_route_plan(moe_plan* plan, const int32_t* topk_idx, void* workspace, void* stream) {
   if (!plan || !workspace || !moe::aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;

@@ -150,6 +150,9 @@ hipError_t launch_gather(const Dims& d, const int32_t* idx, const uint16_t* x, u
                          const Work& w, hipStream_t s);
 hipError_t launch_dedup_dispatch(const Dims& d, const int32_t* idx, const uint16_t* x,
                                  uint16_t* staging, uint16_t* recv, const Work& w, hipStream_t s);
+// Tokens per chunk of a chunked call with node deduplication: 0 the dispatch,
+// 1 the fp8 dispatch, 2 the hierarchical combine.
+int64_t chunk_tokens(const Dims& d, int call);
 hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* wts, void* out,
                           bool out_f32, const Work& w, hipStream_t s);
 // Two-hop combine of a node-deduplicated plan: fp32 partial per staging row,

@@ -212,13 +212,13 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
   }
 }
 
-// Hop 1 over wave-items [item0, item_end) (one chunk of tokens); keep: plain
-// stores for the staging rows.
+// Hop 1 over wave-items [item0, item_end) (one chunk of tokens), block-chunk
+// blk of them; keep: plain stores for the staging rows.
 template <int KMAX, int U>
-__global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* __restrict__ idx,
-                                                         const u32x4* __restrict__ x,
-                                                         u32x4* __restrict__ staging, Work w,
-                                                         int item0, int item_end, int keep) {
+__device__ __forceinline__ void stage_a_body(const Dims& d, const int32_t* __restrict__ idx,
+                                             const u32x4* __restrict__ x,
+                                             u32x4* __restrict__ staging, const Work& w, int blk,
+                                             int item0, int item_end, int keep) {
   const int lane = threadIdx.x % kWave;
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   Item it[U];
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* 
   u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, blockIdx.x, item0, item_end, u);
+    it[u] = wave_item<U>(d, blk, item0, item_end, u);
     lead[u] = 0;
     // x first, so its latency overlaps the plan lookups (DeepSeek-V3-like
     // dispatch 715 -> 695 us); non-temporal here (826 -> 794 us with x read
@@ -268,13 +268,14 @@ __global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* 
   }
 }
 
-// Hop 2, one token per wave-item, over wave-items [item0, item_end): each of
-// the token's staging rows (one per destination node) is read once and
-// written to the token's slots on that node.
+// Hop 2, one token per wave-item, over wave-items [item0, item_end),
+// block-chunk blk of them: each of the token's staging rows (one per
+// destination node) is read once and written to the token's slots on that
+// node.
 template <int KMAX, int U>
-__global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __restrict__ staging,
-                                                         u32x4* __restrict__ recv, Work w,
-                                                         int item0, int item_end) {
+__device__ __forceinline__ void stage_b_body(const Dims& d, const u32x4* __restrict__ staging,
+                                             u32x4* __restrict__ recv, const Work& w, int blk,
+                                             int item0, int item_end) {
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   const bool keep = keep_rows(rows, 2 * d.H);
   Item it[U];
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
   u32x4 v[U][KMAX];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, blockIdx.x, item0, item_end, u);
+    it[u] = wave_item<U>(d, blk, item0, item_end, u);
     const int64_t at = (int64_t)it[u].t * d.k;
     int sj[KMAX], pj[KMAX];
 #pragma unroll
@@ -322,6 +323,41 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
   }
 }
 
+template <int KMAX, int U>
+__global__ __launch_bounds__(kBlock) void stage_a_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                         const u32x4* __restrict__ x,
+                                                         u32x4* __restrict__ staging, Work w,
+                                                         int item0, int item_end, int keep) {
+  stage_a_body<KMAX, U>(d, idx, x, staging, w, blockIdx.x, item0, item_end, keep);
+}
+
+template <int KMAX, int U>
+__global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __restrict__ staging,
+                                                         u32x4* __restrict__ recv, Work w,
+                                                         int item0, int item_end) {
+  stage_b_body<KMAX, U>(d, staging, recv, w, blockIdx.x, item0, item_end);
+}
+
+// Hop 2 of chunk c in the first b_blocks blocks, hop 1 of chunk c + 1 in the
+// others.  The GPU dispatches a grid's blocks in order, so hop 1's blocks
+// start as hop 2's drain and fill its tail, and a chunk boundary costs one
+// launch instead of two (DeepSeek-V3-like dispatch 712 -> 665 us a step,
+// with the route plan).  The two hops touch disjoint rows and plan entries.
+// Hop 2 takes one wave-item a wave here, so the kernel fits 8 waves per SIMD.
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void stage_ab_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                          const u32x4* __restrict__ x,
+                                                          u32x4* __restrict__ staging,
+                                                          u32x4* __restrict__ recv, Work w,
+                                                          int b_blocks, int b_item0, int b_item_end,
+                                                          int a_item0, int a_item_end, int keep) {
+  if ((int)blockIdx.x < b_blocks)
+    stage_b_body<KMAX, 1>(d, staging, recv, w, blockIdx.x, b_item0, b_item_end);
+  else
+    stage_a_body<KMAX, kStageAU>(d, idx, x, staging, w, blockIdx.x - b_blocks, a_item0, a_item_end,
+                                 keep);
+}
+
 // ---- hierarchical combine over the deduplication's staging rows ------------
 // Hop 1 (at the forwarder): one fp32 partial per staging row p = (token t,
 // node n), the fused multiply-add chain over t's slots on n in ascending j.
@@ -329,12 +365,12 @@ __global__ __launch_bounds__(kBlock) void stage_b_kernel(Dims d, const u32x4* __
 // once; each of t's staging rows gets its partial (a row all of whose slots
 // were dropped gets zeros).
 template <int KMAX>
-__global__ __launch_bounds__(kBlock) void combine_part_kernel(Dims d, const u32x4* __restrict__ y,
-                                                              const float* __restrict__ wts,
-                                                              f32x4* __restrict__ part, Work w,
-                                                              int item0, int item_end, int keep) {
+__device__ __forceinline__ void combine_part_body(const Dims& d, const u32x4* __restrict__ y,
+                                                  const float* __restrict__ wts,
+                                                  f32x4* __restrict__ part, const Work& w, int blk,
+                                                  int item0, int item_end, int keep) {
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
-  const Item it = wave_item<1>(d, blockIdx.x, item0, item_end, 0);
+  const Item it = wave_item<1>(d, blk, item0, item_end, 0);
   const int64_t at = (int64_t)it.t * d.k;
   int slot[KMAX], p[KMAX];
   float wj[KMAX];
@@ -387,11 +423,11 @@ __global__ __launch_bounds__(kBlock) void combine_part_kernel(Dims d, const u32x
 // Hop 2 (at the owner): out[t] = sum of t's partials in ascending node order
 // (one partial per node the token reached), then bf16 (nearest even) or fp32.
 template <int KMAX, bool F32OUT>
-__global__ __launch_bounds__(kBlock) void combine_nodes_kernel(Dims d, const f32x4* __restrict__ part,
-                                                               Work w, void* __restrict__ out,
-                                                               int item0, int item_end) {
+__device__ __forceinline__ void combine_nodes_body(const Dims& d, const f32x4* __restrict__ part,
+                                                   const Work& w, void* __restrict__ out, int blk,
+                                                   int item0, int item_end) {
   const uint32_t srows = (uint32_t)d.smax;
-  const Item it = wave_item<1>(d, blockIdx.x, item0, item_end, 0);
+  const Item it = wave_item<1>(d, blk, item0, item_end, 0);
   const int64_t at = (int64_t)it.t * d.k;
   int p[KMAX];
 #pragma unroll
@@ -448,6 +484,36 @@ __global__ __launch_bounds__(kBlock) void combine_nodes_kernel(Dims d, const f32
     for (int q = 0; q < 4; ++q) r[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
     store_chunk(reinterpret_cast<u32x4*>(out) + i, r);
   }
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void combine_part_kernel(Dims d, const u32x4* __restrict__ y,
+                                                              const float* __restrict__ wts,
+                                                              f32x4* __restrict__ part, Work w,
+                                                              int item0, int item_end, int keep) {
+  combine_part_body<KMAX>(d, y, wts, part, w, blockIdx.x, item0, item_end, keep);
+}
+
+template <int KMAX, bool F32OUT>
+__global__ __launch_bounds__(kBlock) void combine_nodes_kernel(Dims d, const f32x4* __restrict__ part,
+                                                               Work w, void* __restrict__ out,
+                                                               int item0, int item_end) {
+  combine_nodes_body<KMAX, F32OUT>(d, part, w, out, blockIdx.x, item0, item_end);
+}
+
+// Hop 2 of chunk c in the first b_blocks blocks and hop 1 of chunk c + 1 in
+// the others, as stage_ab_kernel: one launch per chunk boundary.
+template <int KMAX, bool F32OUT>
+__global__ __launch_bounds__(kBlock) void combine_pn_kernel(Dims d, const u32x4* __restrict__ y,
+                                                            const float* __restrict__ wts,
+                                                            f32x4* __restrict__ part, Work w,
+                                                            void* __restrict__ out, int b_blocks,
+                                                            int n_item0, int n_item_end, int p_item0,
+                                                            int p_item_end, int keep) {
+  if ((int)blockIdx.x < b_blocks)
+    combine_nodes_body<KMAX, F32OUT>(d, part, w, out, blockIdx.x, n_item0, n_item_end);
+  else
+    combine_part_body<KMAX>(d, y, wts, part, w, blockIdx.x - b_blocks, p_item0, p_item_end, keep);
 }
 
 // ---- fp8 payload -----------------------------------------------------------
@@ -507,9 +573,10 @@ struct Item8 {
 };
 
 template <int U>
-__device__ __forceinline__ Item8 wave_item8(const Dims& d, int segs8, int base, int limit, int u) {
+__device__ __forceinline__ Item8 wave_item8(const Dims& d, int segs8, int blk, int base, int limit,
+                                        int u) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int g = __builtin_amdgcn_readfirstlane(base + (blockIdx.x * U + u) * kWaves + wave);
+  const int g = __builtin_amdgcn_readfirstlane(base + (blk * U + u) * kWaves + wave);
   Item8 it;
   it.live = g < limit;
   it.t = it.live ? g / segs8 : 0;
@@ -605,7 +672,7 @@ __global__ __launch_bounds__(kBlock) void gather_fp8_kernel(Dims d, const int32_
   const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  const Item8 it = wave_item8<1>(d, segs8, base, limit, 0);
+  const Item8 it = wave_item8<1>(d, segs8, blockIdx.x, base, limit, 0);
   u32x4 v0, v1;  // x first, so its latency overlaps the slot lookups
   load_piece(d, it, x, v0, v1);
   int slot[KMAX];
@@ -701,16 +768,16 @@ __global__ __launch_bounds__(GW * kWave) void gather_fp8_scan_kernel(Dims d,
 // row per destination node.  Also finishes slot_of / row_src / stage_of /
 // stage_src.
 template <int KMAX>
-__global__ __launch_bounds__(kBlock) void stage_a_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
-                                                             const u32x4* __restrict__ x,
-                                                             uint8_t* __restrict__ stage8,
-                                                             float* __restrict__ sscale, Work w,
-                                                             int item0, int item_end, int keep) {
+__device__ __forceinline__ void stage_a_fp8_body(const Dims& d, const int32_t* __restrict__ idx,
+                                                 const u32x4* __restrict__ x,
+                                                 uint8_t* __restrict__ stage8,
+                                                 float* __restrict__ sscale, const Work& w, int bx,
+                                                 int item0, int item_end, int keep) {
   const int lane = threadIdx.x % kWave;
   const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  const Item8 it = wave_item8<1>(d, segs8, item0, item_end, 0);
+  const Item8 it = wave_item8<1>(d, segs8, bx, item0, item_end, 0);
   u32x4 v0, v1;  // x first, so its latency overlaps the plan lookups
   load_piece(d, it, x, v0, v1);
   int slot[KMAX], p[KMAX];
@@ -754,16 +821,16 @@ __global__ __launch_bounds__(kBlock) void stage_a_fp8_kernel(Dims d, const int32
 // Hop 2, one token per wave-item: each of the token's staging rows (codes and
 // scales) is read once and written to the token's slots on that node.
 template <int KMAX>
-__global__ __launch_bounds__(kBlock) void stage_b_fp8_kernel(Dims d, const uint8_t* __restrict__ stage8,
-                                                             const float* __restrict__ sscale,
-                                                             uint8_t* __restrict__ recv8,
-                                                             float* __restrict__ rscale, Work w,
-                                                             int item0, int item_end) {
+__device__ __forceinline__ void stage_b_fp8_body(const Dims& d, const uint8_t* __restrict__ stage8,
+                                                 const float* __restrict__ sscale,
+                                                 uint8_t* __restrict__ recv8,
+                                                 float* __restrict__ rscale, const Work& w, int bx,
+                                                 int item0, int item_end) {
   const int lane = threadIdx.x % kWave;
   const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
   const uint32_t rows = (uint32_t)(d.T * d.k), srows = (uint32_t)d.smax;
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
-  const Item8 it = wave_item8<1>(d, segs8, item0, item_end, 0);
+  const Item8 it = wave_item8<1>(d, segs8, bx, item0, item_end, 0);
   const bool scale_lane = it.ok0 && (lane % kFp8BlockLanes) == 0;
   const int blk = it.c0 / kFp8BlockChunks;
   const int64_t at = (int64_t)it.t * d.k;
@@ -807,6 +874,42 @@ __global__ __launch_bounds__(kBlock) void stage_b_fp8_kernel(Dims d, const uint8
       }
     }
   }
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void stage_a_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                             const u32x4* __restrict__ x,
+                                                             uint8_t* __restrict__ stage8,
+                                                             float* __restrict__ sscale, Work w,
+                                                             int item0, int item_end, int keep) {
+  stage_a_fp8_body<KMAX>(d, idx, x, stage8, sscale, w, blockIdx.x, item0, item_end, keep);
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void stage_b_fp8_kernel(Dims d, const uint8_t* __restrict__ stage8,
+                                                             const float* __restrict__ sscale,
+                                                             uint8_t* __restrict__ recv8,
+                                                             float* __restrict__ rscale, Work w,
+                                                             int item0, int item_end) {
+  stage_b_fp8_body<KMAX>(d, stage8, sscale, recv8, rscale, w, blockIdx.x, item0, item_end);
+}
+
+// Hop 2 of chunk c and hop 1 of chunk c + 1 in one launch, as stage_ab_kernel.
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void stage_ab_fp8_kernel(Dims d, const int32_t* __restrict__ idx,
+                                                              const u32x4* __restrict__ x,
+                                                              uint8_t* __restrict__ stage8,
+                                                              float* __restrict__ sscale,
+                                                              uint8_t* __restrict__ recv8,
+                                                              float* __restrict__ rscale, Work w,
+                                                              int b_blocks, int b_item0,
+                                                              int b_item_end, int a_item0,
+                                                              int a_item_end, int keep) {
+  if ((int)blockIdx.x < b_blocks)
+    stage_b_fp8_body<KMAX>(d, stage8, sscale, recv8, rscale, w, blockIdx.x, b_item0, b_item_end);
+  else
+    stage_a_fp8_body<KMAX>(d, idx, x, stage8, sscale, w, blockIdx.x - b_blocks, a_item0,
+                           a_item_end, keep);
 }
 
 // Combine of an fp8 payload: codes decoded and scaled (exact), then the same
@@ -937,34 +1040,45 @@ inline int stage_chunk_tokens(const Dims& d, int64_t row_bound) {
 }
 
 // Deduplicated dispatch over chunks of consecutive tokens: hop 1, then hop
-// 2, of each chunk before the next chunk.  A chunk's staging rows (at most
-// tokens * min(k, N) rows) fit in the 256 MB MALL, so hop 2 reads rows
+// 2, of each chunk after the previous chunk's.  A chunk's staging rows (at
+// most tokens * min(k, N) rows) fit in the 256 MB MALL, so hop 2 reads rows
 // hop 1 has just written (DeepSeek-V3-like, 8 chunks: dispatch 799 -> 756
-// us on one stream; one launch holding both hops cost occupancy and was
-// slower).  The rows, and the plan arrays hop 1 finishes, of one chunk are
-// disjoint from every other chunk's.
+// us on one stream).  Launches: hop 1 of chunk 0, then one stage_ab launch
+// per chunk boundary (hop 2 of chunk c with hop 1 of chunk c + 1), then hop
+// 2 of the last chunk.  The rows, and the plan arrays hop 1 finishes, of one
+// chunk are disjoint from every other chunk's.  (Running hop 1 of chunk c +
+// 1 on a second stream beside hop 2 of chunk c instead made both hops far
+// slower, 0.30 and 0.49 of the HBM peak: two write-heavy grids at full width
+// contend.)
 template <int KMAX>
 struct DedupLaunch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint16_t* staging,
                         uint16_t* recv, const Work& w, hipStream_t s) {
     const int64_t row_bound = (int64_t)min(d.k, d.N) * 2 * d.H;  // staging bytes per token, at most
     const int chunk = stage_chunk_tokens(d, row_bound);
-    const int per_block_a = kWaves * kStageAU, per_block_b = kWaves * kStageU;
+    const int nch = (d.T + chunk - 1) / chunk;
     const int keep = (int64_t)chunk * row_bound <= kKeepBytes;
-    for (int t0 = 0; t0 < d.T; t0 += chunk) {
-      const int item0 = t0 * d.segs, item_end = min(d.T, t0 + chunk) * d.segs;
-      const int blocks_a = (item_end - item0 + per_block_a - 1) / per_block_a;
-      const int blocks_b = (item_end - item0 + per_block_b - 1) / per_block_b;
-      hipError_t e = launch(MOE_KERNEL_STAGE_A, stage_a_kernel<KMAX, kStageAU>, dim3(blocks_a),
-                            dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x),
-                            reinterpret_cast<u32x4*>(staging), w, item0, item_end, keep);
-      if (e != hipSuccess) return e;
-      e = launch(MOE_KERNEL_STAGE_B, stage_b_kernel<KMAX, kStageU>, dim3(blocks_b), dim3(kBlock), 0,
-                 s, d, reinterpret_cast<const u32x4*>(staging), reinterpret_cast<u32x4*>(recv), w,
-                 item0, item_end);
-      if (e != hipSuccess) return e;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    u32x4* sv = reinterpret_cast<u32x4*>(staging);
+    u32x4* rv = reinterpret_cast<u32x4*>(recv);
+    auto first = [&](int c) { return c * chunk * d.segs; };
+    auto last = [&](int c) { return min(d.T, (c + 1) * chunk) * d.segs; };
+    auto blocks = [](int items, int per_block) { return (items + per_block - 1) / per_block; };
+    const int per_a = kWaves * kStageAU, per_b = kWaves * kStageU;
+    hipError_t e = launch(MOE_KERNEL_STAGE_A, stage_a_kernel<KMAX, kStageAU>,
+                          dim3(blocks(last(0) - first(0), per_a)), dim3(kBlock), 0, s, d, idx, xv, sv,
+                          w, first(0), last(0), keep);
+    for (int c = 0; c + 1 < nch && e == hipSuccess; ++c) {
+      const int bb = blocks(last(c) - first(c), kWaves);  // one wave-item a wave
+      const int ba = blocks(last(c + 1) - first(c + 1), per_a);
+      e = launch(MOE_KERNEL_STAGE_AB, stage_ab_kernel<KMAX>, dim3(bb + ba), dim3(kBlock), 0, s, d,
+                 idx, xv, sv, rv, w, bb, first(c), last(c), first(c + 1), last(c + 1), keep);
     }
-    return hipSuccess;
+    if (e == hipSuccess)
+      e = launch(MOE_KERNEL_STAGE_B, stage_b_kernel<KMAX, kStageU>,
+                 dim3(blocks(last(nch - 1) - first(nch - 1), per_b)), dim3(kBlock), 0, s, d,
+                 static_cast<const u32x4*>(sv), rv, w, first(nch - 1), last(nch - 1));
+    return e;
   }
 };
 
@@ -1003,7 +1117,16 @@ struct GatherFp8Launch {
   }
 };
 
-// The deduplicated fp8 dispatch in chunks of tokens, as DedupLaunch.
+// Tokens per chunk of the deduplicated fp8 dispatch (codes and scales:
+// min(k, N) * (H + 4 * nb) staging bytes a token, at most).
+inline int stage_chunk_tokens_fp8(const Dims& d) {
+  const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
+  return stage_chunk_tokens(d, (int64_t)min(d.k, d.N) * (d.H + 4 * nb));
+}
+
+// The deduplicated fp8 dispatch in chunks of tokens, with the launches of
+// DedupLaunch: hop 1 of chunk 0, hop 2 of chunk c with hop 1 of chunk c + 1,
+// hop 2 of the last chunk.
 template <int KMAX>
 struct DedupFp8Launch {
   static hipError_t run(const Dims& d, const int32_t* idx, const uint16_t* x, uint8_t* stage8,
@@ -1012,21 +1135,28 @@ struct DedupFp8Launch {
     const int segs8 = (d.chunks + kFp8ItemChunks - 1) / kFp8ItemChunks;
     const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
     const int64_t row_bound = (int64_t)min(d.k, d.N) * (d.H + 4 * nb);  // codes + scales
-    const int chunk = stage_chunk_tokens(d, row_bound);
+    const int chunk = stage_chunk_tokens_fp8(d);
+    const int nch = (d.T + chunk - 1) / chunk;
     const int keep = (int64_t)chunk * row_bound <= kKeepBytes;
-    for (int t0 = 0; t0 < d.T; t0 += chunk) {
-      const int item0 = t0 * segs8, item_end = min(d.T, t0 + chunk) * segs8;
-      const int blocks = (item_end - item0 + kWaves - 1) / kWaves;
-      hipError_t e = launch(MOE_KERNEL_STAGE_A_FP8, stage_a_fp8_kernel<KMAX>, dim3(blocks),
-                            dim3(kBlock), 0, s, d, idx, reinterpret_cast<const u32x4*>(x), stage8,
-                            sscale, w, item0, item_end, keep);
-      if (e != hipSuccess) return e;
-      e = launch(MOE_KERNEL_STAGE_B_FP8, stage_b_fp8_kernel<KMAX>, dim3(blocks), dim3(kBlock), 0, s,
-                 d, static_cast<const uint8_t*>(stage8), static_cast<const float*>(sscale), recv8,
-                 rscale, w, item0, item_end);
-      if (e != hipSuccess) return e;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    auto first = [&](int c) { return c * chunk * segs8; };
+    auto last = [&](int c) { return min(d.T, (c + 1) * chunk) * segs8; };
+    auto blocks = [](int items) { return (items + kWaves - 1) / kWaves; };
+    hipError_t e = launch(MOE_KERNEL_STAGE_A_FP8, stage_a_fp8_kernel<KMAX>,
+                          dim3(blocks(last(0) - first(0))), dim3(kBlock), 0, s, d, idx, xv, stage8,
+                          sscale, w, first(0), last(0), keep);
+    for (int c = 0; c + 1 < nch && e == hipSuccess; ++c) {
+      const int bb = blocks(last(c) - first(c)), ba = blocks(last(c + 1) - first(c + 1));
+      e = launch(MOE_KERNEL_STAGE_AB_FP8, stage_ab_fp8_kernel<KMAX>, dim3(bb + ba), dim3(kBlock), 0,
+                 s, d, idx, xv, stage8, sscale, recv8, rscale, w, bb, first(c), last(c),
+                 first(c + 1), last(c + 1), keep);
     }
-    return hipSuccess;
+    if (e == hipSuccess)
+      e = launch(MOE_KERNEL_STAGE_B_FP8, stage_b_fp8_kernel<KMAX>,
+                 dim3(blocks(last(nch - 1) - first(nch - 1))), dim3(kBlock), 0, s, d,
+                 static_cast<const uint8_t*>(stage8), static_cast<const float*>(sscale), recv8,
+                 rscale, w, first(nch - 1), last(nch - 1));
+    return e;
   }
 };
 
@@ -1046,33 +1176,52 @@ struct CombineFp8Launch {
   }
 };
 
+// Tokens per chunk of the hierarchical combine: even chunks, each with at
+// most kHierChunkBytes of fp32 partial rows (min(k, N) rows a token, at most).
+inline int hier_chunk_tokens(const Dims& d) {
+  const int64_t row_bound = (int64_t)min(d.k, d.N) * 4 * d.H;
+  const int64_t n = std::max<int64_t>(1, ((int64_t)d.T * row_bound + kHierChunkBytes - 1) / kHierChunkBytes);
+  return (int)(((int64_t)d.T + n - 1) / n);
+}
+
 // The hierarchical combine in chunks of consecutive tokens: hop 1, then hop
-// 2, of each chunk before the next, so hop 2 reads partials hop 1 has just
-// written (at most kHierChunkBytes of partial rows a chunk, counting
-// min(k, N) rows a token; the node-limited workload uses about half).
+// 2, of each chunk after the previous chunk's, so hop 2 reads partials hop 1
+// has just written (at most kHierChunkBytes of partial rows a chunk,
+// counting min(k, N) rows a token; the node-limited workload uses about
+// half).  Launches as DedupLaunch: hop 1 of chunk 0, hop 2 of chunk c with
+// hop 1 of chunk c + 1 (combine_pn), hop 2 of the last chunk.
 template <int KMAX>
 struct CombineHierLaunch {
+  template <bool F32OUT>
+  static hipError_t go(const Dims& d, const uint16_t* y, const float* wts, float* part, void* out,
+                       const Work& w, hipStream_t s) {
+    const int64_t row_bound = (int64_t)min(d.k, d.N) * 4 * d.H;  // partial bytes per token, at most
+    const int chunk = hier_chunk_tokens(d);
+    const int nch = (d.T + chunk - 1) / chunk;
+    const int keep = (int64_t)chunk * row_bound <= kKeepBytes;
+    const u32x4* yv = reinterpret_cast<const u32x4*>(y);
+    f32x4* pp = reinterpret_cast<f32x4*>(part);
+    auto first = [&](int c) { return c * chunk * d.segs; };
+    auto last = [&](int c) { return min(d.T, (c + 1) * chunk) * d.segs; };
+    auto blocks = [](int items) { return (items + kWaves - 1) / kWaves; };
+    hipError_t e = launch(MOE_KERNEL_COMBINE_PART, combine_part_kernel<KMAX>,
+                          dim3(blocks(last(0) - first(0))), dim3(kBlock), 0, s, d, yv, wts, pp, w,
+                          first(0), last(0), keep);
+    for (int c = 0; c + 1 < nch && e == hipSuccess; ++c) {
+      const int bb = blocks(last(c) - first(c)), bp = blocks(last(c + 1) - first(c + 1));
+      e = launch(MOE_KERNEL_COMBINE_PN, combine_pn_kernel<KMAX, F32OUT>, dim3(bb + bp), dim3(kBlock),
+                 0, s, d, yv, wts, pp, w, out, bb, first(c), last(c), first(c + 1), last(c + 1),
+                 keep);
+    }
+    if (e == hipSuccess)
+      e = launch(MOE_KERNEL_COMBINE_NODES, combine_nodes_kernel<KMAX, F32OUT>,
+                 dim3(blocks(last(nch - 1) - first(nch - 1))), dim3(kBlock), 0, s, d,
+                 static_cast<const f32x4*>(pp), w, out, first(nch - 1), last(nch - 1));
+    return e;
+  }
   static hipError_t run(const Dims& d, const uint16_t* y, const float* wts,
                         float* part, void* out, bool f32, const Work& w, hipStream_t s) {
-    const int64_t row_bound = (int64_t)min(d.k, d.N) * 4 * d.H;  // partial bytes per token, at most
-    const int64_t n = std::max<int64_t>(1, ((int64_t)d.T * row_bound + kHierChunkBytes - 1) / kHierChunkBytes);
-    const int chunk = (int)(((int64_t)d.T + n - 1) / n);
-    const int keep = (int64_t)chunk * row_bound <= kKeepBytes;
-    f32x4* pp = reinterpret_cast<f32x4*>(part);
-    for (int t0 = 0; t0 < d.T; t0 += chunk) {
-      const int item0 = t0 * d.segs, item_end = min(d.T, t0 + chunk) * d.segs;
-      const int blocks = (item_end - item0 + kWaves - 1) / kWaves;
-      hipError_t e = launch(MOE_KERNEL_COMBINE_PART, combine_part_kernel<KMAX>, dim3(blocks),
-                            dim3(kBlock), 0, s, d, reinterpret_cast<const u32x4*>(y), wts, pp, w,
-                            item0, item_end, keep);
-      if (e != hipSuccess) return e;
-      e = f32 ? launch(MOE_KERNEL_COMBINE_NODES, combine_nodes_kernel<KMAX, true>, dim3(blocks),
-                       dim3(kBlock), 0, s, d, static_cast<const f32x4*>(pp), w, out, item0, item_end)
-              : launch(MOE_KERNEL_COMBINE_NODES, combine_nodes_kernel<KMAX, false>, dim3(blocks),
-                       dim3(kBlock), 0, s, d, static_cast<const f32x4*>(pp), w, out, item0, item_end);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return f32 ? go<true>(d, y, wts, part, out, w, s) : go<false>(d, y, wts, part, out, w, s);
   }
 };
 
@@ -1109,6 +1258,12 @@ hipError_t launch_gather(const Dims& d, const int32_t* idx, const uint16_t* x, u
                          const Work& w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
   return by_topk<GatherLaunch>(d.k, d, idx, x, recv, w, s);
+}
+
+int64_t chunk_tokens(const Dims& d, int call) {
+  if (call == 1) return stage_chunk_tokens_fp8(d);
+  if (call == 2) return hier_chunk_tokens(d);
+  return stage_chunk_tokens(d, (int64_t)min(d.k, d.N) * 2 * d.H);
 }
 
 hipError_t launch_dedup_dispatch(const Dims& d, const int32_t* idx, const uint16_t* x,

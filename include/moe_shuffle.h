@@ -167,6 +167,11 @@ size_t moe_plan_workspace_bytes(const moe_plan* plan);
 int64_t moe_plan_recv_rows(const moe_plan* plan);         /* T*k                          */
 int64_t moe_plan_staging_rows_max(const moe_plan* plan);  /* T*min(k, N) with dedup, else 0 */
 int64_t moe_plan_bands(const moe_plan* plan);             /* nb (1 without bands)          */
+/* Tokens per chunk of the calls that run over chunks of consecutive tokens
+ * with MOE_FLAG_NODE_DEDUP: the batch's tokens [c*n, min((c+1)*n, T)) form
+ * chunk c.  call 0: moe_dispatch, 1: moe_dispatch_fp8, 2: moe_combine_hier.
+ * T without dedup or for any other call. */
+int64_t moe_plan_chunk_tokens(const moe_plan* plan, int32_t call);
 
 /* Route plan: validates routing, builds the per-expert histogram, its
  * exclusive scan and the segment descriptors (and, with dedup, the per-
@@ -201,7 +206,9 @@ moe_status moe_route_plan_static(moe_plan* plan, const int32_t* topk_idx, void* 
  * [T, H] bf16; recv: device [T*k, H] bf16.  staging: device
  * [staging_rows_max, H] bf16 when the plan has MOE_FLAG_NODE_DEDUP, else
  * ignored (may be NULL); with it, the two hops run over chunks of
- * consecutive tokens, both hops of a chunk before the next.  Asynchronous.
+ * consecutive tokens (moe_plan_chunk_tokens), hop 1 of a chunk
+ * before its hop 2, which shares a launch with hop 1 of the next chunk.
+ * Asynchronous.
  * Errors: PLAN_NOT_ROUTED, INVALID_ARGUMENT, HIP. */
 moe_status moe_dispatch(moe_plan* plan, const uint16_t* x, uint16_t* recv, uint16_t* staging,
                         void* stream);
@@ -236,8 +243,9 @@ moe_status moe_combine_hier(moe_plan* plan, const uint16_t* y, const float* topk
  * OCP E4M3 (bias 7, largest finite 448, no infinities).  Every row is cut
  * into blocks of 128 elements (the last may be shorter); each block carries
  * one float32 scale 2^e, the smallest power of two with amax(|block|) <=
- * 448 * 2^e (1 for an all-zero block), and code = E4M3(value / 2^e) rounded
- * to nearest even.  Non-finite inputs give unspecified codes.
+ * 448 * 2^e (1 for an all-zero block, and for a block holding an infinity or
+ * a NaN, whose codes are then unspecified), and code = E4M3(value / 2^e)
+ * rounded to nearest even.
  * Layouts: codes [rows, H] uint8 (16-byte aligned), scales [rows, nb] float32
  * with nb = moe_plan_scale_blocks(plan) = ceil(H / 128). */
 int64_t moe_plan_scale_blocks(const moe_plan* plan);
@@ -309,7 +317,11 @@ typedef enum moe_kernel {
   MOE_KERNEL_COMBINE_FP8 = 16,    /* moe_combine_fp8                                         */
   MOE_KERNEL_PIPELINE = 17,       /* moe_pipeline                                            */
   MOE_KERNEL_COUNTERS_CLEAR = 18, /* moe_pipeline: zeroes the pipeline's counters            */
-  MOE_KERNEL_COUNT = 19
+  MOE_KERNEL_STAGE_AB = 19,       /* deduplicated dispatch: hop 2 of chunk c with hop 1 of
+                                     chunk c + 1 in one launch (one per chunk boundary)       */
+  MOE_KERNEL_STAGE_AB_FP8 = 20,   /* the same for moe_dispatch_fp8                          */
+  MOE_KERNEL_COMBINE_PN = 21,     /* moe_combine_hier: hop 2 of chunk c with hop 1 of c + 1  */
+  MOE_KERNEL_COUNT = 22
 } moe_kernel;
 
 /* Symbol name of a moe_kernel id (static text; "?" outside the enum). */

@@ -194,3 +194,28 @@ def test_timing_host_errors():
     assert L.moe_plan_timing(h, 0) == _abi.OK                     # off: no HIP call
     assert L.moe_plan_timing_read(h, ids, st, ms, 1, ctypes.byref(n)) == _abi.ERR_INVALID_ARGUMENT
     L.moe_plan_destroy(h)
+
+
+@pytest.mark.parametrize("T,H,k,R,G,want", [
+    (16384, 7168, 8, 64, 8, 2048),   # DeepSeek-V3-like: 8 chunks
+    (2500, 7168, 8, 16, 2, 1250),    # 2 chunks
+    (4999, 7168, 8, 8, 1, 1667),     # 3 chunks, the last ragged
+    (300, 64, 4, 8, 2, 300),         # one chunk
+    (4096, 2048, 8, 4, 4, 4096),     # single hop: the whole batch
+])
+def test_dispatch_chunk_tokens(T, H, k, R, G, want):
+    import combine_shuffling_amd as cs
+
+    p = cs.Plan(T, H, 64, k, R, G, R // G > 1)
+    assert p.chunk_tokens["dispatch"] == want
+
+
+def test_chunk_tokens_of_the_fp8_dispatch_and_hierarchical_combine():
+    import combine_shuffling_amd as cs
+
+    p = cs.Plan(16384, 7168, 256, 8, 64, 8, True)
+    # fp8: 8 rows of 7168 codes + 56 scales a token -> 5 chunks; hierarchical
+    # combine: 8 fp32 partial rows a token, at most 448 MiB a chunk -> 8 chunks
+    assert p.chunk_tokens == {"dispatch": 2048, "dispatch_fp8": 3277, "combine_hier": 2048}
+    one = cs.Plan(4096, 2048, 64, 8, 4)
+    assert set(one.chunk_tokens.values()) == {4096}

@@ -57,7 +57,12 @@ def test_kernel_bytes_add_up_to_the_phases(payload):
     d1, c1 = bench.algorithmic_bytes(one, 0, payload)
     assert kb1[f"gather{sfx}_kernel"] == kb1[f"gather{sfx}_scan_kernel"] == d1
     assert kb1[f"combine{sfx}_kernel"] == c1
+    # the fused launches of the chunked calls share out the same bytes
+    tc, dc = [2048] * 8, [8136] * 7 + [D - 7 * 8136]
+    kc = bench.kernel_bytes(wl, D, payload, (tc, dc), (tc, dc))
+    assert kc[f"stage_a{sfx}_kernel"] + kc[f"stage_ab{sfx}_kernel"] + kc[f"stage_b{sfx}_kernel"] == disp
     hd, hc = bench.algorithmic_bytes(wl, D, hier=True)
+    assert kc["combine_part_kernel"] + kc["combine_pn_kernel"] + kc["combine_nodes_kernel"] == hc
     assert kb["combine_part_kernel"] + kb["combine_nodes_kernel"] == hc
     assert kb1["pipeline_kernel"] == sum(bench.algorithmic_bytes(one, 0))
 

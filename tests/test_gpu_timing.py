@@ -34,9 +34,11 @@ def test_every_launch_is_timed_in_order(dedup, dev):
     rec = plan.timing_read()
     names = [n for n, _, _ in rec]
     if dedup:
-        # 5000 tokens of up to 8 staging rows of 14 KiB: three chunks
-        assert names == (["route_count_kernel", "route_scan_kernel"]
-                         + ["stage_a_kernel", "stage_b_kernel"] * 3 + ["combine_kernel"])
+        # 5000 tokens of up to 8 staging rows of 14 KiB: three chunks, hop 2 of
+        # a chunk sharing a launch with hop 1 of the next
+        assert plan.chunk_tokens["dispatch"] == 1667
+        assert names == ["route_count_kernel", "route_scan_kernel", "stage_a_kernel",
+                         "stage_ab_kernel", "stage_ab_kernel", "stage_b_kernel", "combine_kernel"]
     else:
         assert names[0] == "route_count_kernel" and names[-1] == "combine_kernel"
         assert names[-2] in ("gather_kernel", "gather_scan_kernel")
