@@ -122,8 +122,9 @@ def parse(argv=None):
                     help="plan a workload with virtual nodes (dsv3) as one node: the same routing "
                          "moved by the single-hop gather, the lower bound on its bytes")
     ap.add_argument("--no-schedules", action="store_true",
-                    help="leave out the back-to-back schedule passes (for profiler runs, so every "
-                         "traced launch runs in the flushed protocol)")
+                    help="leave out the passes that do not flush before each phase (the back-to-back "
+                         "schedules, the copy ceiling and olmoe's MALL-resident combine), so that in "
+                         "a profiler run every traced launch runs in the flushed protocol")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled by the schedules (0: auto)")
@@ -556,7 +557,7 @@ def run_workload(torch, cs, gen, name, args, dev, flush, primary):
                                       "phase's first kernel (not subtracted)",
                         "phases": phases,
                         "wall_ms_per_step_incl_flush": round(wall_ms, 5)}}
-    if not pipe and wl.name.startswith("olmoe"):
+    if not pipe and wl.name.startswith("olmoe") and not args.no_schedules:
         # The receive rows (128 MiB) fit the MALL: the combine without the
         # flush between the phases, for comparison.
         _, p2r, _, _, _ = protocol_steps(args.steps, flush_mid=False)
