@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void pipeline_kernel(Dims d, const int32_t*
     if (ok) {
       switch (t.role) {
         case kCount: count_tile<KMAX, true>(d, idx, w, t.band * d.tpb + t.r, cl); break;
-        case kScan: scan_band<false, true>(d, w, t.band, sl); break;
+        case kScan: scan_band<true>(d, w, t.band, sl); break;
         case kGather:
           gather_chunk<KMAX, kPipeGatherU, true>(d, idx, x, recv, w, t.r, t0 * d.segs,
                                                  t1 * d.segs);

@@ -11,7 +11,7 @@ namespace {
 // In-place exclusive scan of a[0..n) (n <= 4 * NT) by the whole block of NT
 // threads; returns the total.  s_wsum: NT / 64 ints of LDS.
 template <int NT = kPlanBlock>
-__device__ int block_exclusive_scan(int* a, int n, int* s_wsum) {
+__device__ __forceinline__ int block_exclusive_scan(int* a, int n, int* s_wsum) {
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   int v[4];
   int sum = 0;
@@ -46,6 +46,44 @@ __device__ int block_exclusive_scan(int* a, int n, int* s_wsum) {
   return total;
 }
 
+// Sum of column c of a [nblk, W] tile-major matrix in LDS over tiles
+// [b0, b1), with eight reads in flight at a time (one read and its wait per
+// tile would make the sum a chain of LDS round trips).
+__device__ __forceinline__ int column_sum(const int* s_mat, int W, int c, int b0, int b1) {
+  int sum = 0, b = b0;
+  for (; b + 8 <= b1; b += 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = s_mat[(b + i) * W + c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += v[i];
+  }
+  for (; b < b1; ++b) sum += s_mat[b * W + c];
+  return sum;
+}
+
+// Writes the first row of tiles [b0, b1) of column c, the first of them at
+// `run`, reading the counts eight at a time.
+template <bool COH>
+__device__ __forceinline__ void column_run(const int* s_mat, int W, int c, int b0, int b1, int run,
+                                           int32_t* base) {
+  int b = b0;
+  for (; b + 8 <= b1; b += 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = s_mat[(b + i) * W + c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      st_plan<COH>(&base[(b + i) * W + c], run);
+      run += v[i];
+    }
+  }
+  for (; b < b1; ++b) {
+    st_plan<COH>(&base[b * W + c], run);
+    run += s_mat[b * W + c];
+  }
+}
+
 // Column sums of a [nblk, W] tile-major matrix in LDS by a block of NT
 // threads.  With W <= NT each column is cut into P = min(NT / W, nblk) parts
 // of consecutive tiles, one part a thread (thread q * W + c takes part q of
@@ -54,23 +92,17 @@ __device__ int block_exclusive_scan(int* a, int n, int* s_wsum) {
 // Returns P (0 when W > NT: then each thread sums whole columns and s_part is
 // unused).  Ends with the block synchronised.
 template <int NT>
-__device__ int column_parts(const int* s_mat, int W, int nblk, int* s_part, int* tot) {
+__device__ __forceinline__ int column_parts(const int* s_mat, int W, int nblk, int* s_part, int* tot) {
   const int tid = threadIdx.x;
   if (W > NT) {
-    for (int c = tid; c < W; c += NT) {
-      int sum = 0;
-      for (int b = 0; b < nblk; ++b) sum += s_mat[b * W + c];
-      tot[c] = sum;
-    }
+    for (int c = tid; c < W; c += NT) tot[c] = column_sum(s_mat, W, c, 0, nblk);
     __syncthreads();
     return 0;
   }
   const int P = max(1, min(NT / W, nblk));
   if (tid < P * W) {
     const int q = tid / W, c = tid - q * W;
-    int sum = 0;
-    for (int b = q * nblk / P; b < (q + 1) * nblk / P; ++b) sum += s_mat[b * W + c];
-    s_part[tid] = sum;
+    s_part[tid] = column_sum(s_mat, W, c, q * nblk / P, (q + 1) * nblk / P);
   }
   __syncthreads();
   if (tid < W) {
@@ -90,24 +122,14 @@ __device__ int column_parts(const int* s_mat, int W, int nblk, int* s_part, int*
 // starts at first(c), and each tile adds its count.  P and s_part as left by
 // column_parts (P = 0: one thread per column).
 template <bool COH, int NT, typename F>
-__device__ void column_bases(const int* s_mat, int W, int nblk, int P, const int* s_part,
-                             int32_t* base, F first) {
+__device__ __forceinline__ void column_bases(const int* s_mat, int W, int nblk, int P,
+                                             const int* s_part, int32_t* base, F first) {
   const int tid = threadIdx.x;
   if (P == 0) {
-    for (int c = tid; c < W; c += NT) {
-      int run = first(c);
-      for (int b = 0; b < nblk; ++b) {
-        st_plan<COH>(&base[b * W + c], run);
-        run += s_mat[b * W + c];
-      }
-    }
+    for (int c = tid; c < W; c += NT) column_run<COH>(s_mat, W, c, 0, nblk, first(c), base);
   } else if (tid < P * W) {
     const int q = tid / W, c = tid - q * W;
-    int run = first(c) + s_part[tid];
-    for (int b = q * nblk / P; b < (q + 1) * nblk / P; ++b) {
-      st_plan<COH>(&base[b * W + c], run);
-      run += s_mat[b * W + c];
-    }
+    column_run<COH>(s_mat, W, c, q * nblk / P, (q + 1) * nblk / P, first(c) + s_part[tid], base);
   }
 }
 
@@ -117,8 +139,9 @@ __device__ void column_bases(const int* s_mat, int W, int nblk, int P, const int
 // counted on from row0.  Leaves the offsets from 0 in s_tot; returns the
 // grand total.  Needs W * nblk <= the LDS matrix; s_part holds NT ints.
 template <bool COH = false, int NT = kPlanBlock>
-__device__ int scan_tiles(const int32_t* src, int32_t* base, int32_t* totals, int32_t* off, int W,
-                          int nblk, int row0, int* s_mat, int* s_tot, int* s_wsum, int* s_part) {
+__device__ __forceinline__ int scan_tiles(const int32_t* src, int32_t* base, int32_t* totals,
+                                          int32_t* off, int W, int nblk, int row0, int* s_mat,
+                                          int* s_tot, int* s_wsum, int* s_part) {
   const int tid = threadIdx.x, n = W * nblk;
 #pragma unroll 16
   for (int i = tid; i < n; i += NT) s_mat[i] = ld_plan<COH>(&src[i]);
@@ -287,55 +310,108 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
 // rows stay ordered by (forwarder, token); owners hold ascending token
 // ranges, so inside a forwarder that is (owner, token).  Each pair's first
 // row is its forwarder's first row plus the loads of the forwarder's owners
-// with a lower id: R / G terms, read through a per-node owner-by-rank table.
-// Writes the forwarder table, stage_off and the (tile, pair) bases; returns
-// D.  Needs R * N <= 1024.
+// with a lower id: R / G terms, read through per-node owner-by-rank and
+// load-by-rank tables in LDS.  With R <= 64 a wave takes a node, one lane an
+// owner: a lane's rank counts the lanes ahead of it (R compares against
+// values read from the other lanes), and only that wave reads the node's
+// tables, so no block barrier is needed between writing and reading them.
+// Larger R ranks one pair a thread against the LDS load table.  Writes the forwarder table, stage_off and the (tile, pair) bases;
+// returns D.  Needs R * N <= 1024.
 template <bool COH = false, int NT = kPlanBlock>
-__device__ int scan_load_aware(const Dims& d, const Work& w, int* s_mat, int* s_tot, int* s_wsum,
-                               int* s_part) {
+__device__ __forceinline__ int scan_load_aware(const Dims& d, const Work& w, int* s_mat, int* s_tot,
+                                               int* s_wsum, int* s_part) {
   __shared__ int s_load[MOE_MAX_EXPERTS];   // per pair
-  __shared__ int s_rank[MOE_MAX_EXPERTS];   // per pair: its owner's rank in the node
+  __shared__ int s_rank[MOE_MAX_EXPERTS];   // R > 64: per pair, its owner's rank in the node;
+                                            // R <= 64: per node, load of rank r at n * R + r
   __shared__ int s_order[MOE_MAX_EXPERTS];  // per node n: owner of rank r at n * R + r
   __shared__ int s_first[MOE_MAX_EXPERTS];  // per pair: first staging row
+  __shared__ int s_fwd[MOE_MAX_EXPERTS];    // R <= 64: per pair, its forwarder
   const int tid = threadIdx.x, R = d.R, N = d.N, G = d.G, K = d.fkeys, nblk = d.nblk;
   const int laps = R / G;
 #pragma unroll 16
   for (int i = tid; i < K * nblk; i += NT) s_mat[i] = ld_plan<COH>(&w.tile_fcounts[i]);
   __syncthreads();
   const int P = column_parts<NT>(s_mat, K, nblk, s_part, s_load);
-  for (int c = tid; c < K; c += NT) {
-    const int s = c / N, n = c - (c / N) * N, l = s_load[c];
-    int rank = 0;
-    for (int s2 = 0; s2 < R; ++s2) {
-      const int l2 = s_load[s2 * N + n];
-      rank += (l2 > l || (l2 == l && s2 < s)) ? 1 : 0;
+  int staged;
+  if (R <= kWave) {
+    const int lane = tid % kWave;
+    for (int n = tid / kWave; n < N; n += NT / kWave) {
+      const bool live = lane < R;
+      const int l = live ? s_load[lane * N + n] : 0;
+      // One key orders by load, then owner: a pair's load is at most the
+      // owner's ceil(T / R) tokens, so l * R + R - 1 - lane < 2^32 and keys
+      // are distinct.  Lanes past R hold key 0, which outranks no one.
+      const uint32_t key = live ? (uint32_t)l * R + (R - 1 - lane) : 0u;
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < kWave; ++j)
+        rank += (uint32_t)__builtin_amdgcn_readlane((int)key, j) > key ? 1 : 0;
+      // The node's owners and loads by rank; only this wave reads them.
+      if (live) {
+        s_order[n * R + rank] = lane;
+        s_rank[n * R + rank] = l;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (live) {
+        const int lap = rank / G, pos = rank - lap * G;
+        const int g = (lap & 1) ? G - 1 - pos : pos;
+        int tot = 0, before = 0;
+        for (int l2 = 0; l2 < laps; ++l2) {
+          const int r = n * R + l2 * G + ((l2 & 1) ? G - 1 - g : g);
+          const int v = s_rank[r];
+          tot += v;
+          before += s_order[r] < lane ? v : 0;
+        }
+        if (lap == 0) s_tot[n * G + g] = tot;
+        s_first[lane * N + n] = before;
+        s_fwd[lane * N + n] = n * G + g;
+      }
     }
-    s_rank[c] = rank;
-    s_order[n * R + rank] = s;
-  }
-  __syncthreads();
-  // owner of the forwarder with local index g in node n, lap `lap`
-  auto owner = [&](int n, int g, int lap) { return s_order[n * R + lap * G + ((lap & 1) ? G - 1 - g : g)]; };
-  for (int f = tid; f < R; f += NT) {
-    const int n = f / G, g = f - n * G;
-    int tot = 0;
-    for (int lap = 0; lap < laps; ++lap) tot += s_load[owner(n, g, lap) * N + n];
-    s_tot[f] = tot;
-  }
-  __syncthreads();
-  const int staged = block_exclusive_scan<NT>(s_tot, R, s_wsum);
-  for (int f = tid; f <= R; f += NT) w.stage_off[f] = f < R ? s_tot[f] : staged;
-  for (int c = tid; c < K; c += NT) {
-    const int s = c / N, n = c - (c / N) * N, rank = s_rank[c];
-    const int lap = rank / G, pos = rank - lap * G;
-    const int g = (lap & 1) ? G - 1 - pos : pos;
-    int first = s_tot[n * G + g];
-    for (int l2 = 0; l2 < laps; ++l2) {
-      const int o = owner(n, g, l2);
-      first += o < s ? s_load[o * N + n] : 0;
+    __syncthreads();
+    staged = block_exclusive_scan<NT>(s_tot, R, s_wsum);
+    for (int f = tid; f <= R; f += NT) w.stage_off[f] = f < R ? s_tot[f] : staged;
+    for (int c = tid; c < K; c += NT) {
+      const int f = s_fwd[c];
+      s_first[c] += s_tot[f];
+      w.fwd[c] = f;
     }
-    s_first[c] = first;
-    w.fwd[c] = n * G + g;
+  } else {
+    for (int c = tid; c < K; c += NT) {
+      const int s = c / N, n = c - (c / N) * N, l = s_load[c];
+      int rank = 0;
+      for (int s2 = 0; s2 < R; ++s2) {
+        const int l2 = s_load[s2 * N + n];
+        rank += (l2 > l || (l2 == l && s2 < s)) ? 1 : 0;
+      }
+      s_rank[c] = rank;
+      s_order[n * R + rank] = s;
+    }
+    __syncthreads();
+    // owner of the forwarder with local index g in node n, lap `lap`
+    auto owner = [&](int n, int g, int lap) {
+      return s_order[n * R + lap * G + ((lap & 1) ? G - 1 - g : g)];
+    };
+    for (int f = tid; f < R; f += NT) {
+      const int n = f / G, g = f - n * G;
+      int tot = 0;
+      for (int lap = 0; lap < laps; ++lap) tot += s_load[owner(n, g, lap) * N + n];
+      s_tot[f] = tot;
+    }
+    __syncthreads();
+    staged = block_exclusive_scan<NT>(s_tot, R, s_wsum);
+    for (int f = tid; f <= R; f += NT) w.stage_off[f] = f < R ? s_tot[f] : staged;
+    for (int c = tid; c < K; c += NT) {
+      const int s = c / N, n = c - (c / N) * N, rank = s_rank[c];
+      const int lap = rank / G, pos = rank - lap * G;
+      const int g = (lap & 1) ? G - 1 - pos : pos;
+      int first = s_tot[n * G + g];
+      for (int l2 = 0; l2 < laps; ++l2) {
+        const int o = owner(n, g, l2);
+        first += o < s ? s_load[o * N + n] : 0;
+      }
+      s_first[c] = first;
+      w.fwd[c] = n * G + g;
+    }
   }
   __syncthreads();
   column_bases<COH, NT>(s_mat, K, nblk, P, s_part, w.tile_fbase, [&](int c) { return s_first[c]; });
@@ -351,48 +427,46 @@ struct ScanLds {
   int* part;  // [NT] column parts
 };
 
-// One band by the whole block: scans its [tiles x experts] count matrix (and,
-// with dedup, which runs with one band only, the [tiles x staging keys] one)
-// into base rows, the band's expert and rank offsets and its status.  The
-// band's receive rows start at band * d.band * k.
-template <bool DEDUP = true, bool COH = false, int NT = kPlanBlock>
+// One band by the whole block: scans its [tiles x experts] count matrix into
+// base rows, the band's expert and rank offsets and its status.  The band's
+// receive rows start at band * d.band * k.
+template <bool COH = false, int NT = kPlanBlock>
 __device__ __forceinline__ void scan_band(const Dims& d, const Work& w, int band,
                                           const ScanLds& L) {
-  int* s_mat = L.mat;
   int* s_tot = L.tot;
-  int* s_wsum = L.wsum;
   const int tid = threadIdx.x, E = d.E, R = d.R;
   const int t0 = band * d.tpb, nt = min(d.tpb, d.nblk - t0);
   const int row0 = band * d.band * d.k;
   const int rows = scan_tiles<COH, NT>(w.tile_counts + (int64_t)t0 * E, w.tile_base + (int64_t)t0 * E,
                               w.counts + (int64_t)band * E, w.expert_off + (int64_t)band * (E + 1),
-                              E, nt, row0, s_mat, s_tot, s_wsum, L.part);
+                              E, nt, row0, L.mat, s_tot, L.wsum, L.part);
   int32_t* roff = w.rank_off + (int64_t)band * (R + 1);
   for (int r = tid; r <= R; r += NT) {
     const int first = r * d.ebase + min(r, d.erem);  // first expert of rank r
     roff[r] = row0 + (first < E ? s_tot[first] : rows);
   }
-  int staged = 0;
-  if constexpr (DEDUP) {
-    if (d.dedup) {
-      __syncthreads();
-      if (d.load_aware) {
-        staged = scan_load_aware<COH, NT>(d, w, s_mat, s_tot, s_wsum, L.part);
-      } else {
-        staged = scan_tiles<COH, NT>(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, R, d.nblk,
-                                     0, s_mat, s_tot, s_wsum, L.part);
-        for (int c = tid; c < R * d.N; c += NT)
-          w.fwd[c] = (c % d.N) * d.G + (c / d.N) % d.G;
-      }
-    }
-  }
   int bad = 0;
   for (int b = tid; b < nt; b += NT) bad |= ld_plan<COH>(&w.tile_flags[t0 + b]);
   bad = __syncthreads_or(bad);
-  if (tid == 0) {
-    w.band_status[band] = bad ? MOE_ERR_BAD_ROUTING : MOE_OK;
-    if (DEDUP && d.dedup) w.ctrl[kCtrlStaged] = staged;
+  if (tid == 0) w.band_status[band] = bad ? MOE_ERR_BAD_ROUTING : MOE_OK;
+}
+
+// The staging keys of a deduplicated plan (one band) by the whole block:
+// the [tiles x keys] count matrix into staging base rows, the forwarder
+// offsets and table, and the number of staging rows.  It reads nothing the
+// expert-key scan writes, so the two run in separate blocks side by side.
+template <bool COH = false, int NT = kPlanBlock>
+__device__ __forceinline__ void scan_stage_keys(const Dims& d, const Work& w, const ScanLds& L) {
+  const int tid = threadIdx.x;
+  int staged;
+  if (d.load_aware) {
+    staged = scan_load_aware<COH, NT>(d, w, L.mat, L.tot, L.wsum, L.part);
+  } else {
+    staged = scan_tiles<COH, NT>(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, d.R, d.nblk,
+                                 0, L.mat, L.tot, L.wsum, L.part);
+    for (int c = tid; c < d.R * d.N; c += NT) w.fwd[c] = (c % d.N) * d.G + (c / d.N) % d.G;
   }
+  if (tid == 0) w.ctrl[kCtrlStaged] = staged;
 }
 
 }  // namespace

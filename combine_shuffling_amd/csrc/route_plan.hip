@@ -18,11 +18,13 @@
 //              wait: cheaper than a last-arriving-block ticket with its
 //              release / acquire fences.)
 //
-// With node deduplication the same is done a second time over the keys
-// "forwarder rank of (token, node)" of the first slot of each distinct
-// destination node of a token, which orders staging rows by (forwarder,
-// token) (FUSCO article, "load balancing and cross-node deduplication": one
-// copy per destination node through a forwarding GPU).
+// With node deduplication the same is done over the keys "forwarder rank of
+// (token, node)" of the first slot of each distinct destination node of a
+// token, which orders staging rows by (forwarder, token) (FUSCO article,
+// "load balancing and cross-node deduplication": one copy per destination
+// node through a forwarding GPU).  route_count counts both key sets in one
+// pass; route_scan scans the staging keys in a block of their own, beside
+// the expert keys' block.
 //
 // A slot's receive row is then tile_base[tile][expert] + its in-tile rank:
 // the stable (expert, token) order.  The data-movement kernels that run next
@@ -56,16 +58,18 @@ __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
   count_tile<KMAX>(d, idx, w, blockIdx.x, CountLds{s_mask, s_pre, s_run, s_frun, s_node, &s_bad});
 }
 
-// One block of kScanBlock threads per band: each column of a count matrix
+// One block of kScanBlock threads per band, and with node deduplication (one
+// band) one more block for the staging keys.  Each column of a count matrix
 // is summed, and its tile bases written, by several threads (one run of
-// consecutive tiles each).  DeepSeek-V3-like scan 14.5 -> 11.7 us against
-// 256 threads, load-aware 25.4 -> 21.4 us.
+// consecutive tiles each).
 __global__ __launch_bounds__(kScanBlock) void route_scan_kernel(Dims d, Work w) {
   __shared__ int s_mat[kScanLdsInts];
   __shared__ int s_tot[MOE_MAX_EXPERTS];
   __shared__ int s_wsum[kScanBlock / kWave];
   __shared__ int s_part[kScanBlock];
-  scan_band<true, false, kScanBlock>(d, w, blockIdx.x, ScanLds{s_mat, s_tot, s_wsum, s_part});
+  const ScanLds L{s_mat, s_tot, s_wsum, s_part};
+  if ((int)blockIdx.x < d.nbands) scan_band<false, kScanBlock>(d, w, blockIdx.x, L);
+  else scan_stage_keys<false, kScanBlock>(d, w, L);
 }
 
 // Finishes the plan one token per thread (slot_of, row_src; with dedup
@@ -206,8 +210,8 @@ hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, 
 }
 
 hipError_t launch_route_scan(const Dims& d, const Work& w, hipStream_t s) {
-  return launch(MOE_KERNEL_ROUTE_SCAN, route_scan_kernel, dim3(d.nbands), dim3(kScanBlock), 0, s, d,
-                w);
+  return launch(MOE_KERNEL_ROUTE_SCAN, route_scan_kernel, dim3(d.nbands + (d.dedup ? 1 : 0)),
+                dim3(kScanBlock), 0, s, d, w);
 }
 
 hipError_t launch_route_assign(const Dims& d, const int32_t* idx, const Work& w, hipStream_t s) {

@@ -274,7 +274,10 @@ def test_plan_reads_and_combine_without_dispatch(dev):
 
 @pytest.mark.parametrize("case", [
     (2048, 64, 64, 4, 16, 4), (3001, 40, 30, 5, 6, 2), (777, 24, 1024, 16, 32, 8), (20000, 16, 64, 8, 32, 4),
-    (1800, 32, 64, 16, 32, 1)],   # R * N = 1024 owner-node pairs, the most the scan holds
+    (1800, 32, 64, 16, 32, 1),    # R * N = 1024 owner-node pairs, the most the scan holds
+    (4096, 16, 256, 8, 64, 4),    # 64 owners in each of 16 nodes: a full wave per node
+    (1500, 32, 256, 8, 128, 16),  # more than 64 owners: ranked through the LDS tables
+    (2000, 16, 192, 6, 96, 32)],
     ids=lambda c: "T{}-H{}-E{}-k{}-R{}-G{}".format(*c))
 def test_load_aware_forwarders(case, dev):
     T, H, E, k, R, G = case
