@@ -315,8 +315,9 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
 // owner: a lane's rank counts the lanes ahead of it (R compares against
 // values read from the other lanes), and only that wave reads the node's
 // tables, so no block barrier is needed between writing and reading them.
-// Larger R ranks one pair a thread against the LDS load table.  Writes the forwarder table, stage_off and the (tile, pair) bases;
-// returns D.  Needs R * N <= 1024.
+// Larger R ranks one pair a thread against the LDS load table.  Writes the
+// forwarder table, stage_off and the (tile, pair) bases; returns D.  Needs
+// R * N <= 1024.
 template <bool COH = false, int NT = kPlanBlock>
 __device__ __forceinline__ int scan_load_aware(const Dims& d, const Work& w, int* s_mat, int* s_tot,
                                                int* s_wsum, int* s_part) {
