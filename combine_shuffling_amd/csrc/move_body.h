@@ -22,10 +22,10 @@ constexpr int kStageU = 2;          // wave-items per wave: stage_b
 constexpr int kCombineU = 1;
 // ... of the fp8 combine (one stream: qwen3 step 132.4 -> 122.4 us against two).
 constexpr int kCombine8U = 1;
-// Waves per block of the bf16 combine; best step, against 4-wave blocks:
-// qwen3 205.2 -> 203.9 us, nondiv 339.1 -> 335.6, dsv3 1083.3 -> 1078.2,
-// olmoe unchanged (2-wave blocks: olmoe 48.9 against 48.3, dsv3 1075).
-constexpr int kCombineWaves = 1;
+// Waves per block of the bf16 combine.  Timed alone after a cache flush,
+// against 1-wave blocks: nondiv 160.0 -> 158.2 us, qwen3, dsv3 and olmoe
+// level (4-wave blocks: nondiv 165.8, qwen3 104.6, dsv3 374.5).
+constexpr int kCombineWaves = 2;
 // ... of the fp8 combine: 2-wave blocks made qwen3 fp8 118.1 us against 114.7.
 constexpr int kCombine8Waves = 4;
 // Wave-items per launch at most: a grid is sized in work-items, a 32-bit count,
