@@ -64,20 +64,56 @@ constexpr int64_t kChunkBytes = (int64_t)224 << 20;
 // 1149, 224 MiB 1189, 112 MiB 1356.
 constexpr int64_t kHierChunkBytes = (int64_t)448 << 20;
 
+// The plan inputs a block of the folded-scan gather reads before it can place
+// rows: its share of the tile-count matrix (entries tid + r * GB), and for
+// each wave-item the in-tile rank and expert of its token's slots (lane
+// j < k holds slot j).  The gather loads them before its row loads: a wave's
+// loads complete in issue order, so data loaded after the rows could be used
+// only once the rows had arrived, and the block would scan after its rows
+// load instead of while they do.  Every one of these loads, and every row
+// load after them, is issued by every lane (at a clamped address where the
+// lane has nothing to load, its value then dropped): a load skipped on some
+// path would leave the count of loads in flight unknown, and the wait for
+// the plan inputs would become a wait for everything.
+template <int GB>
+__device__ __forceinline__ void load_tile_counts(const Dims& d, const Work& w,
+                                                 int (&m)[kFusedScanInts / GB]) {
+  const int n = d.nblk * d.E;
+#pragma unroll
+  for (int r = 0; r < kFusedScanInts / GB; ++r) {
+    const int i = threadIdx.x + r * GB;
+    const int v = w.tile_counts[min(i, n - 1)];
+    m[r] = i < n ? v : 0;
+  }
+}
+
+__device__ __forceinline__ void load_slot_inputs(const Dims& d, const int32_t* __restrict__ idx,
+                                                 const Work& w, bool live, int t, int& l, int& e) {
+  const int lane = threadIdx.x % kWave;
+  const bool mine = live && lane < d.k;
+  const int64_t at = (int64_t)(live ? t : 0) * d.k + min(lane, d.k - 1);
+  const int lv = w.lr[at], ev = idx[at];
+  l = mine ? lv : -1;
+  e = mine ? ev : 0;
+}
+
 // The scan folded into the gather of a small plan (nblk * E <=
 // kFusedScanInts; single band).  The block (GB threads, all of which call
-// this) loads the raw tile counts into LDS, sums each expert's column and
-// scans the totals over the experts (one wave with lane shuffles when E <=
-// 64) into s_off.  fused_slot then gives each token's receive rows: the
-// expert's first row, plus its rows in earlier tiles, plus the slot's rank in
-// its tile (the same rows route_scan's tile bases give).
+// this) puts the tile counts it loaded (load_tile_counts) into LDS, sums each
+// expert's column and scans the totals over the experts (one wave with lane
+// shuffles when E <= 64) into s_off.  fused_slot then gives each token's
+// receive rows: the expert's first row, plus its rows in earlier tiles, plus
+// the slot's rank in its tile (the same rows route_scan's tile bases give).
 template <int GB>
-__device__ __forceinline__ void fused_scan_block(const Dims& d, const Work& w, int* s_mat,
-                                                 int* s_off, int* s_wsum, int* s_part) {
+__device__ __forceinline__ void fused_scan_block(const Dims& d, const int (&m)[kFusedScanInts / GB],
+                                                 int* s_mat, int* s_off, int* s_wsum,
+                                                 int* s_part) {
   constexpr int kGBlock = GB;
   const int tid = threadIdx.x, lane = threadIdx.x % kWave;
   const int E = d.E, n = d.nblk * E;
-  for (int i = tid; i < n; i += kGBlock) s_mat[i] = w.tile_counts[i];
+#pragma unroll
+  for (int r = 0; r < kFusedScanInts / GB; ++r)
+    if (tid + r * GB < n) s_mat[tid + r * GB] = m[r];
   __syncthreads();
   if (E <= kWave) {
     // Up to 64 experts: kGBlock / E threads per expert sum parts of its
@@ -85,9 +121,7 @@ __device__ __forceinline__ void fused_scan_block(const Dims& d, const Work& w, i
     const int parts = min(kGBlock / E, d.nblk);
     if (tid < parts * E) {
       const int q = tid / E, e = tid - q * E;
-      int sum = 0;
-      for (int b = q * d.nblk / parts; b < (q + 1) * d.nblk / parts; ++b) sum += s_mat[b * E + e];
-      s_off[tid] = sum;
+      s_off[tid] = column_sum(s_mat, E, e, q * d.nblk / parts, (q + 1) * d.nblk / parts);
     }
     __syncthreads();
     if (tid < kWave) {
@@ -113,9 +147,7 @@ __device__ __forceinline__ void fused_scan_block(const Dims& d, const Work& w, i
     if (parts >= 2) {
       if (tid < parts * E) {
         const int q = tid / E, e = tid - q * E;
-        int sum = 0;
-        for (int b = q * d.nblk / parts; b < (q + 1) * d.nblk / parts; ++b) sum += s_mat[b * E + e];
-        s_part[tid] = sum;
+        s_part[tid] = column_sum(s_mat, E, e, q * d.nblk / parts, (q + 1) * d.nblk / parts);
       }
       __syncthreads();
       if (tid < E) {
@@ -124,11 +156,7 @@ __device__ __forceinline__ void fused_scan_block(const Dims& d, const Work& w, i
         s_off[tid] = tot;
       }
     } else {
-      for (int e = tid; e < E; e += kGBlock) {
-        int sum = 0;
-        for (int b = 0; b < d.nblk; ++b) sum += s_mat[b * E + e];
-        s_off[e] = sum;
-      }
+      for (int e = tid; e < E; e += kGBlock) s_off[e] = column_sum(s_mat, E, e, 0, d.nblk);
     }
     __syncthreads();
     block_exclusive_scan(s_off, E, s_wsum);
@@ -136,23 +164,13 @@ __device__ __forceinline__ void fused_scan_block(const Dims& d, const Work& w, i
 }
 
 // After fused_scan_block: lane j < k of the wave returns the receive row of
-// slot j of token t (-1 for a dropped slot).
-__device__ __forceinline__ int fused_slot(const Dims& d, const int32_t* __restrict__ idx,
-                                          const Work& w, bool live, int t, const int* s_mat,
+// slot j of token t from the slot's in-tile rank l and expert e
+// (load_slot_inputs; -1 for a dropped slot or another lane).
+__device__ __forceinline__ int fused_slot(const Dims& d, int l, int e, int t, const int* s_mat,
                                           const int* s_off) {
-  const int lane = threadIdx.x % kWave, E = d.E;
-  int mine = -1;
-  if (live && lane < d.k) {
-    const int64_t at = (int64_t)t * d.k + lane;
-    const int l = w.lr[at];
-    const int e = min(max(idx[at], 0), E - 1);
-    if (l >= 0) {
-      int base = s_off[e];
-      for (int b = 0; b < t / d.tile; ++b) base += s_mat[b * E + e];
-      mine = base + l;
-    }
-  }
-  return mine;
+  if (l < 0) return -1;
+  e = min(max(e, 0), d.E - 1);
+  return s_off[e] + column_sum(s_mat, d.E, e, 0, t / d.tile) + l;
 }
 
 // Gather for plans whose tile-count matrix is small (nblk * E <=
@@ -178,7 +196,6 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
   const bool keep = keep_rows(rows, 2 * d.H);
   // wave-items g = base + (block * GW + wave) * U + u: U consecutive segments
   Item it[U];
-  u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int g = __builtin_amdgcn_readfirstlane(base + (blockIdx.x * GW + tid / kWave) * U + u);
@@ -186,15 +203,24 @@ __global__ __launch_bounds__(GW * kWave) void gather_scan_kernel(Dims d, const i
     it[u].t = it[u].live ? g / d.segs : 0;
     it[u].c = (g - it[u].t * d.segs) * kWave + lane;
     it[u].ok = it[u].live && it[u].c < d.chunks;
-    if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
   }
+  // plan inputs first, then the rows, all unconditional (load_tile_counts)
+  int m[kFusedScanInts / kGBlock], sl[U], se[U];
+  load_tile_counts<kGBlock>(d, w, m);
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_slot_inputs(d, idx, w, it[u].live, it[u].t, sl[u], se[u]);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    v[u] = load_x_chunk(&x[it[u].ok ? (int64_t)it[u].t * d.chunks + it[u].c : 0]);
 
-  fused_scan_block<kGBlock>(d, w, s_mat, s_off, s_wsum, s_part);
+  fused_scan_block<kGBlock>(d, m, s_mat, s_off, s_wsum, s_part);
   int mine = -1;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (u == 0 || it[u].t != it[u - 1].t)  // wave-uniform: a new token
-      mine = fused_slot(d, idx, w, it[u].live, it[u].t, s_mat, s_off);
+    if (u == 0 || it[u].t != it[u - 1].t)
+      mine = fused_slot(d, sl[u], se[u], it[u].t, s_mat, s_off);
     int slot[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
@@ -724,7 +750,6 @@ __global__ __launch_bounds__(GW * kWave) void gather_fp8_scan_kernel(Dims d,
   const int nb = (d.chunks + kFp8BlockChunks - 1) / kFp8BlockChunks;
   const bool keep = keep_rows(rows, d.H);
   Item8 it[U];  // wave-items g = base + (block * GW + wave) * U + u
-  u32x4 v0[U], v1[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int g = __builtin_amdgcn_readfirstlane(base + (blockIdx.x * GW + threadIdx.x / kWave) * U + u);
@@ -733,18 +758,31 @@ __global__ __launch_bounds__(GW * kWave) void gather_fp8_scan_kernel(Dims d,
     it[u].c0 = (g - it[u].t * segs8) * kFp8ItemChunks + 2 * lane;
     it[u].ok0 = it[u].live && it[u].c0 < d.chunks;
     it[u].ok1 = it[u].live && it[u].c0 + 1 < d.chunks;
-    load_piece(d, it[u], x, v0[u], v1[u]);
   }
-  fused_scan_block<GW * kWave>(d, w, s_mat, s_off, s_wsum, s_part);
+  // plan inputs first, then the rows, all unconditional (load_tile_counts)
+  int m[kFusedScanInts / (GW * kWave)], sl[U], se[U];
+  load_tile_counts<GW * kWave>(d, w, m);
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_slot_inputs(d, idx, w, it[u].live, it[u].t, sl[u], se[u]);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 v0[U], v1[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t xrow = (int64_t)it[u].t * d.chunks;
+    v0[u] = load_x_chunk(&x[it[u].ok0 ? xrow + it[u].c0 : 0]);
+    v1[u] = load_x_chunk(&x[it[u].ok1 ? xrow + it[u].c0 + 1 : 0]);
+  }
+  fused_scan_block<GW * kWave>(d, m, s_mat, s_off, s_wsum, s_part);
   int mine = -1;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (u == 0 || it[u].t != it[u - 1].t)  // wave-uniform: a new token
-      mine = fused_slot(d, idx, w, it[u].live, it[u].t, s_mat, s_off);
+    if (u == 0 || it[u].t != it[u - 1].t)
+      mine = fused_slot(d, sl[u], se[u], it[u].t, s_mat, s_off);
     int slot[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) slot[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
-    const Fp8Piece q = quantize_loaded(v0[u], v1[u]);
+    const u32x4 zero = {0u, 0u, 0u, 0u};  // lanes past the row quantize zeros
+    const Fp8Piece q = quantize_loaded(it[u].ok0 ? v0[u] : zero, it[u].ok1 ? v1[u] : zero);
     const bool scale_lane = it[u].ok0 && (lane % kFp8BlockLanes) == 0;
     const int blk = it[u].c0 / kFp8BlockChunks;
     if (it[u].live && it[u].c0 == 2 * lane && lane < d.k) {  // first segment publishes the slots
