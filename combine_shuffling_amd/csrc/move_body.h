@@ -65,14 +65,31 @@ __device__ __forceinline__ u32x4 load_chunk(const u32x4* p) {
 }
 
 // Row store that another block reads in the same launch (the banded
-// pipeline): a device-scope (sc1) 16-byte store, written through the per-XCD
-// L2 to the coherence point, so the reader needs no cache maintenance.
-template <bool COH>
-__device__ __forceinline__ void store_row_chunk(u32x4* p, u32x4 v, bool keep) {
-  if constexpr (COH)
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
-  else
-    store_row(p, v, keep);
+// pipeline): chunk at byte `off` of row `row` (wave-uniform) of a [rows,
+// chunks] buffer when row < rows, a device-scope (sc1) store, written
+// through the per-XCD L2 to the coherence point so that the reader needs no
+// cache maintenance.  It goes through a buffer descriptor of the row (scalar
+// registers) with the lane's 32-bit offset, and it is issued for every row
+// and lane: the descriptor's range (0 for a row >= rows, the row's bytes
+// otherwise) discards a store that must not land, and so does a lane past
+// the row.  Loads and stores share one counter of operations in flight on
+// this GPU.  With the stores behind branches, or written as inline asm, or
+// with a 64-bit address register per store in that kernel short of
+// registers, the compiler waited for every operation in flight before each
+// store (the previous store included): banded pipeline olmoe 100.9 -> 95.2
+// us, qwen3 273 -> 255, nondiv 460 -> 412 with this store and the lookups
+// ahead of the row loads.  (The separate gather kernels keep plain branches
+// and global stores: the same store there made nondiv's gather 147 -> 186
+// us.)
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, word 3 (gfx9 family)
+constexpr int kCacheSc1 = 1 << 4;         // buffer cache policy: device scope (sc1)
+__device__ __forceinline__ void store_row_coherent(u32x4* base, int row, uint32_t rows,
+                                                   int chunks, uint32_t off, u32x4 v) {
+  const bool valid = (uint32_t)row < rows;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      base + (int64_t)(valid ? row : 0) * chunks, 0, valid ? chunks * (int)sizeof(u32x4) : 0,
+      kBufferWord3);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCacheSc1);
 }
 
 // Token rows of x (dispatch source): plain loads measured faster here.
@@ -120,20 +137,55 @@ __device__ __forceinline__ void gather_chunk(const Dims& d, const int32_t* idx, 
   const int lane = threadIdx.x % kWave;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const bool keep = keep_rows(rows, 2 * d.H);
+  // Every wave-item's slot lookups, then every row load (x after the slot
+  // loads: nondiv gather 152.6 -> 158.8 us the other way round).  With
+  // device-scope plan reads (COH, the banded pipeline) the lookups are vector
+  // loads, which complete in issue order: a lookup issued after a row load
+  // would wait for that row, so all of them go first, in two rounds for all
+  // items (a dead item looks up token 0: t is 0 there).
   Item it[U];
   int slot[U][KMAX];
-  u32x4 v[U];
+  if constexpr (COH) {
+    int l[U][KMAX], e[U][KMAX];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    it[u] = wave_item<U>(d, blk, base, limit, u);
-    if (it[u].live) {
-      token_slots<KMAX, COH>(d, w, idx, it[u].t, slot[u]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) slot[u][j] = -1;
+    for (int u = 0; u < U; ++u) {
+      it[u] = wave_item<U>(d, blk, base, limit, u);
+      token_slot_inputs<KMAX, COH>(d, w, idx, it[u].t, l[u], e[u]);
     }
-    // after the slot loads (loading x first: nondiv gather 152.6 -> 158.8 us)
-    if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      token_slot_rows<KMAX, COH>(d, w, it[u].live, it[u].t, l[u], e[u], slot[u]);
+  } else {  // scalar lookups (their own counter): one item after another
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      it[u] = wave_item<U>(d, blk, base, limit, u);
+      if (it[u].live) {
+        token_slots<KMAX>(d, w, idx, it[u].t, slot[u]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) slot[u][j] = -1;
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 v[U];
+  if constexpr (COH) {
+    // every load and row store issued, the slot stores last (store_row_coherent)
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = load_x_chunk(&x[it[u].ok ? (int64_t)it[u].t * d.chunks + it[u].c : 0]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t off = (uint32_t)it[u].c * (uint32_t)sizeof(u32x4);
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        store_row_coherent(recv, __builtin_amdgcn_readfirstlane(slot[u][j]), rows, d.chunks, off,
+                           v[u]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -143,11 +195,13 @@ __device__ __forceinline__ void gather_chunk(const Dims& d, const int32_t* idx, 
       st_plan<COH>(&w.slot_of[(int64_t)it[u].t * d.k + lane], s);
       if ((uint32_t)s < rows) w.row_src[s] = it[u].t;
     }
-    if (it[u].ok) {
+    if constexpr (!COH) {
+      if (it[u].ok) {
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if ((uint32_t)slot[u][j] < rows)
-          store_row_chunk<COH>(&recv[(int64_t)slot[u][j] * d.chunks + it[u].c], v[u], keep);
+        for (int j = 0; j < KMAX; ++j)
+          if ((uint32_t)slot[u][j] < rows)
+            store_row(&recv[(int64_t)slot[u][j] * d.chunks + it[u].c], v[u], keep);
+      }
     }
   }
 }
@@ -182,6 +236,8 @@ __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, con
                                               const int32_t* slot_of, void* out, int blk, int base,
                                               int limit) {
   const uint32_t rows = (uint32_t)(d.T * d.k);
+  // Every wave-item's slots and weights, then every row load (the order
+  // gather_chunk keeps, for the same reason).
   Item it[U];
   int slot[U][KMAX];
   float wj[U][KMAX];
@@ -204,10 +260,13 @@ __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, con
       slot[u][j] = has && (uint32_t)sj[j] < rows ? sj[j] : -1;
       wj[u][j] = has ? wt[j] : 0.0f;
     }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
       if (slot[u][j] >= 0 && it[u].ok) v[u][j] = load_chunk(&y[(int64_t)slot[u][j] * d.chunks + it[u].c]);
-  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!it[u].ok) continue;
