@@ -42,11 +42,7 @@ __device__ __forceinline__ void st_plan(int32_t* p, int32_t v) {
 // loads below need no branch and all of them issue before the first wait).
 __device__ __forceinline__ int64_t slot_index(int64_t at, int j, int k) { return at + (j < k ? j : 0); }
 
-// Receive row of every slot of token t: the row of (tile, expert) from the
-// scan plus the slot's rank inside the tile; -1 for a dropped slot.  Two
-// rounds of loads: ranks and expert ids, then the tile bases (branch-free,
-// so each round issues together: the gather measured 26.9 -> 26.0 us on
-// olmoe against per-slot loads).
+// Receive rows of a token's slots in two rounds of loads (token_slots).
 // The first round: in-tile ranks and expert ids of token t's slots.
 template <int KMAX, bool COH = false>
 __device__ __forceinline__ void token_slot_inputs(const Dims& d, const Work& w,
@@ -76,6 +72,11 @@ __device__ __forceinline__ void token_slot_rows(const Dims& d, const Work& w, bo
   for (int j = 0; j < KMAX; ++j) slot[j] = (live && j < d.k && l[j] >= 0) ? base[j] + l[j] : -1;
 }
 
+// Receive row of every slot of token t: the row of (tile, expert) from the
+// scan plus the slot's rank inside the tile; -1 for a dropped slot.  Two
+// rounds of loads: ranks and expert ids, then the tile bases (branch-free,
+// so each round issues together: the gather measured 26.9 -> 26.0 us on
+// olmoe against per-slot loads).
 template <int KMAX, bool COH = false>
 __device__ __forceinline__ void token_slots(const Dims& d, const Work& w,
                                             const int32_t* __restrict__ idx, int t,

@@ -266,7 +266,8 @@ __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, con
   for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (slot[u][j] >= 0 && it[u].ok) v[u][j] = load_chunk(&y[(int64_t)slot[u][j] * d.chunks + it[u].c]);
+      if (slot[u][j] >= 0 && it[u].ok)
+        v[u][j] = load_chunk(&y[(int64_t)slot[u][j] * d.chunks + it[u].c]);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!it[u].ok) continue;

@@ -92,7 +92,8 @@ __device__ __forceinline__ void column_run(const int* s_mat, int W, int c, int b
 // Returns P (0 when W > NT: then each thread sums whole columns and s_part is
 // unused).  Ends with the block synchronised.
 template <int NT>
-__device__ __forceinline__ int column_parts(const int* s_mat, int W, int nblk, int* s_part, int* tot) {
+__device__ __forceinline__ int column_parts(const int* s_mat, int W, int nblk, int* s_part,
+                                            int* tot) {
   const int tid = threadIdx.x;
   if (W > NT) {
     for (int c = tid; c < W; c += NT) tot[c] = column_sum(s_mat, W, c, 0, nblk);
@@ -438,9 +439,9 @@ __device__ __forceinline__ void scan_band(const Dims& d, const Work& w, int band
   const int tid = threadIdx.x, E = d.E, R = d.R;
   const int t0 = band * d.tpb, nt = min(d.tpb, d.nblk - t0);
   const int row0 = band * d.band * d.k;
-  const int rows = scan_tiles<COH, NT>(w.tile_counts + (int64_t)t0 * E, w.tile_base + (int64_t)t0 * E,
-                              w.counts + (int64_t)band * E, w.expert_off + (int64_t)band * (E + 1),
-                              E, nt, row0, L.mat, s_tot, L.wsum, L.part);
+  const int rows = scan_tiles<COH, NT>(
+      w.tile_counts + (int64_t)t0 * E, w.tile_base + (int64_t)t0 * E, w.counts + (int64_t)band * E,
+      w.expert_off + (int64_t)band * (E + 1), E, nt, row0, L.mat, s_tot, L.wsum, L.part);
   int32_t* roff = w.rank_off + (int64_t)band * (R + 1);
   for (int r = tid; r <= R; r += NT) {
     const int first = r * d.ebase + min(r, d.erem);  // first expert of rank r
