@@ -37,8 +37,8 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags=(), out: str | None = None) -> str:
     """Compile every source into ``out`` (default LIB_PATH; always recompiles).
 
-    extra_flags: more hipcc flags, e.g. the -D tunables of move.hip
-    (MOE_GATHER_U, MOE_COMBINE_U, MOE_MOVE_WAVES, MOE_NT_STORE).
+    extra_flags: more hipcc flags (for instance -save-temps to keep the
+    gfx950 assembly).
     """
     out = LIB_PATH if out is None else out
     tmp = out + ".tmp"

@@ -42,48 +42,29 @@ __device__ __forceinline__ void st_plan(int32_t* p, int32_t v) {
 // loads below need no branch and all of them issue before the first wait).
 __device__ __forceinline__ int64_t slot_index(int64_t at, int j, int k) { return at + (j < k ? j : 0); }
 
-// Receive rows of a token's slots in two rounds of loads (token_slots).
-// The first round: in-tile ranks and expert ids of token t's slots.
-template <int KMAX, bool COH = false>
-__device__ __forceinline__ void token_slot_inputs(const Dims& d, const Work& w,
-                                                  const int32_t* __restrict__ idx, int t,
-                                                  int (&l)[KMAX], int (&e)[KMAX]) {
-  const int64_t at = (int64_t)t * d.k;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    const int64_t a = slot_index(at, j, d.k);
-    l[j] = ld_plan<COH>(&w.lr[a]);
-    e[j] = idx[a];
-  }
-}
-
-// The second round: the tile bases, and the slots' receive rows (-1 for a
-// dropped slot, and for every slot when `live` is false).
-template <int KMAX, bool COH = false>
-__device__ __forceinline__ void token_slot_rows(const Dims& d, const Work& w, bool live, int t,
-                                                const int (&l)[KMAX], const int (&e)[KMAX],
-                                                int (&slot)[KMAX]) {
-  const int b = t / d.tile;
-  int base[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j)
-    base[j] = ld_plan<COH>(&w.tile_base[b * d.E + min(max(e[j], 0), d.E - 1)]);
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) slot[j] = (live && j < d.k && l[j] >= 0) ? base[j] + l[j] : -1;
-}
-
 // Receive row of every slot of token t: the row of (tile, expert) from the
 // scan plus the slot's rank inside the tile; -1 for a dropped slot.  Two
 // rounds of loads: ranks and expert ids, then the tile bases (branch-free,
 // so each round issues together: the gather measured 26.9 -> 26.0 us on
 // olmoe against per-slot loads).
-template <int KMAX, bool COH = false>
+template <int KMAX>
 __device__ __forceinline__ void token_slots(const Dims& d, const Work& w,
                                             const int32_t* __restrict__ idx, int t,
                                             int (&slot)[KMAX]) {
+  const int64_t at = (int64_t)t * d.k;
   int l[KMAX], e[KMAX];
-  token_slot_inputs<KMAX, COH>(d, w, idx, t, l, e);
-  token_slot_rows<KMAX, COH>(d, w, true, t, l, e, slot);
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int64_t a = slot_index(at, j, d.k);
+    l[j] = w.lr[a];
+    e[j] = idx[a];
+  }
+  const int b = t / d.tile;
+  int base[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) base[j] = w.tile_base[b * d.E + min(max(e[j], 0), d.E - 1)];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) slot[j] = (j < d.k && l[j] >= 0) ? base[j] + l[j] : -1;
 }
 
 // Staging row feeding every slot of token t (node deduplication): the first

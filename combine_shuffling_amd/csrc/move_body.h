@@ -64,31 +64,38 @@ __device__ __forceinline__ u32x4 load_chunk(const u32x4* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// Buffer descriptor of the `bytes` bytes at p, or of an empty range when
+// `valid` is false: a buffer access outside the range is dropped (a store)
+// or reads zero (a load), so an access through it needs no branch.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, word 3 (gfx9 family)
+constexpr int kCacheNt = 1 << 1;          // buffer cache policy: streaming (nt)
+constexpr int kCacheSc1 = 1 << 4;         // buffer cache policy: device scope (sc1)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void* p, bool valid,
+                                                             int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, valid ? bytes : 0,
+                                           kBufferWord3);
+}
+
 // Row store that another block reads in the same launch (the banded
 // pipeline): chunk at byte `off` of row `row` (wave-uniform) of a [rows,
 // chunks] buffer when row < rows, a device-scope (sc1) store, written
 // through the per-XCD L2 to the coherence point so that the reader needs no
-// cache maintenance.  It goes through a buffer descriptor of the row (scalar
-// registers) with the lane's 32-bit offset, and it is issued for every row
-// and lane: the descriptor's range (0 for a row >= rows, the row's bytes
-// otherwise) discards a store that must not land, and so does a lane past
-// the row.  Loads and stores share one counter of operations in flight on
-// this GPU.  With the stores behind branches, or written as inline asm, or
-// with a 64-bit address register per store in that kernel short of
-// registers, the compiler waited for every operation in flight before each
-// store (the previous store included): banded pipeline olmoe 100.9 -> 95.2
-// us, qwen3 273 -> 255, nondiv 460 -> 412 with this store and the lookups
-// ahead of the row loads.  (The separate gather kernels keep plain branches
-// and global stores: the same store there made nondiv's gather 147 -> 186
-// us.)
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, word 3 (gfx9 family)
-constexpr int kCacheSc1 = 1 << 4;         // buffer cache policy: device scope (sc1)
+// cache maintenance.  It is issued for every row and lane, through a
+// descriptor of the row (scalar registers) with the lane's 32-bit offset:
+// the descriptor's range discards a store that must not land.  Loads and
+// stores share one counter of operations in flight on this GPU.  With the
+// stores behind branches, or written as inline asm, or with a 64-bit
+// address register per store in that kernel short of registers, the
+// compiler waited for every operation in flight before each store (the
+// previous store included): banded pipeline olmoe 100.9 -> 95.2 us, qwen3
+// 273 -> 255, nondiv 460 -> 412 with this store and the lookups ahead of
+// the row loads.  (The separate gather kernels keep plain branches and
+// global stores: the same store there made nondiv's gather 147 -> 186 us.)
 __device__ __forceinline__ void store_row_coherent(u32x4* base, int row, uint32_t rows,
                                                    int chunks, uint32_t off, u32x4 v) {
   const bool valid = (uint32_t)row < rows;
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      base + (int64_t)(valid ? row : 0) * chunks, 0, valid ? chunks * (int)sizeof(u32x4) : 0,
-      kBufferWord3);
+  const __amdgpu_buffer_rsrc_t r =
+      row_buffer(base + (int64_t)(valid ? row : 0) * chunks, valid, chunks * (int)sizeof(u32x4));
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCacheSc1);
 }
 
@@ -130,78 +137,99 @@ __device__ __forceinline__ int lane_pick(const int (&v)[KMAX], int lane) {
 }
 
 // Gather-send fused with scatter-recv for the wave-items of block-chunk blk.
-template <int KMAX, int U, bool COH = false>
+template <int KMAX, int U>
 __device__ __forceinline__ void gather_chunk(const Dims& d, const int32_t* idx, const u32x4* x,
                                              u32x4* recv, const Work& w, int blk, int base,
                                              int limit) {
   const int lane = threadIdx.x % kWave;
   const uint32_t rows = (uint32_t)(d.T * d.k);
   const bool keep = keep_rows(rows, 2 * d.H);
-  // Every wave-item's slot lookups, then every row load (x after the slot
-  // loads: nondiv gather 152.6 -> 158.8 us the other way round).  With
-  // device-scope plan reads (COH, the banded pipeline) the lookups are vector
-  // loads, which complete in issue order: a lookup issued after a row load
-  // would wait for that row, so all of them go first, in two rounds for all
-  // items (a dead item looks up token 0: t is 0 there).
+  // Every wave-item's slot lookups (scalar loads, with a counter of their
+  // own), then every row load (x after the slot loads: nondiv gather 152.6 ->
+  // 158.8 us the other way round).
   Item it[U];
   int slot[U][KMAX];
-  if constexpr (COH) {
-    int l[U][KMAX], e[U][KMAX];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      it[u] = wave_item<U>(d, blk, base, limit, u);
-      token_slot_inputs<KMAX, COH>(d, w, idx, it[u].t, l[u], e[u]);
-    }
+  for (int u = 0; u < U; ++u) {
+    it[u] = wave_item<U>(d, blk, base, limit, u);
+    if (it[u].live) {
+      token_slots<KMAX>(d, w, idx, it[u].t, slot[u]);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      token_slot_rows<KMAX, COH>(d, w, it[u].live, it[u].t, l[u], e[u], slot[u]);
-  } else {  // scalar lookups (their own counter): one item after another
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      it[u] = wave_item<U>(d, blk, base, limit, u);
-      if (it[u].live) {
-        token_slots<KMAX>(d, w, idx, it[u].t, slot[u]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) slot[u][j] = -1;
-      }
+      for (int j = 0; j < KMAX; ++j) slot[u][j] = -1;
     }
   }
   __builtin_amdgcn_sched_barrier(0);
   u32x4 v[U];
-  if constexpr (COH) {
-    // every load and row store issued, the slot stores last (store_row_coherent)
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      v[u] = load_x_chunk(&x[it[u].ok ? (int64_t)it[u].t * d.chunks + it[u].c : 0]);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t off = (uint32_t)it[u].c * (uint32_t)sizeof(u32x4);
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        store_row_coherent(recv, __builtin_amdgcn_readfirstlane(slot[u][j]), rows, d.chunks, off,
-                           v[u]);
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
-  }
+  for (int u = 0; u < U; ++u)
+    if (it[u].ok) v[u] = load_x_chunk(&x[(int64_t)it[u].t * d.chunks + it[u].c]);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     // The first segment of a row publishes the token's slots.
     if (it[u].live && it[u].c == lane && lane < d.k) {
       const int s = lane_pick<KMAX>(slot[u], lane);
-      st_plan<COH>(&w.slot_of[(int64_t)it[u].t * d.k + lane], s);
+      w.slot_of[(int64_t)it[u].t * d.k + lane] = s;
       if ((uint32_t)s < rows) w.row_src[s] = it[u].t;
     }
-    if constexpr (!COH) {
-      if (it[u].ok) {
+    if (it[u].ok) {
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j)
-          if ((uint32_t)slot[u][j] < rows)
-            store_row(&recv[(int64_t)slot[u][j] * d.chunks + it[u].c], v[u], keep);
-      }
+      for (int j = 0; j < KMAX; ++j)
+        if ((uint32_t)slot[u][j] < rows)
+          store_row(&recv[(int64_t)slot[u][j] * d.chunks + it[u].c], v[u], keep);
+    }
+  }
+}
+
+// The gather of the banded pipeline, whose plan arrays are read with
+// device-scope loads.  Those are vector loads, which complete in issue order
+// and share one counter with the row loads and stores; a wave-uniform
+// lookup result also has to land before it can move to a scalar register.
+// So lane j (< k) of the wave looks up slot j of each wave-item, all items'
+// lookups in two rounds (ranks and expert ids, then tile bases), and the
+// slots are read out of the lanes (v_readlane) once they have all landed:
+// two round trips a ticket, however many items.  Then every x load, then
+// every row store, unconditional (store_row_coherent).
+template <int KMAX, int U>
+__device__ __forceinline__ void gather_chunk_lanes(const Dims& d, const int32_t* idx,
+                                                   const u32x4* x, u32x4* recv, const Work& w,
+                                                   int blk, int base, int limit) {
+  const int lane = threadIdx.x % kWave;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  Item it[U];
+  int l[U], e[U], slot[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    it[u] = wave_item<U>(d, blk, base, limit, u);
+    const bool has = it[u].live && lane < d.k;
+    const int64_t a = has ? (int64_t)it[u].t * d.k + lane : 0;
+    l[u] = ld_plan<true>(&w.lr[a]);
+    e[u] = idx[a];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int b = it[u].t / d.tile;
+    const int tb = ld_plan<true>(&w.tile_base[b * d.E + min(max(e[u], 0), d.E - 1)]);
+    slot[u] = it[u].live && lane < d.k && l[u] >= 0 ? tb + l[u] : -1;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    v[u] = load_x_chunk(&x[it[u].ok ? (int64_t)it[u].t * d.chunks + it[u].c : 0]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t off = (uint32_t)it[u].c * (uint32_t)sizeof(u32x4);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      store_row_coherent(recv, __builtin_amdgcn_readlane(slot[u], j), rows, d.chunks, off, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    // The first segment of a row publishes the token's slots.
+    if (it[u].live && it[u].c == lane && lane < d.k) {
+      st_plan<true>(&w.slot_of[(int64_t)it[u].t * d.k + lane], slot[u]);
+      if ((uint32_t)slot[u] < rows) w.row_src[slot[u]] = it[u].t;
     }
   }
 }
@@ -231,7 +259,7 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 // Weighted combine for the wave-items of block-chunk blk (W waves a block).
-template <int KMAX, int U, bool F32OUT, bool COH = false, int W = kWaves>
+template <int KMAX, int U, bool F32OUT, int W = kWaves>
 __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, const float* wts,
                                               const int32_t* slot_of, void* out, int blk, int base,
                                               int limit) {
@@ -251,7 +279,7 @@ __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, con
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {  // no branch between the loads: they issue together
       const int64_t a = slot_index(at, j, d.k);
-      sj[j] = ld_plan<COH>(&slot_of[a]);
+      sj[j] = slot_of[a];
       wt[j] = wts[a];
     }
 #pragma unroll
@@ -301,12 +329,93 @@ __device__ __forceinline__ void combine_chunk(const Dims& d, const u32x4* y, con
   }
 }
 
+// The combine of the banded pipeline: slot_of is read with device-scope
+// loads, so, as in gather_chunk_lanes, lane j (< k) looks up slot j and
+// weight j of each wave-item, one round for all items, and the slots and
+// weights are read out of the lanes.  The receive rows are read through a
+// descriptor of the row (an empty one for a dropped slot; a lane past the
+// row reads zero) and the outputs are written through one of the output
+// row, so no load or store sits behind a branch.
+template <int KMAX, int U, bool F32OUT>
+__device__ __forceinline__ void combine_chunk_lanes(const Dims& d, const u32x4* y,
+                                                    const float* wts, const int32_t* slot_of,
+                                                    void* out, int blk, int base, int limit) {
+  const int lane = threadIdx.x % kWave;
+  const uint32_t rows = (uint32_t)(d.T * d.k);
+  const int row_bytes = d.chunks * (int)sizeof(u32x4);
+  Item it[U];
+  int slot[U];
+  float wt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    it[u] = wave_item<U>(d, blk, base, limit, u);
+    const bool has = it[u].live && lane < d.k;
+    const int64_t a = has ? (int64_t)it[u].t * d.k + lane : 0;
+    slot[u] = ld_plan<true>(&slot_of[a]);
+    wt[u] = wts[a];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool has = it[u].live && lane < d.k && (uint32_t)slot[u] < rows;
+    slot[u] = has ? slot[u] : -1;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 v[U][KMAX];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int off = it[u].c * (int)sizeof(u32x4);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const int s = __builtin_amdgcn_readlane(slot[u], j);
+      const __amdgpu_buffer_rsrc_t r = row_buffer(y + (int64_t)(s >= 0 ? s : 0) * d.chunks,
+                                                  s >= 0, row_bytes);
+      v[u][j] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCacheNt);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (__builtin_amdgcn_readlane(slot[u], j) < 0) continue;  // wave-uniform
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[u]), j));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(v[u][j][q] << 16);
+        const float hi = __uint_as_float(v[u][j][q] & 0xffff0000u);
+        acc[2 * q] = __builtin_fmaf(wj, lo, acc[2 * q]);
+        acc[2 * q + 1] = __builtin_fmaf(wj, hi, acc[2 * q + 1]);
+      }
+    }
+    const int64_t row = it[u].live ? it[u].t : 0;
+    if constexpr (F32OUT) {
+      const __amdgpu_buffer_rsrc_t r = row_buffer(reinterpret_cast<f32x4*>(out) + row * 2 * d.chunks,
+                                                  it[u].live, 2 * row_bytes);
+      const f32x4 a = {acc[0], acc[1], acc[2], acc[3]};
+      const f32x4 b = {acc[4], acc[5], acc[6], acc[7]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), r, 2 * it[u].c * 16, 0,
+                                             kCacheNt);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), r, 2 * it[u].c * 16 + 16,
+                                             0, kCacheNt);
+    } else {
+      const __amdgpu_buffer_rsrc_t r =
+          row_buffer(reinterpret_cast<u32x4*>(out) + row * d.chunks, it[u].live, row_bytes);
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
+      __builtin_amdgcn_raw_buffer_store_b128(o, r, it[u].c * 16, 0, kCacheNt);
+    }
+  }
+}
+
 // Wave-items [base, limit) of the batch (one launch of at most kMaxLaunchItems).
 template <int KMAX, int U, bool F32OUT>
 __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(
     Dims d, const u32x4* __restrict__ y, const float* __restrict__ wts,
     const int32_t* __restrict__ slot_of, void* __restrict__ out, int base, int limit) {
-  combine_chunk<KMAX, U, F32OUT, false, kCombineWaves>(d, y, wts, slot_of, out, blockIdx.x, base,
+  combine_chunk<KMAX, U, F32OUT, kCombineWaves>(d, y, wts, slot_of, out, blockIdx.x, base,
                                                        limit);
 }
 

@@ -165,11 +165,11 @@ __global__ __launch_bounds__(kBlock) void pipeline_kernel(Dims d, const int32_t*
         case kCount: count_tile<KMAX, true>(d, idx, w, t.band * d.tpb + t.r, cl); break;
         case kScan: scan_band<true>(d, w, t.band, sl); break;
         case kGather:
-          gather_chunk<KMAX, kPipeGatherU, true>(d, idx, x, recv, w, t.r, t0 * d.segs,
+          gather_chunk_lanes<KMAX, kPipeGatherU>(d, idx, x, recv, w, t.r, t0 * d.segs,
                                                  t1 * d.segs);
           break;
         default:
-          combine_chunk<KMAX, kPipeCombineU, F32OUT, true>(d, recv, wts, w.slot_of, out, t.r,
+          combine_chunk_lanes<KMAX, kPipeCombineU, F32OUT>(d, recv, wts, w.slot_of, out, t.r,
                                                            t0 * d.segs, t1 * d.segs);
           break;
       }
