@@ -9,6 +9,8 @@ same plan: the same kernels' arithmetic in the same order, so receive rows,
 plan arrays and both output types are compared bit for bit.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -174,6 +176,35 @@ def test_pipeline_bad_routing_flagged(dev):
     assert bool((recv_full[plan.recv_rows:] == -1).all())
     slot_of = plan.read("slot_of").reshape(1024, 4)
     assert slot_of[700, 1] == -1 and slot_of[100, 2] == -1
+
+
+def test_pipeline_bad_routing_output(dev):
+    """A dropped slot between kept ones (an id out of range, a repeat): the
+    pipeline's combine skips it as the separate combine does, so both output
+    types match the separate calls bit for bit, and every token is its kept
+    slots' weighted sum (a dropped slot weighs zero)."""
+    batch = gen.make_batch(gen.custom(1024, 64, 16, 4, 4, 4, seed=5))
+    idx = batch.topk_idx.copy()
+    idx[700, 1] = 99
+    idx[100, 2] = idx[100, 0]
+    bad = dataclasses.replace(batch, topk_idx=idx)
+    for out_dtype in (torch.bfloat16, torch.float32):
+        plan_s, recv_s, out_s = run_separate(bad, 256, dev, out_dtype)
+        plan_p, recv_p, out_p = run_pipeline(bad, 256, dev, out_dtype)
+        assert plan_s.status() == 3 and plan_p.status() == 3
+        slot_of = plan_p.read("slot_of").reshape(1024, 4)
+        assert np.array_equal(slot_of, plan_s.read("slot_of").reshape(1024, 4))
+        assert sorted(map(tuple, np.argwhere(slot_of < 0))) == [(100, 2), (700, 1)]
+        y = bits(recv_p)
+        assert np.array_equal(y, bits(recv_s))
+        f32 = out_dtype == torch.float32
+        a = out_p.cpu().numpy().view(np.uint32) if f32 else bits(out_p)
+        b = out_s.cpu().numpy().view(np.uint32) if f32 else bits(out_s)
+        assert np.array_equal(a, b), "pipeline out != separate"
+        kept = slot_of >= 0
+        w = np.where(kept, batch.topk_w, np.float32(0))
+        check_combine(out_p.cpu().numpy() if f32 else a, y, w, np.where(kept, slot_of, 0), f32,
+                      "bad routing")
 
 
 def test_pipeline_empty_batch(dev):
