@@ -120,7 +120,7 @@ __device__ __forceinline__ Item wave_item(const Dims& d, int blk, int base, int 
   Item it;
   it.live = g < limit;
   it.t = it.live ? g / d.segs : 0;
-  const int seg = g - it.t * d.segs;
+  const int seg = it.live ? g - it.t * d.segs : 0;  // a dead item: token 0, segment 0
   it.c = seg * kWave + lane;
   it.ok = it.live && it.c < d.chunks;
   return it;
