@@ -85,10 +85,13 @@ MAX_SETS = 256
 METRIC = "dispatch+combine effective GB/s and % of HBM peak, 1 MI355X"
 SCHEDULES = ("serial", "two_in_flight", "staggered", "plan_ahead")
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("combine_shuffling_amd/csrc/move.hip", "combine_shuffling_amd/csrc/move_body.h",
-                  "combine_shuffling_amd/csrc/pipeline.hip", "combine_shuffling_amd/csrc/plan_body.h",
+# Each kernel is compiled in one translation unit (its .hip file plus the
+# headers every unit includes); a traffic summary is current for a kernel
+# while that unit's sources are unchanged.
+KERNEL_HEADERS = ("combine_shuffling_amd/csrc/move_body.h", "combine_shuffling_amd/csrc/plan_body.h",
                   "combine_shuffling_amd/csrc/moe_device.h",
-                  "combine_shuffling_amd/csrc/moe_internal.h")
+                  "combine_shuffling_amd/csrc/moe_internal.h", "include/moe_shuffle.h")
+KERNEL_UNITS = ("move.hip", "pipeline.hip", "route_plan.hip")
 # Kernels that carry no payload rows (plan metadata, counters).
 PLAN_KERNELS = ("route_count_kernel", "route_scan_kernel", "route_assign_kernel",
                 "traffic_clear_kernel", "traffic_kernel", "counters_clear_kernel")
@@ -143,9 +146,20 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
-def kernel_source_hash():
+def kernel_unit(kernel):
+    """The .hip file that defines `kernel` (short or full name)."""
+    short = _short(kernel).split("<")[0]
+    if short in ("pipeline_kernel", "counters_clear_kernel"):
+        return "pipeline.hip"
+    if short.startswith(("route_", "traffic_")):
+        return "route_plan.hip"
+    return "move.hip"
+
+
+def kernel_source_hash(unit):
+    """Hash of the sources one translation unit is compiled from."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in ("combine_shuffling_amd/csrc/" + unit,) + KERNEL_HEADERS:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -225,7 +239,9 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out, cop
         kernels[_short(name)] = {
             "fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "dispatches": n,
             "traffic_bytes": int(round((fk * f_fetch + wk * f_write) * 1024))}
-    summary = {"source_hash": kernel_source_hash(), "copy_kernel": copy_name[:80],
+    units = sorted({kernel_unit(k) for k in kernels})
+    summary = {"source_hashes": {u: kernel_source_hash(u) for u in units},
+               "copy_kernel": copy_name[:80],
                "copy_known_kib": known_kib, "copy_fetch_kib": round(cf[copy_name][0], 1),
                "copy_write_kib": round(cw[copy_name][0], 1), "fetch_factor": round(f_fetch, 5),
                "write_factor": round(f_write, 5), "kernels": kernels, "command": command}
@@ -256,7 +272,8 @@ def recorded_traffic(workload, kernel):
         return None, None
     text = "".join(ln for ln in open(path) if not ln.startswith("#"))
     s = json.loads(text)
-    if s.get("source_hash") != kernel_source_hash():
+    unit = kernel_unit(kernel)
+    if s.get("source_hashes", {}).get(unit) != kernel_source_hash(unit):
         return None, None
     for name, v in s["kernels"].items():
         if name.split("<")[0] == kernel:

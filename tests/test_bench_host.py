@@ -111,7 +111,8 @@ def test_pmc_summary_scales_by_the_copy_kernel(tmp_path):
     k = s["kernels"]["combine_kernel<8, 1, false>"]
     assert k["dispatches"] == 2
     assert k["traffic_bytes"] == int((101.0 * 2 + 50.0) * 1024)
-    assert s["source_hash"] == bench.kernel_source_hash() and s["command"] == "cmd"
+    assert s["source_hashes"] == {"move.hip": bench.kernel_source_hash("move.hip")}
+    assert s["command"] == "cmd"
 
 
 def test_trace_summary(tmp_path):
@@ -126,9 +127,11 @@ def test_trace_summary(tmp_path):
 
 
 def test_traffic_lookup_needs_current_sources(tmp_path, monkeypatch):
-    summary = {"source_hash": bench.kernel_source_hash(),
+    summary = {"source_hashes": {"move.hip": bench.kernel_source_hash("move.hip"),
+                                 "pipeline.hip": "0" * 16},  # changed since
                "kernels": {"gather_kernel<8, 1>": {"traffic_bytes": 123},
-                           "combine_kernel<8, 1, false>": {"traffic_bytes": 456}}}
+                           "combine_kernel<8, 1, false>": {"traffic_bytes": 456},
+                           "pipeline_kernel<8, false>": {"traffic_bytes": 789}}}
     (tmp_path / "hbm_traffic_w.txt").write_text("# header\n" + json.dumps(summary))
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     assert bench.recorded_traffic("w", "gather_kernel") == ("gather_kernel<8, 1>", 123)
@@ -136,7 +139,18 @@ def test_traffic_lookup_needs_current_sources(tmp_path, monkeypatch):
     assert bench.recorded_traffic("w", "combine_kernel") == ("combine_kernel<8, 1, false>", 456)
     assert bench.recorded_traffic("w", "stage_a_kernel") == (None, None)
     assert bench.recorded_traffic("missing", "gather_kernel") == (None, None)
-    summary["source_hash"] = "0" * 16             # the kernels changed since
+    assert bench.recorded_traffic("w", "pipeline_kernel") == (None, None)
+    summary["source_hashes"]["move.hip"] = "0" * 16   # the kernels changed since
     (tmp_path / "hbm_traffic_w.txt").write_text(json.dumps(summary))
     assert bench.recorded_traffic("w", "gather_kernel") == (None, None)
+
+
+def test_kernel_units():
+    assert bench.kernel_unit("void moe::(anonymous namespace)::pipeline_kernel<8, false>(m") \
+        == "pipeline.hip"
+    assert bench.kernel_unit("counters_clear_kernel") == "pipeline.hip"
+    assert bench.kernel_unit("route_count_kernel<8>") == "route_plan.hip"
+    assert bench.kernel_unit("stage_ab_kernel<8>") == "move.hip"
+    hashes = {u: bench.kernel_source_hash(u) for u in bench.KERNEL_UNITS}
+    assert len(set(hashes.values())) == 3
 
