@@ -100,6 +100,7 @@ Layout make_layout(const Dims& d) {
   take(l.row_src, tk);
   take(l.tile_fcounts, d.dedup ? (int64_t)d.nblk * d.fkeys : 1);
   take(l.tile_fbase, d.dedup ? (int64_t)d.nblk * d.fkeys : 1);
+  take(l.tile_ncounts, d.load_aware ? (int64_t)d.nblk * d.N : 1);
   take(l.fwd, d.dedup ? (int64_t)d.R * d.N : 1);
   take(l.stage_off, d.dedup ? d.R + 1 : 1);
   take(l.fkey, fk);
@@ -131,6 +132,7 @@ Work bind_work(const Layout& l, void* base) {
   w.row_src = p(l.row_src);
   w.tile_fcounts = p(l.tile_fcounts);
   w.tile_fbase = p(l.tile_fbase);
+  w.tile_ncounts = p(l.tile_ncounts);
   w.fwd = p(l.fwd);
   w.stage_off = p(l.stage_off);
   w.fkey = p(l.fkey);

@@ -83,7 +83,7 @@ struct Dims {
   int32_t fused_scan;     // the single-hop gather scans the tile counts itself (small plans)
   int32_t dedup;          // MOE_FLAG_NODE_DEDUP set
   int32_t load_aware;     // MOE_FLAG_LOAD_AWARE_FORWARDERS set
-  int32_t fkeys;          // staging keys: forwarders (R), or (owner, node) pairs (R * N)
+  int32_t fkeys;          // staging keys: forwarders (R), or (node, owner) pairs n * R + s (R * N)
   int32_t chunks;         // 16-byte chunks per row = H / 8
   int32_t segs;           // 64-chunk row segments per row = ceil(chunks / 64)
   int32_t smax;           // staging rows allocated (T * min(k, N) with dedup, else 0)
@@ -105,6 +105,7 @@ struct Work {
   int32_t* row_src;       // [T * k]     receive row -> token
   int32_t* tile_fcounts;  // [nblk * fkeys] staging rows per (tile, key)                 (dedup)
   int32_t* tile_fbase;    // [nblk * fkeys] first staging row of (tile, key)              (dedup)
+  int32_t* tile_ncounts;  // [nblk * N]  staging rows per (tile, node)        (load-aware forwarders)
   int32_t* fwd;           // [R * N]     forwarder of (owner s, node n) at s * N + n      (dedup)
   int32_t* stage_off;     // [R + 1]     first staging row of each forwarder               (dedup)
   int32_t* fkey;          // [T * k]     staging key of the node's first slot; -2-j on later
@@ -125,8 +126,8 @@ inline bool fp8_fused_scan(const Dims& d) { return d.fused_scan && d.E <= kWave;
 // Byte offsets of each Work array from the workspace base, and the total.
 struct Layout {
   size_t ctrl, band_status, pipe, tile_flags, tile_counts, tile_base, counts, expert_off, rank_off, lr, slot_of,
-      row_src, tile_fcounts, tile_fbase, fwd, stage_off, fkey, flr, stage_of, stage_src, send_rows,
-      send_copies, node_copies, total;
+      row_src, tile_fcounts, tile_fbase, tile_ncounts, fwd, stage_off, fkey, flr, stage_of, stage_src,
+      send_rows, send_copies, node_copies, total;
 };
 
 Layout make_layout(const Dims& d);

@@ -276,14 +276,15 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
       for (int i = tid; i < kPlanWaves * K; i += kPlanBlock) s_mask[i] = 0;
       // Key of the first slot of each distinct destination node: the
       // forwarder rank n*G + owner(t) % G, or with load-aware forwarders the
-      // (owner, node) pair owner*N + n (its forwarder is chosen by the scan).
-      // Later slots of the node point back to the first.
+      // (owner, node) pair n*R + owner (its forwarder is chosen by the scan).
+      // Both are node-major, so a node's keys are contiguous.  Later slots
+      // of the node point back to the first.
       const int owner = live ? split_part(t, d.tbase, d.trem) : 0;
       int nd[KMAX], key[KMAX];
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         nd[j] = e[j] >= 0 ? s_node[e[j]] : -1;
-        key[j] = nd[j] < 0 ? -1 : d.load_aware ? owner * d.N + nd[j] : nd[j] * d.G + owner % d.G;
+        key[j] = nd[j] < 0 ? -1 : d.load_aware ? nd[j] * R + owner : nd[j] * d.G + owner % d.G;
 #pragma unroll
         for (int jj = j - 1; jj >= 0; --jj)
           if (nd[j] >= 0 && nd[jj] == nd[j]) key[j] = -2 - jj;
@@ -313,48 +314,86 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
   for (int i = tid; i < E; i += kPlanBlock) st_plan<COH>(&w.tile_counts[tile * E + i], s_run[i]);
   if (d.dedup)
     for (int i = tid; i < K; i += kPlanBlock) st_plan<COH>(&w.tile_fcounts[tile * K + i], s_frun[i]);
+  if (d.load_aware) {
+    // The tile's staging rows per node (the sum of the node's R keys, one
+    // wave a node): the scan places the nodes one after another from these,
+    // so that each node's keys can be scanned by a block of their own.
+    for (int n = wv; n < d.N; n += kPlanWaves) {
+      int v = 0;
+      for (int s = lane; s < R; s += kWave) v += s_frun[n * R + s];
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0) st_plan<COH>(&w.tile_ncounts[tile * d.N + n], v);
+    }
+  }
   if (tid == 0) st_plan<COH>(&w.tile_flags[tile], s_bad);
 }
 
 // Load-aware forwarders (FUSCO article, "load balancing and cross-node
 // deduplication": forwarding follows the load and is spread evenly over a
-// node's GPUs).  Keys are (owner s, node n) pairs, c = s * N + n; the load of
+// node's GPUs).  Keys are (owner s, node n) pairs, c = n * R + s; the load of
 // a pair is its staging rows.  In each node the owners are ranked by load
 // (more first, ties to the lower owner) and dealt to the node's G ranks in
 // snake order, so the forwarder with local index g gets the R / G owners of
 // ranks lap * G + g (even laps) and lap * G + G - 1 - g (odd laps).  Staging
 // rows stay ordered by (forwarder, token); owners hold ascending token
-// ranges, so inside a forwarder that is (owner, token).  Each pair's first
-// row is its forwarder's first row plus the loads of the forwarder's owners
-// with a lower id: R / G terms, read through per-node owner-by-rank and
-// load-by-rank tables in LDS.  With R <= 64 a wave takes a node, one lane an
-// owner: a lane's rank counts the lanes ahead of it (R compares against
-// values read from the other lanes), and only that wave reads the node's
-// tables, so no block barrier is needed between writing and reading them.
-// Larger R ranks one pair a thread against the LDS load table.  Writes the
-// forwarder table, stage_off and the (tile, pair) bases; returns D.  Needs
-// R * N <= 1024.
+// ranges, so inside a forwarder that is (owner, token).
+//
+// Node n by the whole block: a node's forwarders are ranks n * G .. n * G +
+// G - 1, so its staging rows follow those of nodes 0 .. n - 1, whose number
+// comes from the count's per-(tile, node) sums; the rest needs only node n's
+// columns of the [tiles x pairs] matrix (R consecutive ones of the R * N), so
+// the nodes are scanned by blocks of their own, side by side.  Each pair's first row is its
+// forwarder's first row plus the loads of the forwarder's owners with a lower
+// id: R / G terms, read through the node's owner-by-rank and load-by-rank
+// tables.  With R <= 64 one wave ranks the owners, one lane an owner: a
+// lane's rank counts the lanes ahead of it (R compares against values read
+// from the other lanes).  Larger R ranks one owner a thread against the LDS
+// load table.  Writes node n's entries of the forwarder table, stage_off and
+// the (tile, pair) bases; the block of node 0 also writes D to ctrl.  Needs
+// R * N <= 1024 (so R <= 512: load-aware plans have two nodes or more).
 template <bool COH = false, int NT = kPlanBlock>
-__device__ __forceinline__ int scan_load_aware(const Dims& d, const Work& w, int* s_mat, int* s_tot,
-                                               int* s_wsum, int* s_part) {
-  __shared__ int s_load[MOE_MAX_EXPERTS];   // per pair
-  __shared__ int s_rank[MOE_MAX_EXPERTS];   // R > 64: per pair, its owner's rank in the node;
-                                            // R <= 64: per node, load of rank r at n * R + r
-  __shared__ int s_order[MOE_MAX_EXPERTS];  // per node n: owner of rank r at n * R + r
-  __shared__ int s_first[MOE_MAX_EXPERTS];  // per pair: first staging row
-  __shared__ int s_fwd[MOE_MAX_EXPERTS];    // R <= 64: per pair, its forwarder
-  const int tid = threadIdx.x, R = d.R, N = d.N, G = d.G, K = d.fkeys, nblk = d.nblk;
-  const int laps = R / G;
-#pragma unroll 16
-  for (int i = tid; i < K * nblk; i += NT) s_mat[i] = ld_plan<COH>(&w.tile_fcounts[i]);
+__device__ __forceinline__ void scan_load_aware(const Dims& d, const Work& w, int n, int* s_mat,
+                                                int* s_tot, int* s_wsum, int* s_part) {
+  constexpr int kMaxOwners = MOE_MAX_EXPERTS / 2;
+  __shared__ int s_load[kMaxOwners];   // per owner: its staging rows in node n
+  __shared__ int s_lbr[kMaxOwners];    // per rank: load of the owner of that rank
+  __shared__ int s_order[kMaxOwners];  // per rank: owner of that rank
+  __shared__ int s_rank[kMaxOwners];   // R > 64: per owner, its rank
+  __shared__ int s_first[kMaxOwners];  // per owner: first staging row of (owner, n)
+  __shared__ int s_g[kMaxOwners];      // per owner: local index of its forwarder
+  __shared__ int s_red[2];             // staging rows of nodes before n, of all nodes
+  const int tid = threadIdx.x, lane = tid % kWave, R = d.R, N = d.N, G = d.G, K = d.fkeys;
+  const int nblk = d.nblk, laps = R / G;
+  if (tid < 2) s_red[tid] = 0;
+  // Node n's columns as a [tiles x owners] matrix, and the per-(tile, node)
+  // sums, all loaded before any is used.
+#pragma unroll 4
+  for (int i = tid; i < nblk * R; i += NT) {
+    const int b = i / R, s = i - b * R;
+    s_mat[i] = ld_plan<COH>(&w.tile_fcounts[(int64_t)b * K + n * R + s]);
+  }
+  int before = 0, all = 0;
+  for (int i = tid; i < nblk * N; i += NT) {
+    const int v = ld_plan<COH>(&w.tile_ncounts[i]);
+    all += v;
+    before += (i % N) < n ? v : 0;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    before += __shfl_xor(before, o);
+    all += __shfl_xor(all, o);
+  }
   __syncthreads();
-  const int P = column_parts<NT>(s_mat, K, nblk, s_part, s_load);
-  int staged;
+  if (lane == 0 && all != 0) {
+    atomicAdd(&s_red[0], before);
+    atomicAdd(&s_red[1], all);
+  }
+  const int P = column_parts<NT>(s_mat, R, nblk, s_part, s_load);
   if (R <= kWave) {
-    const int lane = tid % kWave;
-    for (int n = tid / kWave; n < N; n += NT / kWave) {
+    if (tid < kWave) {
       const bool live = lane < R;
-      const int l = live ? s_load[lane * N + n] : 0;
+      const int l = live ? s_load[lane] : 0;
       // One key orders by load, then owner: a pair's load is at most the
       // owner's ceil(T / R) tokens, so l * R + R - 1 - lane < 2^32 and keys
       // are distinct.  Lanes past R hold key 0, which outranks no one.
@@ -365,75 +404,87 @@ __device__ __forceinline__ int scan_load_aware(const Dims& d, const Work& w, int
         rank += (uint32_t)__builtin_amdgcn_readlane((int)key, j) > key ? 1 : 0;
       // The node's owners and loads by rank; only this wave reads them.
       if (live) {
-        s_order[n * R + rank] = lane;
-        s_rank[n * R + rank] = l;
+        s_order[rank] = lane;
+        s_lbr[rank] = l;
       }
       __builtin_amdgcn_wave_barrier();
       if (live) {
         const int lap = rank / G, pos = rank - lap * G;
         const int g = (lap & 1) ? G - 1 - pos : pos;
-        int tot = 0, before = 0;
+        int tot = 0, bef = 0;
         for (int l2 = 0; l2 < laps; ++l2) {
-          const int r = n * R + l2 * G + ((l2 & 1) ? G - 1 - g : g);
-          const int v = s_rank[r];
+          const int r = l2 * G + ((l2 & 1) ? G - 1 - g : g);
+          const int v = s_lbr[r];
           tot += v;
-          before += s_order[r] < lane ? v : 0;
+          bef += s_order[r] < lane ? v : 0;
         }
-        if (lap == 0) s_tot[n * G + g] = tot;
-        s_first[lane * N + n] = before;
-        s_fwd[lane * N + n] = n * G + g;
+        if (lap == 0) s_tot[g] = tot;
+        s_first[lane] = bef;
+        s_g[lane] = g;
       }
-    }
-    __syncthreads();
-    staged = block_exclusive_scan<NT>(s_tot, R, s_wsum);
-    for (int f = tid; f <= R; f += NT) w.stage_off[f] = f < R ? s_tot[f] : staged;
-    for (int c = tid; c < K; c += NT) {
-      const int f = s_fwd[c];
-      s_first[c] += s_tot[f];
-      w.fwd[c] = f;
     }
   } else {
-    for (int c = tid; c < K; c += NT) {
-      const int s = c / N, n = c - (c / N) * N, l = s_load[c];
+    for (int s = tid; s < R; s += NT) {
+      const int l = s_load[s];
       int rank = 0;
       for (int s2 = 0; s2 < R; ++s2) {
-        const int l2 = s_load[s2 * N + n];
+        const int l2 = s_load[s2];
         rank += (l2 > l || (l2 == l && s2 < s)) ? 1 : 0;
       }
-      s_rank[c] = rank;
-      s_order[n * R + rank] = s;
+      s_rank[s] = rank;
+      s_order[rank] = s;
     }
     __syncthreads();
-    // owner of the forwarder with local index g in node n, lap `lap`
-    auto owner = [&](int n, int g, int lap) {
-      return s_order[n * R + lap * G + ((lap & 1) ? G - 1 - g : g)];
-    };
-    for (int f = tid; f < R; f += NT) {
-      const int n = f / G, g = f - n * G;
+    // owner of the forwarder with local index g, lap `lap`
+    auto owner = [&](int g, int lap) { return s_order[lap * G + ((lap & 1) ? G - 1 - g : g)]; };
+    for (int g = tid; g < G; g += NT) {
       int tot = 0;
-      for (int lap = 0; lap < laps; ++lap) tot += s_load[owner(n, g, lap) * N + n];
-      s_tot[f] = tot;
+      for (int lap = 0; lap < laps; ++lap) tot += s_load[owner(g, lap)];
+      s_tot[g] = tot;
     }
-    __syncthreads();
-    staged = block_exclusive_scan<NT>(s_tot, R, s_wsum);
-    for (int f = tid; f <= R; f += NT) w.stage_off[f] = f < R ? s_tot[f] : staged;
-    for (int c = tid; c < K; c += NT) {
-      const int s = c / N, n = c - (c / N) * N, rank = s_rank[c];
-      const int lap = rank / G, pos = rank - lap * G;
+    for (int s = tid; s < R; s += NT) {
+      const int rank = s_rank[s], lap = rank / G, pos = rank - lap * G;
       const int g = (lap & 1) ? G - 1 - pos : pos;
-      int first = s_tot[n * G + g];
+      int bef = 0;
       for (int l2 = 0; l2 < laps; ++l2) {
-        const int o = owner(n, g, l2);
-        first += o < s ? s_load[o * N + n] : 0;
+        const int o = owner(g, l2);
+        bef += o < s ? s_load[o] : 0;
       }
-      s_first[c] = first;
-      w.fwd[c] = n * G + g;
+      s_first[s] = bef;
+      s_g[s] = g;
     }
   }
   __syncthreads();
-  column_bases<COH, NT>(s_mat, K, nblk, P, s_part, w.tile_fbase, [&](int c) { return s_first[c]; });
+  const int node_first = s_red[0], staged = s_red[1];
+  block_exclusive_scan<NT>(s_tot, G, s_wsum);  // the node's forwarders, from the node's first row
+  for (int g = tid; g < G; g += NT) w.stage_off[n * G + g] = node_first + s_tot[g];
+  if (tid == 0 && n == N - 1) w.stage_off[R] = staged;
+  if (tid == 0 && n == 0) w.ctrl[kCtrlStaged] = staged;
+  for (int s = tid; s < R; s += NT) {
+    const int g = s_g[s];
+    s_first[s] += node_first + s_tot[g];
+    w.fwd[s * N + n] = n * G + g;
+  }
   __syncthreads();
-  return staged;
+  // First staging row of every (tile, pair) of node n: column s of the
+  // node's matrix is pair n * R + s of the full one.
+  if (P == 0) {
+    for (int s = tid; s < R; s += NT) {
+      int run = s_first[s];
+      for (int b = 0; b < nblk; ++b) {
+        st_plan<COH>(&w.tile_fbase[(int64_t)b * K + n * R + s], run);
+        run += s_mat[b * R + s];
+      }
+    }
+  } else if (tid < P * R) {
+    const int q = tid / R, s = tid - q * R;
+    int run = s_first[s] + s_part[tid];
+    const int b1 = (q + 1) * nblk / P;
+    for (int b = q * nblk / P; b < b1; ++b) {
+      st_plan<COH>(&w.tile_fbase[(int64_t)b * K + n * R + s], run);
+      run += s_mat[b * R + s];
+    }
+  }
 }
 
 // LDS of one band scan.
@@ -472,17 +523,19 @@ __device__ __forceinline__ void scan_band(const Dims& d, const Work& w, int band
 // the [tiles x keys] count matrix into staging base rows, the forwarder
 // offsets and table, and the number of staging rows.  It reads nothing the
 // expert-key scan writes, so the two run in separate blocks side by side.
+// Load-aware forwarders take one block per node (`part` = the node); static
+// ones one block (`part` = 0).
 template <bool COH = false, int NT = kPlanBlock>
-__device__ __forceinline__ void scan_stage_keys(const Dims& d, const Work& w, const ScanLds& L) {
-  const int tid = threadIdx.x;
-  int staged;
+__device__ __forceinline__ void scan_stage_keys(const Dims& d, const Work& w, int part,
+                                                const ScanLds& L) {
   if (d.load_aware) {
-    staged = scan_load_aware<COH, NT>(d, w, L.mat, L.tot, L.wsum, L.part);
-  } else {
-    staged = scan_tiles<COH, NT>(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, d.R, d.nblk,
-                                 0, L.mat, L.tot, L.wsum, L.part);
-    for (int c = tid; c < d.R * d.N; c += NT) w.fwd[c] = (c % d.N) * d.G + (c / d.N) % d.G;
+    scan_load_aware<COH, NT>(d, w, part, L.mat, L.tot, L.wsum, L.part);
+    return;
   }
+  const int tid = threadIdx.x;
+  const int staged = scan_tiles<COH, NT>(w.tile_fcounts, w.tile_fbase, nullptr, w.stage_off, d.R,
+                                         d.nblk, 0, L.mat, L.tot, L.wsum, L.part);
+  for (int c = tid; c < d.R * d.N; c += NT) w.fwd[c] = (c % d.N) * d.G + (c / d.N) % d.G;
   if (tid == 0) w.ctrl[kCtrlStaged] = staged;
 }
 

@@ -59,7 +59,8 @@ __global__ __launch_bounds__(kPlanBlock) void route_count_kernel(Dims d,
 }
 
 // One block of kScanBlock threads per band, and with node deduplication (one
-// band) one more block for the staging keys.  Each column of a count matrix
+// band) one more block for the staging keys (one per node with load-aware
+// forwarders).  Each column of a count matrix
 // is summed, and its tile bases written, by several threads (one run of
 // consecutive tiles each).
 __global__ __launch_bounds__(kScanBlock) void route_scan_kernel(Dims d, Work w) {
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kScanBlock) void route_scan_kernel(Dims d, Work w) 
   __shared__ int s_part[kScanBlock];
   const ScanLds L{s_mat, s_tot, s_wsum, s_part};
   if ((int)blockIdx.x < d.nbands) scan_band<false, kScanBlock>(d, w, blockIdx.x, L);
-  else scan_stage_keys<false, kScanBlock>(d, w, L);
+  else scan_stage_keys<false, kScanBlock>(d, w, blockIdx.x - d.nbands, L);
 }
 
 // Finishes the plan one token per thread (slot_of, row_src; with dedup
@@ -210,7 +211,8 @@ hipError_t launch_route_count(const Dims& d, const int32_t* idx, const Work& w, 
 }
 
 hipError_t launch_route_scan(const Dims& d, const Work& w, hipStream_t s) {
-  return launch(MOE_KERNEL_ROUTE_SCAN, route_scan_kernel, dim3(d.nbands + (d.dedup ? 1 : 0)),
+  const int stage_blocks = d.dedup ? (d.load_aware ? d.N : 1) : 0;
+  return launch(MOE_KERNEL_ROUTE_SCAN, route_scan_kernel, dim3(d.nbands + stage_blocks),
                 dim3(kScanBlock), 0, s, d, w);
 }
 
