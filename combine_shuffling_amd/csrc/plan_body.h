@@ -175,8 +175,14 @@ __device__ __forceinline__ void prefix_table(const unsigned long long* s_mask, i
                                              const int* s_run, int W) {
   for (int i = threadIdx.x; i < kPlanWaves * W; i += kPlanBlock) {
     const int wv = i / W, c = i - wv * W;
+    // The ballots of all the earlier waves a wave can have are read together,
+    // then those before wv added (a loop up to wv waited for each read).
+    unsigned long long m[kPlanWaves - 1];
+#pragma unroll
+    for (int q = 0; q < kPlanWaves - 1; ++q) m[q] = s_mask[q * W + c];
     int n = s_run[c];
-    for (int q = 0; q < wv; ++q) n += __popcll(s_mask[q * W + c]);
+#pragma unroll
+    for (int q = 0; q < kPlanWaves - 1; ++q) n += q < wv ? __popcll(m[q]) : 0;
     s_pre[i] = n;
   }
 }
@@ -261,13 +267,20 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
     __syncthreads();
     prefix_table(s_mask, s_pre, s_run, E);
     __syncthreads();
+    // Both lookups of every slot are issued before any is used (a dropped
+    // slot reads entry 0 and drops the value): behind per-slot branches each
+    // slot's lookups waited for the slot before.
+    int pre[KMAX];
+    unsigned long long msk[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      if (live && j < k) {
-        const int r = e[j] >= 0 ? s_pre[wv * E + e[j]] + __popcll(s_mask[wv * E + e[j]] & below) : -1;
-        st_plan<COH>(&w.lr[at + j], r);
-      }
+      const int c = wv * E + (e[j] >= 0 ? e[j] : 0);
+      pre[j] = s_pre[c];
+      msk[j] = s_mask[c];
     }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (live && j < k) st_plan<COH>(&w.lr[at + j], e[j] >= 0 ? pre[j] + __popcll(msk[j] & below) : -1);
     for (int i = tid; i < E; i += kPlanBlock)
       s_run[i] = s_pre[(kPlanWaves - 1) * E + i] + __popcll(s_mask[(kPlanWaves - 1) * E + i]);
 
@@ -297,12 +310,16 @@ __device__ __forceinline__ void count_tile(const Dims& d, const int32_t* idx, co
       prefix_table(s_mask, s_pre, s_frun, K);
       __syncthreads();
 #pragma unroll
+      for (int j = 0; j < KMAX; ++j) {  // all lookups first, as for the experts
+        const int c = wv * K + (key[j] >= 0 ? key[j] : 0);
+        pre[j] = s_pre[c];
+        msk[j] = s_mask[c];
+      }
+#pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (live && j < k) {
-          const int r =
-              key[j] >= 0 ? s_pre[wv * K + key[j]] + __popcll(s_mask[wv * K + key[j]] & below) : -1;
           w.fkey[at + j] = key[j];
-          w.flr[at + j] = r;
+          w.flr[at + j] = key[j] >= 0 ? pre[j] + __popcll(msk[j] & below) : -1;
         }
       }
       for (int i = tid; i < K; i += kPlanBlock)
