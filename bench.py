@@ -146,14 +146,34 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
+_KERNEL_DEF = re.compile(r"__global__\s+(?:__launch_bounds__\([^)]*\)\s+)?void\s+(\w+)\s*\(")
+
+
+def unit_kernels():
+    """Kernel names of each translation unit: those its .hip file defines, and
+    those a shared header defines that the file names (launches)."""
+    def read(rel):
+        with open(os.path.join(ROOT, rel)) as f:
+            return f.read()
+
+    in_headers = set()
+    for rel in KERNEL_HEADERS:
+        in_headers |= set(_KERNEL_DEF.findall(read(rel)))
+    units = {}
+    for unit in KERNEL_UNITS:
+        src = read("combine_shuffling_amd/csrc/" + unit)
+        units[unit] = set(_KERNEL_DEF.findall(src)) | {
+            k for k in in_headers if re.search(r"\b%s\b" % k, src)}
+    return units
+
+
 def kernel_unit(kernel):
-    """The .hip file that defines `kernel` (short or full name)."""
+    """The .hip file whose translation unit holds `kernel` (short or full name)."""
     short = _short(kernel).split("<")[0]
-    if short in ("pipeline_kernel", "counters_clear_kernel"):
-        return "pipeline.hip"
-    if short.startswith(("route_", "traffic_")):
-        return "route_plan.hip"
-    return "move.hip"
+    hits = [u for u, names in unit_kernels().items() if short in names]
+    if len(hits) != 1:
+        raise ValueError(f"kernel {short!r} found in {len(hits)} translation units")
+    return hits[0]
 
 
 def kernel_source_hash(unit):

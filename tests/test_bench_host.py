@@ -10,6 +10,7 @@ import sys
 import pytest
 
 import bench
+from combine_shuffling_amd import _abi
 from workloads import gen
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -151,6 +152,20 @@ def test_kernel_units():
     assert bench.kernel_unit("counters_clear_kernel") == "pipeline.hip"
     assert bench.kernel_unit("route_count_kernel<8>") == "route_plan.hip"
     assert bench.kernel_unit("stage_ab_kernel<8>") == "move.hip"
+    # defined in a shared header, launched by move.hip
+    assert bench.kernel_unit("combine_kernel<8, 1, false>") == "move.hip"
+    assert bench.kernel_unit("gather_kernel<8, 1>") == "move.hip"
+    with pytest.raises(ValueError):
+        bench.kernel_unit("no_such_kernel")
     hashes = {u: bench.kernel_source_hash(u) for u in bench.KERNEL_UNITS}
     assert len(set(hashes.values())) == 3
+
+
+def test_every_library_kernel_has_one_unit():
+    """Each kernel the library can time (moe_kernel_name) maps to exactly one
+    translation unit, so its traffic summary is checked against the right sources."""
+    names = [_abi.kernel_name(i) for i in range(_abi.KERNEL_COUNT)]
+    assert "?" not in names and len(set(names)) == _abi.KERNEL_COUNT
+    for n in names:
+        bench.kernel_unit(n)
 
