@@ -89,6 +89,37 @@ def test_plan_sizes():
     L.moe_plan_destroy(None)
 
 
+def test_workloads_fit_the_static_workspace():
+    # Every workload's plan fits the static workspace of moe_route_plan_static
+    # (the DeepSeek-V3-like one also with load-aware forwarders), and the
+    # load-aware layout holds, besides the wider [tiles x (owner, node)] count
+    # and base matrices, the per-(tile, node) staging sums.
+    from workloads import gen
+
+    L = _abi.lib()
+    sizes = {}
+    for name in ("tiny", "olmoe", "qwen3", "dsv3", "nondiv"):
+        wl = gen.get(name)
+        flags = _abi.FLAG_NODE_DEDUP if wl.node_dedup else 0
+        st, h = make(wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
+                     wl.ranks_per_node, flags)
+        assert st == _abi.OK, name
+        sizes[name] = L.moe_plan_workspace_bytes(h)
+        L.moe_plan_destroy(h)
+        assert 0 < sizes[name] <= _abi.STATIC_WORKSPACE_BYTES, name
+    wl = gen.get("dsv3")
+    st, h = make(wl.num_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.num_ranks,
+                 wl.ranks_per_node, _abi.FLAG_NODE_DEDUP | _abi.FLAG_LOAD_AWARE_FORWARDERS)
+    assert st == _abi.OK
+    la = L.moe_plan_workspace_bytes(h)
+    L.moe_plan_destroy(h)
+    assert la <= _abi.STATIC_WORKSPACE_BYTES
+    R, N, tiles = wl.num_ranks, wl.num_ranks // wl.ranks_per_node, 64
+    # arrays are 256-byte aligned; the static plan keeps one slot of 256 bytes
+    # in place of the per-node sums
+    assert la - sizes["dsv3"] == 4 * (2 * tiles * (R * N - R) + tiles * N) - 256
+
+
 def test_calls_before_route_are_refused():
     L = _abi.lib()
     st, h = make()
